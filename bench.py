@@ -1,0 +1,280 @@
+"""Benchmark of the InfLLM v2 hot path on one MI355X.
+
+A step is one pass of the whole prefill path over the 128K-token MiniCPM4-8B-shaped layer
+(32 query heads / 2 KV heads, head_dim 128, bf16, block 64, kernels 32/16, top-96 with 1
+initial + 2 local blocks): compress_kernels -> block_scores -> topk_select ->
+sparse_attn_prefill, inputs resident in HBM.  `value` is prefill tokens/s of that pass.
+The line also carries the decode measurement (batch 8 x 128K cache, one token each, 16
+consecutive steps with incremental kernel updates), the roofline of the dominant kernel
+(from HIP events on the launch stream) and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload prefill128k|prefill32k|varlen]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn prefill tokens/s @128K + decode µs/token; % MFMA/HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def attended_keys_total(seq_lens, block, topk):
+    """Keys attended per query head summed over all query tokens (valid keys only)."""
+    tot = 0
+    for L in seq_lens:
+        i = np.arange(L, dtype=np.int64)
+        dense = (i // block) + 1 <= topk
+        tot += int(np.where(dense, i + 1, (topk - 1) * block + (i % block) + 1).sum())
+    return tot
+
+
+def run_prefill(args, torch, pkg, synth):
+    wl = synth.make(args.workload)
+    p = wl.params
+    lens = [int(x) for x in wl.q_len]
+    log(f"workload {args.workload}: seqs {lens}, inputs drawn")
+    seqs = pkg.Seqs.packed_prefill(lens)
+    dt = torch.bfloat16 if p.dtype == "bf16" else torch.float32
+    q = torch.from_numpy(wl.q).cuda().to(dt)
+    k = torch.from_numpy(wl.k).cuda().to(dt)
+    v = torch.from_numpy(wl.v).cuda().to(dt)
+    kc_rows = sum(pkg.num_kernels(L, p.kernel_size, p.kernel_stride) for L in lens)
+    bufs = pkg.pipeline.prefill_buffers(p, seqs, q, kc_rows)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        pkg.compress_kernels(p, seqs, k, bufs["kernels"], stream=stream)
+        if ev: ev[1].record(stream)
+        pkg.block_scores(p, seqs, q, bufs["kernels"], bufs["scores"], stream=stream)
+        if ev: ev[2].record(stream)
+        pkg.topk_select(p, seqs, bufs["scores"], bufs["idx"], stream=stream)
+        if ev: ev[3].record(stream)
+        pkg.sparse_attn_prefill(p, seqs, q, k, v, bufs["idx"], bufs["out"], bufs["lse"],
+                                stream=stream)
+        if ev: ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ["compress", "scores", "topk", "attention"]
+    stage = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+             for i, n in enumerate(names)}
+    T = sum(lens)
+    ms_step = wall * 1e3 / args.steps
+    keys = attended_keys_total(lens, p.block_size, p.topk)
+    flops = 4.0 * p.head_dim * p.num_q_heads * keys
+    tflops = flops / (stage["attention"] * 1e-3) / 1e12
+    d, Hq, Hkv = p.head_dim, p.num_q_heads, p.num_kv_heads
+    C = kc_rows
+    causal_blocks = sum(int(((np.arange(L) // p.block_size) + 1).sum()) for L in lens)
+    bytes_scores = T * Hq * d * 2 + C * Hkv * d * 2 + causal_blocks * Hkv * 4
+    bytes_topk = causal_blocks * Hkv * 4 + T * Hkv * p.topk * 4
+    bytes_compress = T * Hkv * d * 2 + C * Hkv * d * 2
+    result = dict(
+        workload=args.workload, tokens=T, seq_lens=lens, p=p, ms_step=ms_step, stage=stage,
+        flops=flops, tflops=tflops, keys=keys,
+        stage_gbs={"compress": bytes_compress / (stage["compress"] * 1e-3) / 1e9,
+                   "scores": bytes_scores / (stage["scores"] * 1e-3) / 1e9,
+                   "topk": bytes_topk / (stage["topk"] * 1e-3) / 1e9},
+        wl=wl, kernels_gpu=bufs["kernels"])
+    del q, k, v, bufs
+    return result
+
+
+def run_decode(args, torch, pkg, synth):
+    wl = synth.make("decode128k", steps=args.decode_steps)
+    p = wl.params
+    B, Lmax = wl.batch, wl.max_len
+    dt = torch.bfloat16
+    Ck = pkg.num_kernels(Lmax, p.kernel_size, p.kernel_stride)
+    k = torch.from_numpy(wl.k.reshape(B * Lmax, p.num_kv_heads, p.head_dim)).cuda().to(dt)
+    v = torch.from_numpy(wl.v.reshape(B * Lmax, p.num_kv_heads, p.head_dim)).cuda().to(dt)
+    qs = torch.from_numpy(wl.q_steps).cuda().to(dt)
+    kern = torch.zeros((B * Ck, p.num_kv_heads, p.head_dim), dtype=dt, device="cuda")
+    kv0 = wl.kv_len0.astype(np.int64)
+    s0 = pkg.Seqs(np.arange(B), np.zeros(B), np.zeros(B), np.arange(B) * Lmax, kv0,
+                  np.arange(B) * Ck)
+    nb = (Lmax + p.block_size - 1) // p.block_size
+    bufs = pkg.pipeline.decode_buffers(p, B, nb, args.decode_splits, "cuda")
+    stream = torch.cuda.current_stream()
+    seqs = [pkg.Seqs.decode(kv0 + st + 1, Lmax, Ck) for st in range(args.decode_steps)]
+    prevs = [(kv0 + st).astype(np.int32) for st in range(args.decode_steps)]
+
+    def all_steps(ev=None):
+        for st in range(args.decode_steps):
+            if ev: ev[st][0].record(stream)
+            pkg.decode_step(p, seqs[st], qs[st], k, v, kern, prevs[st], bufs, stream=stream)
+            if ev: ev[st][1].record(stream)
+
+    for _ in range(max(1, args.warmup)):
+        pkg.compress_kernels(p, s0, k, kern, stream=stream)
+        all_steps()
+    pkg.compress_kernels(p, s0, k, kern, stream=stream)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.decode_steps)]
+    t0 = time.perf_counter()
+    all_steps(ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[st][0].elapsed_time(ev[st][1]) * 1e3 for st in range(args.decode_steps)]
+    # bytes a step must move: the kernel cache read for scoring, the selected K/V blocks, q/out
+    kv_len = kv0 + args.decode_steps
+    C = np.array([pkg.num_kernels(int(L), p.kernel_size, p.kernel_stride) for L in kv_len])
+    bytes_kern = int(C.sum()) * p.num_kv_heads * p.head_dim * 2
+    keys = sum(min(int(L), (p.topk - 1) * p.block_size + (int(L) - 1) % p.block_size + 1)
+               for L in kv_len)
+    bytes_kv = keys * p.num_kv_heads * p.head_dim * 2 * 2
+    bytes_q = B * p.num_q_heads * p.head_dim * 2 * 2
+    total = bytes_kern + bytes_kv + bytes_q
+    us = float(np.mean(per))
+    out = dict(us_per_step=us, us_per_step_wall=wall * 1e6 / args.decode_steps,
+               tokens_per_s=B / (us * 1e-6), batch=B, cache_len=int(Lmax),
+               steps=args.decode_steps, bytes_per_step=total,
+               roofline={"bound": "hbm", "achieved": total / (us * 1e-6) / 1e9,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": total / (us * 1e-6) / 1e9 / PEAK_HBM_GBS})
+    del k, v, kern, bufs
+    return out
+
+
+def cpu_baseline(pre, budget_s: float):
+    """The float64 oracle on the host cores over a bounded sample of the same workload."""
+    import multiprocessing as mp
+    from oracle import infllm2_oracle as orc
+    wl = pre["wl"]
+    p = wl.params
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    L = int(wl.q_len[0])
+    sl_q, sl_k = wl.seq_slices(0)
+    t0 = time.perf_counter()
+    kern = orc.compress_kernels(wl.k[sl_k], p.kernel_size, p.kernel_stride, p.dtype)
+    t_comp = time.perf_counter() - t0
+    global _CPU_STATE
+    _CPU_STATE = (wl.q[sl_q], wl.k[sl_k], wl.v[sl_k], p, kern)
+    n_rows = 64 * workers
+    rows = np.linspace(0, L - 1, n_rows).astype(np.int64)
+    chunks = np.array_split(rows, workers * 4)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers, initializer=_limit_threads) as pool:
+        t1 = time.perf_counter()
+        done = 0
+        for res in pool.imap_unordered(_cpu_rows, chunks):
+            done += res
+            if time.perf_counter() - t1 > budget_s:
+                break
+        t_rows = time.perf_counter() - t1
+    per_row = t_rows / max(done, 1)
+    tok_s = L / (t_comp + per_row * L)
+    return {"value": tok_s, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"{args_workload_name(pre)}: full kernel compression ({t_comp:.1f} s) + "
+                      f"scores/top-k/attention for {done} of {L} query rows evenly spaced over "
+                      f"the sequence ({t_rows:.1f} s on {workers} processes), float64 numpy"}
+
+
+def args_workload_name(pre):
+    return pre["workload"]
+
+
+_CPU_STATE = None
+
+
+def _limit_threads():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def _cpu_rows(rows):
+    from oracle import infllm2_oracle as orc
+    q, k, v, p, kern = _CPU_STATE
+    orc.run_sequence(q, k, v, p, rows=rows, kernels=kern)
+    return len(rows)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="prefill128k", choices=["prefill128k", "prefill32k", "varlen"])
+    ap.add_argument("--decode-steps", type=int, default=16)
+    ap.add_argument("--decode-splits", type=int, default=0)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_sparse_long_semantic_amd as pkg
+    import synth
+    torch.cuda.set_device(0)
+    pre = run_prefill(args, torch, pkg, synth)
+    p = pre["p"]
+    st = pre["stage"]
+    log(f"prefill stages ms: {st}")
+    line = {
+        "metric": METRIC,
+        "value": pre["tokens"] / (pre["ms_step"] * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["ms_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": pre["workload"], "seq_lens": pre["seq_lens"],
+                   "num_q_heads": p.num_q_heads, "num_kv_heads": p.num_kv_heads,
+                   "head_dim": p.head_dim, "block_size": p.block_size,
+                   "kernel_size": p.kernel_size, "kernel_stride": p.kernel_stride,
+                   "topk": p.topk, "init_blocks": p.num_init_blocks,
+                   "local_blocks": p.num_local_blocks},
+        "stages_ms": st,
+        "stages_gbs": pre["stage_gbs"],
+        "attention_tokens_per_s": pre["tokens"] / (st["attention"] * 1e-3),
+        "roofline": {"kernel": "sparse_attn_prefill", "bound": "mfma",
+                     "achieved": pre["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": pre["tflops"] / PEAK_BF16_TFLOPS, "traffic": None,
+                     "flops_per_launch": pre["flops"], "keys_per_head": pre["keys"]},
+    }
+    if not args.no_decode:
+        line["decode"] = run_decode(args, torch, pkg, synth)
+        log(f"decode: {line['decode']['us_per_step']:.1f} us/step")
+    if not args.no_cpu_baseline:
+        torch.cuda.synchronize()
+        line["cpu_baseline"] = cpu_baseline(pre, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

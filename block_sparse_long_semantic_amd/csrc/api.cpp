@@ -1,0 +1,334 @@
+// C ABI of libinfllm2: host-side validation, work decomposition and kernel dispatch.
+// Every check runs before anything is enqueued; the library keeps no global state other
+// than the thread-local text of the last error.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "internal.h"
+
+using infllm2::Geom;
+using infllm2::SeqTable;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+infllm2_status fail(infllm2_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+infllm2_status ok() {
+  g_last_error.clear();
+  return INFLLM2_OK;
+}
+
+infllm2_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(INFLLM2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+infllm2_status check_params(const infllm2_params* p, Geom* g) {
+  if (p == nullptr) return fail(INFLLM2_ERR_NULL, "params is NULL");
+  if (p->num_q_heads <= 0 || p->num_kv_heads <= 0)
+    return fail(INFLLM2_ERR_SHAPE, "head counts must be positive (Hq=%d, Hkv=%d)",
+                p->num_q_heads, p->num_kv_heads);
+  if (p->num_q_heads % p->num_kv_heads != 0)
+    return fail(INFLLM2_ERR_SHAPE, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)",
+                p->num_q_heads, p->num_kv_heads);
+  if (p->dtype != INFLLM2_F32 && p->dtype != INFLLM2_BF16)
+    return fail(INFLLM2_ERR_UNSUPPORTED, "unknown dtype %d", p->dtype);
+  const int G = p->num_q_heads / p->num_kv_heads;
+  const int d = p->head_dim;
+  if (d < 8 || d > 256 || d % 8 != 0)
+    return fail(INFLLM2_ERR_UNSUPPORTED, "head_dim %d unsupported (multiple of 8, 8..256)", d);
+  if (G > 16 || G * d > 4096)
+    return fail(INFLLM2_ERR_UNSUPPORTED, "group size %d with head_dim %d unsupported (G<=16, G*d<=4096)",
+                G, d);
+  if (p->kernel_stride <= 0 || p->kernel_size <= 0 || p->block_size <= 0)
+    return fail(INFLLM2_ERR_SHAPE, "block_size, kernel_size and kernel_stride must be positive");
+  if (p->kernel_size % p->kernel_stride != 0)
+    return fail(INFLLM2_ERR_SHAPE, "kernel_size (%d) must be a multiple of kernel_stride (%d)",
+                p->kernel_size, p->kernel_stride);
+  if (p->block_size % p->kernel_stride != 0)
+    return fail(INFLLM2_ERR_SHAPE, "block_size (%d) must be a multiple of kernel_stride (%d)",
+                p->block_size, p->kernel_stride);
+  if (p->block_size > 256)
+    return fail(INFLLM2_ERR_UNSUPPORTED, "block_size %d above 256", p->block_size);
+  if (p->topk <= 0 || p->topk > 4096)
+    return fail(INFLLM2_ERR_SHAPE, "topk %d outside 1..4096", p->topk);
+  if (p->num_init_blocks < 0 || p->num_local_blocks < 1)
+    return fail(INFLLM2_ERR_SHAPE, "need num_init_blocks >= 0 and num_local_blocks >= 1 (%d, %d)",
+                p->num_init_blocks, p->num_local_blocks);
+  if (p->num_init_blocks + p->num_local_blocks > p->topk)
+    return fail(INFLLM2_ERR_SHAPE, "forced blocks (%d + %d) exceed topk %d", p->num_init_blocks,
+                p->num_local_blocks, p->topk);
+  if (!isfinite(p->softmax_scale))
+    return fail(INFLLM2_ERR_SHAPE, "softmax_scale is not finite");
+  g->Hq = p->num_q_heads;
+  g->Hkv = p->num_kv_heads;
+  g->G = G;
+  g->d = d;
+  g->B = p->block_size;
+  g->w = p->kernel_size;
+  g->s = p->kernel_stride;
+  g->topk = p->topk;
+  g->n_init = p->num_init_blocks;
+  g->n_local = p->num_local_blocks;
+  g->scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / sqrtf(static_cast<float>(d));
+  return INFLLM2_OK;
+}
+
+// Copies and checks the host sequence metadata.  need_kc: kc_start is required.
+infllm2_status build_table(const infllm2_seqs* s, const Geom& g, bool need_kc, SeqTable* t) {
+  if (s == nullptr) return fail(INFLLM2_ERR_NULL, "seqs is NULL");
+  if (s->num_seqs < 1 || s->num_seqs > infllm2::kMaxSeqs)
+    return fail(INFLLM2_ERR_SHAPE, "num_seqs %d outside 1..%d", s->num_seqs, infllm2::kMaxSeqs);
+  if (!s->q_start || !s->q_len || !s->q_pos0 || !s->kv_start || !s->kv_len)
+    return fail(INFLLM2_ERR_NULL, "a sequence metadata array is NULL");
+  if (need_kc && !s->kc_start) return fail(INFLLM2_ERR_NULL, "kc_start is NULL");
+  memset(t, 0, sizeof(*t));
+  t->n = s->num_seqs;
+  const int64_t lim = (int64_t{1} << 31) - 1;
+  for (int b = 0; b < s->num_seqs; ++b) {
+    const int64_t qs = s->q_start[b], ks = s->kv_start[b];
+    const int64_t kc = need_kc ? s->kc_start[b] : 0;
+    const int32_t ql = s->q_len[b], kl = s->kv_len[b], p0 = s->q_pos0[b];
+    if (qs < 0 || ks < 0 || kc < 0 || ql < 0 || kl < 0 || p0 < 0)
+      return fail(INFLLM2_ERR_SHAPE, "sequence %d: negative start, length or position", b);
+    if (static_cast<int64_t>(p0) + ql > kl)
+      return fail(INFLLM2_ERR_SHAPE, "sequence %d: q_pos0 (%d) + q_len (%d) exceeds kv_len (%d)",
+                  b, p0, ql, kl);
+    const int64_t nk = infllm2::num_kernels(kl, g.w, g.s);
+    if (qs + ql > lim || ks + kl > lim || kc + nk > lim)
+      return fail(INFLLM2_ERR_SHAPE, "sequence %d: row index beyond 2^31", b);
+    t->q_start[b] = static_cast<int32_t>(qs);
+    t->q_len[b] = ql;
+    t->q_pos0[b] = p0;
+    t->kv_start[b] = static_cast<int32_t>(ks);
+    t->kv_len[b] = kl;
+    t->kc_start[b] = static_cast<int32_t>(kc);
+  }
+  return INFLLM2_OK;
+}
+
+// work_prefix over query rows
+void rows_prefix(SeqTable* t) {
+  int acc = 0;
+  for (int b = 0; b < t->n; ++b) {
+    t->work_prefix[b] = acc;
+    acc += t->q_len[b];
+  }
+  t->work_prefix[t->n] = acc;
+}
+
+int max_reachable_blocks(const SeqTable& t, int B) {
+  int m = 0;
+  for (int b = 0; b < t.n; ++b)
+    if (t.q_len[b] > 0) m = std::max(m, (t.q_pos0[b] + t.q_len[b] - 1) / B + 1);
+  return m;
+}
+
+int auto_splits(const Geom& g, int rows) {
+  if (rows <= 0) return 1;
+  long long target = 512;
+  long long s = (target + static_cast<long long>(rows) * g.Hkv - 1) / (static_cast<long long>(rows) * g.Hkv);
+  if (s < 1) s = 1;
+  if (s > g.topk) s = g.topk;
+  return static_cast<int>(s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* infllm2_status_string(infllm2_status st) {
+  switch (st) {
+    case INFLLM2_OK: return "ok";
+    case INFLLM2_ERR_NULL: return "null pointer";
+    case INFLLM2_ERR_SHAPE: return "invalid shape or metadata";
+    case INFLLM2_ERR_UNSUPPORTED: return "unsupported configuration";
+    case INFLLM2_ERR_ALIGN: return "misaligned pointer";
+    case INFLLM2_ERR_WORKSPACE: return "workspace too small";
+    case INFLLM2_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* infllm2_last_error(void) { return g_last_error.c_str(); }
+
+int32_t infllm2_version(void) { return 100; }
+
+infllm2_status infllm2_compress_kernels(const infllm2_params* params, const infllm2_seqs* seqs,
+                                        const void* k, const int32_t* prev_kv_len,
+                                        void* kernels, void* stream) {
+  Geom g;
+  SeqTable t;
+  infllm2_status st = check_params(params, &g);
+  if (st != INFLLM2_OK) return st;
+  if ((st = build_table(seqs, g, true, &t)) != INFLLM2_OK) return st;
+  if (k == nullptr || kernels == nullptr) return fail(INFLLM2_ERR_NULL, "k or kernels is NULL");
+  if (!aligned16(k) || !aligned16(kernels))
+    return fail(INFLLM2_ERR_ALIGN, "k and kernels must be 16-byte aligned");
+  int acc = 0;
+  for (int b = 0; b < t.n; ++b) {
+    const int prev = prev_kv_len ? prev_kv_len[b] : 0;
+    if (prev < 0 || prev > t.kv_len[b])
+      return fail(INFLLM2_ERR_SHAPE, "sequence %d: prev_kv_len %d outside 0..kv_len (%d)", b, prev,
+                  t.kv_len[b]);
+    const int lo = infllm2::num_kernels(prev, g.w, g.s);
+    const int hi = infllm2::num_kernels(t.kv_len[b], g.w, g.s);
+    t.aux[b] = lo;
+    t.work_prefix[b] = acc;
+    acc += (hi - lo + 15) / 16;
+  }
+  t.work_prefix[t.n] = acc;
+  return hip_status(infllm2::launch_compress(g, params->dtype, t, k, kernels,
+                                             static_cast<hipStream_t>(stream)),
+                    "compress_kernels launch");
+}
+
+infllm2_status infllm2_block_scores(const infllm2_params* params, const infllm2_seqs* seqs,
+                                    const void* q, const void* kernels, float* scores,
+                                    int32_t nb_stride, void* stream) {
+  Geom g;
+  SeqTable t;
+  infllm2_status st = check_params(params, &g);
+  if (st != INFLLM2_OK) return st;
+  if ((st = build_table(seqs, g, true, &t)) != INFLLM2_OK) return st;
+  if (q == nullptr || kernels == nullptr || scores == nullptr)
+    return fail(INFLLM2_ERR_NULL, "q, kernels or scores is NULL");
+  if (!aligned16(q) || !aligned16(kernels) || !aligned16(scores))
+    return fail(INFLLM2_ERR_ALIGN, "q, kernels and scores must be 16-byte aligned");
+  const int need = max_reachable_blocks(t, g.B);
+  if (nb_stride < need)
+    return fail(INFLLM2_ERR_SHAPE, "nb_stride %d below the %d reachable blocks", nb_stride, need);
+  const bool mfma = params->dtype == INFLLM2_BF16 && g.B == 64 && g.w == 32 && g.s == 16 &&
+                    (g.d == 64 || g.d == 128);
+  int range_tiles = 0;
+  if (!mfma) {
+    rows_prefix(&t);
+  } else {
+    long long tiles64 = 0;
+    for (int b = 0; b < t.n; ++b) tiles64 += (t.q_len[b] + 63) / 64;
+    const bool decode_like = tiles64 * g.Hkv < 512;
+    range_tiles = decode_like ? 16 : (1 << 28);
+    const int rows_per_tile = decode_like ? 16 : 64;
+    int acc = 0;
+    for (int b = 0; b < t.n; ++b) {
+      t.work_prefix[b] = acc;
+      if (t.q_len[b] == 0) continue;
+      const int pos_last = t.q_pos0[b] + t.q_len[b] - 1;
+      const int nbt = (pos_last / 64 + 1 + 3) / 4;
+      const int chunks = (nbt + range_tiles - 1) / range_tiles;
+      acc += ((t.q_len[b] + rows_per_tile - 1) / rows_per_tile) * chunks;
+    }
+    t.work_prefix[t.n] = acc;
+  }
+  return hip_status(infllm2::launch_scores(g, params->dtype, t, q, kernels, scores, nb_stride,
+                                           range_tiles, static_cast<hipStream_t>(stream)),
+                    "block_scores launch");
+}
+
+infllm2_status infllm2_topk_select(const infllm2_params* params, const infllm2_seqs* seqs,
+                                   const float* scores, int32_t nb_stride, int32_t* block_idx,
+                                   void* stream) {
+  Geom g;
+  SeqTable t;
+  infllm2_status st = check_params(params, &g);
+  if (st != INFLLM2_OK) return st;
+  if ((st = build_table(seqs, g, false, &t)) != INFLLM2_OK) return st;
+  if (scores == nullptr || block_idx == nullptr)
+    return fail(INFLLM2_ERR_NULL, "scores or block_idx is NULL");
+  if (!aligned16(scores) || !aligned16(block_idx))
+    return fail(INFLLM2_ERR_ALIGN, "scores and block_idx must be 16-byte aligned");
+  const int need = max_reachable_blocks(t, g.B);
+  if (nb_stride < need)
+    return fail(INFLLM2_ERR_SHAPE, "nb_stride %d below the %d reachable blocks", nb_stride, need);
+  if (need > 4096)
+    return fail(INFLLM2_ERR_UNSUPPORTED, "%d reachable blocks exceed 4096", need);
+  rows_prefix(&t);
+  return hip_status(infllm2::launch_topk(g, t, scores, nb_stride, need, block_idx,
+                                         static_cast<hipStream_t>(stream)),
+                    "topk_select launch");
+}
+
+static infllm2_status attn_common(const infllm2_params* params, const infllm2_seqs* seqs,
+                                  const void* q, const void* k, const void* v,
+                                  const int32_t* block_idx, void* out, float* lse, Geom* g,
+                                  SeqTable* t) {
+  infllm2_status st = check_params(params, g);
+  if (st != INFLLM2_OK) return st;
+  if ((st = build_table(seqs, *g, false, t)) != INFLLM2_OK) return st;
+  if (!q || !k || !v || !block_idx || !out)
+    return fail(INFLLM2_ERR_NULL, "q, k, v, block_idx or out is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(block_idx) ||
+      !aligned16(out) || (lse && !aligned16(lse)))
+    return fail(INFLLM2_ERR_ALIGN, "attention buffers must be 16-byte aligned");
+  rows_prefix(t);
+  return INFLLM2_OK;
+}
+
+infllm2_status infllm2_sparse_attn_prefill(const infllm2_params* params,
+                                           const infllm2_seqs* seqs, const void* q,
+                                           const void* k, const void* v,
+                                           const int32_t* block_idx, void* out, float* lse,
+                                           void* stream) {
+  Geom g;
+  SeqTable t;
+  infllm2_status st = attn_common(params, seqs, q, k, v, block_idx, out, lse, &g, &t);
+  if (st != INFLLM2_OK) return st;
+  return hip_status(infllm2::launch_attn(g, params->dtype, t, q, k, v, block_idx, 1, out, lse,
+                                         nullptr, static_cast<hipStream_t>(stream)),
+                    "sparse_attn_prefill launch");
+}
+
+size_t infllm2_decode_workspace_size(const infllm2_params* params, int32_t total_q_rows,
+                                     int32_t num_splits) {
+  Geom g;
+  if (check_params(params, &g) != INFLLM2_OK || total_q_rows < 0 || num_splits < 0) return 0;
+  const int splits = num_splits > 0 ? num_splits : auto_splits(g, total_q_rows);
+  return static_cast<size_t>(total_q_rows) * g.Hq * splits * (2 + g.d) * sizeof(float);
+}
+
+infllm2_status infllm2_sparse_attn_decode(const infllm2_params* params, const infllm2_seqs* seqs,
+                                          const void* q, const void* k, const void* v,
+                                          const int32_t* block_idx, int32_t num_splits,
+                                          void* workspace, size_t workspace_bytes, void* out,
+                                          float* lse, void* stream) {
+  Geom g;
+  SeqTable t;
+  infllm2_status st = attn_common(params, seqs, q, k, v, block_idx, out, lse, &g, &t);
+  if (st != INFLLM2_OK) return st;
+  if (num_splits < 0 || num_splits > g.topk)
+    return fail(INFLLM2_ERR_SHAPE, "num_splits %d outside 0..topk", num_splits);
+  const int rows = t.work_prefix[t.n];
+  const int splits = num_splits > 0 ? num_splits : auto_splits(g, rows);
+  const size_t need = static_cast<size_t>(rows) * g.Hq * splits * (2 + g.d) * sizeof(float);
+  if (splits > 1) {
+    if (workspace == nullptr) return fail(INFLLM2_ERR_NULL, "workspace is NULL");
+    if (!aligned16(workspace)) return fail(INFLLM2_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(INFLLM2_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = infllm2::launch_attn(g, params->dtype, t, q, k, v, block_idx, splits, out, lse,
+                                      static_cast<float*>(workspace), s);
+  if (e != hipSuccess || splits == 1) return hip_status(e, "sparse_attn_decode launch");
+  return hip_status(infllm2::launch_attn_combine(g, params->dtype, t, splits,
+                                                 static_cast<const float*>(workspace), out, lse, s),
+                    "sparse_attn_decode combine launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// Internal declarations shared by the HIP translation units of libinfllm2 (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "infllm2.h"
+
+namespace infllm2 {
+
+constexpr int kMaxSeqs = INFLLM2_MAX_SEQS;
+
+// Sequence metadata passed by value as a kernel argument (no device-side metadata buffers).
+// work_prefix[b] is the first work item of sequence b for the launch at hand; work_prefix[n]
+// is the total.  Its meaning (tiles, rows, ...) is defined by each launch.
+struct SeqTable {
+  int32_t n;
+  int32_t q_start[kMaxSeqs];
+  int32_t q_len[kMaxSeqs];
+  int32_t q_pos0[kMaxSeqs];
+  int32_t kv_start[kMaxSeqs];
+  int32_t kv_len[kMaxSeqs];
+  int32_t kc_start[kMaxSeqs];
+  int32_t aux[kMaxSeqs];          // per-launch extra (e.g. first kernel of an incremental pass)
+  int32_t work_prefix[kMaxSeqs + 1];
+};
+
+struct Geom {
+  int32_t Hq, Hkv, G, d;
+  int32_t B, w, s;
+  int32_t topk, n_init, n_local;
+  float scale;
+};
+
+// Sequence owning work item `item` (linear scan; at most kMaxSeqs entries).
+__device__ __forceinline__ int find_seq(const SeqTable& t, int item) {
+  int b = 0;
+  while (b + 1 < t.n && t.work_prefix[b + 1] <= item) ++b;
+  return b;
+}
+
+__host__ __device__ __forceinline__ int num_kernels(int len, int w, int s) {
+  return len < w ? 0 : (len - w) / s + 1;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// float -> bf16, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Launch entry points (one per translation unit).  All return hipSuccess or the launch error.
+hipError_t launch_compress(const Geom& g, int dtype, const SeqTable& t, const void* k,
+                           void* kernels, hipStream_t stream);
+hipError_t launch_scores(const Geom& g, int dtype, const SeqTable& t, const void* q,
+                         const void* kernels, float* scores, int nb_stride, int range_tiles,
+                         hipStream_t stream);
+hipError_t launch_topk(const Geom& g, const SeqTable& t, const float* scores, int nb_stride,
+                       int max_blocks, int32_t* idx, hipStream_t stream);
+// Attention over blocks idx[row, g, k0 .. k1) for split `sp` of `splits`.  With splits == 1
+// the kernels write O and lse; otherwise they write partials to `part` and
+// launch_attn_combine merges them.
+hipError_t launch_attn(const Geom& g, int dtype, const SeqTable& t, const void* q,
+                       const void* k, const void* v, const int32_t* idx, int splits,
+                       void* out, float* lse, float* part, hipStream_t stream);
+hipError_t launch_attn_combine(const Geom& g, int dtype, const SeqTable& t, int splits,
+                               const float* part, void* out, float* lse, hipStream_t stream);
+
+}  // namespace infllm2

@@ -1,0 +1,238 @@
+// Query-block relevance scores (MiniCPM4 paper summary, section 2.1.2: the relevance between
+// query tokens and KV blocks, computed through semantic kernels, shared by one query-head
+// group).  For a query at position i and KV head g:
+//   u[c] = scale * (sum_{h in g} q[h]) . kernel[c]      for kernels whose last token <= i
+//   S[b] = max over kernels overlapping block b of u[c]  (-inf if none is visible)
+// Two implementations:
+//   * scores_mfma  bf16, block 64 / window 32 / stride 16, d in {64, 128}.  The group-summed
+//                  query (float32) is split into bf16 hi + lo parts and both are contracted
+//                  with the bf16 kernels on v_mfma_f32_16x16x32_bf16 (A = 16 kernels x 32
+//                  dims, B = 32 dims x 16 query rows).  The 4x4 output fragment a lane holds
+//                  is exactly one block's four contained kernels for one query row; the
+//                  fifth (halo) kernel 4b-1 comes from the neighbouring lane group.
+//   * scores_simple any dtype and geometry, plain float32 dot products.
+#include "internal.h"
+
+namespace infllm2 {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+
+template <typename T>
+__device__ __forceinline__ float load_elem(const T* p, size_t i);
+template <>
+__device__ __forceinline__ float load_elem<float>(const float* p, size_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, size_t i) {
+  return bf16_to_f32(p[i]);
+}
+
+// ------------------------------------------------------------------------------ simple path
+// One workgroup per (query row, KV head); work_prefix counts query rows.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+scores_simple(Geom g, SeqTable t, const T* __restrict__ q, const T* __restrict__ kern,
+              float* __restrict__ scores, int nb_stride) {
+  __shared__ float qs[256];
+  const int vrow = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = find_seq(t, vrow);
+  const int j = vrow - t.work_prefix[b];
+  const int row = t.q_start[b] + j;
+  const int pos = t.q_pos0[b] + j;
+  for (int e = threadIdx.x; e < g.d; e += kThreads) {
+    float acc = 0.f;
+    for (int h = 0; h < g.G; ++h)
+      acc += load_elem(q, (static_cast<size_t>(row) * g.Hq + kvh * g.G + h) * g.d + e);
+    qs[e] = acc;
+  }
+  __syncthreads();
+  const int C = num_kernels(t.kv_len[b], g.w, g.s);
+  const int nb = pos / g.B + 1;
+  float* out = scores + (static_cast<size_t>(row) * g.Hkv + kvh) * nb_stride;
+  for (int blk = threadIdx.x; blk < nb; blk += kThreads) {
+    const int lo_num = g.B * blk - g.w + 1;
+    const int lo = lo_num <= 0 ? 0 : (lo_num + g.s - 1) / g.s;
+    const int hi = min(C, (g.B * (blk + 1) + g.s - 1) / g.s);
+    float best = -INFINITY;
+    for (int c = lo; c < hi; ++c) {
+      if (g.s * c + g.w - 1 > pos) break;
+      const size_t base = (static_cast<size_t>(t.kc_start[b]) + c) * g.Hkv * g.d +
+                          static_cast<size_t>(kvh) * g.d;
+      float dot = 0.f;
+      for (int e = 0; e < g.d; ++e) dot += qs[e] * load_elem(kern, base + e);
+      best = fmaxf(best, dot);
+    }
+    out[blk] = best * g.scale;
+  }
+}
+
+// ------------------------------------------------------------------------------ MFMA path
+// Work item = (sequence, tile of 16*WR query rows, chunk of `range_tiles` kernel tiles); the
+// 4 waves are WR row groups x (4/WR) kernel sub-ranges.  A kernel tile is 16 kernels = 4
+// blocks.  Prefill uses WR = 4 and one chunk per row tile; decode-like launches (few rows)
+// use WR = 1 and split the kernel range over chunks and waves.
+template <int D, int WR>
+__global__ void __launch_bounds__(kThreads)
+scores_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
+            const uint16_t* __restrict__ kern, float* __restrict__ scores, int nb_stride,
+            int range_tiles) {
+  constexpr int KS = D / 32;
+  constexpr int WK = 4 / WR;
+  const int total = t.work_prefix[t.n];
+  const int item = total - 1 - static_cast<int>(blockIdx.x);   // heaviest (latest) rows first
+  const int kvh = blockIdx.y;
+  const int b = find_seq(t, item);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c16 = lane & 15;
+  const int q4 = lane >> 4;
+  const int q_len = t.q_len[b];
+  const int pos_last = t.q_pos0[b] + q_len - 1;
+  const int nbt_seq = (pos_last / 64 + 1 + 3) / 4;            // kernel tiles of the sequence
+  const int chunks = (nbt_seq + range_tiles - 1) / range_tiles;
+  const int local = item - t.work_prefix[b];
+  const int rt = local / chunks;
+  const int ch = local % chunks;
+  const int rw = wave % WR;
+  const int kw = wave / WR;
+
+  const int r = rt * 16 * WR + rw * 16 + c16;                  // this lane's query row (B column)
+  const bool row_ok = r < q_len;
+  const int pos = t.q_pos0[b] + (row_ok ? r : q_len - 1);
+  const int row = t.q_start[b] + r;
+
+  // rows of this wave: kernel tiles needed by its last valid row
+  const int r_last = min(rt * 16 * WR + rw * 16 + 15, q_len - 1);
+  if (rt * 16 * WR + rw * 16 > q_len - 1) return;             // wave has no rows
+  const int nbt_wave = ((t.q_pos0[b] + r_last) / 64 + 1 + 3) / 4;
+  const int t_chunk0 = ch * range_tiles;
+  const int t_chunk1 = min(nbt_wave, t_chunk0 + range_tiles);
+  if (t_chunk0 >= t_chunk1) return;
+  const int per = (t_chunk1 - t_chunk0 + WK - 1) / WK;
+  const int t_begin = t_chunk0 + kw * per;
+  const int t_end = min(t_chunk1, t_begin + per);
+  if (t_begin >= t_end) return;
+
+  // B operand: group-summed query, hi and lo bf16 parts, dims 32*ks + 8*q4 + 0..7
+  bf16x8 bhi[KS], blo[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    if (row_ok) {
+      for (int h = 0; h < g.G; ++h) {
+        const uint4 v = *reinterpret_cast<const uint4*>(
+            q + (static_cast<size_t>(row) * g.Hq + kvh * g.G + h) * D + 32 * ks + 8 * q4);
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += __uint_as_float(w4[e] << 16);
+          acc[2 * e + 1] += __uint_as_float(w4[e] & 0xFFFF0000u);
+        }
+      }
+    }
+    uint32_t hi4[4], lo4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint16_t h0 = f32_to_bf16(acc[2 * e]), h1 = f32_to_bf16(acc[2 * e + 1]);
+      const uint16_t l0 = f32_to_bf16(acc[2 * e] - bf16_to_f32(h0));
+      const uint16_t l1 = f32_to_bf16(acc[2 * e + 1] - bf16_to_f32(h1));
+      hi4[e] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+      lo4[e] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+    }
+    bhi[ks] = __builtin_bit_cast(bf16x8, make_uint4(hi4[0], hi4[1], hi4[2], hi4[3]));
+    blo[ks] = __builtin_bit_cast(bf16x8, make_uint4(lo4[0], lo4[1], lo4[2], lo4[3]));
+  }
+
+  const int C = num_kernels(t.kv_len[b], g.w, g.s);
+  const int own = pos / 64;
+  const size_t kbase = static_cast<size_t>(t.kc_start[b]) * g.Hkv * D + static_cast<size_t>(kvh) * D;
+  float* srow = scores + (static_cast<size_t>(row) * g.Hkv + kvh) * nb_stride;
+  const unsigned src_lane = static_cast<unsigned>((lane + 48) & 63);   // lane - 16 (mod 64)
+  float carry = -INFINITY;
+  // start one tile early (without writing) to obtain the halo kernel of the first block
+  for (int tt = (t_begin > 0 ? t_begin - 1 : 0); tt < t_end; ++tt) {
+    const int ck = 16 * tt + c16;                                 // A row: kernel
+    const int ck_c = min(ck, C - 1 > 0 ? C - 1 : 0);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 a;
+      if (C > 0) {
+        a = *reinterpret_cast<const bf16x8*>(kern + kbase + static_cast<size_t>(ck_c) * g.Hkv * D +
+                                              32 * ks + 8 * q4);
+      } else {
+        a = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bhi[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, blo[ks], acc, 0, 0, 0);
+    }
+    // lane holds u[kernel 16*tt + 4*q4 + i][row c16]
+    float u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 16 * tt + 4 * q4 + i;
+      u[i] = (c < C && 16 * c + 31 <= pos) ? acc[i] : -INFINITY;
+    }
+    const float h = __shfl(u[3], src_lane);
+    const float halo = (q4 == 0) ? carry : h;
+    carry = h;
+    const float best = fmaxf(fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3])), halo);
+    const int blk = 4 * tt + q4;
+    if (tt >= t_begin && row_ok && blk <= own) srow[blk] = best * g.scale;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_scores(const Geom& g, int dtype, const SeqTable& t, const void* q,
+                         const void* kernels, float* scores, int nb_stride, int range_tiles,
+                         hipStream_t stream) {
+  const bool mfma = dtype == INFLLM2_BF16 && g.B == 64 && g.w == 32 && g.s == 16 &&
+                    (g.d == 64 || g.d == 128);
+  if (!mfma) {
+    // work_prefix must count query rows
+    const int rows = t.work_prefix[t.n];
+    if (rows == 0) return hipSuccess;
+    const dim3 grid(rows, g.Hkv);
+    if (dtype == INFLLM2_BF16)
+      hipLaunchKernelGGL(scores_simple<uint16_t>, grid, dim3(kThreads), 0, stream, g, t,
+                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kernels),
+                         scores, nb_stride);
+    else
+      hipLaunchKernelGGL(scores_simple<float>, grid, dim3(kThreads), 0, stream, g, t,
+                         static_cast<const float*>(q), static_cast<const float*>(kernels), scores,
+                         nb_stride);
+    return hipGetLastError();
+  }
+  // work_prefix counts (row tile x kernel chunk) items, built by the caller for this mode.
+  const int items = t.work_prefix[t.n];
+  if (items == 0) return hipSuccess;
+  const dim3 grid(items, g.Hkv);
+  const bool decode_like = range_tiles > 0 && range_tiles < (1 << 28);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(kernels);
+  if (g.d == 128) {
+    if (decode_like)
+      hipLaunchKernelGGL((scores_mfma<128, 1>), grid, dim3(kThreads), 0, stream, g, t, qq, kk,
+                         scores, nb_stride, range_tiles);
+    else
+      hipLaunchKernelGGL((scores_mfma<128, 4>), grid, dim3(kThreads), 0, stream, g, t, qq, kk,
+                         scores, nb_stride, 1 << 28);
+  } else {
+    if (decode_like)
+      hipLaunchKernelGGL((scores_mfma<64, 1>), grid, dim3(kThreads), 0, stream, g, t, qq, kk,
+                         scores, nb_stride, range_tiles);
+    else
+      hipLaunchKernelGGL((scores_mfma<64, 4>), grid, dim3(kThreads), 0, stream, g, t, qq, kk,
+                         scores, nb_stride, 1 << 28);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace infllm2

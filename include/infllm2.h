@@ -1,0 +1,171 @@
+/*
+ * infllm2.h -- C ABI of an MI355X (gfx950) library for InfLLM v2 block-sparse attention.
+ *
+ * The method (MiniCPM4 paper summary, section 2.1 "InfLLM v2"; arXiv abstract of MiniCPM4):
+ * the key/value cache is divided into fixed-size blocks, each block is represented through
+ * fine-grained "semantic kernels" pooled from its keys, every query token scores the blocks
+ * through those kernels, the query heads of one GQA group share the highest-scoring blocks,
+ * and attention runs only over the chosen blocks, both when prefilling and when decoding.
+ *
+ * The five compute calls below are the steps of that path, in order:
+ *   infllm2_compress_kernels    keys                      -> semantic kernels
+ *   infllm2_block_scores        queries, kernels          -> per-block relevance scores
+ *   infllm2_topk_select         scores                    -> selected block indices
+ *   infllm2_sparse_attn_prefill queries, keys, values, idx-> attention output (+ LSE)
+ *   infllm2_sparse_attn_decode  the same for a few query rows per sequence, split over the
+ *                               selected blocks and merged by log-sum-exp
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Layouts (all row-major, contiguous, device memory, 16-byte aligned base pointers):
+ *   Q, O      [q_rows,  Hq,  d]       dtype of params->dtype
+ *   K, V      [kv_rows, Hkv, d]       dtype of params->dtype
+ *   kernels   [kc_rows, Hkv, d]       dtype of params->dtype
+ *   scores    [q_rows,  Hkv, nb_stride]  float32
+ *   block_idx [q_rows,  Hkv, topk]    int32, ascending, padded with -1
+ *   lse       [q_rows,  Hq]           float32, natural log of the softmax denominator
+ * Query head h reads KV head h / (Hq / Hkv) (contiguous GQA groups).
+ *
+ * Sequences (infllm2_seqs, HOST arrays, read during the call only): sequence b owns query rows
+ * q_start[b] .. q_start[b]+q_len[b]-1, whose positions in the sequence are q_pos0[b]+j; its
+ * keys/values are rows kv_start[b] .. kv_start[b]+kv_len[b]-1 (position t at row kv_start+t);
+ * its semantic kernels are rows kc_start[b] + c, c < floor((kv_len-w)/s)+1.  A packed prefill
+ * uses q_start = kv_start = cu_seqlens and q_pos0 = 0; a decode batch over a padded cache uses
+ * kv_start = b*max_len, q_len = 1, q_pos0 = kv_len-1 (the new token's K/V already stored).
+ * Every query must see its own key: q_pos0 + q_len <= kv_len.
+ *
+ * Ownership and errors: the caller allocates every buffer; the library never allocates,
+ * frees or synchronises.  Calls only enqueue kernels on `stream` (a hipStream_t; NULL = the
+ * default stream) and return.  Arguments are validated on the host before anything is
+ * enqueued; a failed check returns a non-zero status, enqueues nothing and records a message
+ * for infllm2_last_error() (thread-local).  A failed launch returns INFLLM2_ERR_HIP.  Device
+ * contents (values, indices) are trusted; non-finite inputs give undefined results.
+ */
+#ifndef INFLLM2_H
+#define INFLLM2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  INFLLM2_OK = 0,
+  INFLLM2_ERR_NULL = 1,        /* a required pointer is NULL */
+  INFLLM2_ERR_SHAPE = 2,       /* inconsistent sizes or sequence metadata */
+  INFLLM2_ERR_UNSUPPORTED = 3, /* valid but not implemented (dtype, head_dim, ...) */
+  INFLLM2_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
+  INFLLM2_ERR_WORKSPACE = 5,   /* workspace smaller than infllm2_decode_workspace_size() */
+  INFLLM2_ERR_HIP = 6          /* the HIP runtime reported an error */
+} infllm2_status;
+
+typedef enum { INFLLM2_F32 = 0, INFLLM2_BF16 = 1 } infllm2_dtype;
+
+/* Method constants of one attention layer.  The pages fix none of them; the measured
+ * configurations use block 64, kernel window 32, kernel stride 16. */
+typedef struct {
+  int32_t num_q_heads;      /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;     /* Hkv */
+  int32_t head_dim;         /* d: 64 or 128 (bf16); multiple of 8 up to 256 (f32) */
+  int32_t block_size;       /* B: tokens per KV block, multiple of kernel_stride, <= 256 */
+  int32_t kernel_size;      /* w: tokens pooled into one semantic kernel, multiple of s */
+  int32_t kernel_stride;    /* s: distance between consecutive kernels */
+  int32_t topk;             /* blocks per (query token, KV head), forced blocks included */
+  int32_t num_init_blocks;  /* leading blocks always selected (>= 0) */
+  int32_t num_local_blocks; /* blocks ending at the query's own block always selected (>= 1) */
+  float softmax_scale;      /* <= 0 selects 1/sqrt(head_dim) */
+  int32_t dtype;            /* infllm2_dtype of Q, K, V, O and the kernels */
+} infllm2_params;
+
+#define INFLLM2_MAX_SEQS 64
+
+/* Per-sequence metadata, host memory, num_seqs in 1..INFLLM2_MAX_SEQS.  Row indices must be
+ * below 2^31. */
+typedef struct {
+  int32_t num_seqs;
+  const int64_t* q_start;
+  const int32_t* q_len;
+  const int32_t* q_pos0;
+  const int64_t* kv_start;
+  const int32_t* kv_len;
+  const int64_t* kc_start;
+} infllm2_seqs;
+
+/* Semantic kernels (paper summary section 2.1.2: fine-grained semantic kernels represent each
+ * KV block).  Kernel c of a sequence is the mean of the keys of its tokens s*c .. s*c+w-1,
+ * accumulated exactly in float64 and rounded once, to nearest even, to the key dtype.
+ * prev_kv_len (host array, may be NULL = all zeros) makes the call incremental: only kernels
+ * with prev_kv_len[b] < s*c + w <= kv_len[b] are written; other rows of `kernels` are left
+ * untouched.  Reads k, writes kernels. */
+infllm2_status infllm2_compress_kernels(const infllm2_params* params, const infllm2_seqs* seqs,
+                                        const void* k, const int32_t* prev_kv_len,
+                                        void* kernels, void* stream);
+
+/* Query-block relevance (section 2.1.2: the relevance of each query token to each KV block,
+ * shared by the query heads of one group).  For query row at position i and KV head g:
+ *   u[c]  = scale * sum over heads h of group g of  q[h] . kernel[c, g]   for kernels c whose
+ *           last token s*c+w-1 <= i,
+ *   S[b]  = max of u[c] over the kernels overlapping block b ([s*c, s*c+w) meets
+ *           [B*b, B*b+B)), or -inf if none is visible,
+ * written for blocks b = 0 .. floor(i/B) at scores[row, g, b]; entries after floor(i/B) are
+ * not written.  nb_stride >= floor((q_pos0+q_len-1)/B)+1 for every sequence.  bf16 scores use
+ * the group-summed query in float32 split into two bf16 parts on the matrix cores (relative
+ * error about 2^-16 of sum |q . kernel|); f32 scores use float32 arithmetic. */
+infllm2_status infllm2_block_scores(const infllm2_params* params, const infllm2_seqs* seqs,
+                                    const void* q, const void* kernels, float* scores,
+                                    int32_t nb_stride, void* stream);
+
+/* Group-shared top-k (section 2.1.1: each query token picks the highest-scoring blocks;
+ * section 2.1.2: one set per query-head group).  For query row at position i and KV head g,
+ * with E = {0 .. floor(i/B)} the reachable blocks: all of E if |E| <= topk; otherwise the
+ * forced blocks F = {0 .. n_init-1} U {floor(i/B)-n_local+1 .. floor(i/B)} plus the
+ * topk-|F| best other blocks by (score descending, block index ascending; -0 equals +0).
+ * Written ascending to block_idx[row, g, 0..topk-1], padded with -1.  Scores are read for
+ * b <= floor(i/B) only.  At most 4096 reachable blocks per row. */
+infllm2_status infllm2_topk_select(const infllm2_params* params, const infllm2_seqs* seqs,
+                                   const float* scores, int32_t nb_stride, int32_t* block_idx,
+                                   void* stream);
+
+/* Block-sparse attention (section 2.1.3: each token attends only to its most relevant KV
+ * blocks).  For query row at position i, head h, KV head g = h / (Hq/Hkv):
+ *   O[row, h] = sum_j softmax_j(scale * q[h] . k[j, g]) v[j, g]
+ * over the tokens j <= i of the blocks listed in block_idx[row, g] (-1 entries end the list),
+ * and lse[row, h] = log sum_j exp(scale * q . k_j).  lse may be NULL.  Indices must be
+ * ascending, distinct, and within the sequence's blocks. */
+infllm2_status infllm2_sparse_attn_prefill(const infllm2_params* params,
+                                           const infllm2_seqs* seqs, const void* q,
+                                           const void* k, const void* v,
+                                           const int32_t* block_idx, void* out, float* lse,
+                                           void* stream);
+
+/* Bytes of device workspace infllm2_sparse_attn_decode needs for `total_q_rows` query rows
+ * (sum of q_len) split `num_splits` ways (0 = the automatic choice). */
+size_t infllm2_decode_workspace_size(const infllm2_params* params, int32_t total_q_rows,
+                                     int32_t num_splits);
+
+/* The same attention for decoding (arXiv abstract: the sparse attention accelerates both
+ * prefilling and decoding): each row's selected blocks are split into num_splits contiguous
+ * parts (0 = automatic) computed in parallel into `workspace`, then merged by log-sum-exp.
+ * The result does not depend on num_splits beyond float32 rounding. */
+infllm2_status infllm2_sparse_attn_decode(const infllm2_params* params, const infllm2_seqs* seqs,
+                                          const void* q, const void* k, const void* v,
+                                          const int32_t* block_idx, int32_t num_splits,
+                                          void* workspace, size_t workspace_bytes, void* out,
+                                          float* lse, void* stream);
+
+/* Static text for a status code. */
+const char* infllm2_status_string(infllm2_status status);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* infllm2_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t infllm2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INFLLM2_H */

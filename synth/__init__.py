@@ -23,7 +23,7 @@ queries should select those blocks.
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field, replace
+from dataclasses import dataclass, field
 from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -36,11 +36,13 @@ __all__ = [
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    bias = ((u >> np.uint64(16)) & np.uint64(1)) + np.uint64(0x7FFF)
-    u = ((u + bias) & np.uint64(0xFFFF0000)).astype(np.uint32)
-    return u.view(np.float32)
+    x = np.array(x, dtype=np.float32, copy=True, order="C")
+    u = x.view(np.uint32)                       # finite values: u + bias stays below 2^32
+    bias = (u >> np.uint32(16)) & np.uint32(1)
+    bias += np.uint32(0x7FFF)
+    u += bias
+    u &= np.uint32(0xFFFF0000)
+    return x
 
 
 @dataclass(frozen=True)

@@ -1,0 +1,171 @@
+"""The C ABI without a GPU: the library loads, exports what include/infllm2.h declares, and
+every invalid argument is rejected on the host with the right status before anything is
+enqueued (these calls never reach a kernel launch)."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+import block_sparse_long_semantic_amd as lib
+from block_sparse_long_semantic_amd import _lib
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS = 0, 1, 2, 3, 4, 5
+
+
+@pytest.fixture(scope="module")
+def so():
+    return lib.load_library()
+
+
+def test_library_exports_every_declared_symbol(so):
+    assert len(lib.EXPORTED_SYMBOLS) == 9
+    for name in lib.EXPORTED_SYMBOLS:
+        assert hasattr(so, name), name
+    assert lib.version() == 100
+
+
+def test_header_and_binding_agree():
+    with open(_lib._HEADER) as f:
+        text = f.read()
+    assert "INFLLM2_MAX_SEQS 64" in text
+    # struct field order of the binding matches the header
+    fields = [f[0] for f in _lib._CParams._fields_]
+    pos = [text.index(f"int32_t {n};") if n != "softmax_scale" else text.index("float softmax_scale;")
+           for n in fields]
+    assert pos == sorted(pos)
+
+
+def test_status_strings(so):
+    for st in range(7):
+        assert so.infllm2_status_string(st)
+    assert so.infllm2_status_string(99) == b"unknown status"
+
+
+def params(**kw):
+    base = dict(num_q_heads=32, num_kv_heads=2, head_dim=128, block_size=64, kernel_size=32,
+                kernel_stride=16, topk=96, num_init_blocks=1, num_local_blocks=2,
+                softmax_scale=0.0, dtype=lib.BF16)
+    base.update(kw)
+    return lib.Params(**base)
+
+
+def seqs(**kw):
+    base = dict(q_start=[0], q_len=[100], q_pos0=[0], kv_start=[0], kv_len=[100], kc_start=[0])
+    base.update(kw)
+    return lib.Seqs(**base)
+
+
+FAKE = ctypes.c_void_p(1 << 20)          # aligned, never dereferenced: calls fail validation
+MISALIGNED = ctypes.c_void_p((1 << 20) + 4)
+
+
+def call_scores(so, p, s, q=FAKE, kern=FAKE, scores=FAKE, nb=2):
+    cp, cs = p.c(), s.c()
+    return so.infllm2_block_scores(ctypes.byref(cp), ctypes.byref(cs), q, kern, scores, nb, None)
+
+
+def call_compress(so, p, s, k=FAKE, kern=FAKE, prev=None):
+    cp, cs = p.c(), s.c()
+    pv = None
+    if prev is not None:
+        arr = np.asarray(prev, np.int32)
+        pv = arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    return so.infllm2_compress_kernels(ctypes.byref(cp), ctypes.byref(cs), k, pv, kern, None)
+
+
+def call_attn(so, p, s, q=FAKE, idx=FAKE, out=FAKE):
+    cp, cs = p.c(), s.c()
+    return so.infllm2_sparse_attn_prefill(ctypes.byref(cp), ctypes.byref(cs), q, FAKE, FAKE, idx,
+                                          out, None, None)
+
+
+def last(so):
+    return so.infllm2_last_error().decode()
+
+
+@pytest.mark.parametrize("bad,status,text", [
+    (dict(num_q_heads=33), SHAPE, "multiple"),
+    (dict(num_kv_heads=0), SHAPE, "positive"),
+    (dict(dtype=7), UNSUP, "dtype"),
+    (dict(head_dim=100), UNSUP, "head_dim"),
+    (dict(num_q_heads=64, num_kv_heads=2), UNSUP, "group"),
+    (dict(kernel_size=40), SHAPE, "kernel_size"),
+    (dict(block_size=72), SHAPE, "block_size"),
+    (dict(topk=0), SHAPE, "topk"),
+    (dict(num_local_blocks=0), SHAPE, "num_local_blocks"),
+    (dict(topk=2, num_init_blocks=1, num_local_blocks=2), SHAPE, "forced"),
+    (dict(softmax_scale=float("inf")), SHAPE, "softmax_scale"),
+])
+def test_bad_params_rejected(so, bad, status, text):
+    assert call_scores(so, params(**bad), seqs()) == status
+    assert text in last(so)
+
+
+def test_bad_sequences_rejected(so):
+    p = params()
+    assert call_scores(so, p, seqs(q_len=[101])) == SHAPE           # q past kv
+    assert "exceeds kv_len" in last(so)
+    assert call_scores(so, p, seqs(q_pos0=[50])) == SHAPE
+    assert call_scores(so, p, seqs(kv_len=[-1], q_len=[0])) == SHAPE
+    n = 65
+    s = lib.Seqs(np.zeros(n), np.zeros(n), np.zeros(n), np.zeros(n), np.zeros(n), np.zeros(n))
+    assert call_scores(so, p, s) == SHAPE and "num_seqs" in last(so)
+    big = seqs(q_start=[2 ** 31 - 10])
+    assert call_scores(so, p, big) == SHAPE and "2^31" in last(so)
+    cp = p.c()
+    assert so.infllm2_block_scores(ctypes.byref(cp), None, FAKE, FAKE, FAKE, 2, None) == NULL
+
+
+def test_null_and_alignment(so):
+    p, s = params(), seqs()
+    assert call_scores(so, p, s, q=None) == NULL
+    assert call_scores(so, p, s, scores=MISALIGNED) == ALIGN
+    assert call_compress(so, p, s, kern=None) == NULL
+    assert call_attn(so, p, s, idx=MISALIGNED) == ALIGN
+    assert so.infllm2_block_scores(None, None, FAKE, FAKE, FAKE, 2, None) == NULL
+
+
+def test_scores_stride_checked(so):
+    p = params()
+    # 100 tokens -> reachable blocks 0..1
+    assert call_scores(so, p, seqs(), nb=1) == SHAPE and "nb_stride" in last(so)
+    cp, cs = p.c(), seqs(q_len=[1], q_pos0=[2 ** 20 * 64 - 1], kv_len=[2 ** 20 * 64]).c()
+    st = so.infllm2_topk_select(ctypes.byref(cp), ctypes.byref(cs), FAKE, 2 ** 20, FAKE, None)
+    assert st == UNSUP and "4096" in last(so)
+
+
+def test_incremental_range_checked(so):
+    assert call_compress(so, params(), seqs(), prev=[101]) == SHAPE
+    assert "prev_kv_len" in last(so)
+
+
+def test_decode_workspace(so):
+    p = params()
+    d = p.head_dim
+    assert lib.decode_workspace_size(p, 8, 12) == 8 * 32 * 12 * (2 + d) * 4
+    auto = lib.decode_workspace_size(p, 8, 0)
+    assert auto > 0 and auto % (8 * 32 * (2 + d) * 4) == 0
+    cp, cs = p.c(), seqs(q_len=[1], q_pos0=[99]).c()
+    st = so.infllm2_sparse_attn_decode(ctypes.byref(cp), ctypes.byref(cs), FAKE, FAKE, FAKE, FAKE,
+                                       4, FAKE, 16, FAKE, None, None)
+    assert st == WS and "workspace" in last(so)
+    st = so.infllm2_sparse_attn_decode(ctypes.byref(cp), ctypes.byref(cs), FAKE, FAKE, FAKE, FAKE,
+                                       97, FAKE, 1 << 30, FAKE, None, None)
+    assert st == SHAPE
+
+
+def test_last_error_is_thread_local(so):
+    import threading
+    call_scores(so, params(num_q_heads=33), seqs())
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(last(so)))
+    t.start(); t.join()
+    assert seen == [""] and "multiple" in last(so)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setenv("INFLLM2_LIB", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.load_library()

@@ -1,0 +1,248 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on seeded inputs.
+
+Small workloads are compared on every query row; the measured full-size workloads on sampled
+rows (dense region, needle rows, the last rows, a stride).  Rules are in tests/_compare.py.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import infllm2_oracle as orc
+from tests import _compare as cmp
+from tests._gpu import dev, host, kc_starts, log, run_prefill_stages, seqs_for
+
+import block_sparse_long_semantic_amd as lib
+
+pytestmark = pytest.mark.gpu
+
+
+def check_sequence(wl, res, b, rows=None, label=""):
+    """Compare one sequence of a prefill run with the oracle on the given rows (all if None)."""
+    p = wl.params
+    sl_q, sl_k = wl.seq_slices(b)
+    q_seq, k_seq, v_seq = wl.q[sl_q], wl.k[sl_k], wl.v[sl_k]
+    if q_seq.shape[0] == 0:
+        return
+    kc0, _ = kc_starts(wl.kv_len, p)
+    C = orc.num_kernels(k_seq.shape[0], p.kernel_size, p.kernel_stride)
+    kern_ref = orc.compress_kernels(k_seq, p.kernel_size, p.kernel_stride, p.dtype)
+    kern_gpu = res["kernels"][kc0[b]:kc0[b] + C]
+    ndiff = int(np.sum(kern_gpu != kern_ref))
+    assert ndiff == 0, f"{label}: {ndiff} kernel elements differ"
+    rows = np.arange(q_seq.shape[0]) if rows is None else np.asarray(rows)
+    q0 = int(wl.q_pos0[b])
+    ref = orc.run_sequence(q_seq, k_seq, v_seq, p, q_pos0=q0, rows=rows, kernels=kern_ref,
+                           with_attention=False)
+    grow = int(wl.q_start[b]) + rows
+    NB = ref.scores.shape[2]
+    gs = res["scores"][grow][:, :, :NB]
+    bound = cmp.score_bound(q_seq[rows].astype(np.float64), kern_ref, ref.positions, p, NB)
+    worst = cmp.check_scores(gs, ref.scores, bound, ref.positions, p)
+    # selection kernel alone: the oracle's selection applied to the GPU's own scores
+    gidx = res["idx"][grow]
+    own_sel = orc.select_all(gs.astype(np.float64), ref.positions, p)
+    assert np.array_equal(gidx, own_sel), f"{label}: top-k differs on the GPU's own scores"
+    rep = cmp.check_indices(gidx, ref.idx, ref.scores, ref.positions, p)
+    # attention on the GPU's indices
+    O, L = orc.sparse_attention(q_seq[rows].astype(np.float64), ref.positions, k_seq, v_seq,
+                                gidx, p)
+    err, lerr = cmp.check_attention(res["out"][grow], res["lse"][grow], O, L, p.dtype)
+    log(f"{label} seq {b}: rows {len(rows)} score-ratio {worst:.3g} idx exact {rep.exact}/"
+        f"{rep.rows} band {rep.band} out-err {err:.3g} lse-err {lerr:.3g}")
+
+
+# ------------------------------------------------------------------------- small, all rows
+
+def test_tiny_f32_all_rows():
+    wl = synth.make("tiny")
+    log("case tiny f32")
+    res = run_prefill_stages(wl)
+    check_sequence(wl, res, 0, label="tiny")
+
+
+def test_tiny_dense_reduction():
+    """topk >= number of blocks: the HIP output equals dense causal attention."""
+    wl = synth.make("tiny")
+    wl.params = replace(wl.params, topk=8)
+    log("case tiny dense")
+    res = run_prefill_stages(wl)
+    q = torch.from_numpy(wl.q.astype(np.float64)).transpose(0, 1)
+    k = torch.from_numpy(wl.k.astype(np.float64)).transpose(0, 1).repeat_interleave(2, 0)
+    v = torch.from_numpy(wl.v.astype(np.float64)).transpose(0, 1).repeat_interleave(2, 0)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)
+    assert np.abs(res["out"] - ref.transpose(0, 1).numpy()).max() < 1e-4
+
+
+@pytest.mark.parametrize("L", [3000, 1100])
+def test_8b_shape_ragged_all_rows(L):
+    """MiniCPM4-8B head layout, a length that is neither a multiple of 64 nor 16, needles."""
+    p = synth.config_params("prefill32k")
+    wl = synth.make_prefill("8b-ragged", p, [L], seed=31, needles_per_seq=2)
+    log(f"case 8b ragged L={L}")
+    res = run_prefill_stages(wl)
+    check_sequence(wl, res, 0, label=f"8b L={L}")
+    for nd in wl.needles:
+        hit = np.any(res["idx"][nd.query_positions, nd.kv_head, :] == nd.block, axis=1)
+        assert hit.all(), f"needle block {nd.block} missed"
+
+
+def test_varlen_packed_small_all_rows():
+    wl = synth.make("varlen", length_scale=1 / 16)
+    log("case varlen 1/16")
+    res = run_prefill_stages(wl)
+    for b in range(wl.num_seqs):
+        check_sequence(wl, res, b, label="varlen/16")
+
+
+def test_edge_sequences():
+    """Empty, single-token, shorter-than-a-window and one-block sequences packed together."""
+    p = synth.config_params("prefill32k")
+    wl = synth.make_prefill("edge", p, [0, 1, 20, 31, 32, 64, 65, 700], seed=33)
+    log("case edge lengths")
+    res = run_prefill_stages(wl)
+    for b in range(wl.num_seqs):
+        check_sequence(wl, res, b, label="edge")
+
+
+def test_chunked_prefill_against_cache():
+    """Queries for the last tokens only (q_pos0 > 0) attend to the whole cached sequence."""
+    p = synth.config_params("prefill32k")
+    full = synth.make_prefill("chunk", p, [2600], seed=34, needles_per_seq=1)
+    q0 = 1900
+    wl = synth.Workload("chunk", p, full.q[q0:], full.k, full.v, np.array([0]),
+                        np.array([700], np.int32), np.array([q0], np.int32), np.array([0]),
+                        np.array([2600], np.int32))
+    log("case chunked prefill")
+    res = run_prefill_stages(wl)
+    check_sequence(wl, res, 0, label="chunk")
+
+
+def test_results_are_deterministic():
+    wl = synth.make("varlen", length_scale=1 / 32)
+    a = run_prefill_stages(wl)
+    b = run_prefill_stages(wl)
+    for name in ("kernels", "idx", "out", "lse"):
+        assert np.array_equal(a[name], b[name]), name
+
+
+# ------------------------------------------------------------------------- decode
+
+def run_decode(wl, steps, num_splits=0, check=True, label="decode"):
+    p = wl.params
+    B, Lmax = wl.batch, wl.max_len
+    Ck = orc.num_kernels(Lmax, p.kernel_size, p.kernel_stride)
+    k = dev(wl.k.reshape(B * Lmax, p.num_kv_heads, p.head_dim), p.dtype)
+    v = dev(wl.v.reshape(B * Lmax, p.num_kv_heads, p.head_dim), p.dtype)
+    kern = torch.zeros((B * max(Ck, 1), p.num_kv_heads, p.head_dim), dtype=k.dtype, device="cuda")
+    kv0 = wl.kv_len0.astype(np.int64)
+    # prefill the kernel cache to the starting lengths (not timed here)
+    s0 = lib.Seqs.decode(np.maximum(kv0, 1), Lmax, max(Ck, 1))
+    lib.compress_kernels(p, lib.Seqs(s0.q_start, np.zeros(B), np.zeros(B), s0.kv_start, kv0,
+                                     s0.kc_start), k, kern)
+    nb = (Lmax + p.block_size - 1) // p.block_size
+    bufs = lib.pipeline.decode_buffers(p, B, nb, num_splits, "cuda")
+    outs = []
+    prev = kv0.copy()
+    for st in range(steps):
+        kv = kv0 + st + 1
+        seqs = lib.Seqs.decode(kv, Lmax, max(Ck, 1))
+        q = dev(wl.q_steps[st], p.dtype)
+        lib.decode_step(p, seqs, q, k, v, kern, prev.astype(np.int32), bufs)
+        torch.cuda.synchronize()
+        prev = kv.copy()
+        outs.append({n: host(bufs[n]) for n in ("scores", "idx", "out", "lse")})
+        if check:
+            for b in range(B):
+                L = int(kv[b])
+                ks, vs = wl.k[b, :L], wl.v[b, :L]
+                kern_ref = orc.compress_kernels(ks, p.kernel_size, p.kernel_stride, p.dtype)
+                C = kern_ref.shape[0]
+                gk = host(kern[b * Ck:b * Ck + C])
+                assert np.array_equal(gk, kern_ref), f"{label}: kernels differ seq {b} step {st}"
+                ref = orc.run_sequence(wl.q_steps[st][b:b + 1], ks, vs, p, q_pos0=L - 1,
+                                       kernels=kern_ref, with_attention=False)
+                NB = ref.scores.shape[2]
+                gs = outs[-1]["scores"][b:b + 1, :, :NB]
+                bound = cmp.score_bound(wl.q_steps[st][b:b + 1].astype(np.float64), kern_ref,
+                                        ref.positions, p, NB)
+                cmp.check_scores(gs, ref.scores, bound, ref.positions, p)
+                gidx = outs[-1]["idx"][b:b + 1]
+                assert np.array_equal(gidx, orc.select_all(gs.astype(np.float64), ref.positions, p))
+                cmp.check_indices(gidx, ref.idx, ref.scores, ref.positions, p)
+                O, Ls = orc.sparse_attention(wl.q_steps[st][b:b + 1].astype(np.float64),
+                                             ref.positions, ks, vs, gidx, p)
+                cmp.check_attention(outs[-1]["out"][b:b + 1], outs[-1]["lse"][b:b + 1], O, Ls,
+                                    p.dtype)
+    return outs
+
+
+def test_decode_small_ragged_lengths():
+    p = synth.config_params("decode128k")
+    wl = synth.make_decode("dec-small", p, batch=5, max_len=3000, steps=6, seed=41,
+                           kv_len0=[2990, 2000, 1500, 700, 100])
+    log("case decode small")
+    run_decode(wl, 6)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 7])
+def test_decode_split_invariance(splits):
+    p = synth.config_params("decode128k")
+    wl = synth.make_decode("dec-split", p, batch=3, max_len=8192, steps=2, seed=42,
+                           kv_len0=[8000, 6000, 3000])
+    log(f"case decode splits={splits}")
+    base = run_decode(wl, 2, num_splits=1, check=False)
+    other = run_decode(wl, 2, num_splits=splits, check=(splits == 3))
+    for a, b in zip(base, other):
+        assert np.array_equal(a["idx"], b["idx"])
+        assert np.abs(a["out"] - b["out"]).max() <= 1e-2
+        assert np.abs(a["lse"] - b["lse"]).max() <= 1e-4
+
+
+def test_decode_f32_tiny_shape():
+    p = synth.config_params("tiny")
+    wl = synth.make_decode("dec-f32", p, batch=2, max_len=512, steps=3, seed=43,
+                           kv_len0=[500, 300])
+    log("case decode f32")
+    run_decode(wl, 3, num_splits=2)
+
+
+# ------------------------------------------------------------------------- full sizes
+
+def sample_rows(wl, b, extra=()):
+    p = wl.params
+    L = int(wl.q_len[b])
+    dense = min(L, p.topk * p.block_size)
+    rows = set(range(0, dense, 97)) | set(range(max(0, L - 5), L)) | set(range(dense, L, 1777))
+    rows |= {r for r in extra if 0 <= r < L}
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["prefill32k", "varlen", "prefill128k"])
+def test_full_size_prefill_sampled(name):
+    wl = synth.make(name)
+    log(f"case full {name}")
+    res = run_prefill_stages(wl)
+    # every needle query selects its needle, on all rows (not only sampled)
+    for nd in wl.needles:
+        rows = int(wl.q_start[nd.seq]) + nd.query_positions
+        assert np.all(np.any(res["idx"][rows, nd.kv_head, :] == nd.block, axis=1))
+    for b in range(wl.num_seqs):
+        extra = [int(r) for nd in wl.needles if nd.seq == b for r in nd.query_positions[:4]]
+        check_sequence(wl, res, b, rows=sample_rows(wl, b, extra), label=f"full {name}")
+    # sparsity: selected-token fraction per row follows the configured top-k
+    p = wl.params
+    nsel = (res["idx"] >= 0).sum(axis=2)
+    for b in range(wl.num_seqs):
+        pos = np.arange(int(wl.q_len[b]))
+        expect = np.minimum(pos // p.block_size + 1, p.topk)
+        rows = int(wl.q_start[b]) + pos
+        assert np.all(nsel[rows] == expect[:, None])
+
+
+def test_full_size_decode():
+    wl = synth.make("decode128k", steps=2)
+    log("case full decode128k")
+    run_decode(wl, 2, label="full decode")
