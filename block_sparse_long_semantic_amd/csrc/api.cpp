@@ -289,6 +289,17 @@ infllm2_status infllm2_sparse_attn_prefill(const infllm2_params* params,
   SeqTable t;
   infllm2_status st = attn_common(params, seqs, q, k, v, block_idx, out, lse, &g, &t);
   if (st != INFLLM2_OK) return st;
+  if (infllm2::attn_tile_supported(g, params->dtype, t)) {
+    int acc = 0;
+    for (int b = 0; b < t.n; ++b) {
+      t.work_prefix[b] = acc;
+      acc += (t.q_len[b] + 15) / 16;
+    }
+    t.work_prefix[t.n] = acc;
+    return hip_status(infllm2::launch_attn_tile(g, t, q, k, v, block_idx, out, lse,
+                                                static_cast<hipStream_t>(stream)),
+                      "sparse_attn_prefill launch");
+  }
   return hip_status(infllm2::launch_attn(g, params->dtype, t, q, k, v, block_idx, 1, out, lse,
                                          nullptr, static_cast<hipStream_t>(stream)),
                     "sparse_attn_prefill launch");

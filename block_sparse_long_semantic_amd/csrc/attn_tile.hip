@@ -1,0 +1,445 @@
+// Tiled block-sparse prefill attention for gfx950 (MiniCPM4 paper summary, section 2.1.3:
+// each token attends only to its most relevant KV blocks; FlashAttention-style online
+// softmax).
+//
+// Design (one workgroup = 4 waves = one tile of T = 16 consecutive query tokens of one
+// sequence and one KV head):
+//   * Union: the tile's 16 selected-block lists are OR-ed into a per-block 16-bit token mask in
+//     LDS and compacted into an ascending list of (block, mask).  Each union block's K and V
+//     (64 keys x d, bf16) are staged into LDS once for all tokens that chose it.
+//   * Staging: global_load_lds (16 B per lane, straight to LDS, no registers) into a ring of
+//     NSLOT slots; the next block's loads are in flight while the current one is consumed.
+//     Waits are explicit vmcnt counts and raw s_barrier (a fenced __syncthreads would drain
+//     every in-flight load).  Rows are stored row-major with an XOR swizzle of the 16-byte
+//     chunks so that the MFMA operand reads below hit distinct LDS banks.
+//   * Compute: wave w owns tokens 4w..4w+3 (registers: Q operand, O accumulator, running max
+//     and sum).  For every union block it processes only its tokens whose mask bit is set:
+//       S^T = K Q^T   16 keys x 16 heads per v_mfma_f32_16x16x32_bf16 (A = K from LDS)
+//       online softmax over the 64 keys (exp2, running max/sum per head)
+//       O  += P V     16 heads x 16 dims per MFMA; B = V read with ds_read_b64_tr_b16, which
+//                     transposes 4x16 bf16 tiles across each 16-lane group, so V needs no
+//                     transposed copy.  The key order inside each 32-key step makes the
+//                     S^T fragment a lane holds exactly its P operand.
+//   * Scheduling: work items are laid out so that each XCD (blockIdx % 8) runs consecutive
+//     tiles of one KV head, which select from the same blocks and share that XCD's L2.
+#include "internal.h"
+
+namespace infllm2 {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kT = 16;            // query tokens per workgroup
+constexpr int kMaxUnion = 2048;   // reachable blocks per tile handled by this kernel
+constexpr float kLazy = 8.f;      // log2 headroom before the running max is moved
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Wait until at most `later` blocks of PER loads each are still in flight (later clamped to
+// MAXL): the oldest block has landed in LDS.
+template <int PER, int MAXL>
+__device__ __forceinline__ void wait_blocks(int later) {
+  if constexpr (MAXL > 0) {
+    if (later >= MAXL) {
+      wait_vmcnt<MAXL * PER>();
+      return;
+    }
+    wait_blocks<PER, MAXL - 1>(later);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+// XOR swizzle of the 16-byte chunk index within a row (bijective per row).
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  return ((r & 3) | ((r >> 1) & 12)) & (CPR - 1);
+}
+
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+// The 2*NT transposing reads of one 32-key step (n = 0..NT-1, h = 0..1) at immediate offsets
+// 512*(2n + h) from `addr`, waited for inside the same asm statement (the compiler does not
+// track loads it cannot see).  Result vt[n][h] = 4 bf16: V[32s + 8*q4 + 4h + 0..3][16n + c16].
+template <int NT>
+__device__ __forceinline__ void read_v_step(uint32_t addr, uint64_t (&vt)[NT][2]);
+
+template <>
+__device__ __forceinline__ void read_v_step<8>(uint32_t addr, uint64_t (&vt)[8][2]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n"
+      "ds_read_b64_tr_b16 %1, %16 offset:512\n"
+      "ds_read_b64_tr_b16 %2, %16 offset:1024\n"
+      "ds_read_b64_tr_b16 %3, %16 offset:1536\n"
+      "ds_read_b64_tr_b16 %4, %16 offset:2048\n"
+      "ds_read_b64_tr_b16 %5, %16 offset:2560\n"
+      "ds_read_b64_tr_b16 %6, %16 offset:3072\n"
+      "ds_read_b64_tr_b16 %7, %16 offset:3584\n"
+      "ds_read_b64_tr_b16 %8, %16 offset:4096\n"
+      "ds_read_b64_tr_b16 %9, %16 offset:4608\n"
+      "ds_read_b64_tr_b16 %10, %16 offset:5120\n"
+      "ds_read_b64_tr_b16 %11, %16 offset:5632\n"
+      "ds_read_b64_tr_b16 %12, %16 offset:6144\n"
+      "ds_read_b64_tr_b16 %13, %16 offset:6656\n"
+      "ds_read_b64_tr_b16 %14, %16 offset:7168\n"
+      "ds_read_b64_tr_b16 %15, %16 offset:7680\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(vt[0][0]), "=&v"(vt[0][1]), "=&v"(vt[1][0]), "=&v"(vt[1][1]),
+        "=&v"(vt[2][0]), "=&v"(vt[2][1]), "=&v"(vt[3][0]), "=&v"(vt[3][1]),
+        "=&v"(vt[4][0]), "=&v"(vt[4][1]), "=&v"(vt[5][0]), "=&v"(vt[5][1]),
+        "=&v"(vt[6][0]), "=&v"(vt[6][1]), "=&v"(vt[7][0]), "=&v"(vt[7][1])
+      : "v"(addr)
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void read_v_step<4>(uint32_t addr, uint64_t (&vt)[4][2]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n"
+      "ds_read_b64_tr_b16 %1, %8 offset:512\n"
+      "ds_read_b64_tr_b16 %2, %8 offset:1024\n"
+      "ds_read_b64_tr_b16 %3, %8 offset:1536\n"
+      "ds_read_b64_tr_b16 %4, %8 offset:2048\n"
+      "ds_read_b64_tr_b16 %5, %8 offset:2560\n"
+      "ds_read_b64_tr_b16 %6, %8 offset:3072\n"
+      "ds_read_b64_tr_b16 %7, %8 offset:3584\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(vt[0][0]), "=&v"(vt[0][1]), "=&v"(vt[1][0]), "=&v"(vt[1][1]),
+        "=&v"(vt[2][0]), "=&v"(vt[2][1]), "=&v"(vt[3][0]), "=&v"(vt[3][1])
+      : "v"(addr)
+      : "memory");
+}
+
+template <int D, int G, int NSLOT>
+__global__ void __launch_bounds__(256, 1)
+attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+          const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
+          uint16_t* __restrict__ out, float* __restrict__ lse, int n_items) {
+  constexpr int KS = D / 32;
+  constexpr int NT = D / 16;
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int MAT = 64 * D * 2;            // bytes of one 64-key matrix
+  constexpr int LPW = (64 * CPR) / 256;      // 16-byte loads per wave per matrix
+  __shared__ __attribute__((aligned(16))) unsigned char ring[NSLOT][2][MAT];
+  __shared__ uint32_t bitmap[kMaxUnion / 2];
+  __shared__ uint32_t ulist[kMaxUnion];
+  __shared__ int wave_tot[4];
+
+  const int per_xcd = gridDim.x / 8;
+  const int item = static_cast<int>(blockIdx.x % 8) * per_xcd + static_cast<int>(blockIdx.x / 8);
+  if (item >= n_items) return;
+  const int n_tiles = t.work_prefix[t.n];
+  const int kvh = item / n_tiles;
+  const int tile = item - kvh * n_tiles;
+  const int b = find_seq(t, tile);
+  const int r0 = (tile - t.work_prefix[b]) * kT;
+  const int nq = min(kT, t.q_len[b] - r0);
+  const int row0 = t.q_start[b] + r0;
+  const int pos0 = t.q_pos0[b] + r0;
+  const int kv0 = t.kv_start[b];
+  const int kv_len = t.kv_len[b];
+  const int nbt = (pos0 + nq - 1) / 64 + 1;  // reachable blocks of the tile (<= kMaxUnion)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int c16 = lane & 15;
+  const int q4 = lane >> 4;
+  const int Hq = g.Hq, Hkv = g.Hkv;
+
+  // ---- union of the tile's selected blocks
+  for (int e = tid; e < (nbt + 1) / 2; e += 256) bitmap[e] = 0u;
+  __syncthreads();
+  for (int e = tid; e < nq * g.topk; e += 256) {
+    const int tok = e / g.topk;
+    const int blk = idx[(static_cast<size_t>(row0 + tok) * Hkv + kvh) * g.topk + (e - tok * g.topk)];
+    if (blk >= 0) atomicOr(&bitmap[blk >> 1], (1u << tok) << (16 * (blk & 1)));
+  }
+  __syncthreads();
+  {
+    // each thread compacts 8 consecutive blocks; block-wide exclusive scan of the counts
+    const int b0 = tid * 8;
+    uint32_t m8[8];
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int blk = b0 + e;
+      m8[e] = blk < nbt ? (bitmap[blk >> 1] >> (16 * (blk & 1))) & 0xFFFFu : 0u;
+      cnt += m8[e] != 0u;
+    }
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) wave_tot[w] = incl;
+    __syncthreads();
+    int base = incl - cnt;
+    for (int ww = 0; ww < w; ++ww) base += wave_tot[ww];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (m8[e] != 0u) ulist[base++] = (static_cast<uint32_t>(b0 + e) << 16) | m8[e];
+  }
+  __syncthreads();
+  const int n_union = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+
+  // ---- staging.  global_load_lds writes lane l's 16 bytes at LDS unit base+l, and each lane
+  // picks its own source, so both matrices are stored in the order their readers want:
+  //   K: unit 64*J + lane holds the A-operand chunk that lane reads for MFMA step J, i.e.
+  //      J = (2s + tp)*KS + ks, row 32s + 8(c16/4) + 4tp + c16%4, chunk 4ks + q4;
+  //   V: unit 32*((s*NT + n)*2 + h) + 8q + 2j + a1 holds row 32s + 8q + 4h + j, chunk 2n + a1,
+  //      so every transposing read of (s, n, h) covers 512 contiguous bytes.
+  const size_t rowstride = static_cast<size_t>(Hkv) * D;        // elements
+  uint32_t koff[LPW], voff[LPW];                                // element offsets in a block
+  int krow[LPW], vrow[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int J = w * LPW + i;                                  // K: 64 units per J
+    const int s_ = J / (2 * KS), tp_ = (J / KS) % 2, ks_ = J % KS;
+    krow[i] = 32 * s_ + 8 * (c16 >> 2) + 4 * tp_ + (c16 & 3);
+    koff[i] = static_cast<uint32_t>(krow[i] * rowstride + 8 * (4 * ks_ + q4));
+    const int p = J * 64 + lane;                                // V: 32 units per group I
+    const int I = p >> 5, lo = p & 31;
+    const int h_ = I & 1, n_ = (I >> 1) % NT, sv_ = (I >> 1) / NT;
+    vrow[i] = 32 * sv_ + 8 * (lo >> 3) + 4 * h_ + ((lo >> 1) & 3);
+    voff[i] = static_cast<uint32_t>(vrow[i] * rowstride + 8 * (2 * n_ + (lo & 1)));
+  }
+  const uint16_t* kbase = k + static_cast<size_t>(kv0) * rowstride + static_cast<size_t>(kvh) * D;
+  const uint16_t* vbase = v + static_cast<size_t>(kv0) * rowstride + static_cast<size_t>(kvh) * D;
+  auto stage = [&](int u, int slot) {
+    const int key0 = __builtin_amdgcn_readfirstlane(static_cast<int>(ulist[u] >> 16)) * 64;
+    const bool tail = key0 + 64 > kv_len;                       // ragged end: clamp rows
+    const int last = kv_len - 1 - key0;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      int dk = 0, dv = 0;
+      if (tail) {
+        dk = ((krow[i] < last ? krow[i] : last) - krow[i]) * static_cast<int>(rowstride);
+        dv = ((vrow[i] < last ? vrow[i] : last) - vrow[i]) * static_cast<int>(rowstride);
+      }
+      const uint16_t* gk = kbase + static_cast<size_t>(key0) * rowstride + koff[i] + dk;
+      const uint16_t* gv = vbase + static_cast<size_t>(key0) * rowstride + voff[i] + dv;
+      __builtin_amdgcn_global_load_lds(gk, (lds_void*)(&ring[slot][0][(w * LPW + i) * 1024]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(gv, (lds_void*)(&ring[slot][1][(w * LPW + i) * 1024]), 16, 0, 0);
+    }
+  };
+
+  // ---- per-token state (token tw = 4w + tt).  m_run is shared by the 4 lanes of a head (log2
+  // units, possibly stale by < kLazy); l_run is this lane's partial row sum.
+  bf16x8 qf[4][KS];
+  f32x4 o[4][NT];
+  float m_run[4], l_run[4];
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int tw = 4 * w + tt;
+    m_run[tt] = -INFINITY;
+    l_run[tt] = 0.f;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) o[tt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (tw < nq && c16 < G)
+        qf[tt][ks] = *reinterpret_cast<const bf16x8*>(
+            q + (static_cast<size_t>(row0 + tw) * Hq + kvh * G + c16) * D + 32 * ks + 8 * q4);
+      else
+        qf[tt][ks] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NSLOT - 1; ++u)
+    if (u < n_union) stage(u, u);
+  const float qscale = g.scale * kLog2e;
+  const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&ring[0][0][0]));
+  const uint32_t k_lane = ring_lds + 16 * lane;                                 // + slot, + 1KB*J
+  const uint32_t v_lane = ring_lds + MAT + 16 * (8 * q4 + 2 * (c16 >> 2) + ((c16 & 3) >> 1)) +
+                          8 * (c16 & 1);                                         // + slot, + 512*I
+
+  for (int u = 0; u < n_union; ++u) {
+    // block u landed (this wave's loads); up to NSLOT-2 later blocks stay in flight
+    wait_blocks<2 * LPW, NSLOT - 2>(n_union - 1 - u);
+    lds_barrier();
+    // every wave is past block u-1: its slot takes block u + NSLOT - 1
+    if (u + NSLOT - 1 < n_union) stage(u + NSLOT - 1, (u + NSLOT - 1) % NSLOT);
+    const uint32_t ent = __builtin_amdgcn_readfirstlane(ulist[u]);
+    const int slot = u % NSLOT;
+    const int key0 = static_cast<int>(ent >> 16) * 64;
+    const uint32_t wm = (ent >> (4 * w)) & 15u;
+    const uint32_t slot_off = static_cast<uint32_t>(slot) * (2 * MAT);
+    const lds_bf16x8* Kp = (const lds_bf16x8*)(uintptr_t)(k_lane + slot_off);
+    const uint32_t vaddr = v_lane + slot_off;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      if (!(wm & (1u << tt))) continue;
+      const int pos = pos0 + 4 * w + tt;
+      // S^T tiles: tile (s, tp) row r' -> key 32s + 8(r'/4) + 4tp + (r'%4); the lane then
+      // holds keys 32s + 8*q4 + 4*tp + i for head c16 (raw, unscaled dot products).
+      float sv[2][2][4];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 a = Kp[((2 * s + tp) * KS + ks) * 64];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[tt][ks], acc, 0, 0, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sv[s][tp][i] = acc[i];
+        }
+      }
+      // keys past the query or the sequence end (only in the query's own block or the tail)
+      if (key0 + 63 > pos || key0 + 64 > kv_len) {
+        const int lim = min(pos, kv_len - 1) - key0;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (32 * s + 8 * q4 + 4 * tp + i > lim) sv[s][tp][i] = -INFINITY;
+      }
+      float mx = sv[0][0][0];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sv[s][tp][i]);
+      mx *= qscale;
+      // lazy rescaling: the running max moves only when some head's block max exceeds it by
+      // more than kLazy (probabilities then stay below 2^kLazy), decided for the whole wave
+      if (__ballot(mx > m_run[tt] + kLazy) != 0ull) {
+        float bm = fmaxf(mx, __shfl_xor(mx, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float m_new = fmaxf(m_run[tt], bm);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[tt] - m_new);
+        l_run[tt] *= alpha;
+        m_run[tt] = m_new;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a_i = __shfl(alpha, 4 * q4 + i);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) o[tt][n][i] *= a_i;
+        }
+      }
+      const float mneg = -m_run[tt];
+      float psum = 0.f;
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sv[s][tp][i], qscale, mneg));
+            sv[s][tp][i] = p;
+            psum += p;
+          }
+      l_run[tt] += psum;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        // P operand: head c16, keys 32s + 8*q4 + 0..7
+        const bf16x2 p01 = __builtin_convertvector((f32x2){sv[s][0][0], sv[s][0][1]}, bf16x2);
+        const bf16x2 p23 = __builtin_convertvector((f32x2){sv[s][0][2], sv[s][0][3]}, bf16x2);
+        const bf16x2 p45 = __builtin_convertvector((f32x2){sv[s][1][0], sv[s][1][1]}, bf16x2);
+        const bf16x2 p67 = __builtin_convertvector((f32x2){sv[s][1][2], sv[s][1][3]}, bf16x2);
+        const bf16x2 pp[4] = {p01, p23, p45, p67};
+        const bf16x8 pa = __builtin_bit_cast(bf16x8, pp);
+        uint64_t vt[NT][2];
+        read_v_step<NT>(vaddr + 512u * (2 * NT * s), vt);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const uint64_t both[2] = {vt[n][0], vt[n][1]};
+          const bf16x8 vb = __builtin_bit_cast(bf16x8, both);
+          o[tt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[tt][n], 0, 0, 0);
+        }
+      }
+    }
+    // this wave's reads of the slot are complete before the next barrier lets it be refilled
+    wait_lgkm0();
+  }
+
+  // ---- epilogue: combine the 4 lanes' partial sums, normalise and store
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int tw = 4 * w + tt;
+    if (tw >= nq) continue;
+    float l = l_run[tt];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const size_t orow = static_cast<size_t>(row0 + tw) * Hq + kvh * G;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * q4 + i;
+      const float inv = 1.f / __shfl(l, h);
+      if (h < G) {
+        uint16_t* op = out + (orow + h) * D;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) op[16 * n + c16] = f32_to_bf16(o[tt][n][i] * inv);
+      }
+    }
+    if (lse != nullptr && q4 == 0 && c16 < G)
+      lse[orow + c16] = (m_run[tt] + log2f(l)) * kLn2;
+  }
+}
+
+}  // namespace
+
+bool attn_tile_supported(const Geom& g, int dtype, const SeqTable& t) {
+  if (dtype != INFLLM2_BF16 || g.B != 64 || !(g.d == 64 || g.d == 128) || !(g.G == 8 || g.G == 16))
+    return false;
+  for (int b = 0; b < t.n; ++b)
+    if (t.q_len[b] > 0 && (t.q_pos0[b] + t.q_len[b] - 1) / 64 + 1 > kMaxUnion) return false;
+  return true;
+}
+
+// work_prefix of `t` must count tiles of 16 query rows per sequence.
+hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, const void* k,
+                            const void* v, const int32_t* idx, void* out, float* lse,
+                            hipStream_t stream) {
+  const int n_items = t.work_prefix[t.n] * g.Hkv;
+  if (n_items == 0) return hipSuccess;
+  const int grid = (n_items + 7) / 8 * 8;
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const uint16_t* vv = static_cast<const uint16_t*>(v);
+  uint16_t* oo = static_cast<uint16_t*>(out);
+#define INFLLM2_TILE_CASE(DD, GG, NS)                                                         \
+  if (g.d == DD && g.G == GG) {                                                               \
+    hipLaunchKernelGGL((attn_tile<DD, GG, NS>), dim3(grid), dim3(256), 0, stream, g, t, qq, kk, \
+                       vv, idx, oo, lse, n_items);                                            \
+    return hipGetLastError();                                                                 \
+  }
+  INFLLM2_TILE_CASE(128, 16, 4)
+  INFLLM2_TILE_CASE(128, 8, 4)
+  INFLLM2_TILE_CASE(64, 16, 8)
+  INFLLM2_TILE_CASE(64, 8, 8)
+#undef INFLLM2_TILE_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace infllm2

@@ -68,6 +68,11 @@ hipError_t launch_topk(const Geom& g, const SeqTable& t, const float* scores, in
 hipError_t launch_attn(const Geom& g, int dtype, const SeqTable& t, const void* q,
                        const void* k, const void* v, const int32_t* idx, int splits,
                        void* out, float* lse, float* part, hipStream_t stream);
+// Tiled prefill attention (tiles of 16 query rows sharing staged K/V blocks).
+bool attn_tile_supported(const Geom& g, int dtype, const SeqTable& t);
+hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, const void* k,
+                            const void* v, const int32_t* idx, void* out, float* lse,
+                            hipStream_t stream);
 hipError_t launch_attn_combine(const Geom& g, int dtype, const SeqTable& t, int splits,
                                const float* part, void* out, float* lse, hipStream_t stream);
 
