@@ -38,6 +38,7 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kT = 16;            // query tokens per workgroup
+constexpr int kWaves = 8;         // waves per workgroup (tokens per wave = kT / kWaves)
 constexpr int kMaxUnion = 2048;   // reachable blocks per tile handled by this kernel
 constexpr float kLazy = 8.f;      // log2 headroom before the running max is moved
 
@@ -133,8 +134,8 @@ __device__ __forceinline__ void read_v_step<4>(uint32_t addr, uint64_t (&vt)[4][
       : "memory");
 }
 
-template <int D, int G, int NSLOT>
-__global__ void __launch_bounds__(256, 1)
+template <int D, int G, int NSLOT, int NW, int TPW>
+__global__ void __launch_bounds__(64 * NW, 1)
 attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
           const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
           uint16_t* __restrict__ out, float* __restrict__ lse, int n_items) {
@@ -142,11 +143,13 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   constexpr int NT = D / 16;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int MAT = 64 * D * 2;            // bytes of one 64-key matrix
-  constexpr int LPW = (64 * CPR) / 256;      // 16-byte loads per wave per matrix
+  constexpr int LPW = CPR / NW;              // 16-byte loads per wave per matrix
+  constexpr int NTHR = 64 * NW;
+  static_assert(TPW * NW == kT, "tile = waves x tokens per wave");
   __shared__ __attribute__((aligned(16))) unsigned char ring[NSLOT][2][MAT];
   __shared__ uint32_t bitmap[kMaxUnion / 2];
   __shared__ uint32_t ulist[kMaxUnion];
-  __shared__ int wave_tot[4];
+  __shared__ int wave_tot[NW];
 
   const int per_xcd = gridDim.x / 8;
   const int item = static_cast<int>(blockIdx.x % 8) * per_xcd + static_cast<int>(blockIdx.x / 8);
@@ -171,21 +174,22 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   const int Hq = g.Hq, Hkv = g.Hkv;
 
   // ---- union of the tile's selected blocks
-  for (int e = tid; e < (nbt + 1) / 2; e += 256) bitmap[e] = 0u;
+  for (int e = tid; e < (nbt + 1) / 2; e += NTHR) bitmap[e] = 0u;
   __syncthreads();
-  for (int e = tid; e < nq * g.topk; e += 256) {
+  for (int e = tid; e < nq * g.topk; e += NTHR) {
     const int tok = e / g.topk;
     const int blk = idx[(static_cast<size_t>(row0 + tok) * Hkv + kvh) * g.topk + (e - tok * g.topk)];
     if (blk >= 0) atomicOr(&bitmap[blk >> 1], (1u << tok) << (16 * (blk & 1)));
   }
   __syncthreads();
   {
-    // each thread compacts 8 consecutive blocks; block-wide exclusive scan of the counts
-    const int b0 = tid * 8;
-    uint32_t m8[8];
+    // each thread compacts KPT consecutive blocks; block-wide exclusive scan of the counts
+    constexpr int KPT = kMaxUnion / NTHR;
+    const int b0 = tid * KPT;
+    uint32_t m8[KPT];
     int cnt = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < KPT; ++e) {
       const int blk = b0 + e;
       m8[e] = blk < nbt ? (bitmap[blk >> 1] >> (16 * (blk & 1))) & 0xFFFFu : 0u;
       cnt += m8[e] != 0u;
@@ -201,11 +205,13 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
     int base = incl - cnt;
     for (int ww = 0; ww < w; ++ww) base += wave_tot[ww];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int e = 0; e < KPT; ++e)
       if (m8[e] != 0u) ulist[base++] = (static_cast<uint32_t>(b0 + e) << 16) | m8[e];
   }
   __syncthreads();
-  const int n_union = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+  int n_union = 0;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) n_union += wave_tot[ww];
 
   // ---- staging.  global_load_lds writes lane l's 16 bytes at LDS unit base+l, and each lane
   // picks its own source, so both matrices are stored in the order their readers want:
@@ -248,14 +254,14 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
     }
   };
 
-  // ---- per-token state (token tw = 4w + tt).  m_run is shared by the 4 lanes of a head (log2
+  // ---- per-token state (token tw = TPW*w + tt).  m_run is shared by the 4 lanes of a head (log2
   // units, possibly stale by < kLazy); l_run is this lane's partial row sum.
-  bf16x8 qf[4][KS];
-  f32x4 o[4][NT];
-  float m_run[4], l_run[4];
+  bf16x8 qf[TPW][KS];
+  f32x4 o[TPW][NT];
+  float m_run[TPW], l_run[TPW];
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    const int tw = 4 * w + tt;
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int tw = TPW * w + tt;
     m_run[tt] = -INFINITY;
     l_run[tt] = 0.f;
 #pragma unroll
@@ -287,14 +293,14 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
     const uint32_t ent = __builtin_amdgcn_readfirstlane(ulist[u]);
     const int slot = u % NSLOT;
     const int key0 = static_cast<int>(ent >> 16) * 64;
-    const uint32_t wm = (ent >> (4 * w)) & 15u;
+    const uint32_t wm = (ent >> (TPW * w)) & ((1u << TPW) - 1u);
     const uint32_t slot_off = static_cast<uint32_t>(slot) * (2 * MAT);
     const lds_bf16x8* Kp = (const lds_bf16x8*)(uintptr_t)(k_lane + slot_off);
     const uint32_t vaddr = v_lane + slot_off;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
+    for (int tt = 0; tt < TPW; ++tt) {
       if (!(wm & (1u << tt))) continue;
-      const int pos = pos0 + 4 * w + tt;
+      const int pos = pos0 + TPW * w + tt;
       // S^T tiles: tile (s, tp) row r' -> key 32s + 8(r'/4) + 4tp + (r'%4); the lane then
       // holds keys 32s + 8*q4 + 4*tp + i for head c16 (raw, unscaled dot products).
       float sv[2][2][4];
@@ -385,8 +391,8 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
 
   // ---- epilogue: combine the 4 lanes' partial sums, normalise and store
 #pragma unroll
-  for (int tt = 0; tt < 4; ++tt) {
-    const int tw = 4 * w + tt;
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int tw = TPW * w + tt;
     if (tw >= nq) continue;
     float l = l_run[tt];
     l += __shfl_xor(l, 16);
@@ -430,8 +436,8 @@ hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, con
   uint16_t* oo = static_cast<uint16_t*>(out);
 #define INFLLM2_TILE_CASE(DD, GG, NS)                                                         \
   if (g.d == DD && g.G == GG) {                                                               \
-    hipLaunchKernelGGL((attn_tile<DD, GG, NS>), dim3(grid), dim3(256), 0, stream, g, t, qq, kk, \
-                       vv, idx, oo, lse, n_items);                                            \
+    hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWaves, kT / kWaves>), dim3(grid),              \
+                       dim3(64 * kWaves), 0, stream, g, t, qq, kk, vv, idx, oo, lse, n_items); \
     return hipGetLastError();                                                                 \
   }
   INFLLM2_TILE_CASE(128, 16, 4)
