@@ -22,6 +22,8 @@
 //                     S^T fragment a lane holds exactly its P operand.
 //   * Scheduling: work items are laid out so that each XCD (blockIdx % 8) runs consecutive
 //     tiles of one KV head, which select from the same blocks and share that XCD's L2.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace infllm2 {
@@ -39,8 +41,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kT = 16;            // query tokens per workgroup
 constexpr int kWaves = 8;         // waves per workgroup (tokens per wave = kT / kWaves)
+constexpr bool kRounds = true;    // launch items in rounds of one workgroup per CU
 constexpr int kMaxUnion = 2048;   // reachable blocks per tile handled by this kernel
 constexpr float kLazy = 8.f;      // log2 headroom before the running max is moved
+constexpr int kSpinLimit = 1 << 20;  // bounded waits (about 30 ms): a protocol error never hangs
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
@@ -82,42 +86,14 @@ __device__ __forceinline__ int swz(int r) {
 
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
-// The 2*NT transposing reads of one 32-key step (n = 0..NT-1, h = 0..1) at immediate offsets
-// 512*(2n + h) from `addr`, waited for inside the same asm statement (the compiler does not
-// track loads it cannot see).  Result vt[n][h] = 4 bf16: V[32s + 8*q4 + 4h + 0..3][16n + c16].
-template <int NT>
-__device__ __forceinline__ void read_v_step(uint32_t addr, uint64_t (&vt)[NT][2]);
+// Transposing reads of V for 2*NH MFMA B-operands (tiles n = 0..NH-1, h = 0..1) at immediate
+// offsets 512*(2n + h) from `addr`, waited for inside the same asm statement (the compiler does
+// not track loads it cannot see).  vt[n][h] = 4 bf16: V[32s + 8*q4 + 4h + 0..3][16n' + c16].
+template <int NH>
+__device__ __forceinline__ void read_v_half(uint32_t addr, uint64_t (&vt)[NH][2]);
 
 template <>
-__device__ __forceinline__ void read_v_step<8>(uint32_t addr, uint64_t (&vt)[8][2]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %16\n"
-      "ds_read_b64_tr_b16 %1, %16 offset:512\n"
-      "ds_read_b64_tr_b16 %2, %16 offset:1024\n"
-      "ds_read_b64_tr_b16 %3, %16 offset:1536\n"
-      "ds_read_b64_tr_b16 %4, %16 offset:2048\n"
-      "ds_read_b64_tr_b16 %5, %16 offset:2560\n"
-      "ds_read_b64_tr_b16 %6, %16 offset:3072\n"
-      "ds_read_b64_tr_b16 %7, %16 offset:3584\n"
-      "ds_read_b64_tr_b16 %8, %16 offset:4096\n"
-      "ds_read_b64_tr_b16 %9, %16 offset:4608\n"
-      "ds_read_b64_tr_b16 %10, %16 offset:5120\n"
-      "ds_read_b64_tr_b16 %11, %16 offset:5632\n"
-      "ds_read_b64_tr_b16 %12, %16 offset:6144\n"
-      "ds_read_b64_tr_b16 %13, %16 offset:6656\n"
-      "ds_read_b64_tr_b16 %14, %16 offset:7168\n"
-      "ds_read_b64_tr_b16 %15, %16 offset:7680\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(vt[0][0]), "=&v"(vt[0][1]), "=&v"(vt[1][0]), "=&v"(vt[1][1]),
-        "=&v"(vt[2][0]), "=&v"(vt[2][1]), "=&v"(vt[3][0]), "=&v"(vt[3][1]),
-        "=&v"(vt[4][0]), "=&v"(vt[4][1]), "=&v"(vt[5][0]), "=&v"(vt[5][1]),
-        "=&v"(vt[6][0]), "=&v"(vt[6][1]), "=&v"(vt[7][0]), "=&v"(vt[7][1])
-      : "v"(addr)
-      : "memory");
-}
-
-template <>
-__device__ __forceinline__ void read_v_step<4>(uint32_t addr, uint64_t (&vt)[4][2]) {
+__device__ __forceinline__ void read_v_half<4>(uint32_t addr, uint64_t (&vt)[4][2]) {
   asm volatile(
       "ds_read_b64_tr_b16 %0, %8\n"
       "ds_read_b64_tr_b16 %1, %8 offset:512\n"
@@ -134,25 +110,63 @@ __device__ __forceinline__ void read_v_step<4>(uint32_t addr, uint64_t (&vt)[4][
       : "memory");
 }
 
-template <int D, int G, int NSLOT, int NW, int TPW>
+template <>
+__device__ __forceinline__ void read_v_half<2>(uint32_t addr, uint64_t (&vt)[2][2]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n"
+      "ds_read_b64_tr_b16 %1, %4 offset:512\n"
+      "ds_read_b64_tr_b16 %2, %4 offset:1024\n"
+      "ds_read_b64_tr_b16 %3, %4 offset:1536\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(vt[0][0]), "=&v"(vt[0][1]), "=&v"(vt[1][0]), "=&v"(vt[1][1])
+      : "v"(addr)
+      : "memory");
+}
+
+__device__ __forceinline__ int lds_load(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_store(int* p, int x) {
+  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Number of TPW-bit token groups (waves) with any bit set in a 16-bit token mask.
+template <int TPW>
+__device__ __forceinline__ int count_wave_groups(uint32_t m) {
+  if constexpr (TPW == 1) {
+    return __builtin_popcount(m);
+  } else if constexpr (TPW == 2) {
+    return __builtin_popcount((m | (m >> 1)) & 0x5555u);
+  } else {
+    static_assert(TPW == 4, "tokens per wave");
+    m |= m >> 1;
+    m |= m >> 2;
+    return __builtin_popcount(m & 0x1111u);
+  }
+}
+
+template <int D, int G, int NS, int NW, int TPW>
 __global__ void __launch_bounds__(64 * NW, 1)
 attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
           const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
-          uint16_t* __restrict__ out, float* __restrict__ lse, int n_items) {
+          uint16_t* __restrict__ out, float* __restrict__ lse, int n_items, int item_base) {
   constexpr int KS = D / 32;
   constexpr int NT = D / 16;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int MAT = 64 * D * 2;            // bytes of one 64-key matrix
-  constexpr int LPW = CPR / NW;              // 16-byte loads per wave per matrix
   constexpr int NTHR = 64 * NW;
   static_assert(TPW * NW == kT, "tile = waves x tokens per wave");
-  __shared__ __attribute__((aligned(16))) unsigned char ring[NSLOT][2][MAT];
+  __shared__ __attribute__((aligned(16))) unsigned char ring[NS][2][MAT];
   __shared__ uint32_t bitmap[kMaxUnion / 2];
   __shared__ uint32_t ulist[kMaxUnion];
   __shared__ int wave_tot[NW];
+  __shared__ int ready[NS];
+  __shared__ int done[NS];
 
+  // XCD-aware: workgroup b runs on XCD b % 8; the XCD's workgroups take consecutive items
   const int per_xcd = gridDim.x / 8;
-  const int item = static_cast<int>(blockIdx.x % 8) * per_xcd + static_cast<int>(blockIdx.x / 8);
+  const int item =
+      item_base + static_cast<int>(blockIdx.x % 8) * per_xcd + static_cast<int>(blockIdx.x / 8);
   if (item >= n_items) return;
   const int n_tiles = t.work_prefix[t.n];
   const int kvh = item / n_tiles;
@@ -219,38 +233,35 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   //      J = (2s + tp)*KS + ks, row 32s + 8(c16/4) + 4tp + c16%4, chunk 4ks + q4;
   //   V: unit 32*((s*NT + n)*2 + h) + 8q + 2j + a1 holds row 32s + 8q + 4h + j, chunk 2n + a1,
   //      so every transposing read of (s, n, h) covers 512 contiguous bytes.
-  const size_t rowstride = static_cast<size_t>(Hkv) * D;        // elements
-  uint32_t koff[LPW], voff[LPW];                                // element offsets in a block
-  int krow[LPW], vrow[LPW];
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int J = w * LPW + i;                                  // K: 64 units per J
-    const int s_ = J / (2 * KS), tp_ = (J / KS) % 2, ks_ = J % KS;
-    krow[i] = 32 * s_ + 8 * (c16 >> 2) + 4 * tp_ + (c16 & 3);
-    koff[i] = static_cast<uint32_t>(krow[i] * rowstride + 8 * (4 * ks_ + q4));
-    const int p = J * 64 + lane;                                // V: 32 units per group I
-    const int I = p >> 5, lo = p & 31;
-    const int h_ = I & 1, n_ = (I >> 1) % NT, sv_ = (I >> 1) / NT;
-    vrow[i] = 32 * sv_ + 8 * (lo >> 3) + 4 * h_ + ((lo >> 1) & 3);
-    voff[i] = static_cast<uint32_t>(vrow[i] * rowstride + 8 * (2 * n_ + (lo & 1)));
-  }
+  // Both offsets split into a lane part (VGPR) and a part that depends only on the load J.
+  const int rowstride = Hkv * D;                                // elements per key row
+  const int k_lrow = 8 * (c16 >> 2) + (c16 & 3);
+  const int v_lrow = 8 * ((lane & 31) >> 3) + 4 * (lane >> 5) + ((lane >> 1) & 3);
+  const int k_lane_off = k_lrow * rowstride + 8 * q4;
+  const int v_lane_off = v_lrow * rowstride + 8 * (lane & 1);
   const uint16_t* kbase = k + static_cast<size_t>(kv0) * rowstride + static_cast<size_t>(kvh) * D;
   const uint16_t* vbase = v + static_cast<size_t>(kv0) * rowstride + static_cast<size_t>(kvh) * D;
-  auto stage = [&](int u, int slot) {
+  // Loads J in [j0, CPR) step dj of union block u into ring slot `slot`.
+  auto produce = [&](int u, int slot, int j0, int dj) {
     const int key0 = __builtin_amdgcn_readfirstlane(static_cast<int>(ulist[u] >> 16)) * 64;
     const bool tail = key0 + 64 > kv_len;                       // ragged end: clamp rows
     const int last = kv_len - 1 - key0;
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      int dk = 0, dv = 0;
+    const uint16_t* kb = kbase + static_cast<size_t>(key0) * rowstride;
+    const uint16_t* vb = vbase + static_cast<size_t>(key0) * rowstride;
+    for (int J = j0; J < CPR; J += dj) {
+      const int krow0 = 32 * (J / (2 * KS)) + 4 * ((J / KS) % 2);
+      const int vrow0 = 32 * (J / NT);
+      int ko = k_lane_off + krow0 * rowstride + 32 * (J % KS);
+      int vo = v_lane_off + vrow0 * rowstride + 16 * (J % NT);
       if (tail) {
-        dk = ((krow[i] < last ? krow[i] : last) - krow[i]) * static_cast<int>(rowstride);
-        dv = ((vrow[i] < last ? vrow[i] : last) - vrow[i]) * static_cast<int>(rowstride);
+        const int kr = krow0 + k_lrow, vr = vrow0 + v_lrow;
+        ko += ((kr < last ? kr : last) - kr) * rowstride;
+        vo += ((vr < last ? vr : last) - vr) * rowstride;
       }
-      const uint16_t* gk = kbase + static_cast<size_t>(key0) * rowstride + koff[i] + dk;
-      const uint16_t* gv = vbase + static_cast<size_t>(key0) * rowstride + voff[i] + dv;
-      __builtin_amdgcn_global_load_lds(gk, (lds_void*)(&ring[slot][0][(w * LPW + i) * 1024]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(gv, (lds_void*)(&ring[slot][1][(w * LPW + i) * 1024]), 16, 0, 0);
+      const uint16_t* gk = kb + ko;
+      const uint16_t* gv = vb + vo;
+      __builtin_amdgcn_global_load_lds(gk, (lds_void*)(&ring[slot][0][J * 1024]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(gv, (lds_void*)(&ring[slot][1][J * 1024]), 16, 0, 0);
     }
   };
 
@@ -275,25 +286,48 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
         qf[tt][ks] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
     }
   }
-#pragma unroll
-  for (int u = 0; u < NSLOT - 1; ++u)
-    if (u < n_union) stage(u, u);
+  // the first NS union blocks are loaded by all waves together
+  for (int u = 0; u < NS && u < n_union; ++u) produce(u, u, w, NW);
+  if (tid < NS) {
+    ready[tid] = tid < n_union ? tid : -1;
+    done[tid] = 0;
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
   const float qscale = g.scale * kLog2e;
   const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&ring[0][0][0]));
   const uint32_t k_lane = ring_lds + 16 * lane;                                 // + slot, + 1KB*J
   const uint32_t v_lane = ring_lds + MAT + 16 * (8 * q4 + 2 * (c16 >> 2) + ((c16 & 3) >> 1)) +
                           8 * (c16 & 1);                                         // + slot, + 512*I
 
+  // ---- main loop.  Each wave walks the union list in order and works only on blocks its tokens
+  // chose.  Slot u % NS holds block u once ready[slot] == u.  The last wave to finish a block
+  // (counted in done[slot] against the number of waves that need it) refills the slot with block
+  // u + NS and publishes it after its loads have landed: right away if it is about to wait for a
+  // block itself, otherwise after its next block of work.  Every wait is bounded.
+  int pending = -1;
+  bool stalled = false;
   for (int u = 0; u < n_union; ++u) {
-    // block u landed (this wave's loads); up to NSLOT-2 later blocks stay in flight
-    wait_blocks<2 * LPW, NSLOT - 2>(n_union - 1 - u);
-    lds_barrier();
-    // every wave is past block u-1: its slot takes block u + NSLOT - 1
-    if (u + NSLOT - 1 < n_union) stage(u + NSLOT - 1, (u + NSLOT - 1) % NSLOT);
     const uint32_t ent = __builtin_amdgcn_readfirstlane(ulist[u]);
-    const int slot = u % NSLOT;
-    const int key0 = static_cast<int>(ent >> 16) * 64;
     const uint32_t wm = (ent >> (TPW * w)) & ((1u << TPW) - 1u);
+    if (wm == 0u) continue;
+    const int slot = u % NS;
+    if (lds_load(&ready[slot]) != u) {
+      if (pending >= 0) {
+        wait_vmcnt<0>();
+        lds_store(&ready[pending % NS], pending);
+        pending = -1;
+      }
+      int spins = 0;
+      while (lds_load(&ready[slot]) != u) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit) { stalled = true; break; }
+      }
+      if (stalled) break;
+    }
+    asm volatile("" ::: "memory");
+    const int key0 = static_cast<int>(ent >> 16) * 64;
     const uint32_t slot_off = static_cast<uint32_t>(slot) * (2 * MAT);
     const lds_bf16x8* Kp = (const lds_bf16x8*)(uintptr_t)(k_lane + slot_off);
     const uint32_t vaddr = v_lane + slot_off;
@@ -375,18 +409,43 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
         const bf16x2 p67 = __builtin_convertvector((f32x2){sv[s][1][2], sv[s][1][3]}, bf16x2);
         const bf16x2 pp[4] = {p01, p23, p45, p67};
         const bf16x8 pa = __builtin_bit_cast(bf16x8, pp);
-        uint64_t vt[NT][2];
-        read_v_step<NT>(vaddr + 512u * (2 * NT * s), vt);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) {
-          const uint64_t both[2] = {vt[n][0], vt[n][1]};
-          const bf16x8 vb = __builtin_bit_cast(bf16x8, both);
-          o[tt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[tt][n], 0, 0, 0);
+        for (int half = 0; half < 2; ++half) {
+          uint64_t vt[NT / 2][2];
+          read_v_half<NT / 2>(vaddr + 512u * (2 * NT * s + NT * half), vt);
+#pragma unroll
+          for (int n = 0; n < NT / 2; ++n) {
+            const uint64_t both[2] = {vt[n][0], vt[n][1]};
+            const bf16x8 vb = __builtin_bit_cast(bf16x8, both);
+            o[tt][half * (NT / 2) + n] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[tt][half * (NT / 2) + n], 0, 0, 0);
+          }
         }
       }
     }
-    // this wave's reads of the slot are complete before the next barrier lets it be refilled
     wait_lgkm0();
+    if (pending >= 0) {                      // publish the block loaded one step earlier
+      wait_vmcnt<0>();
+      lds_store(&ready[pending % NS], pending);
+      pending = -1;
+    }
+    // done accounting; the last of the block's waves refills the slot
+    const uint32_t mk = ent & 0xFFFFu;
+    const int needers = count_wave_groups<TPW>(mk);
+    int old = 0;
+    if (lane == 0) old = atomicAdd(&done[slot], 1);
+    old = __shfl(old, 0);
+    if (old + 1 == needers) {
+      if (lane == 0) lds_store(&done[slot], 0);
+      if (u + NS < n_union) {
+        produce(u + NS, slot, 0, 1);
+        pending = u + NS;
+      }
+    }
+  }
+  if (pending >= 0) {
+    wait_vmcnt<0>();
+    lds_store(&ready[pending % NS], pending);
   }
 
   // ---- epilogue: combine the 4 lanes' partial sums, normalise and store
@@ -397,6 +456,7 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
     float l = l_run[tt];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
+    if (stalled) l = __builtin_nanf("");     // never expected: flags the row instead of hanging
     const size_t orow = static_cast<size_t>(row0 + tw) * Hq + kvh * G;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -423,29 +483,53 @@ bool attn_tile_supported(const Geom& g, int dtype, const SeqTable& t) {
   return true;
 }
 
-// work_prefix of `t` must count tiles of 16 query rows per sequence.
+// Number of compute units of the current device (cached per device).
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// work_prefix of `t` must count tiles of 16 query rows per sequence.  Items are launched in
+// rounds of one workgroup per compute unit, so that the workgroups sharing an XCD start
+// together on neighbouring tiles and walk the same KV blocks at the same time (their L2 then
+// serves each block to all of them).
 hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, const void* k,
                             const void* v, const int32_t* idx, void* out, float* lse,
                             hipStream_t stream) {
   const int n_items = t.work_prefix[t.n] * g.Hkv;
   if (n_items == 0) return hipSuccess;
-  const int grid = (n_items + 7) / 8 * 8;
+  const int round = kRounds ? (device_cus() / 8) * 8 : (n_items + 7) / 8 * 8;
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   uint16_t* oo = static_cast<uint16_t*>(out);
+  for (int base = 0; base < n_items; base += round) {
+    const int grid = std::min(round, (n_items - base + 7) / 8 * 8);
 #define INFLLM2_TILE_CASE(DD, GG, NS)                                                         \
   if (g.d == DD && g.G == GG) {                                                               \
     hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWaves, kT / kWaves>), dim3(grid),              \
-                       dim3(64 * kWaves), 0, stream, g, t, qq, kk, vv, idx, oo, lse, n_items); \
-    return hipGetLastError();                                                                 \
+                       dim3(64 * kWaves), 0, stream, g, t, qq, kk, vv, idx, oo, lse, n_items, \
+                       base);                                                                 \
+    const hipError_t e = hipGetLastError();                                                   \
+    if (e != hipSuccess) return e;                                                            \
+    continue;                                                                                 \
   }
-  INFLLM2_TILE_CASE(128, 16, 4)
-  INFLLM2_TILE_CASE(128, 8, 4)
-  INFLLM2_TILE_CASE(64, 16, 8)
-  INFLLM2_TILE_CASE(64, 8, 8)
+    INFLLM2_TILE_CASE(128, 16, 4)
+    INFLLM2_TILE_CASE(128, 8, 4)
+    INFLLM2_TILE_CASE(64, 16, 8)
+    INFLLM2_TILE_CASE(64, 8, 8)
 #undef INFLLM2_TILE_CASE
-  return hipErrorInvalidValue;
+    return hipErrorInvalidValue;
+  }
+  return hipSuccess;
 }
 
 }  // namespace infllm2
