@@ -64,6 +64,8 @@ def _declare(lib):
         "infllm2_decode_workspace_size": (ctypes.c_size_t, [P, ctypes.c_int32, ctypes.c_int32]),
         "infllm2_sparse_attn_decode": (st, [P, S, vp, vp, vp, vp, ctypes.c_int32, vp,
                                             ctypes.c_size_t, vp, vp, vp]),
+        "infllm2_decode_step": (st, [P, S, vp, vp, vp, vp, _I32P, vp, ctypes.c_int32, vp,
+                                     ctypes.c_int32, vp, ctypes.c_size_t, vp, vp, vp]),
         "infllm2_status_string": (ctypes.c_char_p, [st]),
         "infllm2_last_error": (ctypes.c_char_p, []),
         "infllm2_version": (ctypes.c_int32, []),
@@ -304,3 +306,25 @@ def sparse_attn_decode(params, seqs: Seqs, q, k, v, block_idx, out, lse=None, nu
         _ptr(block_idx, "block_idx", torch.int32), int(num_splits), ws_ptr, ws_bytes,
         _ptr(out, "out", dt), _ptr(lse, "lse", torch.float32) if lse is not None else None,
         _stream(stream, q.device)), "infllm2_sparse_attn_decode")
+
+
+def decode_step_fused(params, seqs: Seqs, q, k_cache, v_cache, kernels, prev_kv_len, scores,
+                      block_idx, out, lse, workspace, num_splits=0, stream=None):
+    """infllm2_decode_step: the four decode stages in one library call."""
+    p = Params.from_any(params)
+    lib = load_library()
+    dt = _elem_dtype(p)
+    torch = _torch()
+    prev = None
+    if prev_kv_len is not None:
+        prev_arr = np.ascontiguousarray(prev_kv_len, dtype=np.int32)
+        prev = prev_arr.ctypes.data_as(_I32P)
+    cp, cs = p.c(), seqs.c()
+    _check(lib.infllm2_decode_step(
+        ctypes.byref(cp), ctypes.byref(cs), _ptr(q, "q", dt), _ptr(k_cache, "k_cache", dt),
+        _ptr(v_cache, "v_cache", dt), _ptr(kernels, "kernels", dt), prev,
+        _ptr(scores, "scores", torch.float32, 3), int(scores.shape[2]),
+        _ptr(block_idx, "block_idx", torch.int32), int(num_splits), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _ptr(out, "out", dt),
+        _ptr(lse, "lse", torch.float32) if lse is not None else None,
+        _stream(stream, q.device)), "infllm2_decode_step")

@@ -224,17 +224,16 @@ infllm2_status infllm2_block_scores(const infllm2_params* params, const infllm2_
     for (int b = 0; b < t.n; ++b) tiles64 += (t.q_len[b] + 63) / 64;
     const bool decode_like = tiles64 * g.Hkv < 512;
     range_tiles = decode_like ? 16 : (1 << 28);
-    const int rows_per_tile = decode_like ? 16 : 64;
-    int acc = 0;
-    for (int b = 0; b < t.n; ++b) {
-      t.work_prefix[b] = acc;
-      if (t.q_len[b] == 0) continue;
-      const int pos_last = t.q_pos0[b] + t.q_len[b] - 1;
-      const int nbt = (pos_last / 64 + 1 + 3) / 4;
-      const int chunks = (nbt + range_tiles - 1) / range_tiles;
-      acc += ((t.q_len[b] + rows_per_tile - 1) / rows_per_tile) * chunks;
+    if (decode_like) {
+      rows_prefix(&t);
+    } else {
+      int acc = 0;
+      for (int b = 0; b < t.n; ++b) {
+        t.work_prefix[b] = acc;
+        acc += (t.q_len[b] + 63) / 64;
+      }
+      t.work_prefix[t.n] = acc;
     }
-    t.work_prefix[t.n] = acc;
   }
   return hip_status(infllm2::launch_scores(g, params->dtype, t, q, kernels, scores, nb_stride,
                                            range_tiles, static_cast<hipStream_t>(stream)),
@@ -305,12 +304,23 @@ infllm2_status infllm2_sparse_attn_prefill(const infllm2_params* params,
                     "sparse_attn_prefill launch");
 }
 
+static int decode_splits(const Geom& g, int dtype, int rows, int num_splits) {
+  if (num_splits > 0) return num_splits;
+  if (infllm2::attn_decode_supported(g, dtype)) return (g.topk + 3) / 4;
+  return auto_splits(g, rows);
+}
+
+static size_t decode_ws_bytes(const Geom& g, int rows, int splits) {
+  // partials (m, l, O[d]) per (row, query head, split), then one counter per (row, kv head)
+  return static_cast<size_t>(rows) * g.Hq * splits * (2 + g.d) * sizeof(float) +
+         static_cast<size_t>(rows) * g.Hkv * sizeof(int);
+}
+
 size_t infllm2_decode_workspace_size(const infllm2_params* params, int32_t total_q_rows,
                                      int32_t num_splits) {
   Geom g;
   if (check_params(params, &g) != INFLLM2_OK || total_q_rows < 0 || num_splits < 0) return 0;
-  const int splits = num_splits > 0 ? num_splits : auto_splits(g, total_q_rows);
-  return static_cast<size_t>(total_q_rows) * g.Hq * splits * (2 + g.d) * sizeof(float);
+  return decode_ws_bytes(g, total_q_rows, decode_splits(g, params->dtype, total_q_rows, num_splits));
 }
 
 infllm2_status infllm2_sparse_attn_decode(const infllm2_params* params, const infllm2_seqs* seqs,
@@ -325,8 +335,8 @@ infllm2_status infllm2_sparse_attn_decode(const infllm2_params* params, const in
   if (num_splits < 0 || num_splits > g.topk)
     return fail(INFLLM2_ERR_SHAPE, "num_splits %d outside 0..topk", num_splits);
   const int rows = t.work_prefix[t.n];
-  const int splits = num_splits > 0 ? num_splits : auto_splits(g, rows);
-  const size_t need = static_cast<size_t>(rows) * g.Hq * splits * (2 + g.d) * sizeof(float);
+  const int splits = decode_splits(g, params->dtype, rows, num_splits);
+  const size_t need = decode_ws_bytes(g, rows, splits);
   if (splits > 1) {
     if (workspace == nullptr) return fail(INFLLM2_ERR_NULL, "workspace is NULL");
     if (!aligned16(workspace)) return fail(INFLLM2_ERR_ALIGN, "workspace must be 16-byte aligned");
@@ -334,12 +344,32 @@ infllm2_status infllm2_sparse_attn_decode(const infllm2_params* params, const in
       return fail(INFLLM2_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
   }
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (infllm2::attn_decode_supported(g, params->dtype))
+    return hip_status(infllm2::launch_attn_decode(g, t, q, k, v, block_idx, splits, workspace, out,
+                                                  lse, s),
+                      "sparse_attn_decode launch");
   hipError_t e = infllm2::launch_attn(g, params->dtype, t, q, k, v, block_idx, splits, out, lse,
                                       static_cast<float*>(workspace), s);
   if (e != hipSuccess || splits == 1) return hip_status(e, "sparse_attn_decode launch");
   return hip_status(infllm2::launch_attn_combine(g, params->dtype, t, splits,
                                                  static_cast<const float*>(workspace), out, lse, s),
                     "sparse_attn_decode combine launch");
+}
+
+infllm2_status infllm2_decode_step(const infllm2_params* params, const infllm2_seqs* seqs,
+                                  const void* q, const void* k_cache, const void* v_cache,
+                                  void* kernels, const int32_t* prev_kv_len, float* scores,
+                                  int32_t nb_stride, int32_t* block_idx, int32_t num_splits,
+                                  void* workspace, size_t workspace_bytes, void* out, float* lse,
+                                  void* stream) {
+  infllm2_status st = infllm2_compress_kernels(params, seqs, k_cache, prev_kv_len, kernels, stream);
+  if (st != INFLLM2_OK) return st;
+  st = infllm2_block_scores(params, seqs, q, kernels, scores, nb_stride, stream);
+  if (st != INFLLM2_OK) return st;
+  st = infllm2_topk_select(params, seqs, scores, nb_stride, block_idx, stream);
+  if (st != INFLLM2_OK) return st;
+  return infllm2_sparse_attn_decode(params, seqs, q, k_cache, v_cache, block_idx, num_splits,
+                                    workspace, workspace_bytes, out, lse, stream);
 }
 
 }  // extern "C"

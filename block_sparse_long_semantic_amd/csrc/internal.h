@@ -73,6 +73,12 @@ bool attn_tile_supported(const Geom& g, int dtype, const SeqTable& t);
 hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, const void* k,
                             const void* v, const int32_t* idx, void* out, float* lse,
                             hipStream_t stream);
+// Split-KV decoding attention with the merge done by the last workgroup of each (row, kv head).
+bool attn_decode_supported(const Geom& g, int dtype);
+size_t attn_decode_workspace(const Geom& g, int rows, int nsplit);
+hipError_t launch_attn_decode(const Geom& g, const SeqTable& t, const void* q, const void* k,
+                              const void* v, const int32_t* idx, int nsplit, void* workspace,
+                              void* out, float* lse, hipStream_t stream);
 hipError_t launch_attn_combine(const Geom& g, int dtype, const SeqTable& t, int splits,
                                const float* part, void* out, float* lse, hipStream_t stream);
 

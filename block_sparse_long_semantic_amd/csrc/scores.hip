@@ -11,6 +11,8 @@
 //                  is exactly one block's four contained kernels for one query row; the
 //                  fifth (halo) kernel 4b-1 comes from the neighbouring lane group.
 //   * scores_simple any dtype and geometry, plain float32 dot products.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace infllm2 {
@@ -73,8 +75,8 @@ scores_simple(Geom g, SeqTable t, const T* __restrict__ q, const T* __restrict__
 // ------------------------------------------------------------------------------ MFMA path
 // Work item = (sequence, tile of 16*WR query rows, chunk of `range_tiles` kernel tiles); the
 // 4 waves are WR row groups x (4/WR) kernel sub-ranges.  A kernel tile is 16 kernels = 4
-// blocks.  Prefill uses WR = 4 and one chunk per row tile; decode-like launches (few rows)
-// use WR = 1 and split the kernel range over chunks and waves.
+// blocks.  Prefill uses WR = 4 and one chunk per row tile (decode-like launches with few
+// rows go to scores_decode below instead).
 template <int D, int WR>
 __global__ void __launch_bounds__(kThreads)
 scores_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
@@ -188,6 +190,82 @@ scores_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
   }
 }
 
+
+// ------------------------------------------------------------------------------ decode path
+// Few query rows (decoding): the work is streaming every semantic kernel of the sequence once,
+// so it is spread over chunks of 64 blocks (256 kernels + the halo kernel before them) per
+// workgroup.  The group-summed query stays in float32; each kernel row is read by D/8 lanes
+// (16 bytes each, one coalesced row per lane group), dotted with float32 FMAs and reduced with
+// lane shuffles.  Kernel scores go to LDS, then 64 threads max-pool them onto the chunk's
+// blocks and write one coalesced row segment.
+template <int D>
+__global__ void __launch_bounds__(kThreads)
+scores_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q,
+              const uint16_t* __restrict__ kern, float* __restrict__ scores, int nb_stride) {
+  constexpr int LPR = D / 8;              // lanes per kernel row
+  constexpr int RPI = 64 / LPR;           // rows per wave instruction
+  constexpr int NROW = 257;               // kernels c0-1 .. c0+255
+  __shared__ float qs[D];
+  __shared__ float u[NROW + 3];
+  const int chunk = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int vrow = blockIdx.z;
+  const int b = find_seq(t, vrow);
+  const int j = vrow - t.work_prefix[b];
+  const int row = t.q_start[b] + j;
+  const int pos = t.q_pos0[b] + j;
+  const int own = pos / 64;
+  const int blk0 = chunk * 64;
+  if (blk0 > own) return;                 // whole workgroup
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  for (int e = tid; e < D; e += kThreads) {
+    float acc = 0.f;
+    for (int h = 0; h < g.G; ++h)
+      acc += bf16_to_f32(q[(static_cast<size_t>(row) * g.Hq + kvh * g.G + h) * D + e]);
+    qs[e] = acc;
+  }
+  __syncthreads();
+  const int C = num_kernels(t.kv_len[b], g.w, g.s);
+  const int c0 = 4 * blk0;
+  const int col = (lane % LPR) * 8;
+  float qv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qv[e] = qs[col + e];
+  const size_t kbase = static_cast<size_t>(t.kc_start[b]) * g.Hkv * D + static_cast<size_t>(kvh) * D;
+  constexpr int NIT = (NROW + RPI - 1) / RPI;
+  for (int it = w; it < NIT; it += kThreads / 64) {
+    const int r = it * RPI + lane / LPR;                   // 0 .. NROW-1 (+ padding)
+    const int c = c0 - 1 + r;
+    const bool ok = r < NROW && c >= 0 && c < C && 16 * c + 31 <= pos;
+    float dot = 0.f;
+    if (ok) {
+      const uint4 v = *reinterpret_cast<const uint4*>(kern + kbase + static_cast<size_t>(c) * g.Hkv * D + col);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dot = fmaf(__uint_as_float(w4[e] << 16), qv[2 * e], dot);
+        dot = fmaf(__uint_as_float(w4[e] & 0xFFFF0000u), qv[2 * e + 1], dot);
+      }
+    }
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
+    if (lane % LPR == 0 && r < NROW) u[r] = ok ? dot : -INFINITY;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int blk = blk0 + tid;
+    if (blk <= own) {
+      // block blk's kernels 4blk-1 .. 4blk+3 sit at u[4*tid .. 4*tid+4]
+      float best = u[4 * tid];
+#pragma unroll
+      for (int e = 1; e < 5; ++e) best = fmaxf(best, u[4 * tid + e]);
+      scores[(static_cast<size_t>(row) * g.Hkv + kvh) * nb_stride + blk] = best * g.scale;
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_scores(const Geom& g, int dtype, const SeqTable& t, const void* q,
@@ -210,28 +288,37 @@ hipError_t launch_scores(const Geom& g, int dtype, const SeqTable& t, const void
                          nb_stride);
     return hipGetLastError();
   }
+  const bool decode_like = range_tiles > 0 && range_tiles < (1 << 28);
+  if (decode_like) {
+    // work_prefix counts query rows; one workgroup per (64-block chunk, kv head, row)
+    const int rows = t.work_prefix[t.n];
+    if (rows == 0) return hipSuccess;
+    int max_blocks = 0;
+    for (int b = 0; b < t.n; ++b)
+      if (t.q_len[b] > 0) max_blocks = std::max(max_blocks, (t.q_pos0[b] + t.q_len[b] - 1) / 64 + 1);
+    const dim3 grid((max_blocks + 63) / 64, g.Hkv, rows);
+    if (g.d == 128)
+      hipLaunchKernelGGL(scores_decode<128>, grid, dim3(kThreads), 0, stream, g, t,
+                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kernels),
+                         scores, nb_stride);
+    else
+      hipLaunchKernelGGL(scores_decode<64>, grid, dim3(kThreads), 0, stream, g, t,
+                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kernels),
+                         scores, nb_stride);
+    return hipGetLastError();
+  }
   // work_prefix counts (row tile x kernel chunk) items, built by the caller for this mode.
   const int items = t.work_prefix[t.n];
   if (items == 0) return hipSuccess;
   const dim3 grid(items, g.Hkv);
-  const bool decode_like = range_tiles > 0 && range_tiles < (1 << 28);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(kernels);
-  if (g.d == 128) {
-    if (decode_like)
-      hipLaunchKernelGGL((scores_mfma<128, 1>), grid, dim3(kThreads), 0, stream, g, t, qq, kk,
-                         scores, nb_stride, range_tiles);
-    else
-      hipLaunchKernelGGL((scores_mfma<128, 4>), grid, dim3(kThreads), 0, stream, g, t, qq, kk,
-                         scores, nb_stride, 1 << 28);
-  } else {
-    if (decode_like)
-      hipLaunchKernelGGL((scores_mfma<64, 1>), grid, dim3(kThreads), 0, stream, g, t, qq, kk,
-                         scores, nb_stride, range_tiles);
-    else
-      hipLaunchKernelGGL((scores_mfma<64, 4>), grid, dim3(kThreads), 0, stream, g, t, qq, kk,
-                         scores, nb_stride, 1 << 28);
-  }
+  if (g.d == 128)
+    hipLaunchKernelGGL((scores_mfma<128, 4>), grid, dim3(kThreads), 0, stream, g, t, qq, kk,
+                       scores, nb_stride, 1 << 28);
+  else
+    hipLaunchKernelGGL((scores_mfma<64, 4>), grid, dim3(kThreads), 0, stream, g, t, qq, kk,
+                       scores, nb_stride, 1 << 28);
   return hipGetLastError();
 }
 

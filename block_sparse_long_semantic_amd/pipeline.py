@@ -9,8 +9,8 @@ from __future__ import annotations
 
 from typing import Dict, Optional
 
-from ._lib import (BF16, Params, Seqs, block_scores, compress_kernels, decode_workspace_size,
-                   sparse_attn_decode, sparse_attn_prefill, topk_select)
+from ._lib import (BF16, Params, Seqs, block_scores, compress_kernels, decode_step_fused,
+                   decode_workspace_size, sparse_attn_decode, sparse_attn_prefill, topk_select)
 
 
 def num_kernels(length: int, kernel_size: int, kernel_stride: int) -> int:
@@ -73,7 +73,8 @@ def decode_buffers(params, batch: int, num_blocks: int, num_splits: int, device)
         idx=torch.empty((batch, p.num_kv_heads, p.topk), dtype=torch.int32, device=device),
         out=torch.empty((batch, p.num_q_heads, p.head_dim), dtype=_dtype(p), device=device),
         lse=torch.empty((batch, p.num_q_heads), dtype=torch.float32, device=device),
-        workspace=torch.empty((max(1, ws // 4),), dtype=torch.float32, device=device),
+        # partials + completion counters; must start zero-filled (calls leave it zeroed)
+        workspace=torch.zeros((max(1, ws // 4),), dtype=torch.float32, device=device),
         num_splits=num_splits,
     )
 
@@ -83,6 +84,15 @@ def decode_step(params, seqs: Seqs, q, k_cache, v_cache, kernels_cache, prev_kv_
     """One decode step for a batch: q [batch, Hq, d]; caches [batch*max_len, Hkv, d] (padded);
     kernels_cache [batch*max_kernels, Hkv, d]; seqs from Seqs.decode(kv_len, ...), where kv_len
     already counts the new token.  prev_kv_len: lengths when kernels_cache was last updated."""
+    decode_step_fused(params, seqs, q, k_cache, v_cache, kernels_cache, prev_kv_len,
+                      bufs["scores"], bufs["idx"], bufs["out"], bufs["lse"], bufs["workspace"],
+                      num_splits=bufs["num_splits"], stream=stream)
+    return bufs
+
+
+def decode_step_staged(params, seqs: Seqs, q, k_cache, v_cache, kernels_cache, prev_kv_len,
+                       bufs: Dict[str, object], stream=None) -> Dict[str, object]:
+    """The same step as four separate library calls."""
     p = Params.from_any(params)
     compress_kernels(p, seqs, k_cache, kernels_cache, prev_kv_len=prev_kv_len, stream=stream)
     block_scores(p, seqs, q, kernels_cache, bufs["scores"], stream=stream)

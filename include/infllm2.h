@@ -141,7 +141,9 @@ infllm2_status infllm2_sparse_attn_prefill(const infllm2_params* params,
                                            void* stream);
 
 /* Bytes of device workspace infllm2_sparse_attn_decode needs for `total_q_rows` query rows
- * (sum of q_len) split `num_splits` ways (0 = the automatic choice). */
+ * (sum of q_len) split `num_splits` ways (0 = the automatic choice).  The workspace holds the
+ * per-split partial results and one completion counter per (row, KV head): it must be
+ * zero-filled before its first use, and every call leaves it zero-filled again. */
 size_t infllm2_decode_workspace_size(const infllm2_params* params, int32_t total_q_rows,
                                      int32_t num_splits);
 
@@ -154,6 +156,18 @@ infllm2_status infllm2_sparse_attn_decode(const infllm2_params* params, const in
                                           const int32_t* block_idx, int32_t num_splits,
                                           void* workspace, size_t workspace_bytes, void* out,
                                           float* lse, void* stream);
+
+/* One decoding step, the calls above chained on `stream` in the method's order: semantic
+ * kernels completed since prev_kv_len (host array, may be NULL), block scores into `scores`
+ * (nb_stride floats per (row, KV head)), top-k into block_idx, then split-KV attention.
+ * Arguments mean what they mean in those calls; the first failing call's status is returned
+ * and nothing after it is enqueued. */
+infllm2_status infllm2_decode_step(const infllm2_params* params, const infllm2_seqs* seqs,
+                                  const void* q, const void* k_cache, const void* v_cache,
+                                  void* kernels, const int32_t* prev_kv_len, float* scores,
+                                  int32_t nb_stride, int32_t* block_idx, int32_t num_splits,
+                                  void* workspace, size_t workspace_bytes, void* out, float* lse,
+                                  void* stream);
 
 /* Static text for a status code. */
 const char* infllm2_status_string(infllm2_status status);

@@ -19,7 +19,7 @@ def so():
 
 
 def test_library_exports_every_declared_symbol(so):
-    assert len(lib.EXPORTED_SYMBOLS) == 9
+    assert len(lib.EXPORTED_SYMBOLS) == 10
     for name in lib.EXPORTED_SYMBOLS:
         assert hasattr(so, name), name
     assert lib.version() == 100
@@ -143,9 +143,12 @@ def test_incremental_range_checked(so):
 def test_decode_workspace(so):
     p = params()
     d = p.head_dim
-    assert lib.decode_workspace_size(p, 8, 12) == 8 * 32 * 12 * (2 + d) * 4
+    # per (row, query head, split): running max, denominator and d partial outputs (float32),
+    # then one int32 completion counter per (row, KV head)
+    counters = 8 * p.num_kv_heads * 4
+    assert lib.decode_workspace_size(p, 8, 12) == 8 * 32 * 12 * (2 + d) * 4 + counters
     auto = lib.decode_workspace_size(p, 8, 0)
-    assert auto > 0 and auto % (8 * 32 * (2 + d) * 4) == 0
+    assert auto > counters and (auto - counters) % (8 * 32 * (2 + d) * 4) == 0
     cp, cs = p.c(), seqs(q_len=[1], q_pos0=[99]).c()
     st = so.infllm2_sparse_attn_decode(ctypes.byref(cp), ctypes.byref(cs), FAKE, FAKE, FAKE, FAKE,
                                        4, FAKE, 16, FAKE, None, None)

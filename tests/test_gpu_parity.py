@@ -130,7 +130,8 @@ def test_results_are_deterministic():
 
 # ------------------------------------------------------------------------- decode
 
-def run_decode(wl, steps, num_splits=0, check=True, label="decode"):
+def run_decode(wl, steps, num_splits=0, check=True, label="decode", step_fn=None):
+    step_fn = step_fn or lib.decode_step
     p = wl.params
     B, Lmax = wl.batch, wl.max_len
     Ck = orc.num_kernels(Lmax, p.kernel_size, p.kernel_stride)
@@ -150,7 +151,7 @@ def run_decode(wl, steps, num_splits=0, check=True, label="decode"):
         kv = kv0 + st + 1
         seqs = lib.Seqs.decode(kv, Lmax, max(Ck, 1))
         q = dev(wl.q_steps[st], p.dtype)
-        lib.decode_step(p, seqs, q, k, v, kern, prev.astype(np.int32), bufs)
+        step_fn(p, seqs, q, k, v, kern, prev.astype(np.int32), bufs)
         torch.cuda.synchronize()
         prev = kv.copy()
         outs.append({n: host(bufs[n]) for n in ("scores", "idx", "out", "lse")})
@@ -246,3 +247,18 @@ def test_full_size_decode():
     wl = synth.make("decode128k", steps=2)
     log("case full decode128k")
     run_decode(wl, 2, label="full decode")
+
+
+def test_decode_fused_call_matches_staged_calls():
+    p = synth.config_params("decode128k")
+    wl = synth.make_decode("dec-fused", p, batch=4, max_len=4096, steps=2, seed=44,
+                           kv_len0=[4000, 2500, 1000, 64])
+    log("case decode fused vs staged")
+    fused = run_decode(wl, 2, check=False)
+    staged = run_decode(wl, 2, check=False, step_fn=lib.pipeline.decode_step_staged)
+    for st, (a, b) in enumerate(zip(fused, staged)):
+        for n in ("idx", "out", "lse"):
+            assert np.array_equal(a[n], b[n]), n
+        for r in range(wl.batch):   # scores past the query's own block are left unwritten
+            nb = (int(wl.kv_len0[r]) + st) // p.block_size + 1
+            assert np.array_equal(a["scores"][r, :, :nb], b["scores"][r, :, :nb])
