@@ -13,6 +13,9 @@ consecutive steps with incremental kernel updates), the roofline of the dominant
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -27,6 +30,9 @@ sys.path.insert(0, ROOT)
 METRIC = "sparse-attn prefill tokens/s @128K + decode µs/token; % MFMA/HBM roofline"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+TILE_TOKENS = 16          # query tokens per attention work item
+ATTN_SOURCES = ["block_sparse_long_semantic_amd/csrc/attn_tile.hip",
+                "block_sparse_long_semantic_amd/csrc/internal.h"]
 
 
 def log(msg):
@@ -79,6 +85,8 @@ def run_prefill(args, torch, pkg, synth):
         step(evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration)
     names = ["compress", "scores", "topk", "attention"]
     stage = {n: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
              for i, n in enumerate(names)}
@@ -93,15 +101,55 @@ def run_prefill(args, torch, pkg, synth):
     bytes_scores = T * Hq * d * 2 + C * Hkv * d * 2 + causal_blocks * Hkv * 4
     bytes_topk = causal_blocks * Hkv * 4 + T * Hkv * p.topk * 4
     bytes_compress = T * Hkv * d * 2 + C * Hkv * d * 2
+    # the attention call launches its tiles in rounds of one workgroup per compute unit
+    items = sum((L + TILE_TOKENS - 1) // TILE_TOKENS for L in lens) * Hkv
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    launches = (items + cus // 8 * 8 - 1) // (cus // 8 * 8)
     result = dict(
         workload=args.workload, tokens=T, seq_lens=lens, p=p, ms_step=ms_step, stage=stage,
-        flops=flops, tflops=tflops, keys=keys,
+        flops=flops, tflops=tflops, keys=keys, launches=launches,
         stage_gbs={"compress": bytes_compress / (stage["compress"] * 1e-3) / 1e9,
                    "scores": bytes_scores / (stage["scores"] * 1e-3) / 1e9,
                    "topk": bytes_topk / (stage["topk"] * 1e-3) / 1e9},
         wl=wl, kernels_gpu=bufs["kernels"])
     del q, k, v, bufs
     return result
+
+
+def copy_calibration(torch, mib: int):
+    """A plain streaming kernel of known traffic (read mib MiB, write mib MiB), for scaling the
+    FETCH_SIZE / WRITE_SIZE counters: out = -in over bf16 elements."""
+    n = (mib << 20) // 2
+    src = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {mib} MiB read + {mib} MiB written")
+    del src, dst
+
+
+def source_digest(paths) -> str:
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention call from the committed counter summary, or None when there is
+    none for this workload or the kernel's source has changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"attn_tile_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("bench-data: "):
+                rec = json.loads(line[len("bench-data: "):])
+                if rec.get("source_sha256") != source_digest(ATTN_SOURCES):
+                    return None
+                return rec
+    return None
 
 
 def run_decode(args, torch, pkg, synth):
@@ -174,9 +222,10 @@ def cpu_baseline(pre, budget_s: float):
     t_comp = time.perf_counter() - t0
     global _CPU_STATE
     _CPU_STATE = (wl.q[sl_q], wl.k[sl_k], wl.v[sl_k], p, kern)
-    n_rows = 64 * workers
-    rows = np.linspace(0, L - 1, n_rows).astype(np.int64)
-    chunks = np.array_split(rows, workers * 4)
+    # chunk c holds rows c, c + n_chunks, ...: every chunk spans the whole sequence, so the
+    # chunks finished within the budget are an evenly spread sample of its rows
+    n_chunks = max(1, L // 8)
+    chunks = (np.arange(c, L, n_chunks) for c in range(n_chunks))
     ctx = mp.get_context("fork")
     with ctx.Pool(workers, initializer=_limit_threads) as pool:
         t1 = time.perf_counter()
@@ -190,8 +239,10 @@ def cpu_baseline(pre, budget_s: float):
     tok_s = L / (t_comp + per_row * L)
     return {"value": tok_s, "unit": "tokens/s", "cores": workers, "kind": "oracle",
             "sample": f"{args_workload_name(pre)}: full kernel compression ({t_comp:.1f} s) + "
-                      f"scores/top-k/attention for {done} of {L} query rows evenly spaced over "
-                      f"the sequence ({t_rows:.1f} s on {workers} processes), float64 numpy"}
+                      f"block scores, top-k and attention for {done} of {L} query rows spread evenly "
+                      f"over the sequence ({t_rows:.1f} s on {workers} single-threaded "
+                      f"processes), float64 numpy; tokens/s = L / (compression + L x mean "
+                      f"time per row)"}
 
 
 def args_workload_name(pre):
@@ -216,6 +267,73 @@ def _cpu_rows(rows):
     return len(rows)
 
 
+def _short(name: str) -> str:
+    name = name.replace("infllm2::(anonymous namespace)::", "")
+    cut = name.find("(")
+    head = name[:cut] if cut > 0 else name
+    if head.startswith("void "):
+        head = head[5:]
+    return head[:90]
+
+
+def _csv_rows(directory: str, suffix: str):
+    files = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    with open(files[0], newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profile(argv):
+    """Markdown summary of rocprofv3 output (kernel statistics, or per-kernel HBM traffic from
+    a FETCH_SIZE run and a WRITE_SIZE run scaled by the copy-calibration kernel)."""
+    if argv[0] == "stats":
+        rows = _csv_rows(argv[1], "kernel_stats.csv")
+        print("| kernel | calls | total ms | avg us | min us | max us | % |")
+        print("|---|---:|---:|---:|---:|---:|---:|")
+        for r in rows[:12]:
+            print(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} "
+                  f"| {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} "
+                  f"| {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+        return
+    if argv[0] != "traffic" or len(argv) != 5:
+        raise SystemExit("usage: --summarize-profile traffic FETCH_DIR WRITE_DIR WORKLOAD MIB")
+    fetch_dir, write_dir, workload, mib = argv[1], argv[2], argv[3], int(argv[4])
+    per = {}
+    for key, directory, counter in (("fetch", fetch_dir, "FETCH_SIZE"),
+                                    ("write", write_dir, "WRITE_SIZE")):
+        for r in _csv_rows(directory, "counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            k = _short(r["Kernel_Name"])
+            d = per.setdefault(k, {"fetch": [], "write": []})
+            d[key].append(float(r["Counter_Value"]) * 1024.0)      # counters are in KiB
+    copy = [k for k in per if "neg_kernel" in k]
+    if not copy:
+        raise SystemExit("no copy-calibration kernel in the counter output")
+    known = float(mib << 20)
+    cf = per[copy[0]]
+    f_fetch = known / cf["fetch"][-1]
+    f_write = known / cf["write"][-1]
+    print(f"copy calibration kernel `{copy[0]}`: {mib} MiB read and written; FETCH_SIZE read "
+          f"{cf['fetch'][-1] / 2**20:.1f} MiB (factor {f_fetch:.4f}), WRITE_SIZE "
+          f"{cf['write'][-1] / 2**20:.1f} MiB (factor {f_write:.4f})\n")
+    print("| kernel | dispatches | FETCH MiB (scaled) | WRITE MiB (scaled) |")
+    print("|---|---:|---:|---:|")
+    for k, d in sorted(per.items(), key=lambda kv: -sum(kv[1]["fetch"])):
+        print(f"| `{k}` | {len(d['fetch'])} | {sum(d['fetch']) * f_fetch / 2**20:.1f} "
+              f"| {sum(d['write']) * f_write / 2**20:.1f} |")
+    attn = [k for k in per if k.startswith("attn_tile")]
+    if attn:
+        d = per[attn[0]]
+        rec = {"kernel": attn[0], "workload": workload,
+               "source_sha256": source_digest(ATTN_SOURCES),
+               "fetch_bytes_per_call": sum(d["fetch"]) * f_fetch,
+               "write_bytes_per_call": sum(d["write"]) * f_write,
+               "dispatches_per_call": len(d["fetch"])}
+        print("\nbench-data: " + json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,7 +345,16 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a streaming copy of MIB MiB (counter calibration)")
+    ap.add_argument("--summarize-profile", nargs="+", metavar="ARG",
+                    help="stats DIR | traffic FETCH_DIR WRITE_DIR WORKLOAD MIB: print a "
+                         "summary of rocprofv3 csv output and exit (the traffic runs must "
+                         "time one step with no warmup and --copy-calibration MIB)")
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -262,11 +389,19 @@ def main():
         "stages_ms": st,
         "stages_gbs": pre["stage_gbs"],
         "attention_tokens_per_s": pre["tokens"] / (st["attention"] * 1e-3),
-        "roofline": {"kernel": "sparse_attn_prefill", "bound": "mfma",
+        "roofline": {"kernel": "attn_tile (sparse_attn_prefill)", "bound": "mfma",
                      "achieved": pre["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": pre["tflops"] / PEAK_BF16_TFLOPS, "traffic": None,
-                     "flops_per_launch": pre["flops"], "keys_per_head": pre["keys"]},
+                     "flops_per_call": pre["flops"], "keys_per_head": pre["keys"],
+                     "launches_per_call": pre["launches"],
+                     "avg_launch_us": st["attention"] * 1e3 / pre["launches"]},
     }
+    tr = measured_traffic(pre["workload"])
+    if tr is not None:
+        line["roofline"]["traffic"] = tr["fetch_bytes_per_call"] + tr["write_bytes_per_call"]
+        line["roofline"]["traffic_split"] = {"fetch": tr["fetch_bytes_per_call"],
+                                             "write": tr["write_bytes_per_call"],
+                                             "unit": "bytes per call"}
     if not args.no_decode:
         line["decode"] = run_decode(args, torch, pkg, synth)
         log(f"decode: {line['decode']['us_per_step']:.1f} us/step")
