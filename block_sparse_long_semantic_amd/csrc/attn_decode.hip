@@ -4,10 +4,11 @@
 // A decoding batch has one (or a few) query rows per sequence, so the selected blocks of a
 // row are spread over many workgroups: workgroup (row, kv head, split) owns a contiguous range
 // of the row's block list, and each of its 4 waves takes every 4th block of that range.  A wave
-// loads its block's K and V straight into its own LDS slot with global_load_lds (same operand
-// orders as the prefill kernel: K lane-contiguous per MFMA step, V for transposing reads) and
-// folds it into a running (max, sum, output) for the 16 stacked heads of the group.  The 4
-// waves then merge through LDS, and the workgroup writes its partial.  The last workgroup of a
+// loads its block's K straight into registers, already in MFMA A-operand order (16 bytes per
+// lane per step), and its block's V into its own LDS slot with global_load_lds, in the order the
+// transposing LDS reads need; it folds the block into a running (max, sum, output) for the 16
+// stacked heads of the group.  The 4 waves then merge through LDS, and the workgroup writes its
+// partial.  The last workgroup of a
 // (row, kv head) to finish -- counted with an agent-scope atomic in the workspace -- merges all
 // partials by log-sum-exp and writes the output, so no separate combine launch is needed.  It
 // resets the counter, leaving the workspace ready for the next call.
@@ -50,16 +51,32 @@ __device__ __forceinline__ void read_v8(uint32_t addr, uint64_t (&vt)[4][2]) {
       : "memory");
 }
 
-// Workspace: partial (m, l, O[d]) per (row, kv head, split, head of group), then counters.
+__device__ __forceinline__ uint64_t pack2(float a, float b) {
+  return static_cast<uint64_t>(__float_as_uint(a)) | (static_cast<uint64_t>(__float_as_uint(b)) << 32);
+}
+__device__ __forceinline__ float lo_f32(uint64_t v) { return __uint_as_float(static_cast<uint32_t>(v)); }
+__device__ __forceinline__ float hi_f32(uint64_t v) { return __uint_as_float(static_cast<uint32_t>(v >> 32)); }
+__device__ __forceinline__ void agent_store(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t agent_load(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workspace: partial outputs O[d] per (row, kv head, split, head of group), then the partial
+// (max, sum) pairs in the same order, then one counter per (row, kv head).
 struct DecodeWs {
-  float* part;
+  float* part_o;
+  float* part_ml;
   int* count;
 };
 
 __device__ __forceinline__ DecodeWs ws_of(void* ws, int rows, int Hkv, int nsplit, int G, int D) {
   DecodeWs w;
-  w.part = static_cast<float*>(ws);
-  w.count = reinterpret_cast<int*>(w.part + static_cast<size_t>(rows) * Hkv * nsplit * G * (D + 2));
+  const size_t n = static_cast<size_t>(rows) * Hkv * nsplit * G;
+  w.part_o = static_cast<float*>(ws);
+  w.part_ml = w.part_o + n * D;
+  w.count = reinterpret_cast<int*>(w.part_ml + n * 2);
   return w;
 }
 
@@ -71,8 +88,8 @@ attn_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* 
   constexpr int KS = D / 32;
   constexpr int NT = D / 16;
   constexpr int CPR = D / 8;
-  constexpr int MAT = 64 * D * 2;
-  __shared__ __attribute__((aligned(16))) unsigned char ring[kWaves][2][MAT];
+  constexpr int MAT = 64 * D * 2;                          // one block of V
+  __shared__ __attribute__((aligned(16))) unsigned char ring[kWaves][MAT];
   __shared__ float wm_s[kWaves][16], wl_s[kWaves][16];
   __shared__ int s_last;
 
@@ -95,14 +112,15 @@ attn_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* 
   const int rowstride = Hkv * D;
 
   const int32_t* sel = idx + (static_cast<size_t>(row) * Hkv + kvh) * g.topk;
+  // the valid entries form a prefix (ascending, then -1): count them with ballots
   int nsel = 0;
-  {
-    int lo = 0, hi = g.topk;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (sel[mid] >= 0) lo = mid + 1; else hi = mid;
-    }
-    nsel = lo;
+  for (int base = 0; base < g.topk; base += 128) {
+    const int e0 = base + lane, e1 = base + 64 + lane;
+    const bool v0 = e0 < g.topk && sel[e0] >= 0;
+    const bool v1 = e1 < g.topk && sel[e1] >= 0;
+    const unsigned long long m1 = __ballot(v1);
+    nsel += __popcll(__ballot(v0)) + __popcll(m1);
+    if (~m1 != 0ull) break;
   }
   const int per = (nsel + nsplit - 1) / nsplit;
   const int k_begin = min(nsel, sp * per);
@@ -129,9 +147,8 @@ attn_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* 
   const int v_lane_off = v_lrow * rowstride + 8 * (lane & 1);
   const uint16_t* kbase = k + static_cast<size_t>(kv0) * rowstride + static_cast<size_t>(kvh) * D;
   const uint16_t* vbase = v + static_cast<size_t>(kv0) * rowstride + static_cast<size_t>(kvh) * D;
-  const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&ring[w][0][0]));
-  const lds_bf16x8* Kp = (const lds_bf16x8*)(uintptr_t)(ring_lds + 16 * lane);
-  const uint32_t vaddr = ring_lds + MAT + 16 * (8 * q4 + 2 * (c16 >> 2) + ((c16 & 3) >> 1)) + 8 * (c16 & 1);
+  const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&ring[w][0]));
+  const uint32_t vaddr = ring_lds + 16 * (8 * q4 + 2 * (c16 >> 2) + ((c16 & 3) >> 1)) + 8 * (c16 & 1);
 
   for (int kk = k_begin + w; kk < k_end; kk += kWaves) {
     const int key0 = sel[kk] * 64;
@@ -139,21 +156,21 @@ attn_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* 
     const int last = kv_len - 1 - key0;
     const uint16_t* kb = kbase + static_cast<size_t>(key0) * rowstride;
     const uint16_t* vb = vbase + static_cast<size_t>(key0) * rowstride;
+    bf16x8 kr[CPR];                 // A operand of MFMA step J = (2s + tp) * KS + ks
 #pragma unroll
     for (int J = 0; J < CPR; ++J) {
       const int krow0 = 32 * (J / (2 * KS)) + 4 * ((J / KS) % 2);
       const int vrow0 = 32 * (J / NT);
       int ko = k_lane_off + krow0 * rowstride + 32 * (J % KS);
       int vo = v_lane_off + vrow0 * rowstride + 16 * (J % NT);
-      if (tail) {
-        const int kr = krow0 + k_lrow, vr = vrow0 + v_lrow;
-        ko += ((kr < last ? kr : last) - kr) * rowstride;
+      if (tail) {                   // rows past the cache end repeat its last row (masked)
+        const int kr0 = krow0 + k_lrow, vr = vrow0 + v_lrow;
+        ko += ((kr0 < last ? kr0 : last) - kr0) * rowstride;
         vo += ((vr < last ? vr : last) - vr) * rowstride;
       }
-      const uint16_t* gk = kb + ko;
       const uint16_t* gv = vb + vo;
-      __builtin_amdgcn_global_load_lds(gk, (lds_void*)(&ring[w][0][J * 1024]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(gv, (lds_void*)(&ring[w][1][J * 1024]), 16, 0, 0);
+      kr[J] = *reinterpret_cast<const bf16x8*>(kb + ko);
+      __builtin_amdgcn_global_load_lds(gv, (lds_void*)(&ring[w][J * 1024]), 16, 0, 0);
     }
     wait_vmcnt<0>();
     asm volatile("" ::: "memory");
@@ -165,8 +182,8 @@ attn_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* 
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kp[((2 * s + tp) * KS + ks) * 64], qf[ks],
-                                                        acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[(2 * s + tp) * KS + ks], qf[ks], acc,
+                                                        0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sv[s][tp][i] = acc[i];
       }
@@ -242,7 +259,7 @@ attn_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* 
     wl_s[w][c16] = l;
   }
   __syncthreads();
-  float* obuf = reinterpret_cast<float*>(&ring[0][0][0]);            // [wave][16][D] floats
+  float* obuf = reinterpret_cast<float*>(&ring[0][0]);               // [wave][16][D] floats
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int h = 4 * q4 + i;
@@ -286,39 +303,57 @@ attn_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* 
 
   // ---- partial of this split, then the last split of (row, kv head) merges all of them
   DecodeWs ws = ws_of(workspace, rows, Hkv, nsplit, G, D);
-  const size_t pbase = ((static_cast<size_t>(vrow) * Hkv + kvh) * nsplit) * G * (D + 2);
+  const size_t ebase = (static_cast<size_t>(vrow) * Hkv + kvh) * nsplit * G;   // entry of split 0
+  // Partials cross workgroups (and XCDs, whose L2s are not coherent with each other) through
+  // agent-scope atomic stores and loads, which are coherent at that scope by themselves; a
+  // fence would instead write back and invalidate the whole L2 of the XCD.
   if (h < G && d0 < D) {
-    float* pp = ws.part + pbase + (static_cast<size_t>(sp) * G + h) * (D + 2);
-    if (d0 == 0) {
-      pp[0] = M;
-      pp[1] = L;
-    }
+    const size_t e = ebase + static_cast<size_t>(sp) * G + h;
+    uint64_t* po = reinterpret_cast<uint64_t*>(ws.part_o + e * D + d0);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pp[2 + d0 + e] = acc[e];
+    for (int i = 0; i < 4; ++i)
+      agent_store(po + i, pack2(acc[2 * i], acc[2 * i + 1]));
+    if (d0 == 0) agent_store(reinterpret_cast<uint64_t*>(ws.part_ml + e * 2), pack2(M, L));
   }
-  __threadfence();
+  wait_vmcnt<0>();                                   // this wave's stores are complete
   __syncthreads();
   int* cnt = ws.count + static_cast<size_t>(vrow) * Hkv + kvh;
-  if (tid == 0) s_last = (atomicAdd(cnt, 1) == nsplit - 1);
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             nsplit - 1;
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   if (h < G && d0 < D) {
-    float MM = -INFINITY;
-    for (int s2 = 0; s2 < nsplit; ++s2)
-      MM = fmaxf(MM, __builtin_nontemporal_load(ws.part + pbase + (static_cast<size_t>(s2) * G + h) * (D + 2)));
-    float LL = 0.f;
+    // online log-sum-exp merge; the loads of 8 splits are issued before any is used
+    float MM = -INFINITY, LL = 0.f;
     float a2[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) a2[e] = 0.f;
-    for (int s2 = 0; s2 < nsplit; ++s2) {
-      const float* pp = ws.part + pbase + (static_cast<size_t>(s2) * G + h) * (D + 2);
-      const float ms = __builtin_nontemporal_load(pp);
-      if (ms == -INFINITY) continue;
-      const float f = __builtin_amdgcn_exp2f(ms - MM);
-      LL += __builtin_nontemporal_load(pp + 1) * f;
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+      uint64_t ml[8], ov[8][4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a2[e] += __builtin_nontemporal_load(pp + 2 + d0 + e) * f;
+      for (int u = 0; u < 8; ++u) {
+        const size_t e = ebase + static_cast<size_t>(min(s0 + u, nsplit - 1)) * G + h;
+        ml[u] = agent_load(reinterpret_cast<const uint64_t*>(ws.part_ml + e * 2));
+        const uint64_t* po = reinterpret_cast<const uint64_t*>(ws.part_o + e * D + d0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[u][i] = agent_load(po + i);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float ms = lo_f32(ml[u]);
+        if (s0 + u >= nsplit || ms == -INFINITY) continue;      // duplicate or empty split
+        const float Mn = fmaxf(MM, ms);
+        const float fo = __builtin_amdgcn_exp2f(MM - Mn);
+        const float fn = __builtin_amdgcn_exp2f(ms - Mn);
+        LL = LL * fo + hi_f32(ml[u]) * fn;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a2[2 * i] = a2[2 * i] * fo + lo_f32(ov[u][i]) * fn;
+          a2[2 * i + 1] = a2[2 * i + 1] * fo + hi_f32(ov[u][i]) * fn;
+        }
+        MM = Mn;
+      }
     }
     uint16_t* op = out + (static_cast<size_t>(row) * Hq + kvh * G + h) * D + d0;
     const float inv = 1.f / LL;
@@ -326,7 +361,7 @@ attn_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* 
     for (int e = 0; e < 8; ++e) op[e] = f32_to_bf16(a2[e] * inv);
     if (lse != nullptr && d0 == 0) lse[static_cast<size_t>(row) * Hq + kvh * G + h] = (MM + log2f(LL)) * kLn2;
   }
-  if (tid == 0) atomicExch(cnt, 0);           // ready for the next call
+  if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
 }
 
 }  // namespace

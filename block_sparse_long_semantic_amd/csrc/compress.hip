@@ -45,6 +45,7 @@ compress_kernel(Geom g, SeqTable t, const void* __restrict__ k, void* __restrict
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0;
     const size_t row0 = static_cast<size_t>(t.kv_start[b]) + static_cast<size_t>(g.s) * c;
+#pragma unroll 8
     for (int r = 0; r < g.w; ++r) {
       const size_t off = (row0 + r) * cols + static_cast<size_t>(cg) * 8;
       if constexpr (kBf16) {

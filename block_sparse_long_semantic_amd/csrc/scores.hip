@@ -220,6 +220,24 @@ scores_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int C = num_kernels(t.kv_len[b], g.w, g.s);
+  const int c0 = 4 * blk0;
+  const int col = (lane % LPR) * 8;
+  const size_t kbase = static_cast<size_t>(t.kc_start[b]) * g.Hkv * D + static_cast<size_t>(kvh) * D;
+  constexpr int NIT = (NROW + RPI - 1) / RPI;
+  constexpr int NW = kThreads / 64;
+  constexpr int PER = (NIT + NW - 1) / NW;                // row groups per wave
+  // the kernel rows do not depend on the query: every load is issued before the query sum
+  uint4 kv[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int it = w + NW * i;
+    const int r = it * RPI + lane / LPR;                   // 0 .. NROW-1 (+ padding)
+    const int c = c0 - 1 + r;
+    const bool ok = it < NIT && r < NROW && c >= 0 && c < C && 16 * c + 31 <= pos;
+    kv[i] = ok ? *reinterpret_cast<const uint4*>(kern + kbase + static_cast<size_t>(c) * g.Hkv * D + col)
+               : make_uint4(0u, 0u, 0u, 0u);
+  }
   for (int e = tid; e < D; e += kThreads) {
     float acc = 0.f;
     for (int h = 0; h < g.G; ++h)
@@ -227,31 +245,25 @@ scores_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q,
     qs[e] = acc;
   }
   __syncthreads();
-  const int C = num_kernels(t.kv_len[b], g.w, g.s);
-  const int c0 = 4 * blk0;
-  const int col = (lane % LPR) * 8;
   float qv[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) qv[e] = qs[col + e];
-  const size_t kbase = static_cast<size_t>(t.kc_start[b]) * g.Hkv * D + static_cast<size_t>(kvh) * D;
-  constexpr int NIT = (NROW + RPI - 1) / RPI;
-  for (int it = w; it < NIT; it += kThreads / 64) {
-    const int r = it * RPI + lane / LPR;                   // 0 .. NROW-1 (+ padding)
-    const int c = c0 - 1 + r;
-    const bool ok = r < NROW && c >= 0 && c < C && 16 * c + 31 <= pos;
-    float dot = 0.f;
-    if (ok) {
-      const uint4 v = *reinterpret_cast<const uint4*>(kern + kbase + static_cast<size_t>(c) * g.Hkv * D + col);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dot = fmaf(__uint_as_float(w4[e] << 16), qv[2 * e], dot);
-        dot = fmaf(__uint_as_float(w4[e] & 0xFFFF0000u), qv[2 * e + 1], dot);
-      }
+  for (int i = 0; i < PER; ++i) {
+    const int it = w + NW * i;
+    const int r = it * RPI + lane / LPR;
+    const int c = c0 - 1 + r;
+    const bool ok = it < NIT && r < NROW && c >= 0 && c < C && 16 * c + 31 <= pos;
+    const uint32_t w4[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dot = fmaf(__uint_as_float(w4[e] << 16), qv[2 * e], dot);
+      dot = fmaf(__uint_as_float(w4[e] & 0xFFFF0000u), qv[2 * e + 1], dot);
     }
 #pragma unroll
     for (int off = LPR / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
-    if (lane % LPR == 0 && r < NROW) u[r] = ok ? dot : -INFINITY;
+    if (lane % LPR == 0 && it < NIT && r < NROW) u[r] = ok ? dot : -INFINITY;
   }
   __syncthreads();
   if (tid < 64) {

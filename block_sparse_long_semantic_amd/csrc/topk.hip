@@ -95,12 +95,122 @@ topk_kernel(Geom g, SeqTable t, const float* __restrict__ scores, int nb_stride,
   for (int p = base + lane; p < g.topk; p += 64) out[p] = -1;
 }
 
+// The same selection with one workgroup of 16 waves per (query row, KV head), for launches
+// with few rows (decoding): block b = 1024*e + thread, counts summed across the waves in LDS.
+constexpr int kWideWaves = 16;
+constexpr int kWideThreads = 64 * kWideWaves;
+
+__device__ __forceinline__ int wide_sum(int (*buf)[kWideWaves], int slot, int w, int lane, int v,
+                                        int* before) {
+  if (lane == 0) buf[slot][w] = v;
+  __syncthreads();
+  int tot = 0, pre = 0;
+#pragma unroll
+  for (int i = 0; i < kWideWaves; ++i) {
+    const int c = buf[slot][i];
+    tot += c;
+    pre += i < w ? c : 0;
+  }
+  if (before) *before = pre;
+  return tot;
+}
+
+template <int NPT>
+__global__ void __launch_bounds__(kWideThreads)
+topk_wide(Geom g, SeqTable t, const float* __restrict__ scores, int nb_stride,
+          int32_t* __restrict__ idx) {
+  __shared__ int cnt[2 + 2 * NPT][kWideWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int item = blockIdx.x;
+  const int vrow = item / g.Hkv;
+  const int kvh = item % g.Hkv;
+  const int b = find_seq(t, vrow);
+  const int j = vrow - t.work_prefix[b];
+  const int row = t.q_start[b] + j;
+  const int pos = t.q_pos0[b] + j;
+  const int own = pos / g.B;
+  const int nb = own + 1;
+  int32_t* out = idx + (static_cast<size_t>(row) * g.Hkv + kvh) * g.topk;
+  if (nb <= g.topk) {                                       // uniform over the workgroup
+    for (int e = tid; e < g.topk; e += kWideThreads) out[e] = e < nb ? e : -1;
+    return;
+  }
+  const float* srow = scores + (static_cast<size_t>(row) * g.Hkv + kvh) * nb_stride;
+  const int local_lo = max(0, own - g.n_local + 1);
+  const int init_end = min(g.n_init, nb);
+  const int n_forced = init_end + (own - local_lo + 1) - max(0, init_end - local_lo);
+  const int want = g.topk - n_forced;
+
+  uint32_t key[NPT];
+#pragma unroll
+  for (int e = 0; e < NPT; ++e) {
+    const int blk = kWideThreads * e + tid;
+    const bool forced = blk < g.n_init || blk >= local_lo;
+    key[e] = (blk < nb && !forced) ? order_key(srow[blk]) : 0u;
+  }
+
+  // bitwise search for the threshold; buffers alternate so one barrier per step suffices
+  uint32_t thr = 0u;
+  int step = 0;
+  for (int bit = 31; bit >= 0; --bit, ++step) {
+    const uint32_t cand = thr | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < NPT; ++e) c += __popcll(__ballot(key[e] >= cand));
+    const int tot = wide_sum(cnt, step & 1, w, lane, c, nullptr);
+    if (tot >= want) {
+      thr = cand;
+      if (tot == want) break;                              // same decision in every wave
+    }
+  }
+  __syncthreads();                                         // the last step's counts are read
+  int c_gt = 0;
+#pragma unroll
+  for (int e = 0; e < NPT; ++e) c_gt += __popcll(__ballot(key[e] > thr));
+  const int need_eq = want - wide_sum(cnt, 0, w, lane, c_gt, nullptr);
+
+  int base_eq = 0, base = 0;
+#pragma unroll
+  for (int e = 0; e < NPT; ++e) {
+    const int blk = kWideThreads * e + tid;
+    const bool eq = key[e] == thr && key[e] != 0u;
+    const unsigned long long meq = __ballot(eq);
+    int eq_before;
+    const int eq_tot = wide_sum(cnt, 2 + 2 * e, w, lane, __popcll(meq), &eq_before);
+    const bool take_eq = eq && (base_eq + eq_before + prefix_count(meq)) < need_eq;
+    base_eq += eq_tot;
+    const bool forced = blk < nb && (blk < g.n_init || blk >= local_lo);
+    const bool sel = forced || key[e] > thr || take_eq;
+    const unsigned long long ms = __ballot(sel);
+    int sel_before;
+    const int sel_tot = wide_sum(cnt, 3 + 2 * e, w, lane, __popcll(ms), &sel_before);
+    if (sel) out[base + sel_before + prefix_count(ms)] = blk;
+    base += sel_tot;
+  }
+  for (int p = base + tid; p < g.topk; p += kWideThreads) out[p] = -1;
+}
+
 }  // namespace
 
 hipError_t launch_topk(const Geom& g, const SeqTable& t, const float* scores, int nb_stride,
                        int max_blocks, int32_t* idx, hipStream_t stream) {
   const int items = t.work_prefix[t.n] * g.Hkv;
   if (items == 0) return hipSuccess;
+  if (items <= 1024 && max_blocks <= 4 * kWideThreads) {
+    const int npt = (max_blocks + kWideThreads - 1) / kWideThreads;
+#define INFLLM2_TOPK_WIDE(N)                                                                  \
+    if (npt <= N) {                                                                           \
+      hipLaunchKernelGGL(topk_wide<N>, dim3(items), dim3(kWideThreads), 0, stream, g, t,     \
+                         scores, nb_stride, idx);                                             \
+      return hipGetLastError();                                                               \
+    }
+    INFLLM2_TOPK_WIDE(1)
+    INFLLM2_TOPK_WIDE(2)
+    INFLLM2_TOPK_WIDE(4)
+#undef INFLLM2_TOPK_WIDE
+  }
   const dim3 grid((items + kWaves - 1) / kWaves);
   const dim3 block(64 * kWaves);
   const int npl = (max_blocks + 63) / 64;
