@@ -111,6 +111,34 @@ __device__ __forceinline__ void read_v_half<4>(uint32_t addr, uint64_t (&vt)[4][
 }
 
 template <>
+__device__ __forceinline__ void read_v_half<8>(uint32_t addr, uint64_t (&vt)[8][2]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n"
+      "ds_read_b64_tr_b16 %1, %16 offset:512\n"
+      "ds_read_b64_tr_b16 %2, %16 offset:1024\n"
+      "ds_read_b64_tr_b16 %3, %16 offset:1536\n"
+      "ds_read_b64_tr_b16 %4, %16 offset:2048\n"
+      "ds_read_b64_tr_b16 %5, %16 offset:2560\n"
+      "ds_read_b64_tr_b16 %6, %16 offset:3072\n"
+      "ds_read_b64_tr_b16 %7, %16 offset:3584\n"
+      "ds_read_b64_tr_b16 %8, %16 offset:4096\n"
+      "ds_read_b64_tr_b16 %9, %16 offset:4608\n"
+      "ds_read_b64_tr_b16 %10, %16 offset:5120\n"
+      "ds_read_b64_tr_b16 %11, %16 offset:5632\n"
+      "ds_read_b64_tr_b16 %12, %16 offset:6144\n"
+      "ds_read_b64_tr_b16 %13, %16 offset:6656\n"
+      "ds_read_b64_tr_b16 %14, %16 offset:7168\n"
+      "ds_read_b64_tr_b16 %15, %16 offset:7680\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(vt[0][0]), "=&v"(vt[0][1]), "=&v"(vt[1][0]), "=&v"(vt[1][1]),
+        "=&v"(vt[2][0]), "=&v"(vt[2][1]), "=&v"(vt[3][0]), "=&v"(vt[3][1]),
+        "=&v"(vt[4][0]), "=&v"(vt[4][1]), "=&v"(vt[5][0]), "=&v"(vt[5][1]),
+        "=&v"(vt[6][0]), "=&v"(vt[6][1]), "=&v"(vt[7][0]), "=&v"(vt[7][1])
+      : "v"(addr)
+      : "memory");
+}
+
+template <>
 __device__ __forceinline__ void read_v_half<2>(uint32_t addr, uint64_t (&vt)[2][2]) {
   asm volatile(
       "ds_read_b64_tr_b16 %0, %4\n"
@@ -308,10 +336,16 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   // block itself, otherwise after its next block of work.  Every wait is bounded.
   int pending = -1;
   bool stalled = false;
-  for (int u = 0; u < n_union; ++u) {
-    const uint32_t ent = __builtin_amdgcn_readfirstlane(ulist[u]);
+  // The wave reads 64 list entries at a time and jumps straight to the blocks its tokens chose.
+  for (int ubase = 0; ubase < n_union && !stalled; ubase += 64) {
+    const uint32_t chunk = ubase + lane < n_union ? ulist[ubase + lane] : 0u;
+    unsigned long long todo = __ballot(((chunk >> (TPW * w)) & ((1u << TPW) - 1u)) != 0u);
+   while (todo != 0ull) {
+    const int bit = __builtin_ctzll(todo);
+    todo &= todo - 1ull;
+    const int u = ubase + bit;
+    const uint32_t ent = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(chunk), bit));
     const uint32_t wm = (ent >> (TPW * w)) & ((1u << TPW) - 1u);
-    if (wm == 0u) continue;
     const int slot = u % NS;
     if (lds_load(&ready[slot]) != u) {
       if (pending >= 0) {
@@ -337,21 +371,27 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
       const int pos = pos0 + TPW * w + tt;
       // S^T tiles: tile (s, tp) row r' -> key 32s + 8(r'/4) + 4tp + (r'%4); the lane then
       // holds keys 32s + 8*q4 + 4*tp + i for head c16 (raw, unscaled dot products).
+      // the four (s, tp) accumulator chains advance together, one k-step at a time
+      f32x4 acc4[2][2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) acc4[s][tp] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int tp = 0; tp < 2; ++tp)
+            acc4[s][tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                Kp[((2 * s + tp) * KS + ks) * 64], qf[tt][ks], acc4[s][tp], 0, 0, 0);
       float sv[2][2][4];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int tp = 0; tp < 2; ++tp) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 a = Kp[((2 * s + tp) * KS + ks) * 64];
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[tt][ks], acc, 0, 0, 0);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sv[s][tp][i] = acc[i];
-        }
-      }
+          for (int i = 0; i < 4; ++i) sv[s][tp][i] = acc4[s][tp][i];
       // keys past the query or the sequence end (only in the query's own block or the tail)
       if (key0 + 63 > pos || key0 + 64 > kv_len) {
         const int lim = min(pos, kv_len - 1) - key0;
@@ -409,17 +449,13 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
         const bf16x2 p67 = __builtin_convertvector((f32x2){sv[s][1][2], sv[s][1][3]}, bf16x2);
         const bf16x2 pp[4] = {p01, p23, p45, p67};
         const bf16x8 pa = __builtin_bit_cast(bf16x8, pp);
+        uint64_t vt[NT][2];
+        read_v_half<NT>(vaddr + 512u * (2 * NT * s), vt);
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          uint64_t vt[NT / 2][2];
-          read_v_half<NT / 2>(vaddr + 512u * (2 * NT * s + NT * half), vt);
-#pragma unroll
-          for (int n = 0; n < NT / 2; ++n) {
-            const uint64_t both[2] = {vt[n][0], vt[n][1]};
-            const bf16x8 vb = __builtin_bit_cast(bf16x8, both);
-            o[tt][half * (NT / 2) + n] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[tt][half * (NT / 2) + n], 0, 0, 0);
-          }
+        for (int n = 0; n < NT; ++n) {
+          const uint64_t both[2] = {vt[n][0], vt[n][1]};
+          const bf16x8 vb = __builtin_bit_cast(bf16x8, both);
+          o[tt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[tt][n], 0, 0, 0);
         }
       }
     }
@@ -442,6 +478,7 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
         pending = u + NS;
       }
     }
+   }
   }
   if (pending >= 0) {
     wait_vmcnt<0>();
