@@ -45,6 +45,7 @@ constexpr bool kRounds = true;    // launch items in rounds of one workgroup per
 constexpr int kMaxUnion = 2048;   // reachable blocks per tile handled by this kernel
 constexpr float kLazy = 8.f;      // log2 headroom before the running max is moved
 constexpr int kSpinLimit = 1 << 20;  // bounded waits (about 30 ms): a protocol error never hangs
+constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3 for gfx9-family raw buffers
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
@@ -149,6 +150,16 @@ __device__ __forceinline__ void read_v_half<2>(uint32_t addr, uint64_t (&vt)[2][
       : "=&v"(vt[0][0]), "=&v"(vt[0][1]), "=&v"(vt[1][0]), "=&v"(vt[1][1])
       : "v"(addr)
       : "memory");
+}
+
+// LDS read for polling flags written by other waves.  Written as one asm statement that waits
+// for its own result: an atomic load would make the compiler first wait for every LDS-DMA load
+// this wave has in flight.
+__device__ __forceinline__ int lds_peek(const int* p) {
+  int v;
+  const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void*)p));
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+  return v;
 }
 
 __device__ __forceinline__ int lds_load(const int* p) {
@@ -269,23 +280,43 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   const int v_lane_off = v_lrow * rowstride + 8 * (lane & 1);
   const uint16_t* kbase = k + static_cast<size_t>(kv0) * rowstride + static_cast<size_t>(kvh) * D;
   const uint16_t* vbase = v + static_cast<size_t>(kv0) * rowstride + static_cast<size_t>(kvh) * D;
-  // Loads J in [j0, CPR) step dj of union block u into ring slot `slot`.
+  // Loads J in [j0, CPR) step dj of union block u into ring slot `slot`.  Full blocks use buffer
+  // loads: a uniform base (descriptor), the lane's fixed byte offset and a scalar offset per J,
+  // so no per-load address arithmetic.  The ragged last block clamps rows per lane instead.
+  const int k_lane_bytes = 2 * k_lane_off;
+  const int v_lane_bytes = 2 * v_lane_off;
   auto produce = [&](int u, int slot, int j0, int dj) {
     const int key0 = __builtin_amdgcn_readfirstlane(static_cast<int>(ulist[u] >> 16)) * 64;
-    const bool tail = key0 + 64 > kv_len;                       // ragged end: clamp rows
-    const int last = kv_len - 1 - key0;
+    const bool tail = key0 + 64 > kv_len;
     const uint16_t* kb = kbase + static_cast<size_t>(key0) * rowstride;
     const uint16_t* vb = vbase + static_cast<size_t>(key0) * rowstride;
+    if (!tail) {
+      const int nbytes = (63 * rowstride + D) * 2;               // the block's rows of this head
+      const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(kb), 0, nbytes, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(vb), 0, nbytes, kBufferWord3);
+      for (int J = j0; J < CPR; J += dj) {
+        const int krow0 = 32 * (J / (2 * KS)) + 4 * ((J / KS) % 2);
+        const int vrow0 = 32 * (J / NT);
+        const int ks_off = (krow0 * rowstride + 32 * (J % KS)) * 2;
+        const int vs_off = (vrow0 * rowstride + 16 * (J % NT)) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(&ring[slot][0][J * 1024]), 16,
+                                                 k_lane_bytes, ks_off, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(&ring[slot][1][J * 1024]), 16,
+                                                 v_lane_bytes, vs_off, 0, 0);
+      }
+      return;
+    }
+    const int last = kv_len - 1 - key0;
     for (int J = j0; J < CPR; J += dj) {
       const int krow0 = 32 * (J / (2 * KS)) + 4 * ((J / KS) % 2);
       const int vrow0 = 32 * (J / NT);
       int ko = k_lane_off + krow0 * rowstride + 32 * (J % KS);
       int vo = v_lane_off + vrow0 * rowstride + 16 * (J % NT);
-      if (tail) {
-        const int kr = krow0 + k_lrow, vr = vrow0 + v_lrow;
-        ko += ((kr < last ? kr : last) - kr) * rowstride;
-        vo += ((vr < last ? vr : last) - vr) * rowstride;
-      }
+      const int kr = krow0 + k_lrow, vr = vrow0 + v_lrow;
+      ko += ((kr < last ? kr : last) - kr) * rowstride;
+      vo += ((vr < last ? vr : last) - vr) * rowstride;
       const uint16_t* gk = kb + ko;
       const uint16_t* gv = vb + vo;
       __builtin_amdgcn_global_load_lds(gk, (lds_void*)(&ring[slot][0][J * 1024]), 16, 0, 0);
@@ -347,14 +378,14 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
     const uint32_t ent = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(chunk), bit));
     const uint32_t wm = (ent >> (TPW * w)) & ((1u << TPW) - 1u);
     const int slot = u % NS;
-    if (lds_load(&ready[slot]) != u) {
+    if (lds_peek(&ready[slot]) != u) {
       if (pending >= 0) {
         wait_vmcnt<0>();
         lds_store(&ready[pending % NS], pending);
         pending = -1;
       }
       int spins = 0;
-      while (lds_load(&ready[slot]) != u) {
+      while (lds_peek(&ready[slot]) != u) {
         __builtin_amdgcn_s_sleep(1);
         if (++spins > kSpinLimit) { stalled = true; break; }
       }
