@@ -73,17 +73,18 @@ scores_simple(Geom g, SeqTable t, const T* __restrict__ q, const T* __restrict__
 }
 
 // ------------------------------------------------------------------------------ MFMA path
-// Work item = (sequence, tile of 16*WR query rows, chunk of `range_tiles` kernel tiles); the
-// 4 waves are WR row groups x (4/WR) kernel sub-ranges.  A kernel tile is 16 kernels = 4
-// blocks.  Prefill uses WR = 4 and one chunk per row tile (decode-like launches with few
-// rows go to scores_decode below instead).
-template <int D, int WR>
+// Work item = (sequence, tile of 64 query rows, KV head).  Every wave holds the group-summed
+// queries of all 64 rows as MFMA B operands (4 row groups of 16; float32 sums split into hi and
+// lo bf16 parts) and streams a quarter of the kernel tiles the rows can see (a kernel tile is 16
+// kernels = 4 blocks), so each kernel fragment it loads feeds 8 MFMAs.  Block scores are
+// max-pooled in registers: a lane holds 4 consecutive kernels of one row, and the kernel before
+// them (shared with the previous block) comes from the lane 16 below, or from the previous tile.
+template <int D>
 __global__ void __launch_bounds__(kThreads)
 scores_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
-            const uint16_t* __restrict__ kern, float* __restrict__ scores, int nb_stride,
-            int range_tiles) {
+            const uint16_t* __restrict__ kern, float* __restrict__ scores, int nb_stride) {
   constexpr int KS = D / 32;
-  constexpr int WK = 4 / WR;
+  constexpr int RG = 4;                                        // row groups of 16 per wave
   const int total = t.work_prefix[t.n];
   const int item = total - 1 - static_cast<int>(blockIdx.x);   // heaviest (latest) rows first
   const int kvh = blockIdx.y;
@@ -93,43 +94,32 @@ scores_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
   const int c16 = lane & 15;
   const int q4 = lane >> 4;
   const int q_len = t.q_len[b];
-  const int pos_last = t.q_pos0[b] + q_len - 1;
-  const int nbt_seq = (pos_last / 64 + 1 + 3) / 4;            // kernel tiles of the sequence
-  const int chunks = (nbt_seq + range_tiles - 1) / range_tiles;
-  const int local = item - t.work_prefix[b];
-  const int rt = local / chunks;
-  const int ch = local % chunks;
-  const int rw = wave % WR;
-  const int kw = wave / WR;
-
-  const int r = rt * 16 * WR + rw * 16 + c16;                  // this lane's query row (B column)
-  const bool row_ok = r < q_len;
-  const int pos = t.q_pos0[b] + (row_ok ? r : q_len - 1);
-  const int row = t.q_start[b] + r;
-
-  // rows of this wave: kernel tiles needed by its last valid row
-  const int r_last = min(rt * 16 * WR + rw * 16 + 15, q_len - 1);
-  if (rt * 16 * WR + rw * 16 > q_len - 1) return;             // wave has no rows
-  const int nbt_wave = ((t.q_pos0[b] + r_last) / 64 + 1 + 3) / 4;
-  const int t_chunk0 = ch * range_tiles;
-  const int t_chunk1 = min(nbt_wave, t_chunk0 + range_tiles);
-  if (t_chunk0 >= t_chunk1) return;
-  const int per = (t_chunk1 - t_chunk0 + WK - 1) / WK;
-  const int t_begin = t_chunk0 + kw * per;
-  const int t_end = min(t_chunk1, t_begin + per);
+  const int r0 = (item - t.work_prefix[b]) * 64;
+  const int r_last = min(r0 + 63, q_len - 1);
+  const int nbt = ((t.q_pos0[b] + r_last) / 64 + 1 + 3) / 4;  // kernel tiles of the last row
+  const int per = (nbt + 3) / 4;
+  const int t_begin = wave * per;
+  const int t_end = min(nbt, t_begin + per);
   if (t_begin >= t_end) return;
 
-  // B operand: group-summed query, hi and lo bf16 parts, dims 32*ks + 8*q4 + 0..7
-  bf16x8 bhi[KS], blo[KS];
+  // B operands: group-summed query of row r0 + 16*rg + c16, dims 32*ks + 8*q4 + 0..7
+  bf16x8 bhi[RG][KS], blo[RG][KS];
+  int pos[RG];
+  bool row_ok[RG];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    float acc[8];
+  for (int rg = 0; rg < RG; ++rg) {
+    const int r = r0 + 16 * rg + c16;
+    row_ok[rg] = r < q_len;
+    pos[rg] = t.q_pos0[b] + (row_ok[rg] ? r : q_len - 1);
+    const size_t row = static_cast<size_t>(t.q_start[b]) + (row_ok[rg] ? r : q_len - 1);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    if (row_ok) {
+    for (int ks = 0; ks < KS; ++ks) {
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
       for (int h = 0; h < g.G; ++h) {
         const uint4 v = *reinterpret_cast<const uint4*>(
-            q + (static_cast<size_t>(row) * g.Hq + kvh * g.G + h) * D + 32 * ks + 8 * q4);
+            q + (row * g.Hq + kvh * g.G + h) * D + 32 * ks + 8 * q4);
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -137,56 +127,65 @@ scores_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
           acc[2 * e + 1] += __uint_as_float(w4[e] & 0xFFFF0000u);
         }
       }
-    }
-    uint32_t hi4[4], lo4[4];
+      uint32_t hi4[4], lo4[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint16_t h0 = f32_to_bf16(acc[2 * e]), h1 = f32_to_bf16(acc[2 * e + 1]);
-      const uint16_t l0 = f32_to_bf16(acc[2 * e] - bf16_to_f32(h0));
-      const uint16_t l1 = f32_to_bf16(acc[2 * e + 1] - bf16_to_f32(h1));
-      hi4[e] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-      lo4[e] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t h0 = f32_to_bf16(acc[2 * e]), h1 = f32_to_bf16(acc[2 * e + 1]);
+        const uint16_t l0 = f32_to_bf16(acc[2 * e] - bf16_to_f32(h0));
+        const uint16_t l1 = f32_to_bf16(acc[2 * e + 1] - bf16_to_f32(h1));
+        hi4[e] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+        lo4[e] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+      }
+      bhi[rg][ks] = __builtin_bit_cast(bf16x8, make_uint4(hi4[0], hi4[1], hi4[2], hi4[3]));
+      blo[rg][ks] = __builtin_bit_cast(bf16x8, make_uint4(lo4[0], lo4[1], lo4[2], lo4[3]));
     }
-    bhi[ks] = __builtin_bit_cast(bf16x8, make_uint4(hi4[0], hi4[1], hi4[2], hi4[3]));
-    blo[ks] = __builtin_bit_cast(bf16x8, make_uint4(lo4[0], lo4[1], lo4[2], lo4[3]));
   }
 
   const int C = num_kernels(t.kv_len[b], g.w, g.s);
-  const int own = pos / 64;
   const size_t kbase = static_cast<size_t>(t.kc_start[b]) * g.Hkv * D + static_cast<size_t>(kvh) * D;
-  float* srow = scores + (static_cast<size_t>(row) * g.Hkv + kvh) * nb_stride;
   const unsigned src_lane = static_cast<unsigned>((lane + 48) & 63);   // lane - 16 (mod 64)
-  float carry = -INFINITY;
+  float carry[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) carry[rg] = -INFINITY;
   // start one tile early (without writing) to obtain the halo kernel of the first block
   for (int tt = (t_begin > 0 ? t_begin - 1 : 0); tt < t_end; ++tt) {
     const int ck = 16 * tt + c16;                                 // A row: kernel
     const int ck_c = min(ck, C - 1 > 0 ? C - 1 : 0);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 a[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 a;
-      if (C > 0) {
-        a = *reinterpret_cast<const bf16x8*>(kern + kbase + static_cast<size_t>(ck_c) * g.Hkv * D +
-                                              32 * ks + 8 * q4);
-      } else {
-        a = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    for (int ks = 0; ks < KS; ++ks)
+      a[ks] = C > 0 ? *reinterpret_cast<const bf16x8*>(kern + kbase +
+                                                      static_cast<size_t>(ck_c) * g.Hkv * D +
+                                                      32 * ks + 8 * q4)
+                    : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    f32x4 acc[RG];
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) acc[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+        acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bhi[rg][ks], acc[rg], 0, 0, 0);
+        acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], blo[rg][ks], acc[rg], 0, 0, 0);
       }
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bhi[ks], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, blo[ks], acc, 0, 0, 0);
-    }
-    // lane holds u[kernel 16*tt + 4*q4 + i][row c16]
-    float u[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = 16 * tt + 4 * q4 + i;
-      u[i] = (c < C && 16 * c + 31 <= pos) ? acc[i] : -INFINITY;
-    }
-    const float h = __shfl(u[3], src_lane);
-    const float halo = (q4 == 0) ? carry : h;
-    carry = h;
-    const float best = fmaxf(fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3])), halo);
     const int blk = 4 * tt + q4;
-    if (tt >= t_begin && row_ok && blk <= own) srow[blk] = best * g.scale;
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      // lane holds u[kernel 16*tt + 4*q4 + i][row 16*rg + c16]
+      float u[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 16 * tt + 4 * q4 + i;
+        u[i] = (c < C && 16 * c + 31 <= pos[rg]) ? acc[rg][i] : -INFINITY;
+      }
+      const float h = __shfl(u[3], src_lane);
+      const float halo = (q4 == 0) ? carry[rg] : h;
+      carry[rg] = h;
+      const float best = fmaxf(fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3])), halo);
+      if (tt >= t_begin && row_ok[rg] && blk <= pos[rg] / 64)
+        scores[(static_cast<size_t>(t.q_start[b]) + r0 + 16 * rg + c16) * g.Hkv * nb_stride +
+               static_cast<size_t>(kvh) * nb_stride + blk] = best * g.scale;
+    }
   }
 }
 
@@ -319,18 +318,18 @@ hipError_t launch_scores(const Geom& g, int dtype, const SeqTable& t, const void
                          scores, nb_stride);
     return hipGetLastError();
   }
-  // work_prefix counts (row tile x kernel chunk) items, built by the caller for this mode.
+  // work_prefix counts tiles of 64 query rows, built by the caller for this mode.
   const int items = t.work_prefix[t.n];
   if (items == 0) return hipSuccess;
   const dim3 grid(items, g.Hkv);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(kernels);
   if (g.d == 128)
-    hipLaunchKernelGGL((scores_mfma<128, 4>), grid, dim3(kThreads), 0, stream, g, t, qq, kk,
-                       scores, nb_stride, 1 << 28);
+    hipLaunchKernelGGL(scores_mfma<128>, grid, dim3(kThreads), 0, stream, g, t, qq, kk, scores,
+                       nb_stride);
   else
-    hipLaunchKernelGGL((scores_mfma<64, 4>), grid, dim3(kThreads), 0, stream, g, t, qq, kk,
-                       scores, nb_stride, 1 << 28);
+    hipLaunchKernelGGL(scores_mfma<64>, grid, dim3(kThreads), 0, stream, g, t, qq, kk, scores,
+                       nb_stride);
   return hipGetLastError();
 }
 

@@ -120,6 +120,21 @@ def test_chunked_prefill_against_cache():
     check_sequence(wl, res, 0, label="chunk")
 
 
+@pytest.mark.parametrize("name,lens", [("prefill32k", [20000, 13001, 77]),
+                                       ("varlen", [16421, 9000, 30])])
+def test_mfma_scores_ragged_tiles(name, lens):
+    """Enough 64-row tiles for the matrix-core scoring path, with lengths that leave ragged last
+    tiles (and a tiny sequence beside them); rows sampled across the tiles and every tail row."""
+    p = synth.config_params(name)
+    wl = synth.make_prefill("mfma-ragged", p, lens, seed=35, needles_per_seq=1)
+    assert sum((L + 63) // 64 for L in lens) * p.num_kv_heads >= 512
+    log(f"case mfma scores ragged {name} {lens}")
+    res = run_prefill_stages(wl)
+    for b, L in enumerate(lens):
+        rows = sorted(set(range(0, L, 211)) | set(range(max(0, L - 70), L)))
+        check_sequence(wl, res, b, rows=np.array(rows), label=f"mfma-ragged {name} seq {b}")
+
+
 def test_results_are_deterministic():
     wl = synth.make("varlen", length_scale=1 / 32)
     a = run_prefill_stages(wl)
