@@ -75,16 +75,24 @@ scores_simple(Geom g, SeqTable t, const T* __restrict__ q, const T* __restrict__
 // ------------------------------------------------------------------------------ MFMA path
 // Work item = (sequence, tile of 64 query rows, KV head).  Every wave holds the group-summed
 // queries of all 64 rows as MFMA B operands (4 row groups of 16; float32 sums split into hi and
-// lo bf16 parts) and streams a quarter of the kernel tiles the rows can see (a kernel tile is 16
-// kernels = 4 blocks), so each kernel fragment it loads feeds 8 MFMAs.  Block scores are
-// max-pooled in registers: a lane holds 4 consecutive kernels of one row, and the kernel before
-// them (shared with the previous block) comes from the lane 16 below, or from the previous tile.
+// lo bf16 parts; wave w sums row group w and the groups are exchanged through LDS) and streams
+// a quarter of the kernel tiles the rows can see (a kernel tile is 16 kernels = 4 blocks), so
+// each kernel fragment it loads feeds 8 MFMAs.  Block scores are max-pooled in registers: a lane
+// holds 4 consecutive kernels of one row, and the kernel before them (shared with the previous
+// block) comes from the lane 16 below, or from the previous tile.  Scores are collected per wave
+// in LDS for 16 kernel tiles (64 blocks) and written out as whole row segments.
+constexpr int kChunkTiles = 16;                  // kernel tiles per staged chunk (64 blocks)
+constexpr int kStageRow = 4 * kChunkTiles + 1;   // floats per staged row (+1: bank offset)
+
 template <int D>
 __global__ void __launch_bounds__(kThreads)
 scores_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
             const uint16_t* __restrict__ kern, float* __restrict__ scores, int nb_stride) {
   constexpr int KS = D / 32;
   constexpr int RG = 4;                                        // row groups of 16 per wave
+  constexpr int QOP_BYTES = RG * KS * 2 * 64 * 16;             // exchanged B operands
+  constexpr int STAGE_BYTES = 4 * 64 * kStageRow * 4;          // per-wave score staging
+  __shared__ __attribute__((aligned(16))) unsigned char smem[QOP_BYTES > STAGE_BYTES ? QOP_BYTES : STAGE_BYTES];
   const int total = t.work_prefix[t.n];
   const int item = total - 1 - static_cast<int>(blockIdx.x);   // heaviest (latest) rows first
   const int kvh = blockIdx.y;
@@ -100,18 +108,12 @@ scores_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
   const int per = (nbt + 3) / 4;
   const int t_begin = wave * per;
   const int t_end = min(nbt, t_begin + per);
-  if (t_begin >= t_end) return;
 
-  // B operands: group-summed query of row r0 + 16*rg + c16, dims 32*ks + 8*q4 + 0..7
-  bf16x8 bhi[RG][KS], blo[RG][KS];
-  int pos[RG];
-  bool row_ok[RG];
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-    const int r = r0 + 16 * rg + c16;
-    row_ok[rg] = r < q_len;
-    pos[rg] = t.q_pos0[b] + (row_ok[rg] ? r : q_len - 1);
-    const size_t row = static_cast<size_t>(t.q_start[b]) + (row_ok[rg] ? r : q_len - 1);
+  // ---- B operands: wave w sums row group w (rows r0 + 16w + c16, dims 32ks + 8q4 + 0..7)
+  uint4* qop = reinterpret_cast<uint4*>(smem);                 // [rg][ks][hi/lo][lane]
+  {
+    const int r = r0 + 16 * wave + c16;
+    const size_t row = static_cast<size_t>(t.q_start[b]) + (r < q_len ? r : q_len - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       float acc[8];
@@ -136,10 +138,28 @@ scores_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
         hi4[e] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
         lo4[e] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
       }
-      bhi[rg][ks] = __builtin_bit_cast(bf16x8, make_uint4(hi4[0], hi4[1], hi4[2], hi4[3]));
-      blo[rg][ks] = __builtin_bit_cast(bf16x8, make_uint4(lo4[0], lo4[1], lo4[2], lo4[3]));
+      qop[((wave * KS + ks) * 2 + 0) * 64 + lane] = make_uint4(hi4[0], hi4[1], hi4[2], hi4[3]);
+      qop[((wave * KS + ks) * 2 + 1) * 64 + lane] = make_uint4(lo4[0], lo4[1], lo4[2], lo4[3]);
     }
   }
+  __syncthreads();
+  bf16x8 bhi[RG][KS], blo[RG][KS];
+  int pos[RG];
+  bool row_ok[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const int r = r0 + 16 * rg + c16;
+    row_ok[rg] = r < q_len;
+    pos[rg] = t.q_pos0[b] + (row_ok[rg] ? r : q_len - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bhi[rg][ks] = __builtin_bit_cast(bf16x8, qop[((rg * KS + ks) * 2 + 0) * 64 + lane]);
+      blo[rg][ks] = __builtin_bit_cast(bf16x8, qop[((rg * KS + ks) * 2 + 1) * 64 + lane]);
+    }
+  }
+  __syncthreads();                                             // smem becomes score staging
+  if (t_begin >= t_end) return;
+  float* stage = reinterpret_cast<float*>(smem) + wave * 64 * kStageRow;   // [row][block]
 
   const int C = num_kernels(t.kv_len[b], g.w, g.s);
   const size_t kbase = static_cast<size_t>(t.kc_start[b]) * g.Hkv * D + static_cast<size_t>(kvh) * D;
@@ -147,45 +167,57 @@ scores_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
   float carry[RG];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) carry[rg] = -INFINITY;
-  // start one tile early (without writing) to obtain the halo kernel of the first block
-  for (int tt = (t_begin > 0 ? t_begin - 1 : 0); tt < t_end; ++tt) {
-    const int ck = 16 * tt + c16;                                 // A row: kernel
-    const int ck_c = min(ck, C - 1 > 0 ? C - 1 : 0);
-    bf16x8 a[KS];
+  for (int c0 = t_begin; c0 < t_end; c0 += kChunkTiles) {
+    const int c1 = min(t_end, c0 + kChunkTiles);
+    // the first chunk starts one tile early (not staged) for the halo kernel of its first block
+    for (int tt = (c0 == t_begin && t_begin > 0) ? t_begin - 1 : c0; tt < c1; ++tt) {
+      const int ck = 16 * tt + c16;                               // A row: kernel
+      const int ck_c = min(ck, C - 1 > 0 ? C - 1 : 0);
+      bf16x8 a[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      a[ks] = C > 0 ? *reinterpret_cast<const bf16x8*>(kern + kbase +
-                                                      static_cast<size_t>(ck_c) * g.Hkv * D +
-                                                      32 * ks + 8 * q4)
-                    : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-    f32x4 acc[RG];
+      for (int ks = 0; ks < KS; ++ks)
+        a[ks] = C > 0 ? *reinterpret_cast<const bf16x8*>(kern + kbase +
+                                                        static_cast<size_t>(ck_c) * g.Hkv * D +
+                                                        32 * ks + 8 * q4)
+                      : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+      f32x4 acc[RG];
 #pragma unroll
-    for (int rg = 0; rg < RG; ++rg) acc[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rg = 0; rg < RG; ++rg) acc[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+          acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bhi[rg][ks], acc[rg], 0, 0, 0);
+          acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], blo[rg][ks], acc[rg], 0, 0, 0);
+        }
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) {
-        acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bhi[rg][ks], acc[rg], 0, 0, 0);
-        acc[rg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], blo[rg][ks], acc[rg], 0, 0, 0);
-      }
-    const int blk = 4 * tt + q4;
+        // lane holds u[kernel 16*tt + 4*q4 + i][row 16*rg + c16]
+        float u[4];
 #pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-      // lane holds u[kernel 16*tt + 4*q4 + i][row 16*rg + c16]
-      float u[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = 16 * tt + 4 * q4 + i;
-        u[i] = (c < C && 16 * c + 31 <= pos[rg]) ? acc[rg][i] : -INFINITY;
+        for (int i = 0; i < 4; ++i) {
+          const int c = 16 * tt + 4 * q4 + i;
+          u[i] = (c < C && 16 * c + 31 <= pos[rg]) ? acc[rg][i] : -INFINITY;
+        }
+        const float h = __shfl(u[3], src_lane);
+        const float halo = (q4 == 0) ? carry[rg] : h;
+        carry[rg] = h;
+        const float best = fmaxf(fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3])), halo);
+        if (tt >= c0) stage[(16 * rg + c16) * kStageRow + 4 * (tt - c0) + q4] = best * g.scale;
       }
-      const float h = __shfl(u[3], src_lane);
-      const float halo = (q4 == 0) ? carry[rg] : h;
-      carry[rg] = h;
-      const float best = fmaxf(fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3])), halo);
-      if (tt >= t_begin && row_ok[rg] && blk <= pos[rg] / 64)
-        scores[(static_cast<size_t>(t.q_start[b]) + r0 + 16 * rg + c16) * g.Hkv * nb_stride +
-               static_cast<size_t>(kvh) * nb_stride + blk] = best * g.scale;
     }
+    asm volatile("" ::: "memory");
+    // write the chunk: one row per instruction, blocks 4*c0 .. 4*c1 - 1 up to the row's own block
+    const int blk = 4 * c0 + lane;
+    for (int rr = 0; rr < 64; ++rr) {
+      const int r = r0 + rr;
+      if (r >= q_len) break;
+      const int own = (t.q_pos0[b] + r) / 64;
+      if (lane < 4 * (c1 - c0) && blk <= own)
+        scores[(static_cast<size_t>(t.q_start[b]) + r) * g.Hkv * nb_stride +
+               static_cast<size_t>(kvh) * nb_stride + blk] = stage[rr * kStageRow + lane];
+    }
+    asm volatile("" ::: "memory");
   }
 }
 

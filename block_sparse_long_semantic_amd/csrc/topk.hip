@@ -26,6 +26,14 @@ __device__ __forceinline__ int prefix_count(unsigned long long mask) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
 }
 
+// Sum over the wave of a small per-lane count (< 128): one ballot per bit of the count.
+__device__ __forceinline__ int wave_count(int c) {
+  int tot = 0;
+#pragma unroll
+  for (int bit = 0; bit < 7; ++bit) tot += __popcll(__ballot((c >> bit) & 1)) << bit;
+  return tot;
+}
+
 // work_prefix counts query rows.
 template <int NPL>
 __global__ void __launch_bounds__(64 * kWaves)
@@ -54,29 +62,35 @@ topk_kernel(Geom g, SeqTable t, const float* __restrict__ scores, int nb_stride,
   const int n_forced = init_end + (own - local_lo + 1) - max(0, init_end - local_lo);
   const int want = g.topk - n_forced;
 
+  // every load is issued (index clamped into the row) before any is used
+  float sc[NPL];
+#pragma unroll
+  for (int e = 0; e < NPL; ++e) sc[e] = srow[min(64 * e + lane, nb - 1)];
   uint32_t key[NPL];
 #pragma unroll
   for (int e = 0; e < NPL; ++e) {
     const int blk = 64 * e + lane;
     const bool forced = blk < g.n_init || blk >= local_lo;
-    key[e] = (blk < nb && !forced) ? order_key(srow[blk]) : 0u;   // 0: not a candidate
+    key[e] = (blk < nb && !forced) ? order_key(sc[e]) : 0u;     // 0: not a candidate
   }
 
+  // bitwise search: each lane counts its keys >= the candidate, the wave sums the counts
   uint32_t thr = 0u;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = thr | (1u << bit);
-    int cnt = 0;
+    int c = 0;
 #pragma unroll
-    for (int e = 0; e < NPL; ++e) cnt += __popcll(__ballot(key[e] >= cand));
+    for (int e = 0; e < NPL; ++e) c += key[e] >= cand ? 1 : 0;
+    const int cnt = wave_count(c);
     if (cnt >= want) {
       thr = cand;
       if (cnt == want) break;
     }
   }
-  int n_gt = 0;
+  int c_gt = 0;
 #pragma unroll
-  for (int e = 0; e < NPL; ++e) n_gt += __popcll(__ballot(key[e] > thr));
-  const int need_eq = want - n_gt;
+  for (int e = 0; e < NPL; ++e) c_gt += key[e] > thr ? 1 : 0;
+  const int need_eq = want - wave_count(c_gt);
 
   int base_eq = 0, base = 0;
 #pragma unroll
