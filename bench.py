@@ -31,6 +31,8 @@ METRIC = "sparse-attn prefill tokens/s @128K + decode µs/token; % MFMA/HBM roof
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 TILE_TOKENS = 16          # query tokens per attention work item
+SPIN_CYCLES = 24_000_000  # GPU spin before the timed decode steps (about 10 ms at 2.4 GHz)
+SPIN_SECONDS = 0.008      # enqueueing must finish well inside the spin
 ATTN_SOURCES = ["block_sparse_long_semantic_amd/csrc/attn_tile.hip",
                 "block_sparse_long_semantic_amd/csrc/internal.h"]
 
@@ -180,13 +182,47 @@ def run_decode(args, torch, pkg, synth):
     for _ in range(max(1, args.warmup)):
         pkg.compress_kernels(p, s0, k, kern, stream=stream)
         all_steps()
+    # host-inclusive: every step's Python marshalling and launches, synchronised at the end
     pkg.compress_kernels(p, s0, k, kern, stream=stream)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.decode_steps)]
     t0 = time.perf_counter()
-    all_steps(ev)
+    all_steps()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # GPU time per step: the GPU spins (about 10 ms) while the host enqueues all steps, so the
+    # events bracket device work only, not the binding's per-call host overhead
+    pkg.compress_kernels(p, s0, k, kern, stream=stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.decode_steps)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(SPIN_CYCLES)
+    t1 = time.perf_counter()
+    all_steps(ev)
+    enqueue = time.perf_counter() - t1
+    torch.cuda.synchronize()
+    # the same steps as separate calls, events between the stages (breakdown; the second of two
+    # passes is kept, each interval includes one event's own cost)
+    for _ in range(2):
+      pkg.compress_kernels(p, s0, k, kern, stream=stream)
+      sev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.decode_steps)]
+      torch.cuda.synchronize()
+      torch.cuda._sleep(SPIN_CYCLES)
+      for st in range(args.decode_steps):
+        e = sev[st]
+        e[0].record(stream)
+        pkg.compress_kernels(p, seqs[st], k, kern, prev_kv_len=prevs[st], stream=stream)
+        e[1].record(stream)
+        pkg.block_scores(p, seqs[st], qs[st], kern, bufs["scores"], stream=stream)
+        e[2].record(stream)
+        pkg.topk_select(p, seqs[st], bufs["scores"], bufs["idx"], stream=stream)
+        e[3].record(stream)
+        pkg.sparse_attn_decode(p, seqs[st], qs[st], k, v, bufs["idx"], bufs["out"], bufs["lse"],
+                               num_splits=bufs["num_splits"], workspace=bufs["workspace"],
+                               stream=stream)
+        e[4].record(stream)
+      torch.cuda.synchronize()
+    stage_us = {n: float(np.mean([sev[st][i].elapsed_time(sev[st][i + 1]) * 1e3
+                                  for st in range(args.decode_steps)]))
+                for i, n in enumerate(["compress", "scores", "topk", "attention"])}
     per = [ev[st][0].elapsed_time(ev[st][1]) * 1e3 for st in range(args.decode_steps)]
     # bytes a step must move: the kernel cache read for scoring, the selected K/V blocks, q/out
     kv_len = kv0 + args.decode_steps
@@ -199,6 +235,8 @@ def run_decode(args, torch, pkg, synth):
     total = bytes_kern + bytes_kv + bytes_q
     us = float(np.mean(per))
     out = dict(us_per_step=us, us_per_step_wall=wall * 1e6 / args.decode_steps,
+               host_enqueue_us_per_step=enqueue * 1e6 / args.decode_steps,
+               gpu_busy_while_enqueueing=bool(enqueue < SPIN_SECONDS), stages_us=stage_us,
                tokens_per_s=B / (us * 1e-6), batch=B, cache_len=int(Lmax),
                steps=args.decode_steps, bytes_per_step=total,
                roofline={"bound": "hbm", "achieved": total / (us * 1e-6) / 1e9,
