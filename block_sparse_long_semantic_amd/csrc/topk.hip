@@ -9,30 +9,12 @@
 //   * keys equal to the threshold are taken in ascending block order (ties -> lower index);
 //   * the selection is written in ascending block order with ballot prefix counts.
 #include "internal.h"
+#include "select.h"
 
 namespace infllm2 {
 namespace {
 
 constexpr int kWaves = 4;
-
-__device__ __forceinline__ uint32_t order_key(float x) {
-  if (x == 0.f) x = 0.f;                          // -0 ranks as +0
-  const uint32_t u = __float_as_uint(x);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ int prefix_count(unsigned long long mask) {
-  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
-                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
-}
-
-// Sum over the wave of a small per-lane count (< 128): one ballot per bit of the count.
-__device__ __forceinline__ int wave_count(int c) {
-  int tot = 0;
-#pragma unroll
-  for (int bit = 0; bit < 7; ++bit) tot += __popcll(__ballot((c >> bit) & 1)) << bit;
-  return tot;
-}
 
 // work_prefix counts query rows.
 template <int NPL>
@@ -110,33 +92,16 @@ topk_kernel(Geom g, SeqTable t, const float* __restrict__ scores, int nb_stride,
 }
 
 // The same selection with one workgroup of 16 waves per (query row, KV head), for launches
-// with few rows (decoding): block b = 1024*e + thread, counts summed across the waves in LDS.
+// with few rows (decoding): block b = 1024*e + thread.
 constexpr int kWideWaves = 16;
 constexpr int kWideThreads = 64 * kWideWaves;
-
-__device__ __forceinline__ int wide_sum(int (*buf)[kWideWaves], int slot, int w, int lane, int v,
-                                        int* before) {
-  if (lane == 0) buf[slot][w] = v;
-  __syncthreads();
-  int tot = 0, pre = 0;
-#pragma unroll
-  for (int i = 0; i < kWideWaves; ++i) {
-    const int c = buf[slot][i];
-    tot += c;
-    pre += i < w ? c : 0;
-  }
-  if (before) *before = pre;
-  return tot;
-}
 
 template <int NPT>
 __global__ void __launch_bounds__(kWideThreads)
 topk_wide(Geom g, SeqTable t, const float* __restrict__ scores, int nb_stride,
           int32_t* __restrict__ idx) {
-  __shared__ int cnt[2 + 2 * NPT][kWideWaves];
+  __shared__ SelectScratch<kWideWaves, NPT> sm;
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
   const int item = blockIdx.x;
   const int vrow = item / g.Hkv;
   const int kvh = item % g.Hkv;
@@ -153,57 +118,15 @@ topk_wide(Geom g, SeqTable t, const float* __restrict__ scores, int nb_stride,
   }
   const float* srow = scores + (static_cast<size_t>(row) * g.Hkv + kvh) * nb_stride;
   const int local_lo = max(0, own - g.n_local + 1);
-  const int init_end = min(g.n_init, nb);
-  const int n_forced = init_end + (own - local_lo + 1) - max(0, init_end - local_lo);
-  const int want = g.topk - n_forced;
-
   uint32_t key[NPT];
 #pragma unroll
   for (int e = 0; e < NPT; ++e) {
     const int blk = kWideThreads * e + tid;
+    const float sc = srow[min(blk, nb - 1)];
     const bool forced = blk < g.n_init || blk >= local_lo;
-    key[e] = (blk < nb && !forced) ? order_key(srow[blk]) : 0u;
+    key[e] = (blk < nb && !forced) ? order_key(sc) : 0u;
   }
-
-  // bitwise search for the threshold; buffers alternate so one barrier per step suffices
-  uint32_t thr = 0u;
-  int step = 0;
-  for (int bit = 31; bit >= 0; --bit, ++step) {
-    const uint32_t cand = thr | (1u << bit);
-    int c = 0;
-#pragma unroll
-    for (int e = 0; e < NPT; ++e) c += __popcll(__ballot(key[e] >= cand));
-    const int tot = wide_sum(cnt, step & 1, w, lane, c, nullptr);
-    if (tot >= want) {
-      thr = cand;
-      if (tot == want) break;                              // same decision in every wave
-    }
-  }
-  __syncthreads();                                         // the last step's counts are read
-  int c_gt = 0;
-#pragma unroll
-  for (int e = 0; e < NPT; ++e) c_gt += __popcll(__ballot(key[e] > thr));
-  const int need_eq = want - wide_sum(cnt, 0, w, lane, c_gt, nullptr);
-
-  int base_eq = 0, base = 0;
-#pragma unroll
-  for (int e = 0; e < NPT; ++e) {
-    const int blk = kWideThreads * e + tid;
-    const bool eq = key[e] == thr && key[e] != 0u;
-    const unsigned long long meq = __ballot(eq);
-    int eq_before;
-    const int eq_tot = wide_sum(cnt, 2 + 2 * e, w, lane, __popcll(meq), &eq_before);
-    const bool take_eq = eq && (base_eq + eq_before + prefix_count(meq)) < need_eq;
-    base_eq += eq_tot;
-    const bool forced = blk < nb && (blk < g.n_init || blk >= local_lo);
-    const bool sel = forced || key[e] > thr || take_eq;
-    const unsigned long long ms = __ballot(sel);
-    int sel_before;
-    const int sel_tot = wide_sum(cnt, 3 + 2 * e, w, lane, __popcll(ms), &sel_before);
-    if (sel) out[base + sel_before + prefix_count(ms)] = blk;
-    base += sel_tot;
-  }
-  for (int p = base + tid; p < g.topk; p += kWideThreads) out[p] = -1;
+  wg_select<kWideWaves, NPT>(key, own, g.topk, g.n_init, g.n_local, out, sm);
 }
 
 }  // namespace
