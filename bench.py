@@ -306,7 +306,7 @@ def _cpu_rows(rows):
 
 
 def _short(name: str) -> str:
-    name = name.replace("infllm2::(anonymous namespace)::", "")
+    name = name.replace("infllm2::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
     cut = name.find("(")
     head = name[:cut] if cut > 0 else name
     if head.startswith("void "):
