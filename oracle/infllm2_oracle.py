@@ -25,6 +25,11 @@ abstract for the prefill and decode use):
      (section 2.1.3: each token attends only to its most relevant blocks), scale 1/sqrt(d)
      as in the skill page's textbook attention snippet.                      -> sparse_attention
 
+  6. the gradients of that attention (the mechanism is trainable: model card, "Efficient Model
+     Architecture"; arXiv abstract; paper summary section 2.1): with the selected blocks held
+     fixed -- the selection is piecewise constant in Q and K, so its derivative is zero almost
+     everywhere -- dQ, dK and dV of step 5 for an upstream gradient dO.     -> sparse_attention_backward
+
 The pages give no formula, constant or worked example for steps 2-4.  Where they are silent
 the oracle takes the plainest reading; every such reading is listed in the repository's
 design notes and pinned by the tests in tests/test_oracle_*.py.  Functions are written for
@@ -262,6 +267,40 @@ def sparse_attention(q_rows: np.ndarray, positions: np.ndarray, keys: np.ndarray
             O[r, g * G:(g + 1) * G, :] = (e / den) @ values[J, g, :].astype(np.float64)
             lse[r, g * G:(g + 1) * G] = (m + np.log(den))[:, 0]
     return O, lse
+
+
+def sparse_attention_backward(q_rows: np.ndarray, positions: np.ndarray, keys: np.ndarray,
+                              values: np.ndarray, idx: np.ndarray, dout: np.ndarray, p):
+    """Gradients of sparse_attention for the upstream gradient dout [n, Hq, d], the block
+    selection idx held fixed.  For each query row and head, with z_j = scale q . k_j over the
+    attended tokens j, P = softmax(z), O = sum_j P_j v_j:
+        dV_j += P_j dO,   dP_j = dO . v_j,   dz_j = P_j (dP_j - dO . O),
+        dQ = scale sum_j dz_j k_j,   dK_j += scale dz_j q.
+    Returns dQ [n, Hq, d] and dK, dV [kv_len, Hkv, d] (zero for tokens no row attends to)."""
+    n, Hq, d = q_rows.shape
+    G = p.group
+    kv_len = keys.shape[0]
+    dQ = np.zeros((n, Hq, d), dtype=np.float64)
+    dK = np.zeros((kv_len, p.num_kv_heads, d), dtype=np.float64)
+    dV = np.zeros((kv_len, p.num_kv_heads, d), dtype=np.float64)
+    for r in range(n):
+        pos = int(positions[r])
+        for g in range(p.num_kv_heads):
+            J = attended_keys(idx[r, g], pos, kv_len, p.block_size)
+            kg = keys[J, g, :].astype(np.float64)                       # [|J|, d]
+            vg = values[J, g, :].astype(np.float64)
+            qh = q_rows[r, g * G:(g + 1) * G, :].astype(np.float64)     # [G, d]
+            do = dout[r, g * G:(g + 1) * G, :].astype(np.float64)
+            z = p.scale * (qh @ kg.T)                                   # [G, |J|]
+            e = np.exp(z - z.max(axis=1, keepdims=True))
+            P = e / e.sum(axis=1, keepdims=True)
+            O = P @ vg
+            dP = do @ vg.T
+            dz = P * (dP - (do * O).sum(axis=1, keepdims=True))
+            dQ[r, g * G:(g + 1) * G, :] = p.scale * (dz @ kg)
+            np.add.at(dK[:, g, :], J, p.scale * (dz.T @ qh))
+            np.add.at(dV[:, g, :], J, P.T @ do)
+    return dQ, dK, dV
 
 
 # ---------------------------------------------------------------------------------------

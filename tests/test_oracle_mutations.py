@@ -14,7 +14,8 @@ from tests import test_oracle_pins as pins
 ORIG = {name: getattr(orc, name) for name in (
     "round_to_storage", "exact_window_means", "compress_kernels", "kernel_visible",
     "kernels_of_block", "kernel_scores", "block_scores", "forced_blocks", "select_blocks",
-    "attended_keys", "sparse_attention", "attended_key_count", "lse_merge")}
+    "attended_keys", "sparse_attention", "attended_key_count", "lse_merge",
+    "sparse_attention_backward")}
 
 # cheapest first; each entry is a pin from test_oracle_pins with its arguments bound
 PINS = [
@@ -38,6 +39,8 @@ PINS = [
     ("selection_invariants", pins.test_selection_invariants),
     ("incremental", pins.test_incremental_kernels_equal_full_compress),
     ("presum", pins.test_presum_identity),
+    ("backward_fd", pins.test_backward_matches_finite_differences),
+    ("backward_autograd", pins.test_backward_dense_reduction_equals_autograd),
 ]
 
 
@@ -188,6 +191,28 @@ def m_merge_no_exp(pm, pl, po):
     return (wts[..., None] * po).sum(axis=0) / den[..., None], m + np.log(den)
 
 
+def _backward(q_rows, positions, keys, values, idx, dout, p, variant):
+    dQ, dK, dV = ORIG["sparse_attention_backward"](q_rows, positions, keys, values, idx, dout, p)
+    if variant == "no_delta":        # dz = P dP (the dO . O term dropped)
+        n, Hq, d = q_rows.shape
+        G = p.group
+        dQ = np.zeros_like(dQ); dK = np.zeros_like(dK)
+        for r in range(n):
+            for g in range(p.num_kv_heads):
+                J = orc.attended_keys(idx[r, g], int(positions[r]), keys.shape[0], p.block_size)
+                qh = q_rows[r, g * G:(g + 1) * G, :]
+                z = p.scale * (qh @ keys[J, g, :].T)
+                P = np.exp(z - z.max(1, keepdims=True)); P /= P.sum(1, keepdims=True)
+                dz = P * (dout[r, g * G:(g + 1) * G, :] @ values[J, g, :].T)
+                dQ[r, g * G:(g + 1) * G, :] = p.scale * dz @ keys[J, g, :]
+                np.add.at(dK[:, g, :], J, p.scale * dz.T @ qh)
+    elif variant == "dk_unscaled":
+        dK = dK / p.scale
+    elif variant == "dv_transposed_heads":
+        dV = dV[:, ::-1, :].copy() if p.num_kv_heads > 1 else -dV
+    return dQ, dK, dV
+
+
 MUTATIONS = {
     "rounding truncates": ("round_to_storage", m_round_truncates),
     "window mean divides by w-1": ("exact_window_means", m_window_divisor),
@@ -211,6 +236,12 @@ MUTATIONS = {
     "lse in log2": ("sparse_attention", lambda *a: _attention(*a, variant="log2")),
     "closed-form count off by one": ("attended_key_count", m_count_off_by_one),
     "lse merge without exp": ("lse_merge", m_merge_no_exp),
+    "backward drops the dO . O term": (
+        "sparse_attention_backward", lambda *a: _backward(*a, variant="no_delta")),
+    "backward dK without the scale": (
+        "sparse_attention_backward", lambda *a: _backward(*a, variant="dk_unscaled")),
+    "backward dV on the wrong KV head": (
+        "sparse_attention_backward", lambda *a: _backward(*a, variant="dv_transposed_heads")),
 }
 
 

@@ -325,3 +325,57 @@ def test_sparsity_matches_golden_and_page_claim():
     last = orc.attended_key_count(131071, p)
     assert last == gold["last_token_128k"]["keys"]
     assert last / 131072 < gold["last_token_128k"]["page_bound_fraction"]
+
+
+# ----------------------------------------------------------------------------- backward
+
+def _loss(q, k, v, idx, positions, dout, p):
+    O, _ = orc.sparse_attention(q, positions, k, v, idx, p)
+    return float((O * dout).sum())
+
+
+def test_backward_matches_finite_differences():
+    """Gradients of sum(O * dO) by central differences of the oracle's own forward, the
+    selection held fixed (float64 inputs; sampled entries of Q, K and V)."""
+    p = small_params(dtype="f32", topk=3, num_local_blocks=1, num_init_blocks=1)
+    wl = synth.make_prefill("bwd", p, [70], seed=51)
+    q, k, v = (a.astype(np.float64) for a in (wl.q, wl.k, wl.v))
+    res = orc.run_sequence(wl.q, wl.k, wl.v, p, with_attention=False)
+    idx, pos = res.idx, res.positions
+    dout = np.random.default_rng(52).standard_normal(q.shape)
+    dQ, dK, dV = orc.sparse_attention_backward(q, pos, k, v, idx, dout, p)
+    rng = np.random.default_rng(53)
+    eps = 1e-6
+    for name, arr, grad in (("q", q, dQ), ("k", k, dK), ("v", v, dV)):
+        flat = rng.choice(arr.size, 40, replace=False)
+        for f in flat:
+            ix = np.unravel_index(f, arr.shape)
+            saved = arr[ix]
+            arr[ix] = saved + eps
+            up = _loss(q, k, v, idx, pos, dout, p)
+            arr[ix] = saved - eps
+            dn = _loss(q, k, v, idx, pos, dout, p)
+            arr[ix] = saved
+            fd = (up - dn) / (2 * eps)
+            assert abs(fd - grad[ix]) <= 1e-6 * (1 + abs(fd)), (name, ix, fd, grad[ix])
+
+
+def test_backward_dense_reduction_equals_autograd():
+    """With topk covering every block the gradients are those of plain causal attention
+    (torch autograd through scaled_dot_product_attention, float64)."""
+    wl = synth.make("tiny")
+    p = replace(wl.params, topk=8)
+    res = orc.run_sequence(wl.q, wl.k, wl.v, p, with_attention=False)
+    q, k, v = (a.astype(np.float64) for a in (wl.q, wl.k, wl.v))
+    dout = np.random.default_rng(54).standard_normal(q.shape)
+    dQ, dK, dV = orc.sparse_attention_backward(q, res.positions, k, v, res.idx, dout, p)
+    G = p.group
+    tq = torch.from_numpy(q).transpose(0, 1).requires_grad_(True)          # [Hq, L, d]
+    tk = torch.from_numpy(k).transpose(0, 1).requires_grad_(True)          # [Hkv, L, d]
+    tv = torch.from_numpy(v).transpose(0, 1).requires_grad_(True)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk.repeat_interleave(G, 0), tv.repeat_interleave(G, 0), is_causal=True)
+    out.backward(torch.from_numpy(dout).transpose(0, 1))
+    np.testing.assert_allclose(dQ, tq.grad.transpose(0, 1).numpy(), rtol=0, atol=1e-10)
+    np.testing.assert_allclose(dK, tk.grad.transpose(0, 1).numpy(), rtol=0, atol=1e-10)
+    np.testing.assert_allclose(dV, tv.grad.transpose(0, 1).numpy(), rtol=0, atol=1e-10)
