@@ -66,6 +66,9 @@ def _declare(lib):
                                             ctypes.c_size_t, vp, vp, vp]),
         "infllm2_decode_step": (st, [P, S, vp, vp, vp, vp, _I32P, vp, ctypes.c_int32, vp,
                                      ctypes.c_int32, vp, ctypes.c_size_t, vp, vp, vp]),
+        "infllm2_backward_workspace_size": (ctypes.c_size_t, [P, S]),
+        "infllm2_sparse_attn_backward": (st, [P, S, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                              ctypes.c_size_t, vp]),
         "infllm2_status_string": (ctypes.c_char_p, [st]),
         "infllm2_last_error": (ctypes.c_char_p, []),
         "infllm2_version": (ctypes.c_int32, []),
@@ -328,3 +331,27 @@ def decode_step_fused(params, seqs: Seqs, q, k_cache, v_cache, kernels, prev_kv_
         workspace.numel() * workspace.element_size(), _ptr(out, "out", dt),
         _ptr(lse, "lse", torch.float32) if lse is not None else None,
         _stream(stream, q.device)), "infllm2_decode_step")
+
+
+def backward_workspace_size(params, seqs: Seqs) -> int:
+    """Bytes of workspace sparse_attn_backward needs (0: invalid or unsupported arguments)."""
+    p = Params.from_any(params)
+    cp, cs = p.c(), seqs.c()
+    return int(load_library().infllm2_backward_workspace_size(ctypes.byref(cp), ctypes.byref(cs)))
+
+
+def sparse_attn_backward(params, seqs: Seqs, q, k, v, block_idx, out, lse, dout, dq, dk, dv,
+                         workspace, stream=None):
+    """infllm2_sparse_attn_backward: float32 dq, dk, dv for the upstream gradient dout."""
+    p = Params.from_any(params)
+    lib = load_library()
+    dt = _elem_dtype(p)
+    torch = _torch()
+    f32 = torch.float32
+    cp, cs = p.c(), seqs.c()
+    _check(lib.infllm2_sparse_attn_backward(
+        ctypes.byref(cp), ctypes.byref(cs), _ptr(q, "q", dt), _ptr(k, "k", dt), _ptr(v, "v", dt),
+        _ptr(block_idx, "block_idx", torch.int32), _ptr(out, "out", dt), _ptr(lse, "lse", f32),
+        _ptr(dout, "dout", dt), _ptr(dq, "dq", f32), _ptr(dk, "dk", f32), _ptr(dv, "dv", f32),
+        _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream, q.device)), "infllm2_sparse_attn_backward")

@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libinfllm2.so")
-SOURCES = ["compress.hip", "scores.hip", "topk.hip", "attn.hip", "attn_tile.hip", "attn_decode.hip", "api.cpp"]
+SOURCES = ["compress.hip", "scores.hip", "topk.hip", "attn.hip", "attn_tile.hip", "attn_decode.hip",
+           "attn_bwd.hip", "api.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

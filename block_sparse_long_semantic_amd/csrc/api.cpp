@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 
 #include "internal.h"
@@ -354,6 +355,64 @@ infllm2_status infllm2_sparse_attn_decode(const infllm2_params* params, const in
   return hip_status(infllm2::launch_attn_combine(g, params->dtype, t, splits,
                                                  static_cast<const float*>(workspace), out, lse, s),
                     "sparse_attn_decode combine launch");
+}
+
+// Backward metadata: work_prefix over rows, aux[b] = first global KV block of sequence b.
+static infllm2_status bwd_common(const infllm2_params* params, const infllm2_seqs* seqs, Geom* g,
+                                 SeqTable* t, int* n_blocks, int* q_rows) {
+  infllm2_status st = check_params(params, g);
+  if (st != INFLLM2_OK) return st;
+  if ((st = build_table(seqs, *g, false, t)) != INFLLM2_OK) return st;
+  rows_prefix(t);
+  if (!infllm2::attn_tile_supported(*g, params->dtype, *t))
+    return fail(INFLLM2_ERR_UNSUPPORTED,
+                "backward needs bf16, block_size 64, head_dim 64 or 128, group size 8 or 16 and "
+                "at most 2048 reachable blocks per sequence");
+  long long nb = 0, qr = 0;
+  for (int b = 0; b < t->n; ++b) {
+    t->aux[b] = static_cast<int32_t>(nb);
+    nb += (t->kv_len[b] + g->B - 1) / g->B;
+    if (t->q_len[b] > 0) qr = std::max<long long>(qr, static_cast<long long>(t->q_start[b]) + t->q_len[b]);
+  }
+  const long long lim = (1LL << 31) - 1;
+  if (nb * g->Hkv > lim || static_cast<long long>(t->work_prefix[t->n]) * g->Hkv * g->topk > lim)
+    return fail(INFLLM2_ERR_SHAPE, "backward index beyond 2^31 entries");
+  *n_blocks = static_cast<int>(nb);
+  *q_rows = static_cast<int>(qr);
+  return INFLLM2_OK;
+}
+
+size_t infllm2_backward_workspace_size(const infllm2_params* params, const infllm2_seqs* seqs) {
+  Geom g;
+  SeqTable t;
+  int nb = 0, qr = 0;
+  if (bwd_common(params, seqs, &g, &t, &nb, &qr) != INFLLM2_OK) return 0;
+  return infllm2::bwd_workspace(g, t, nb, qr);
+}
+
+infllm2_status infllm2_sparse_attn_backward(const infllm2_params* params,
+                                            const infllm2_seqs* seqs, const void* q,
+                                            const void* k, const void* v,
+                                            const int32_t* block_idx, const void* out,
+                                            const float* lse, const void* dout, float* dq,
+                                            float* dk, float* dv, void* workspace,
+                                            size_t workspace_bytes, void* stream) {
+  Geom g;
+  SeqTable t;
+  int nb = 0, qr = 0;
+  infllm2_status st = bwd_common(params, seqs, &g, &t, &nb, &qr);
+  if (st != INFLLM2_OK) return st;
+  if (!q || !k || !v || !block_idx || !out || !lse || !dout || !dq || !dk || !dv || !workspace)
+    return fail(INFLLM2_ERR_NULL, "a backward tensor or the workspace is NULL");
+  const void* ptrs[] = {q, k, v, block_idx, out, lse, dout, dq, dk, dv, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(INFLLM2_ERR_ALIGN, "backward buffers must be 16-byte aligned");
+  const size_t need = infllm2::bwd_workspace(g, t, nb, qr);
+  if (workspace_bytes < need)
+    return fail(INFLLM2_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  return hip_status(infllm2::launch_attn_bwd(g, t, nb, qr, q, k, v, block_idx, out, lse, dout, dq,
+                                             dk, dv, workspace, static_cast<hipStream_t>(stream)),
+                    "sparse_attn_backward launch");
 }
 
 infllm2_status infllm2_decode_step(const infllm2_params* params, const infllm2_seqs* seqs,

@@ -184,18 +184,24 @@ __device__ __forceinline__ int count_wave_groups(uint32_t m) {
   }
 }
 
-template <int D, int G, int NS, int NW, int TPW>
+// BWD = false: the attention itself (writes out, lse).  BWD = true: dQ for upstream gradient
+// dout, given the forward's lse (natural log) and delta[row, head] = dout . out; the slot then
+// also holds V in A-operand order and K in transposing-read order.
+template <int D, int G, int NS, int NW, int TPW, bool BWD>
 __global__ void __launch_bounds__(64 * NW, 1)
 attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
           const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
-          uint16_t* __restrict__ out, float* __restrict__ lse, int n_items, int item_base) {
+          uint16_t* __restrict__ out, float* __restrict__ lse, int n_items, int item_base,
+          const uint16_t* __restrict__ dout, const float* __restrict__ lse_in,
+          const float* __restrict__ delta, float* __restrict__ dq) {
   constexpr int KS = D / 32;
   constexpr int NT = D / 16;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int MAT = 64 * D * 2;            // bytes of one 64-key matrix
   constexpr int NTHR = 64 * NW;
   static_assert(TPW * NW == kT, "tile = waves x tokens per wave");
-  __shared__ __attribute__((aligned(16))) unsigned char ring[NS][2][MAT];
+  constexpr int NMAT = BWD ? 3 : 2;          // matrices per slot
+  __shared__ __attribute__((aligned(16))) unsigned char ring[NS][NMAT][MAT];
   __shared__ uint32_t bitmap[kMaxUnion / 2];
   __shared__ uint32_t ulist[kMaxUnion];
   __shared__ int wave_tot[NW];
@@ -303,8 +309,15 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
         const int vs_off = (vrow0 * rowstride + 16 * (J % NT)) * 2;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(&ring[slot][0][J * 1024]), 16,
                                                  k_lane_bytes, ks_off, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(&ring[slot][1][J * 1024]), 16,
-                                                 v_lane_bytes, vs_off, 0, 0);
+        if constexpr (BWD) {       // V in A-operand order, K in transposing-read order
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(&ring[slot][1][J * 1024]), 16,
+                                                   k_lane_bytes, ks_off, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(&ring[slot][2][J * 1024]), 16,
+                                                   v_lane_bytes, vs_off, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(&ring[slot][1][J * 1024]), 16,
+                                                   v_lane_bytes, vs_off, 0, 0);
+        }
       }
       return;
     }
@@ -317,18 +330,26 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
       const int kr = krow0 + k_lrow, vr = vrow0 + v_lrow;
       ko += ((kr < last ? kr : last) - kr) * rowstride;
       vo += ((vr < last ? vr : last) - vr) * rowstride;
-      const uint16_t* gk = kb + ko;
-      const uint16_t* gv = vb + vo;
-      __builtin_amdgcn_global_load_lds(gk, (lds_void*)(&ring[slot][0][J * 1024]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(gv, (lds_void*)(&ring[slot][1][J * 1024]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(kb + ko, (lds_void*)(&ring[slot][0][J * 1024]), 16, 0, 0);
+      if constexpr (BWD) {
+        __builtin_amdgcn_global_load_lds(vb + ko, (lds_void*)(&ring[slot][1][J * 1024]), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(kb + vo, (lds_void*)(&ring[slot][2][J * 1024]), 16, 0, 0);
+      } else {
+        __builtin_amdgcn_global_load_lds(vb + vo, (lds_void*)(&ring[slot][1][J * 1024]), 16, 0, 0);
+      }
     }
   };
 
   // ---- per-token state (token tw = TPW*w + tt).  m_run is shared by the 4 lanes of a head (log2
   // units, possibly stale by < kLazy); l_run is this lane's partial row sum.
+  // Backward: dof = dout in the same B-operand order as q, lse2 = lse * log2(e) and dl = delta
+  // for head c16 (+inf / 0 on unused lanes, so their probabilities are 0), o accumulates the
+  // dQ^T tiles (dims x heads).
   bf16x8 qf[TPW][KS];
+  bf16x8 dof[TPW][KS];
   f32x4 o[TPW][NT];
   float m_run[TPW], l_run[TPW];
+  float lse2[TPW], dl[TPW];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
     const int tw = TPW * w + tt;
@@ -336,13 +357,19 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
     l_run[tt] = 0.f;
 #pragma unroll
     for (int n = 0; n < NT; ++n) o[tt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool live = tw < nq && c16 < G;
+    const size_t hrow = static_cast<size_t>(row0 + tw) * Hq + kvh * G + c16;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (tw < nq && c16 < G)
-        qf[tt][ks] = *reinterpret_cast<const bf16x8*>(
-            q + (static_cast<size_t>(row0 + tw) * Hq + kvh * G + c16) * D + 32 * ks + 8 * q4);
-      else
-        qf[tt][ks] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+      qf[tt][ks] = live ? *reinterpret_cast<const bf16x8*>(q + hrow * D + 32 * ks + 8 * q4)
+                        : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+      if constexpr (BWD)
+        dof[tt][ks] = live ? *reinterpret_cast<const bf16x8*>(dout + hrow * D + 32 * ks + 8 * q4)
+                           : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    }
+    if constexpr (BWD) {
+      lse2[tt] = live ? lse_in[hrow] * kLog2e : INFINITY;
+      dl[tt] = live ? delta[hrow] : 0.f;
     }
   }
   // the first NS union blocks are loaded by all waves together
@@ -357,8 +384,9 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   const float qscale = g.scale * kLog2e;
   const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&ring[0][0][0]));
   const uint32_t k_lane = ring_lds + 16 * lane;                                 // + slot, + 1KB*J
-  const uint32_t v_lane = ring_lds + MAT + 16 * (8 * q4 + 2 * (c16 >> 2) + ((c16 & 3) >> 1)) +
-                          8 * (c16 & 1);                                         // + slot, + 512*I
+  // the transposing-read matrix is the last of the slot (V forward, K backward)
+  const uint32_t v_lane = ring_lds + (NMAT - 1) * MAT +
+                          16 * (8 * q4 + 2 * (c16 >> 2) + ((c16 & 3) >> 1)) + 8 * (c16 & 1);
 
   // ---- main loop.  Each wave walks the union list in order and works only on blocks its tokens
   // chose.  Slot u % NS holds block u once ready[slot] == u.  The last wave to finish a block
@@ -393,13 +421,69 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
     }
     asm volatile("" ::: "memory");
     const int key0 = static_cast<int>(ent >> 16) * 64;
-    const uint32_t slot_off = static_cast<uint32_t>(slot) * (2 * MAT);
+    const uint32_t slot_off = static_cast<uint32_t>(slot) * (NMAT * MAT);
     const lds_bf16x8* Kp = (const lds_bf16x8*)(uintptr_t)(k_lane + slot_off);
     const uint32_t vaddr = v_lane + slot_off;
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
       if (!(wm & (1u << tt))) continue;
       const int pos = pos0 + TPW * w + tt;
+      if constexpr (BWD) {
+        // S^T = K Q^T and dP^T = V dO^T in the same key order; P = exp(S*scale - lse) from the
+        // forward's statistics (no running max), dS = P (dP - delta), dQ += dS K.
+        const lds_bf16x8* Vp = (const lds_bf16x8*)(uintptr_t)(k_lane + slot_off + MAT);
+        f32x4 sa[2][2], pa4[2][2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int tp = 0; tp < 2; ++tp) {
+            sa[s][tp] = f32x4{0.f, 0.f, 0.f, 0.f};
+            pa4[s][tp] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp) {
+              const int J = ((2 * s + tp) * KS + ks) * 64;
+              sa[s][tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kp[J], qf[tt][ks], sa[s][tp], 0, 0, 0);
+              pa4[s][tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Vp[J], dof[tt][ks], pa4[s][tp], 0, 0, 0);
+            }
+        const int lim = (key0 + 63 > pos || key0 + 64 > kv_len) ? min(pos, kv_len - 1) - key0 : 63;
+        const float nl = -lse2[tt];
+        const float dd = dl[tt];
+        float dsv[2][2][4];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float p = 32 * s + 8 * q4 + 4 * tp + i > lim
+                                  ? 0.f
+                                  : __builtin_amdgcn_exp2f(fmaf(sa[s][tp][i], qscale, nl));
+              dsv[s][tp][i] = p * (pa4[s][tp][i] - dd);
+            }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x2 d01 = __builtin_convertvector((f32x2){dsv[s][0][0], dsv[s][0][1]}, bf16x2);
+          const bf16x2 d23 = __builtin_convertvector((f32x2){dsv[s][0][2], dsv[s][0][3]}, bf16x2);
+          const bf16x2 d45 = __builtin_convertvector((f32x2){dsv[s][1][0], dsv[s][1][1]}, bf16x2);
+          const bf16x2 d67 = __builtin_convertvector((f32x2){dsv[s][1][2], dsv[s][1][3]}, bf16x2);
+          const bf16x2 dp[4] = {d01, d23, d45, d67};
+          const bf16x8 dsa = __builtin_bit_cast(bf16x8, dp);
+          uint64_t kt[NT][2];
+          read_v_half<NT>(vaddr + 512u * (2 * NT * s), kt);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            const uint64_t both[2] = {kt[n][0], kt[n][1]};
+            o[tt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsa, __builtin_bit_cast(bf16x8, both),
+                                                               o[tt][n], 0, 0, 0);
+          }
+        }
+        continue;
+      }
       // S^T tiles: tile (s, tp) row r' -> key 32s + 8(r'/4) + 4tp + (r'%4); the lane then
       // holds keys 32s + 8*q4 + 4*tp + i for head c16 (raw, unscaled dot products).
       // the four (s, tp) accumulator chains advance together, one k-step at a time
@@ -516,6 +600,27 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
     lds_store(&ready[pending % NS], pending);
   }
 
+  if constexpr (BWD) {
+    // dQ = scale * sum_j dS_j k_j, fp32, same [row, head, dim] layout as q
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      const int tw = TPW * w + tt;
+      if (tw >= nq) continue;
+      const float f = stalled ? __builtin_nanf("") : g.scale;
+      const size_t orow = static_cast<size_t>(row0 + tw) * Hq + kvh * G;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = 4 * q4 + i;
+        if (h < G) {
+          float* dp = dq + (orow + h) * D;
+#pragma unroll
+          for (int n = 0; n < NT; ++n) dp[16 * n + c16] = o[tt][n][i] * f;
+        }
+      }
+    }
+    return;
+  }
+
   // ---- epilogue: combine the 4 lanes' partial sums, normalise and store
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
@@ -583,9 +688,9 @@ hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, con
     const int grid = std::min(round, (n_items - base + 7) / 8 * 8);
 #define INFLLM2_TILE_CASE(DD, GG, NS)                                                         \
   if (g.d == DD && g.G == GG) {                                                               \
-    hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWaves, kT / kWaves>), dim3(grid),              \
+    hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWaves, kT / kWaves, false>), dim3(grid),       \
                        dim3(64 * kWaves), 0, stream, g, t, qq, kk, vv, idx, oo, lse, n_items, \
-                       base);                                                                 \
+                       base, nullptr, nullptr, nullptr, nullptr);                             \
     const hipError_t e = hipGetLastError();                                                   \
     if (e != hipSuccess) return e;                                                            \
     continue;                                                                                 \
@@ -595,6 +700,41 @@ hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, con
     INFLLM2_TILE_CASE(64, 16, 8)
     INFLLM2_TILE_CASE(64, 8, 8)
 #undef INFLLM2_TILE_CASE
+    return hipErrorInvalidValue;
+  }
+  return hipSuccess;
+}
+
+// Gradient of the queries for the same tiles (work_prefix counts tiles of 16 rows): dout is the
+// upstream gradient of out, lse the forward's natural-log statistics and delta[row, head] =
+// dout . out.  Writes dq (fp32, [row, Hq, d]) for every row of every sequence.
+hipError_t launch_attn_tile_dq(const Geom& g, const SeqTable& t, const void* q, const void* k,
+                               const void* v, const int32_t* idx, const void* dout,
+                               const float* lse, const float* delta, float* dq,
+                               hipStream_t stream) {
+  const int n_items = t.work_prefix[t.n] * g.Hkv;
+  if (n_items == 0) return hipSuccess;
+  const int round = kRounds ? (device_cus() / 8) * 8 : (n_items + 7) / 8 * 8;
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const uint16_t* vv = static_cast<const uint16_t*>(v);
+  const uint16_t* dd = static_cast<const uint16_t*>(dout);
+  for (int base = 0; base < n_items; base += round) {
+    const int grid = std::min(round, (n_items - base + 7) / 8 * 8);
+#define INFLLM2_DQ_CASE(DD, GG, NS)                                                           \
+  if (g.d == DD && g.G == GG) {                                                               \
+    hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWaves, kT / kWaves, true>), dim3(grid),        \
+                       dim3(64 * kWaves), 0, stream, g, t, qq, kk, vv, idx, nullptr, nullptr, \
+                       n_items, base, dd, lse, delta, dq);                                    \
+    const hipError_t e = hipGetLastError();                                                   \
+    if (e != hipSuccess) return e;                                                            \
+    continue;                                                                                 \
+  }
+    INFLLM2_DQ_CASE(128, 16, 3)
+    INFLLM2_DQ_CASE(128, 8, 3)
+    INFLLM2_DQ_CASE(64, 16, 6)
+    INFLLM2_DQ_CASE(64, 8, 6)
+#undef INFLLM2_DQ_CASE
     return hipErrorInvalidValue;
   }
   return hipSuccess;

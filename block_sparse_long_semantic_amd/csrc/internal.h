@@ -73,6 +73,19 @@ bool attn_tile_supported(const Geom& g, int dtype, const SeqTable& t);
 hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, const void* k,
                             const void* v, const int32_t* idx, void* out, float* lse,
                             hipStream_t stream);
+// Gradient of the queries by the tile kernel (work_prefix over tiles of 16 rows); delta[row, h]
+// = dout . out.  Writes dq as float32 [row, Hq, d].
+hipError_t launch_attn_tile_dq(const Geom& g, const SeqTable& t, const void* q, const void* k,
+                               const void* v, const int32_t* idx, const void* dout,
+                               const float* lse, const float* delta, float* dq,
+                               hipStream_t stream);
+// Whole backward (dq, dk, dv as float32).  t: work_prefix over query rows, aux[b] the first
+// global KV block of sequence b, n_blocks their total; q_rows bounds every row index + 1.
+size_t bwd_workspace(const Geom& g, const SeqTable& t, int n_blocks, int q_rows);
+hipError_t launch_attn_bwd(const Geom& g, const SeqTable& t, int n_blocks, int q_rows,
+                           const void* q, const void* k, const void* v, const int32_t* idx,
+                           const void* out, const float* lse, const void* dout, float* dq,
+                           float* dk, float* dv, void* workspace, hipStream_t stream);
 // Split-KV decoding attention with the merge done by the last workgroup of each (row, kv head).
 bool attn_decode_supported(const Geom& g, int dtype);
 size_t attn_decode_workspace(const Geom& g, int rows, int nsplit);

@@ -14,6 +14,7 @@
  *   infllm2_sparse_attn_prefill queries, keys, values, idx-> attention output (+ LSE)
  *   infllm2_sparse_attn_decode  the same for a few query rows per sequence, split over the
  *                               selected blocks and merged by log-sum-exp
+ * and, for training, infllm2_sparse_attn_backward (gradients of the prefill attention).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -57,7 +58,7 @@ typedef enum {
   INFLLM2_ERR_SHAPE = 2,       /* inconsistent sizes or sequence metadata */
   INFLLM2_ERR_UNSUPPORTED = 3, /* valid but not implemented (dtype, head_dim, ...) */
   INFLLM2_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
-  INFLLM2_ERR_WORKSPACE = 5,   /* workspace smaller than infllm2_decode_workspace_size() */
+  INFLLM2_ERR_WORKSPACE = 5,   /* workspace smaller than the matching *_workspace_size() */
   INFLLM2_ERR_HIP = 6          /* the HIP runtime reported an error */
 } infllm2_status;
 
@@ -139,6 +140,34 @@ infllm2_status infllm2_sparse_attn_prefill(const infllm2_params* params,
                                            const void* k, const void* v,
                                            const int32_t* block_idx, void* out, float* lse,
                                            void* stream);
+
+/* Bytes of device workspace infllm2_sparse_attn_backward needs for these sequences (0 if the
+ * arguments are invalid or the geometry is unsupported).  It holds delta, the reverse block
+ * index and its offsets; its contents need no initialisation and are scratch between calls. */
+size_t infllm2_backward_workspace_size(const infllm2_params* params, const infllm2_seqs* seqs);
+
+/* Gradients of infllm2_sparse_attn_prefill (model card "Efficient Model Architecture" and
+ * paper summary section 2.1: the sparse attention is trainable), with block_idx held fixed
+ * (the selection is piecewise constant in q and k).  For query row at position i, head h,
+ * KV head g, over the same attended tokens j, with P_j the softmax weights,
+ * delta = dout[row, h] . out[row, h] and dS_j = P_j (dout[row, h] . v[j, g] - delta):
+ *   dq[row, h] = scale * sum_j dS_j k[j, g]
+ *   dk[j, g]  += scale * dS_j q[row, h],   dv[j, g] += P_j dout[row, h]
+ * Inputs are the forward's: q, k, v, block_idx, out and lse (natural log, not NULL) exactly
+ * as infllm2_sparse_attn_prefill wrote them, plus dout [q_rows, Hq, d] (bf16).  Outputs are
+ * float32: dq [q_rows, Hq, d] (every row of every sequence written), dk and dv
+ * [kv_rows, Hkv, d] (every key row of every sequence overwritten; keys no row attends to get
+ * 0).  Supported: bf16, block_size 64, head_dim 64 or 128, Hq/Hkv 8 or 16, at most 2048
+ * reachable blocks per sequence (else INFLLM2_ERR_UNSUPPORTED).  dk and dv are summed with
+ * atomic float32 additions, so their last bits may differ between calls; sequences that
+ * share key rows receive the sum of their gradients. */
+infllm2_status infllm2_sparse_attn_backward(const infllm2_params* params,
+                                            const infllm2_seqs* seqs, const void* q,
+                                            const void* k, const void* v,
+                                            const int32_t* block_idx, const void* out,
+                                            const float* lse, const void* dout, float* dq,
+                                            float* dk, float* dv, void* workspace,
+                                            size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace infllm2_sparse_attn_decode needs for `total_q_rows` query rows
  * (sum of q_len) split `num_splits` ways (0 = the automatic choice).  The workspace holds the

@@ -30,7 +30,7 @@ import numpy as np
 
 __all__ = [
     "Params", "Workload", "DecodeWorkload", "Needle", "round_to_bf16", "make",
-    "make_prefill", "make_decode", "CONFIG_NAMES", "config_params",
+    "make_prefill", "make_decode", "CONFIG_NAMES", "config_params", "make_upstream_grad",
 ]
 
 
@@ -207,6 +207,13 @@ def make_decode(name: str, params: Params, batch: int, max_len: int, steps: int,
         raise ValueError("decode steps run past the cache")
     return DecodeWorkload(name=name, params=p, k=_finish(k, p.dtype), v=_finish(v, p.dtype),
                           q_steps=_finish(q, p.dtype), kv_len0=kv_len0)
+
+
+def make_upstream_grad(shape, seed: int, dtype: str = "bf16") -> np.ndarray:
+    """Upstream gradient of the attention output for backward tests and benchmarks: standard
+    normals (the scale of dO does not matter to the backward's relative accuracy)."""
+    rng = np.random.default_rng(seed)
+    return _finish(_normal(rng, tuple(shape)), dtype)
 
 
 # ---------------------------------------------------------------------------------------

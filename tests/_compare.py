@@ -9,6 +9,8 @@ Parity rules:
               1e-3 relative; forced blocks always present; sizes equal
   attention   max |O - O_oracle(on the HIP path's own indices)| <= 2e-2 (bf16) / 1e-4 (f32);
               |lse - lse_oracle| <= 1e-3 (bf16) / 1e-5 (f32)
+  gradients   |g - g_oracle| <= 2^-7 * m elementwise, m the magnitude of the same sum taken
+              over absolute values (backward_magnitudes); see there for the error budget
 """
 from __future__ import annotations
 
@@ -101,3 +103,61 @@ def check_attention(out: np.ndarray, lse: np.ndarray, ref_out: np.ndarray, ref_l
     assert err <= OUT_TOL[dtype], f"output max-abs error {err} > {OUT_TOL[dtype]}"
     assert lerr <= LSE_TOL[dtype], f"lse max-abs error {lerr} > {LSE_TOL[dtype]}"
     return err, lerr
+
+
+BWD_REL = 2.0 ** -7
+
+
+def backward_magnitudes(q_rows, positions, keys, values, idx, dout, p):
+    """Elementwise error scales of the bf16 backward, from the oracle's own quantities.
+
+    The HIP backward rounds dS (and P, for dV) to bf16 before its matrix products (relative
+    2^-9 each) and forms delta = dO . O from the forward's output, whose error is at most
+    2^-9 (|O_d| + sum_j P_j |v_j,d|) (bf16 P in the forward's P V product, then the bf16
+    store).  With, per (row, head),
+        A   = sum_d |dO_d| (|O_d| + sum_j P_j |v_j,d|)
+        E_j = |dS_j| + P_j (A + sum_d |dO_d| |v_j,d|)
+    the error of dS_j before rounding is below 2^-9 P_j A (delta) plus float32 terms (P from
+    the stored lse, dP summed in float32: about 2^-20 E_j), and its rounding adds 2^-9 E_j:
+    2^-8 E_j in all.  The budget 2^-7 leaves a factor 2 over that worst case, for
+        m_dQ  = scale sum_j E_j |k_j|,   m_dK_j = scale sum E_j |q|,   m_dV_j = sum P_j |dO|."""
+    n, Hq, d = q_rows.shape
+    G = p.group
+    kv_len = keys.shape[0]
+    mq = np.zeros((n, Hq, d))
+    mk = np.zeros((kv_len, p.num_kv_heads, d))
+    mv = np.zeros((kv_len, p.num_kv_heads, d))
+    for r in range(n):
+        pos = int(positions[r])
+        for g in range(p.num_kv_heads):
+            J = orc.attended_keys(idx[r, g], pos, kv_len, p.block_size)
+            kg = keys[J, g, :].astype(np.float64)
+            vg = values[J, g, :].astype(np.float64)
+            qh = q_rows[r, g * G:(g + 1) * G, :].astype(np.float64)
+            do = dout[r, g * G:(g + 1) * G, :].astype(np.float64)
+            z = p.scale * (qh @ kg.T)
+            e = np.exp(z - z.max(axis=1, keepdims=True))
+            P = e / e.sum(axis=1, keepdims=True)                        # [G, |J|]
+            O = P @ vg
+            dS = P * (do @ vg.T - (do * O).sum(axis=1, keepdims=True))
+            A = (np.abs(do) * (np.abs(O) + P @ np.abs(vg))).sum(axis=1, keepdims=True)
+            E = np.abs(dS) + P * (A + np.abs(do) @ np.abs(vg).T)         # [G, |J|]
+            mq[r, g * G:(g + 1) * G, :] = p.scale * (E @ np.abs(kg))
+            mk[J, g, :] += p.scale * (E.T @ np.abs(qh))                  # J has no repeats
+            mv[J, g, :] += P.T @ np.abs(do)
+    return mq, mk, mv
+
+
+def check_gradient(name: str, gpu: np.ndarray, ref: np.ndarray, mag: np.ndarray) -> float:
+    """Returns max |gpu - ref| / (BWD_REL * mag); raises on a violation or a non-finite value."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    assert np.all(np.isfinite(gpu)), f"{name}: non-finite values"
+    d = np.abs(gpu - ref)
+    lim = BWD_REL * mag + 1e-30
+    ratio = float((d / lim).max()) if d.size else 0.0
+    bad = d > lim
+    if bad.any():
+        i = np.unravel_index(int(np.argmax(d / lim)), d.shape)
+        raise AssertionError(f"{name}: error beyond bound at {i}: {gpu[i]} vs {ref[i]} "
+                             f"(bound {lim[i]}, {int(bad.sum())} elements)")
+    return ratio

@@ -19,7 +19,7 @@ def so():
 
 
 def test_library_exports_every_declared_symbol(so):
-    assert len(lib.EXPORTED_SYMBOLS) == 10
+    assert len(lib.EXPORTED_SYMBOLS) == 12
     for name in lib.EXPORTED_SYMBOLS:
         assert hasattr(so, name), name
     assert lib.version() == 100
@@ -156,6 +156,31 @@ def test_decode_workspace(so):
     st = so.infllm2_sparse_attn_decode(ctypes.byref(cp), ctypes.byref(cs), FAKE, FAKE, FAKE, FAKE,
                                        97, FAKE, 1 << 30, FAKE, None, None)
     assert st == SHAPE
+
+
+def call_bwd(so, p, s, lse=FAKE, dq=FAKE, ws=FAKE, ws_bytes=1 << 30):
+    cp, cs = p.c(), s.c()
+    return so.infllm2_sparse_attn_backward(ctypes.byref(cp), ctypes.byref(cs), FAKE, FAKE, FAKE,
+                                           FAKE, FAKE, lse, FAKE, dq, FAKE, FAKE, ws, ws_bytes,
+                                           None)
+
+
+def test_backward_workspace_and_checks(so):
+    p, s = params(), seqs()
+    # delta (rows x Hq float32), then per (KV head, block) segment a count, two offset tables
+    # with a final total each, and the row list (rows x Hkv x topk int32), each 256-byte aligned
+    al = lambda x: (x + 255) // 256 * 256
+    n_seg = 2 * 2                                     # 100 keys -> 2 blocks, 2 KV heads
+    want = al(100 * 32 * 4) + al(n_seg * 4) + 2 * al((n_seg + 1) * 4) + al(100 * 2 * 96 * 4)
+    assert lib.backward_workspace_size(p, s) == want
+    assert call_bwd(so, p, s, ws_bytes=want - 1) == WS and "workspace" in last(so)
+    assert call_bwd(so, p, s, lse=None) == NULL
+    assert call_bwd(so, p, s, dq=MISALIGNED) == ALIGN
+    for bad in (dict(dtype=lib.F32), dict(head_dim=96), dict(num_q_heads=8, num_kv_heads=2)):
+        assert call_bwd(so, params(**bad), s) == UNSUP and "backward" in last(so)
+        assert lib.backward_workspace_size(params(**bad), s) == 0
+    far = seqs(q_len=[1], q_pos0=[2048 * 64], kv_len=[2048 * 64 + 1])
+    assert call_bwd(so, p, far) == UNSUP
 
 
 def test_last_error_is_thread_local(so):
