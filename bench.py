@@ -5,8 +5,10 @@ A step is one pass of the whole prefill path over the 128K-token MiniCPM4-8B-sha
 initial + 2 local blocks): compress_kernels -> block_scores -> topk_select ->
 sparse_attn_prefill, inputs resident in HBM.  `value` is prefill tokens/s of that pass.
 The line also carries the decode measurement (batch 8 x 128K cache, one token each, 16
-consecutive steps with incremental kernel updates), the roofline of the dominant kernel
-(from HIP events on the launch stream) and the CPU oracle timed on a bounded sample.
+consecutive steps with incremental kernel updates), the backward of the attention on the same
+layer (dQ, dK, dV for a seeded upstream gradient, the forward's selection held fixed), the
+roofline of the dominant kernel (from HIP events on the launch stream) and the CPU oracle
+timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--workload prefill128k|prefill32k|varlen]
 """
@@ -35,6 +37,14 @@ SPIN_CYCLES = 24_000_000  # GPU spin before the timed decode steps (about 10 ms 
 SPIN_SECONDS = 0.008      # enqueueing must finish well inside the spin
 ATTN_SOURCES = ["block_sparse_long_semantic_amd/csrc/attn_tile.hip",
                 "block_sparse_long_semantic_amd/csrc/internal.h"]
+BWD_SOURCES = ["block_sparse_long_semantic_amd/csrc/attn_bwd.hip",
+               "block_sparse_long_semantic_amd/csrc/internal.h"]
+# kernels whose HBM traffic the committed counter summary records: role -> (name test, sources)
+TRAFFIC_ROLES = {
+    "prefill_attention": (lambda k: k.startswith("attn_tile") and k.endswith("false>"), ATTN_SOURCES),
+    "backward_dq": (lambda k: k.startswith("attn_tile") and k.endswith("true>"), ATTN_SOURCES),
+    "backward_dkv": (lambda k: k.startswith("bwd_dkv"), BWD_SOURCES),
+}
 
 
 def log(msg):
@@ -114,8 +124,85 @@ def run_prefill(args, torch, pkg, synth):
                    "scores": bytes_scores / (stage["scores"] * 1e-3) / 1e9,
                    "topk": bytes_topk / (stage["topk"] * 1e-3) / 1e9},
         wl=wl, kernels_gpu=bufs["kernels"])
-    del q, k, v, bufs
+    if args.no_backward:
+        del q, k, v, bufs
+    else:
+        result["device"] = dict(q=q, k=k, v=v, seqs=seqs, idx=bufs["idx"], out=bufs["out"],
+                                lse=bufs["lse"])
+        del bufs
     return result
+
+
+def run_backward(args, torch, pkg, synth, pre):
+    """Backward of the attention call on the prefill workload: dout seeded, dq/dk/dv float32."""
+    p, dv_ = pre["p"], pre.pop("device")
+    q, k, v, seqs = dv_["q"], dv_["k"], dv_["v"], dv_["seqs"]
+    dout = torch.from_numpy(synth.make_upstream_grad(tuple(q.shape), 62)).cuda().to(q.dtype)
+    dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    dk = torch.empty(k.shape, dtype=torch.float32, device="cuda")
+    dvv = torch.empty(v.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(pkg.backward_workspace_size(p, seqs), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        pkg.sparse_attn_backward(p, seqs, q, k, v, dv_["idx"], dv_["out"], dv_["lse"], dout, dq,
+                                 dk, dvv, ws, stream=stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        call()
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    # algorithmic work: the five products of an attention backward (S recomputed, dP, dV, dQ,
+    # dK), 2 d flops per (query head, attended key) each
+    flops = 10.0 * p.head_dim * p.num_q_heads * pre["keys"]
+    tflops = flops / (ms * 1e-3) / 1e12
+    # (row, KV head, selected block) pairs; the dK/dV kernel stages, per pair, the row's q and
+    # dout for the group's G heads (bf16) and their lse and delta (float32)
+    lens = pre["seq_lens"]
+    pairs = p.num_kv_heads * sum(int(np.minimum(np.arange(L) // p.block_size + 1, p.topk).sum())
+                                 for L in lens)
+    G = p.num_q_heads // p.num_kv_heads
+    staged = pairs * G * (2 * p.head_dim * 2 + 2 * 4)
+    out = dict(ms_per_call=ms, tokens_per_s=pre["tokens"] / (ms * 1e-3),
+               flops_per_call=flops, tflops=tflops, frac_of_bf16_peak=tflops / PEAK_BF16_TFLOPS,
+               workspace_bytes=int(ws.numel()),
+               note="one infllm2_sparse_attn_backward call (zero-fill, delta and reverse index, "
+                    "dQ kernel, dK/dV kernel); per-kernel times in the committed profile",
+               kernels={
+                   "dq": {"kernel": "attn_tile (gradient form)",
+                          "flops_per_call": 6.0 * p.head_dim * p.num_q_heads * pre["keys"],
+                          "traffic": measured_traffic(pre["workload"], "backward_dq")},
+                   "dkv": {"kernel": "bwd_dkv", "pairs": pairs, "staged_bytes_per_call": staged,
+                           "flops_per_call": 8.0 * p.head_dim * p.num_q_heads * pre["keys"],
+                           "traffic": measured_traffic(pre["workload"], "backward_dkv")}})
+    # the oracle's backward on a bounded sample of rows (every row attends topk blocks)
+    if not args.no_cpu_baseline:
+        from oracle import infllm2_oracle as orc
+        wl = pre["wl"]
+        L = pre["seq_lens"][0]
+        rows = np.linspace(p.topk * p.block_size, L - 1, 4096).astype(np.int64)
+        idx = dv_["idx"][torch.from_numpy(rows).cuda()].cpu().numpy()
+        do = dout[torch.from_numpy(rows).cuda()].float().cpu().numpy()
+        done, t0 = 0, time.perf_counter()
+        while done < len(rows) and time.perf_counter() - t0 < args.cpu_budget / 3:
+            r = slice(done, done + 8)
+            orc.sparse_attention_backward(wl.q[rows[r]], rows[r], wl.k, wl.v, idx[r], do[r], p)
+            done += 8
+        el = time.perf_counter() - t0
+        out["cpu_oracle"] = {"rows_per_s": done / el, "rows": done, "seconds": el,
+                             "cores": int(os.environ.get("OMP_NUM_THREADS", "1")),
+                             "kind": "oracle (float64 numpy, one process)",
+                             "sample": f"{done} rows spread over positions "
+                                       f"{rows[0]}..{rows[min(done, len(rows)) - 1]}",
+                             "speedup_gpu_over_oracle": (pre["tokens"] / (ms * 1e-3)) / (done / el)}
+    del dq, dk, dvv, ws, dout
+    return out
 
 
 def copy_calibration(torch, mib: int):
@@ -138,17 +225,19 @@ def source_digest(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per attention call from the committed counter summary, or None when there is
-    none for this workload or the kernel's source has changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"attn_tile_{workload}_hbm_traffic.md")
+def measured_traffic(workload: str, role: str = "prefill_attention"):
+    """HBM bytes per call of one kernel (TRAFFIC_ROLES) from the committed counter summary, or
+    None when there is none for this workload or the kernel's source has changed since."""
+    path = os.path.join(ROOT, "profiles", f"attention_{workload}_hbm_traffic.md")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         for line in f:
             if line.startswith("bench-data: "):
                 rec = json.loads(line[len("bench-data: "):])
-                if rec.get("source_sha256") != source_digest(ATTN_SOURCES):
+                if rec.get("role") != role:
+                    continue
+                if rec.get("source_sha256") != source_digest(TRAFFIC_ROLES[role][1]):
                     return None
                 return rec
     return None
@@ -361,15 +450,18 @@ def summarize_profile(argv):
     for k, d in sorted(per.items(), key=lambda kv: -sum(kv[1]["fetch"])):
         print(f"| `{k}` | {len(d['fetch'])} | {sum(d['fetch']) * f_fetch / 2**20:.1f} "
               f"| {sum(d['write']) * f_write / 2**20:.1f} |")
-    attn = [k for k in per if k.startswith("attn_tile")]
-    if attn:
-        d = per[attn[0]]
-        rec = {"kernel": attn[0], "workload": workload,
-               "source_sha256": source_digest(ATTN_SOURCES),
+    print()
+    for role, (match, sources) in TRAFFIC_ROLES.items():
+        found = [k for k in per if match(k)]
+        if not found:
+            continue
+        d = per[found[0]]
+        rec = {"role": role, "kernel": found[0], "workload": workload,
+               "source_sha256": source_digest(sources),
                "fetch_bytes_per_call": sum(d["fetch"]) * f_fetch,
                "write_bytes_per_call": sum(d["write"]) * f_write,
                "dispatches_per_call": len(d["fetch"])}
-        print("\nbench-data: " + json.dumps(rec))
+        print("bench-data: " + json.dumps(rec))
 
 
 def main():
@@ -381,6 +473,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=16)
     ap.add_argument("--decode-splits", type=int, default=0)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -440,6 +533,9 @@ def main():
         line["roofline"]["traffic_split"] = {"fetch": tr["fetch_bytes_per_call"],
                                              "write": tr["write_bytes_per_call"],
                                              "unit": "bytes per call"}
+    if not args.no_backward:
+        line["backward"] = run_backward(args, torch, pkg, synth, pre)
+        log(f"backward: {line['backward']['ms_per_call']:.2f} ms/call")
     if not args.no_decode:
         line["decode"] = run_decode(args, torch, pkg, synth)
         log(f"decode: {line['decode']['us_per_step']:.1f} us/step")

@@ -124,22 +124,93 @@ __device__ __forceinline__ void read_tr<4>(const uint32_t (&a0)[4], const uint32
 // LDS reads of the dK/dV kernel's ring and row list.  Written as asm statements that wait for
 // their own results: a plain LDS load would make the compiler first wait for every LDS-DMA
 // load in flight, which would stall the ring's prefetch on every step.
-__device__ __forceinline__ int lds_read_i32(uint32_t addr) {
-  int x;
-  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(x) : "v"(addr) : "memory");
-  return x;
+
+// N 4-byte reads at independent addresses, one wait.
+template <int N>
+__device__ __forceinline__ void lds_read_i32s(const uint32_t (&a)[N], int (&r)[N]);
+
+template <>
+__device__ __forceinline__ void lds_read_i32s<5>(const uint32_t (&a)[5], int (&r)[5]) {
+  asm volatile(
+      "ds_read_b32 %0, %5\n"
+      "ds_read_b32 %1, %6\n"
+      "ds_read_b32 %2, %7\n"
+      "ds_read_b32 %3, %8\n"
+      "ds_read_b32 %4, %9\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4])
+      : "memory");
 }
 
-// Four 16-byte reads at addr + 0, 64, 128, 192.
-__device__ __forceinline__ void lds_read_4x16(uint32_t addr, f32x4 (&r)[4]) {
+template <>
+__device__ __forceinline__ void lds_read_i32s<3>(const uint32_t (&a)[3], int (&r)[3]) {
   asm volatile(
-      "ds_read_b128 %0, %4\n"
-      "ds_read_b128 %1, %4 offset:64\n"
-      "ds_read_b128 %2, %4 offset:128\n"
-      "ds_read_b128 %3, %4 offset:192\n"
+      "ds_read_b32 %0, %3\n"
+      "ds_read_b32 %1, %4\n"
+      "ds_read_b32 %2, %5\n"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-      : "v"(addr)
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2])
+      : "memory");
+}
+
+// First reads of a step: A operands of row tile 0 (q[ks] at a[ks], dout[ks] at a[ks] + OFF),
+// the lse and delta of both row tiles (ld[0..3] at la + 0, 64, 128, 192) and the rows of the
+// two tiles' tokens (p0 at e0, p1 at e1).
+template <int KS, int OFF>
+__device__ __forceinline__ void read_first(const uint32_t (&a)[KS], uint32_t la, uint32_t e0,
+                                           uint32_t e1, bf16x8 (&qa)[KS], bf16x8 (&da)[KS],
+                                           f32x4 (&ld)[4], int& p0, int& p1);
+
+template <>
+__device__ __forceinline__ void read_first<4, 8192>(const uint32_t (&a)[4], uint32_t la,
+                                                    uint32_t e0, uint32_t e1, bf16x8 (&qa)[4],
+                                                    bf16x8 (&da)[4], f32x4 (&ld)[4], int& p0,
+                                                    int& p1) {
+  asm volatile(
+      "ds_read_b128 %0, %14\n"
+      "ds_read_b128 %1, %14 offset:8192\n"
+      "ds_read_b128 %2, %15\n"
+      "ds_read_b128 %3, %15 offset:8192\n"
+      "ds_read_b128 %4, %16\n"
+      "ds_read_b128 %5, %16 offset:8192\n"
+      "ds_read_b128 %6, %17\n"
+      "ds_read_b128 %7, %17 offset:8192\n"
+      "ds_read_b128 %8, %18\n"
+      "ds_read_b128 %9, %18 offset:64\n"
+      "ds_read_b128 %10, %18 offset:128\n"
+      "ds_read_b128 %11, %18 offset:192\n"
+      "ds_read_b32 %12, %19\n"
+      "ds_read_b32 %13, %20\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(qa[0]), "=&v"(da[0]), "=&v"(qa[1]), "=&v"(da[1]), "=&v"(qa[2]), "=&v"(da[2]),
+        "=&v"(qa[3]), "=&v"(da[3]), "=&v"(ld[0]), "=&v"(ld[1]), "=&v"(ld[2]), "=&v"(ld[3]),
+        "=&v"(p0), "=&v"(p1)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(la), "v"(e0), "v"(e1)
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void read_first<2, 4096>(const uint32_t (&a)[2], uint32_t la,
+                                                    uint32_t e0, uint32_t e1, bf16x8 (&qa)[2],
+                                                    bf16x8 (&da)[2], f32x4 (&ld)[4], int& p0,
+                                                    int& p1) {
+  asm volatile(
+      "ds_read_b128 %0, %10\n"
+      "ds_read_b128 %1, %10 offset:4096\n"
+      "ds_read_b128 %2, %11\n"
+      "ds_read_b128 %3, %11 offset:4096\n"
+      "ds_read_b128 %4, %12\n"
+      "ds_read_b128 %5, %12 offset:64\n"
+      "ds_read_b128 %6, %12 offset:128\n"
+      "ds_read_b128 %7, %12 offset:192\n"
+      "ds_read_b32 %8, %13\n"
+      "ds_read_b32 %9, %14\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(qa[0]), "=&v"(da[0]), "=&v"(qa[1]), "=&v"(da[1]), "=&v"(ld[0]), "=&v"(ld[1]),
+        "=&v"(ld[2]), "=&v"(ld[3]), "=&v"(p0), "=&v"(p1)
+      : "v"(a[0]), "v"(a[1]), "v"(la), "v"(e0), "v"(e1)
       : "memory");
 }
 
@@ -405,24 +476,33 @@ bwd_dkv(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __re
     // (waves 2, 3).
     auto issue = [&](int j, int sl) {
       unsigned char* base = &ring[sl][0];
+      constexpr int NJ = CPR / 4;
+      // the rows of every load of this lane (entries past the chunk repeat entry 0)
+      uint32_t ea[NJ + 1];
 #pragma unroll
-      for (int J = 0; J < CPR / 4; ++J) {
+      for (int J = 0; J <= NJ; ++J) {
+        const int U = 256 * J + 64 * w + lane;
+        const int row = J < NJ ? (U / CPR) % 32 : 4 * ((4 * w + lane) & 7);
+        const int e = j * TPS + row / G;
+        ea[J] = ents_lds + 4u * static_cast<uint32_t>(e < ne ? e : 0);
+      }
+      int grow[NJ + 1];
+      lds_read_i32s<NJ + 1>(ea, grow);
+#pragma unroll
+      for (int J = 0; J < NJ; ++J) {
         const int U = 256 * J + 64 * w + lane;
         const int mat = U / (32 * CPR);
         const int row = (U / CPR) % 32;
         const int ch = (U % CPR) ^ (row & (CPR - 1));
-        const int e = j * TPS + row / G;
-        const int grow = lds_read_i32(ents_lds + 4u * static_cast<uint32_t>(e < ne ? e : 0));
         const uint16_t* src = (mat ? dout : q) +
-                              (static_cast<size_t>(grow) * Hq + kvh * G + row % G) * D + 8 * ch;
+                              (static_cast<size_t>(grow[J]) * Hq + kvh * G + row % G) * D + 8 * ch;
         __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + (256 * J + 64 * w) * 16), 16, 0, 0);
       }
       if (lane < 4) {
         const int vv = 4 * w + lane;               // 16-byte unit of the lse|delta area
         const int row = 4 * (vv & 7);
-        const int e = j * TPS + row / G;
-        const int grow = lds_read_i32(ents_lds + 4u * static_cast<uint32_t>(e < ne ? e : 0));
-        const float* src = (vv >> 3 ? delta : lse) + static_cast<size_t>(grow) * Hq + kvh * G + row % G;
+        const float* src =
+            (vv >> 3 ? delta : lse) + static_cast<size_t>(grow[NJ]) * Hq + kvh * G + row % G;
         __builtin_amdgcn_global_load_lds(src, (lds_void*)(base + 2 * MATB + 64 * w), 16, 0, 0);
       }
     };
@@ -434,6 +514,8 @@ bwd_dkv(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __re
       const uint32_t slot = ring_lds + static_cast<uint32_t>((j % kSlots) * SLOT);
       // S and dP for the two row tiles
       f32x4 sacc[2], pacc[2];
+      f32x4 ld[4];                                       // lse u0, lse u1, delta u0, delta u1
+      int prow[2];                                       // the tiles' query rows
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         sacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -444,7 +526,14 @@ bwd_dkv(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __re
           aa[ks] = slot + static_cast<uint32_t>(u * 16 * D * 2) + arow +
                    16u * static_cast<uint32_t>((4 * ks + q4) ^ ax);
         bf16x8 qa[KS], da[KS];
-        read_a<KS, MATB>(aa, qa, da);
+        if (u == 0) {
+          const int e0 = min(j * TPS + (4 * q4) / G, kChunk - 1);
+          const int e1 = min(j * TPS + (16 + 4 * q4) / G, kChunk - 1);
+          read_first<KS, MATB>(aa, slot + 2 * MATB + 16 * q4, ents_lds + 4u * e0, ents_lds + 4u * e1,
+                               qa, da, ld, prow[0], prow[1]);
+        } else {
+          read_a<KS, MATB>(aa, qa, da);
+        }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           sacc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kf[ks], sacc[u], 0, 0, 0);
@@ -454,12 +543,10 @@ bwd_dkv(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __re
       // P and dS; rows 16u + 4q4 + i belong to token j*TPS + (16u + 4q4)/G
       const int key = key0 + 16 * w + c16;
       float pv[2][4], dsv[2][4];
-      f32x4 ld[4];                                       // lse u0, lse u1, delta u0, delta u1
-      lds_read_4x16(slot + 2 * MATB + 16 * q4, ld);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int e = j * TPS + (16 * u + 4 * q4) / G;
-        const int pos = e < ne ? lds_read_i32(ents_lds + 4u * static_cast<uint32_t>(e)) + pos_shift : -1;
+        const int pos = e < ne ? prow[u] + pos_shift : -1;
         const f32x4 l4 = ld[u];
         const f32x4 d4 = ld[2 + u];
 #pragma unroll
@@ -569,17 +656,17 @@ hipError_t launch_attn_bwd(const Geom& g, const SeqTable& t, int n_blocks, int q
                      cnt, n_seg);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (g.d == 128) {
-    hipLaunchKernelGGL(bwd_prep<128>, dim3(rows), dim3(256), 0, stream, g, t, oo, dd, idx, delta, cnt,
-                       n_blocks);
+    hipLaunchKernelGGL(bwd_prep<128>, dim3(rows), dim3(256), 0, stream, g, t, oo, dd, idx,
+                       delta, cnt, n_blocks);
   } else {
-    hipLaunchKernelGGL(bwd_prep<64>, dim3(rows), dim3(256), 0, stream, g, t, oo, dd, idx, delta, cnt,
-                       n_blocks);
+    hipLaunchKernelGGL(bwd_prep<64>, dim3(rows), dim3(256), 0, stream, g, t, oo, dd, idx,
+                       delta, cnt, n_blocks);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_scan, dim3(1), dim3(1024), 0, stream, cnt, seg_off, item_off, n_seg);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_scatter, dim3(rows), dim3(256), 0, stream, g, t, idx, cnt, seg_off, list,
-                     n_blocks);
+  hipLaunchKernelGGL(bwd_scatter, dim3(rows), dim3(256), 0, stream, g, t, idx, cnt, seg_off,
+                     list, n_blocks);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   // dQ: the forward's tile kernel in its gradient form (tiles of 16 rows)

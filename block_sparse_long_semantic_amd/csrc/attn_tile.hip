@@ -186,7 +186,7 @@ __device__ __forceinline__ int count_wave_groups(uint32_t m) {
 
 // BWD = false: the attention itself (writes out, lse).  BWD = true: dQ for upstream gradient
 // dout, given the forward's lse (natural log) and delta[row, head] = dout . out; the slot then
-// also holds V in A-operand order and K in transposing-read order.
+// holds V in the same A-operand order as K, and K's transposing reads come from K's own copy.
 template <int D, int G, int NS, int NW, int TPW, bool BWD>
 __global__ void __launch_bounds__(64 * NW, 1)
 attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -200,8 +200,7 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   constexpr int MAT = 64 * D * 2;            // bytes of one 64-key matrix
   constexpr int NTHR = 64 * NW;
   static_assert(TPW * NW == kT, "tile = waves x tokens per wave");
-  constexpr int NMAT = BWD ? 3 : 2;          // matrices per slot
-  __shared__ __attribute__((aligned(16))) unsigned char ring[NS][NMAT][MAT];
+  __shared__ __attribute__((aligned(16))) unsigned char ring[NS][2][MAT];
   __shared__ uint32_t bitmap[kMaxUnion / 2];
   __shared__ uint32_t ulist[kMaxUnion];
   __shared__ int wave_tot[NW];
@@ -309,11 +308,9 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
         const int vs_off = (vrow0 * rowstride + 16 * (J % NT)) * 2;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(&ring[slot][0][J * 1024]), 16,
                                                  k_lane_bytes, ks_off, 0, 0);
-        if constexpr (BWD) {       // V in A-operand order, K in transposing-read order
+        if constexpr (BWD) {       // V in A-operand order
           __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(&ring[slot][1][J * 1024]), 16,
                                                    k_lane_bytes, ks_off, 0, 0);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(&ring[slot][2][J * 1024]), 16,
-                                                   v_lane_bytes, vs_off, 0, 0);
         } else {
           __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(&ring[slot][1][J * 1024]), 16,
                                                    v_lane_bytes, vs_off, 0, 0);
@@ -333,7 +330,6 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
       __builtin_amdgcn_global_load_lds(kb + ko, (lds_void*)(&ring[slot][0][J * 1024]), 16, 0, 0);
       if constexpr (BWD) {
         __builtin_amdgcn_global_load_lds(vb + ko, (lds_void*)(&ring[slot][1][J * 1024]), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(kb + vo, (lds_void*)(&ring[slot][2][J * 1024]), 16, 0, 0);
       } else {
         __builtin_amdgcn_global_load_lds(vb + vo, (lds_void*)(&ring[slot][1][J * 1024]), 16, 0, 0);
       }
@@ -384,9 +380,13 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   const float qscale = g.scale * kLog2e;
   const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&ring[0][0][0]));
   const uint32_t k_lane = ring_lds + 16 * lane;                                 // + slot, + 1KB*J
-  // the transposing-read matrix is the last of the slot (V forward, K backward)
-  const uint32_t v_lane = ring_lds + (NMAT - 1) * MAT +
-                          16 * (8 * q4 + 2 * (c16 >> 2) + ((c16 & 3) >> 1)) + 8 * (c16 & 1);
+  // Transposing reads: forward, V (matrix 1, stored for them); backward, K (matrix 0, stored in
+  // A-operand order).  In K's order, keys 32s + 8q + 4h + (0..3), dims 16n + 4c .. 4c+3 sit in
+  // unit 64((2s + h)KS + n/2) + 16(2(n%2) + c/2) + 4q + (0..3), half c%2, so a lane's reads of
+  // (h, n) are 512 (NT h + n) bytes apart and each read covers 512 contiguous bytes.
+  const uint32_t v_lane =
+      BWD ? ring_lds + 256 * ((c16 & 3) >> 1) + 64 * q4 + 16 * (c16 >> 2) + 8 * (c16 & 1)
+          : ring_lds + MAT + 16 * (8 * q4 + 2 * (c16 >> 2) + ((c16 & 3) >> 1)) + 8 * (c16 & 1);
 
   // ---- main loop.  Each wave walks the union list in order and works only on blocks its tokens
   // chose.  Slot u % NS holds block u once ready[slot] == u.  The last wave to finish a block
@@ -421,7 +421,7 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
     }
     asm volatile("" ::: "memory");
     const int key0 = static_cast<int>(ent >> 16) * 64;
-    const uint32_t slot_off = static_cast<uint32_t>(slot) * (NMAT * MAT);
+    const uint32_t slot_off = static_cast<uint32_t>(slot) * (2 * MAT);
     const lds_bf16x8* Kp = (const lds_bf16x8*)(uintptr_t)(k_lane + slot_off);
     const uint32_t vaddr = v_lane + slot_off;
 #pragma unroll
@@ -473,11 +473,11 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
           const bf16x2 d67 = __builtin_convertvector((f32x2){dsv[s][1][2], dsv[s][1][3]}, bf16x2);
           const bf16x2 dp[4] = {d01, d23, d45, d67};
           const bf16x8 dsa = __builtin_bit_cast(bf16x8, dp);
-          uint64_t kt[NT][2];
+          uint64_t kt[NT][2];   // read x = NT h + n lands in kt[x / 2][x % 2]
           read_v_half<NT>(vaddr + 512u * (2 * NT * s), kt);
 #pragma unroll
           for (int n = 0; n < NT; ++n) {
-            const uint64_t both[2] = {kt[n][0], kt[n][1]};
+            const uint64_t both[2] = {kt[n / 2][n % 2], kt[NT / 2 + n / 2][n % 2]};
             o[tt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsa, __builtin_bit_cast(bf16x8, both),
                                                                o[tt][n], 0, 0, 0);
           }
@@ -730,10 +730,10 @@ hipError_t launch_attn_tile_dq(const Geom& g, const SeqTable& t, const void* q, 
     if (e != hipSuccess) return e;                                                            \
     continue;                                                                                 \
   }
-    INFLLM2_DQ_CASE(128, 16, 3)
-    INFLLM2_DQ_CASE(128, 8, 3)
-    INFLLM2_DQ_CASE(64, 16, 6)
-    INFLLM2_DQ_CASE(64, 8, 6)
+    INFLLM2_DQ_CASE(128, 16, 4)
+    INFLLM2_DQ_CASE(128, 8, 4)
+    INFLLM2_DQ_CASE(64, 16, 8)
+    INFLLM2_DQ_CASE(64, 8, 8)
 #undef INFLLM2_DQ_CASE
     return hipErrorInvalidValue;
   }
