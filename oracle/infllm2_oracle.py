@@ -29,6 +29,9 @@ abstract for the prefill and decode use):
      Architecture"; arXiv abstract; paper summary section 2.1): with the selected blocks held
      fixed -- the selection is piecewise constant in Q and K, so its derivative is zero almost
      everywhere -- dQ, dK and dV of step 5 for an upstream gradient dO.     -> sparse_attention_backward
+  7. sliding-window attention, the second attention workload the pages name (csdn summary,
+     section 4.1.3: the speculative draft model uses it): causal softmax attention over the
+     `window` most recent tokens, the query's own included.          -> window_attention
 
 The pages give no formula, constant or worked example for steps 2-4.  Where they are silent
 the oracle takes the plainest reading; every such reading is listed in the repository's
@@ -301,6 +304,28 @@ def sparse_attention_backward(q_rows: np.ndarray, positions: np.ndarray, keys: n
             np.add.at(dK[:, g, :], J, p.scale * (dz.T @ qh))
             np.add.at(dV[:, g, :], J, P.T @ do)
     return dQ, dK, dV
+
+
+def window_attention(q_rows: np.ndarray, positions: np.ndarray, keys: np.ndarray,
+                     values: np.ndarray, window: int, p):
+    """O[n, h] = softmax_j(scale * q[n,h] . k[j,g]) v[j,g] over the tokens pos - window < j <= pos
+    (the last `window` tokens up to and including the query), and lse[n, h] (natural log)."""
+    n, Hq, d = q_rows.shape
+    G = p.group
+    O = np.zeros((n, Hq, d), dtype=np.float64)
+    lse = np.zeros((n, Hq), dtype=np.float64)
+    for r in range(n):
+        pos = int(positions[r])
+        J = np.arange(max(0, pos - window + 1), pos + 1)
+        for g in range(p.num_kv_heads):
+            qh = q_rows[r, g * G:(g + 1) * G, :].astype(np.float64)
+            z = p.scale * (qh @ keys[J, g, :].astype(np.float64).T)
+            m = z.max(axis=1, keepdims=True)
+            e = np.exp(z - m)
+            den = e.sum(axis=1, keepdims=True)
+            O[r, g * G:(g + 1) * G, :] = (e / den) @ values[J, g, :].astype(np.float64)
+            lse[r, g * G:(g + 1) * G] = (m + np.log(den))[:, 0]
+    return O, lse
 
 
 # ---------------------------------------------------------------------------------------

@@ -15,7 +15,7 @@ ORIG = {name: getattr(orc, name) for name in (
     "round_to_storage", "exact_window_means", "compress_kernels", "kernel_visible",
     "kernels_of_block", "kernel_scores", "block_scores", "forced_blocks", "select_blocks",
     "attended_keys", "sparse_attention", "attended_key_count", "lse_merge",
-    "sparse_attention_backward")}
+    "sparse_attention_backward", "window_attention")}
 
 # cheapest first; each entry is a pin from test_oracle_pins with its arguments bound
 PINS = [
@@ -41,6 +41,8 @@ PINS = [
     ("presum", pins.test_presum_identity),
     ("backward_fd", pins.test_backward_matches_finite_differences),
     ("backward_autograd", pins.test_backward_dense_reduction_equals_autograd),
+    ("window_one", pins.test_window_of_one_returns_own_value),
+    ("window_sdpa", lambda: pins.test_window_attention_matches_banded_sdpa(64)),
 ]
 
 
@@ -213,6 +215,26 @@ def _backward(q_rows, positions, keys, values, idx, dout, p, variant):
     return dQ, dK, dV
 
 
+def m_window(q_rows, positions, keys, values, window, p, variant):
+    n, Hq, d = q_rows.shape
+    G = p.group
+    O = np.zeros((n, Hq, d))
+    lse = np.zeros((n, Hq))
+    for r in range(n):
+        pos = int(positions[r])
+        lo = max(0, pos - window) if variant == "one_more" else max(0, pos - window + 1)
+        hi = pos if variant == "no_self" else pos + 1
+        J = np.arange(lo, max(hi, lo + 1))
+        for g in range(p.num_kv_heads):
+            z = p.scale * (q_rows[r, g * G:(g + 1) * G, :] @ keys[J, g, :].T)
+            m = z.max(axis=1, keepdims=True)
+            e = np.exp(z - m)
+            den = e.sum(axis=1, keepdims=True)
+            O[r, g * G:(g + 1) * G, :] = (e / den) @ values[J, g, :]
+            lse[r, g * G:(g + 1) * G] = (m + np.log(den))[:, 0]
+    return O, lse
+
+
 MUTATIONS = {
     "rounding truncates": ("round_to_storage", m_round_truncates),
     "window mean divides by w-1": ("exact_window_means", m_window_divisor),
@@ -242,6 +264,9 @@ MUTATIONS = {
         "sparse_attention_backward", lambda *a: _backward(*a, variant="dk_unscaled")),
     "backward dV on the wrong KV head": (
         "sparse_attention_backward", lambda *a: _backward(*a, variant="dv_transposed_heads")),
+    "window one token too long": ("window_attention", lambda *a: m_window(*a, variant="one_more")),
+    "window leaves out the query's own token": (
+        "window_attention", lambda *a: m_window(*a, variant="no_self")),
 }
 
 

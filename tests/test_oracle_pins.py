@@ -379,3 +379,60 @@ def test_backward_dense_reduction_equals_autograd():
     np.testing.assert_allclose(dQ, tq.grad.transpose(0, 1).numpy(), rtol=0, atol=1e-10)
     np.testing.assert_allclose(dK, tk.grad.transpose(0, 1).numpy(), rtol=0, atol=1e-10)
     np.testing.assert_allclose(dV, tv.grad.transpose(0, 1).numpy(), rtol=0, atol=1e-10)
+
+
+# ------------------------------------------------------------------------- sliding window
+
+@pytest.mark.parametrize("window", [1, 5, 64, 100, 1000])
+def test_window_attention_matches_banded_sdpa(window):
+    """Sliding-window attention equals torch SDPA (float64) with an explicit band mask
+    pos - window < j <= pos, for GQA heads; lse equals the band's log-sum-exp (torch)."""
+    p = small_params(dtype="f32", num_q_heads=4, num_kv_heads=2)
+    rng = np.random.default_rng(81)
+    L = 150
+    q = rng.standard_normal((L, 4, p.head_dim))
+    k = rng.standard_normal((L, 2, p.head_dim))
+    v = rng.standard_normal((L, 2, p.head_dim))
+    rows = np.arange(L)
+    O, lse = orc.window_attention(q, rows, k, v, window, p)
+    i = torch.arange(L)[:, None]
+    j = torch.arange(L)[None, :]
+    band = (j <= i) & (j > i - window)
+    qt = torch.from_numpy(q).transpose(0, 1)
+    kt = torch.from_numpy(k).transpose(0, 1).repeat_interleave(2, 0)
+    vt = torch.from_numpy(v).transpose(0, 1).repeat_interleave(2, 0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=band,
+                                                           scale=p.scale)
+    np.testing.assert_allclose(O, ref.transpose(0, 1).numpy(), rtol=0, atol=1e-12)
+    z = p.scale * torch.einsum("hid,hjd->hij", qt, kt).masked_fill(~band, float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(z, dim=2).transpose(0, 1).numpy(),
+                               rtol=0, atol=1e-12)
+
+
+def test_window_of_one_returns_own_value():
+    """A window of one token: the output is that token's value and lse its own scaled logit."""
+    p = small_params(dtype="f32")
+    rng = np.random.default_rng(82)
+    L = 40
+    q = rng.standard_normal((L, p.num_q_heads, p.head_dim))
+    k = rng.standard_normal((L, p.num_kv_heads, p.head_dim))
+    v = rng.standard_normal((L, p.num_kv_heads, p.head_dim))
+    O, lse = orc.window_attention(q, np.arange(L), k, v, 1, p)
+    G = p.group
+    for h in range(p.num_q_heads):
+        np.testing.assert_array_equal(O[:, h], v[:, h // G])
+        np.testing.assert_allclose(lse[:, h], p.scale * (q[:, h] * k[:, h // G]).sum(1),
+                                   rtol=0, atol=1e-13)
+
+
+def test_window_covering_the_past_is_sparse_attention_over_all_blocks():
+    """A window at least as long as the sequence is plain causal attention, which is also what
+    the block-sparse attention computes when every block is selected."""
+    wl = synth.make("tiny")
+    p = replace(wl.params, topk=8)
+    pos = np.arange(512)
+    idx = np.tile(np.arange(8, dtype=np.int32), (512, 1, 1))
+    O1, L1 = orc.window_attention(wl.q, pos, wl.k, wl.v, 512, p)
+    O2, L2 = orc.sparse_attention(wl.q, pos, wl.k, wl.v, idx, p)
+    np.testing.assert_allclose(O1, O2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(L1, L2, rtol=0, atol=1e-13)
