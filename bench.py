@@ -33,6 +33,7 @@ METRIC = "sparse-attn prefill tokens/s @128K + decode µs/token; % MFMA/HBM roof
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 TILE_TOKENS = 16          # query tokens per attention work item
+WINDOW = 6144             # sliding-window leg: 96 blocks x 64 tokens
 SPIN_CYCLES = 24_000_000  # GPU spin before the timed decode steps (about 10 ms at 2.4 GHz)
 SPIN_SECONDS = 0.008      # enqueueing must finish well inside the spin
 ATTN_SOURCES = ["block_sparse_long_semantic_amd/csrc/attn_tile.hip",
@@ -41,8 +42,11 @@ BWD_SOURCES = ["block_sparse_long_semantic_amd/csrc/attn_bwd.hip",
                "block_sparse_long_semantic_amd/csrc/internal.h"]
 # kernels whose HBM traffic the committed counter summary records: role -> (name test, sources)
 TRAFFIC_ROLES = {
-    "prefill_attention": (lambda k: k.startswith("attn_tile") and k.endswith("false>"), ATTN_SOURCES),
-    "backward_dq": (lambda k: k.startswith("attn_tile") and k.endswith("true>"), ATTN_SOURCES),
+    "prefill_attention": (lambda k: k.startswith("attn_tile") and k.endswith("false, false>"),
+                          ATTN_SOURCES),
+    "backward_dq": (lambda k: k.startswith("attn_tile") and k.endswith("true, false>"), ATTN_SOURCES),
+    "window_attention": (lambda k: k.startswith("attn_tile") and k.endswith("false, true>"),
+                         ATTN_SOURCES),
     "backward_dkv": (lambda k: k.startswith("bwd_dkv"), BWD_SOURCES),
 }
 
@@ -124,13 +128,47 @@ def run_prefill(args, torch, pkg, synth):
                    "scores": bytes_scores / (stage["scores"] * 1e-3) / 1e9,
                    "topk": bytes_topk / (stage["topk"] * 1e-3) / 1e9},
         wl=wl, kernels_gpu=bufs["kernels"])
-    if args.no_backward:
+    if args.no_backward and args.no_window:
         del q, k, v, bufs
     else:
         result["device"] = dict(q=q, k=k, v=v, seqs=seqs, idx=bufs["idx"], out=bufs["out"],
                                 lse=bufs["lse"])
         del bufs
     return result
+
+
+def run_window(args, torch, pkg, pre):
+    """Sliding-window attention over the same 128K layer (window WINDOW tokens: the keys a
+    top-96 selection of 64-token blocks covers), timed like the sparse attention call."""
+    p, dv_ = pre["p"], pre["device"]
+    q, k, v, seqs = dv_["q"], dv_["k"], dv_["v"], dv_["seqs"]
+    out = torch.empty_like(q)
+    lse = torch.empty((q.shape[0], p.num_q_heads), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        pkg.sliding_window_attn(p, seqs, WINDOW, q, k, v, out, lse, stream=stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        call()
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    keys = sum(int(np.minimum(np.arange(L) + 1, WINDOW).sum()) for L in pre["seq_lens"])
+    flops = 4.0 * p.head_dim * p.num_q_heads * keys
+    tflops = flops / (ms * 1e-3) / 1e12
+    del out, lse
+    return dict(window=WINDOW, ms_per_call=ms, tokens_per_s=pre["tokens"] / (ms * 1e-3),
+                keys_per_head=keys, flops_per_call=flops,
+                roofline={"kernel": "attn_tile (window form)", "bound": "mfma", "achieved": tflops,
+                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                          "frac": tflops / PEAK_BF16_TFLOPS,
+                          "traffic": measured_traffic(pre["workload"], "window_attention")})
 
 
 def run_backward(args, torch, pkg, synth, pre):
@@ -474,6 +512,7 @@ def main():
     ap.add_argument("--decode-splits", type=int, default=0)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-window", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -533,6 +572,9 @@ def main():
         line["roofline"]["traffic_split"] = {"fetch": tr["fetch_bytes_per_call"],
                                              "write": tr["write_bytes_per_call"],
                                              "unit": "bytes per call"}
+    if not args.no_window:
+        line["window"] = run_window(args, torch, pkg, pre)
+        log(f"window: {line['window']['ms_per_call']:.2f} ms/call")
     if not args.no_backward:
         line["backward"] = run_backward(args, torch, pkg, synth, pre)
         log(f"backward: {line['backward']['ms_per_call']:.2f} ms/call")

@@ -66,6 +66,7 @@ def _declare(lib):
                                             ctypes.c_size_t, vp, vp, vp]),
         "infllm2_decode_step": (st, [P, S, vp, vp, vp, vp, _I32P, vp, ctypes.c_int32, vp,
                                      ctypes.c_int32, vp, ctypes.c_size_t, vp, vp, vp]),
+        "infllm2_sliding_window_attn": (st, [P, S, ctypes.c_int32, vp, vp, vp, vp, vp, vp]),
         "infllm2_backward_workspace_size": (ctypes.c_size_t, [P, S]),
         "infllm2_sparse_attn_backward": (st, [P, S, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                               ctypes.c_size_t, vp]),
@@ -355,3 +356,17 @@ def sparse_attn_backward(params, seqs: Seqs, q, k, v, block_idx, out, lse, dout,
         _ptr(dout, "dout", dt), _ptr(dq, "dq", f32), _ptr(dk, "dk", f32), _ptr(dv, "dv", f32),
         _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream, q.device)), "infllm2_sparse_attn_backward")
+
+
+def sliding_window_attn(params, seqs: Seqs, window: int, q, k, v, out, lse=None, stream=None):
+    """infllm2_sliding_window_attn: attention over the last `window` tokens of each query."""
+    p = Params.from_any(params)
+    lib = load_library()
+    dt = _elem_dtype(p)
+    torch = _torch()
+    cp, cs = p.c(), seqs.c()
+    _check(lib.infllm2_sliding_window_attn(
+        ctypes.byref(cp), ctypes.byref(cs), int(window), _ptr(q, "q", dt), _ptr(k, "k", dt),
+        _ptr(v, "v", dt), _ptr(out, "out", dt),
+        _ptr(lse, "lse", torch.float32) if lse is not None else None,
+        _stream(stream, q.device)), "infllm2_sliding_window_attn")

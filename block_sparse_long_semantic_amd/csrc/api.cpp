@@ -88,6 +88,7 @@ infllm2_status check_params(const infllm2_params* p, Geom* g) {
   g->n_init = p->num_init_blocks;
   g->n_local = p->num_local_blocks;
   g->scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / sqrtf(static_cast<float>(d));
+  g->window = 0;
   return INFLLM2_OK;
 }
 
@@ -303,6 +304,35 @@ infllm2_status infllm2_sparse_attn_prefill(const infllm2_params* params,
   return hip_status(infllm2::launch_attn(g, params->dtype, t, q, k, v, block_idx, 1, out, lse,
                                          nullptr, static_cast<hipStream_t>(stream)),
                     "sparse_attn_prefill launch");
+}
+
+infllm2_status infllm2_sliding_window_attn(const infllm2_params* params,
+                                           const infllm2_seqs* seqs, int32_t window,
+                                           const void* q, const void* k, const void* v,
+                                           void* out, float* lse, void* stream) {
+  Geom g;
+  SeqTable t;
+  infllm2_status st = check_params(params, &g);
+  if (st != INFLLM2_OK) return st;
+  if ((st = build_table(seqs, g, false, &t)) != INFLLM2_OK) return st;
+  if (window < 1) return fail(INFLLM2_ERR_SHAPE, "window %d must be at least 1", window);
+  if (!q || !k || !v || !out) return fail(INFLLM2_ERR_NULL, "q, k, v or out is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (lse && !aligned16(lse)))
+    return fail(INFLLM2_ERR_ALIGN, "attention buffers must be 16-byte aligned");
+  if (!infllm2::attn_tile_supported(g, params->dtype, t))
+    return fail(INFLLM2_ERR_UNSUPPORTED,
+                "sliding-window attention needs bf16, block_size 64, head_dim 64 or 128, group "
+                "size 8 or 16 and queries at positions below 2048 * 64");
+  g.window = window;
+  int acc = 0;
+  for (int b = 0; b < t.n; ++b) {
+    t.work_prefix[b] = acc;
+    acc += (t.q_len[b] + 15) / 16;
+  }
+  t.work_prefix[t.n] = acc;
+  return hip_status(infllm2::launch_attn_tile_window(g, t, q, k, v, out, lse,
+                                                     static_cast<hipStream_t>(stream)),
+                    "sliding_window_attn launch");
 }
 
 static int decode_splits(const Geom& g, int dtype, int rows, int num_splits) {

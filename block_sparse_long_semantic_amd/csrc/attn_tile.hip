@@ -187,7 +187,9 @@ __device__ __forceinline__ int count_wave_groups(uint32_t m) {
 // BWD = false: the attention itself (writes out, lse).  BWD = true: dQ for upstream gradient
 // dout, given the forward's lse (natural log) and delta[row, head] = dout . out; the slot then
 // holds V in the same A-operand order as K, and K's transposing reads come from K's own copy.
-template <int D, int G, int NS, int NW, int TPW, bool BWD>
+// WIN = true (forward only): sliding-window attention over keys pos - g.window < j <= pos; the
+// blocks come from the positions instead of idx.
+template <int D, int G, int NS, int NW, int TPW, bool BWD, bool WIN = false>
 __global__ void __launch_bounds__(64 * NW, 1)
 attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
           const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
@@ -234,10 +236,23 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   // ---- union of the tile's selected blocks
   for (int e = tid; e < (nbt + 1) / 2; e += NTHR) bitmap[e] = 0u;
   __syncthreads();
-  for (int e = tid; e < nq * g.topk; e += NTHR) {
-    const int tok = e / g.topk;
-    const int blk = idx[(static_cast<size_t>(row0 + tok) * Hkv + kvh) * g.topk + (e - tok * g.topk)];
-    if (blk >= 0) atomicOr(&bitmap[blk >> 1], (1u << tok) << (16 * (blk & 1)));
+  if constexpr (WIN) {
+    // token tok needs the blocks meeting [pos - window + 1, pos]
+    const int blo = max(0, pos0 - g.window + 1) / 64;
+    for (int blk = blo + tid; blk < nbt; blk += NTHR) {
+      uint32_t m = 0u;
+      for (int tok = 0; tok < nq; ++tok) {
+        const int pos = pos0 + tok;
+        if (64 * blk <= pos && 64 * blk + 63 > pos - g.window) m |= 1u << tok;
+      }
+      if (m != 0u) atomicOr(&bitmap[blk >> 1], m << (16 * (blk & 1)));
+    }
+  } else {
+    for (int e = tid; e < nq * g.topk; e += NTHR) {
+      const int tok = e / g.topk;
+      const int blk = idx[(static_cast<size_t>(row0 + tok) * Hkv + kvh) * g.topk + (e - tok * g.topk)];
+      if (blk >= 0) atomicOr(&bitmap[blk >> 1], (1u << tok) << (16 * (blk & 1)));
+    }
   }
   __syncthreads();
   {
@@ -507,16 +522,20 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
         for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
           for (int i = 0; i < 4; ++i) sv[s][tp][i] = acc4[s][tp][i];
-      // keys past the query or the sequence end (only in the query's own block or the tail)
-      if (key0 + 63 > pos || key0 + 64 > kv_len) {
+      // keys past the query or the sequence end (only in the query's own block or the tail),
+      // and with a window, keys before it
+      if (key0 + 63 > pos || key0 + 64 > kv_len || (WIN && key0 <= pos - g.window)) {
         const int lim = min(pos, kv_len - 1) - key0;
+        const int lo = WIN ? pos - g.window + 1 - key0 : 0;
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
           for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (32 * s + 8 * q4 + 4 * tp + i > lim) sv[s][tp][i] = -INFINITY;
+            for (int i = 0; i < 4; ++i) {
+              const int kk = 32 * s + 8 * q4 + 4 * tp + i;
+              if (kk > lim || kk < lo) sv[s][tp][i] = -INFINITY;
+            }
       }
       float mx = sv[0][0][0];
 #pragma unroll
@@ -735,6 +754,36 @@ hipError_t launch_attn_tile_dq(const Geom& g, const SeqTable& t, const void* q, 
     INFLLM2_DQ_CASE(64, 16, 8)
     INFLLM2_DQ_CASE(64, 8, 8)
 #undef INFLLM2_DQ_CASE
+    return hipErrorInvalidValue;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_attn_tile_window(const Geom& g, const SeqTable& t, const void* q, const void* k,
+                                   const void* v, void* out, float* lse, hipStream_t stream) {
+  const int n_items = t.work_prefix[t.n] * g.Hkv;
+  if (n_items == 0) return hipSuccess;
+  const int round = kRounds ? (device_cus() / 8) * 8 : (n_items + 7) / 8 * 8;
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const uint16_t* vv = static_cast<const uint16_t*>(v);
+  uint16_t* oo = static_cast<uint16_t*>(out);
+  for (int base = 0; base < n_items; base += round) {
+    const int grid = std::min(round, (n_items - base + 7) / 8 * 8);
+#define INFLLM2_WIN_CASE(DD, GG, NS)                                                          \
+  if (g.d == DD && g.G == GG) {                                                               \
+    hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWaves, kT / kWaves, false, true>), dim3(grid), \
+                       dim3(64 * kWaves), 0, stream, g, t, qq, kk, vv, nullptr, oo, lse,      \
+                       n_items, base, nullptr, nullptr, nullptr, nullptr);                    \
+    const hipError_t e = hipGetLastError();                                                   \
+    if (e != hipSuccess) return e;                                                            \
+    continue;                                                                                 \
+  }
+    INFLLM2_WIN_CASE(128, 16, 4)
+    INFLLM2_WIN_CASE(128, 8, 4)
+    INFLLM2_WIN_CASE(64, 16, 8)
+    INFLLM2_WIN_CASE(64, 8, 8)
+#undef INFLLM2_WIN_CASE
     return hipErrorInvalidValue;
   }
   return hipSuccess;

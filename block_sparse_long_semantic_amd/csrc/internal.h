@@ -30,6 +30,7 @@ struct Geom {
   int32_t B, w, s;
   int32_t topk, n_init, n_local;
   float scale;
+  int32_t window;       // sliding-window attention: keys pos - window < j <= pos (0 = unused)
 };
 
 // Sequence owning work item `item` (linear scan; at most kMaxSeqs entries).
@@ -73,6 +74,10 @@ bool attn_tile_supported(const Geom& g, int dtype, const SeqTable& t);
 hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, const void* k,
                             const void* v, const int32_t* idx, void* out, float* lse,
                             hipStream_t stream);
+// Sliding-window attention by the tile kernel (work_prefix over tiles of 16 rows; g.window >= 1):
+// the blocks each tile needs follow from the positions, no index array.
+hipError_t launch_attn_tile_window(const Geom& g, const SeqTable& t, const void* q, const void* k,
+                                   const void* v, void* out, float* lse, hipStream_t stream);
 // Gradient of the queries by the tile kernel (work_prefix over tiles of 16 rows); delta[row, h]
 // = dout . out.  Writes dq as float32 [row, Hq, d].
 hipError_t launch_attn_tile_dq(const Geom& g, const SeqTable& t, const void* q, const void* k,

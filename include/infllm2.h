@@ -14,7 +14,8 @@
  *   infllm2_sparse_attn_prefill queries, keys, values, idx-> attention output (+ LSE)
  *   infllm2_sparse_attn_decode  the same for a few query rows per sequence, split over the
  *                               selected blocks and merged by log-sum-exp
- * and, for training, infllm2_sparse_attn_backward (gradients of the prefill attention).
+ * and, for training, infllm2_sparse_attn_backward (gradients of the prefill attention), and
+ * infllm2_sliding_window_attn (dense attention over a window of recent tokens).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -140,6 +141,20 @@ infllm2_status infllm2_sparse_attn_prefill(const infllm2_params* params,
                                            const void* k, const void* v,
                                            const int32_t* block_idx, void* out, float* lse,
                                            void* stream);
+
+/* Sliding-window attention, the second attention workload the pages name (paper summary,
+ * section 4.1.3: the speculative draft model uses sliding-window attention to keep the first
+ * token's latency low).  For query row at position i, head h, KV head g = h / (Hq/Hkv):
+ *   O[row, h] = sum_j softmax_j(scale * q[h] . k[j, g]) v[j, g]  over i - window < j <= i,
+ * and lse[row, h] = log sum_j exp(scale * q . k_j) (may be NULL).  No block selection and no
+ * block_idx: the window is given in tokens (>= 1; window >= i + 1 is causal attention).  Same
+ * layouts as infllm2_sparse_attn_prefill; params->topk and the kernel constants are validated
+ * but unused.  Supported: bf16, block_size 64, head_dim 64 or 128, Hq/Hkv 8 or 16, query
+ * positions below 2048 * 64 (else INFLLM2_ERR_UNSUPPORTED). */
+infllm2_status infllm2_sliding_window_attn(const infllm2_params* params,
+                                           const infllm2_seqs* seqs, int32_t window,
+                                           const void* q, const void* k, const void* v,
+                                           void* out, float* lse, void* stream);
 
 /* Bytes of device workspace infllm2_sparse_attn_backward needs for these sequences (0 if the
  * arguments are invalid or the geometry is unsupported).  It holds delta, the reverse block

@@ -19,7 +19,7 @@ def so():
 
 
 def test_library_exports_every_declared_symbol(so):
-    assert len(lib.EXPORTED_SYMBOLS) == 12
+    assert len(lib.EXPORTED_SYMBOLS) == 13
     for name in lib.EXPORTED_SYMBOLS:
         assert hasattr(so, name), name
     assert lib.version() == 100
@@ -181,6 +181,18 @@ def test_backward_workspace_and_checks(so):
         assert lib.backward_workspace_size(params(**bad), s) == 0
     far = seqs(q_len=[1], q_pos0=[2048 * 64], kv_len=[2048 * 64 + 1])
     assert call_bwd(so, p, far) == UNSUP
+
+
+def test_sliding_window_checks(so):
+    p, s = params(), seqs()
+    cp, cs = p.c(), s.c()
+    call = lambda w, q=FAKE, lse=None, pp=cp: so.infllm2_sliding_window_attn(
+        ctypes.byref(pp), ctypes.byref(cs), w, q, FAKE, FAKE, FAKE, lse, None)
+    assert call(0) == SHAPE and "window" in last(so)
+    assert call(16, q=None) == NULL
+    assert call(16, lse=MISALIGNED) == ALIGN
+    cf = params(dtype=lib.F32).c()
+    assert call(16, pp=cf) == UNSUP and "sliding-window" in last(so)
 
 
 def test_last_error_is_thread_local(so):
