@@ -80,6 +80,28 @@ def block_score(q_i, kern, g: int, G: int, pos: int, b: int, B: int, w: int, s: 
     return best
 
 
+def block_score_softmax(q_i, kern, g: int, G: int, pos: int, b: int, B: int, w: int, s: int,
+                        scale: float) -> float:
+    """Score mode 1: each head's logits scale * q_h . kernel over the kernels whose window ends
+    at or before pos are turned into probabilities (exp over the fsum of exps); the block's score
+    is the max, over those kernels whose window meets block b, of the sum of the group's
+    probabilities; -inf if there is none."""
+    seen = [c for c in range(len(kern)) if s * c + w - 1 <= pos]
+    block_tokens = set(range(B * b, B * (b + 1)))
+    meets = [c for c in seen if set(range(s * c, s * c + w)) & block_tokens]
+    if not meets:
+        return -math.inf
+    total = {c: 0.0 for c in meets}
+    for h in range(g * G, (g + 1) * G):
+        logits = {c: scale * math.fsum(q_i[h][e] * kern[c][g][e] for e in range(len(kern[c][g])))
+                  for c in seen}
+        top = max(logits.values())
+        den = math.fsum(math.exp(z - top) for z in logits.values())
+        for c in meets:
+            total[c] += math.exp(logits[c] - top) / den
+    return max(total.values())
+
+
 def choose(scores: List[float], pos: int, B: int, k: int, n_init: int, n_local: int) -> List[int]:
     own = pos // B
     cand = list(range(own + 1))
@@ -93,7 +115,7 @@ def choose(scores: List[float], pos: int, B: int, k: int, n_init: int, n_local: 
 
 
 def run(q, keys, values, Hkv: int, B: int, w: int, s: int, k: int, n_init: int, n_local: int,
-        dtype: str, scale: float, rows=None):
+        dtype: str, scale: float, rows=None, score_mode: int = 0):
     """q: [T][Hq][d] with query t at position t; keys/values: [T][Hkv][d].
     Returns (kernels, scores[t][g][b], idx[t][g], out[t][h][d], lse[t][h])."""
     T = len(keys)
@@ -107,7 +129,8 @@ def run(q, keys, values, Hkv: int, B: int, w: int, s: int, k: int, n_init: int, 
         O_t = [[0.0] * d for _ in range(Hq)]
         L_t = [0.0] * Hq
         for g in range(Hkv):
-            sc = [block_score(q[t], kern, g, G, t, b, B, w, s, scale) if b <= t // B else -math.inf
+            score = block_score_softmax if score_mode == 1 else block_score
+            sc = [score(q[t], kern, g, G, t, b, B, w, s, scale) if b <= t // B else -math.inf
                   for b in range(NB)]
             sel = choose(sc, t, B, k, n_init, n_local)
             S_t.append(sc); I_t.append(sel)

@@ -29,6 +29,10 @@ abstract for the prefill and decode use):
      Architecture"; arXiv abstract; paper summary section 2.1): with the selected blocks held
      fixed -- the selection is piecewise constant in Q and K, so its derivative is zero almost
      everywhere -- dQ, dK and dV of step 5 for an upstream gradient dO.     -> sparse_attention_backward
+  3'. a second reading of step 3's relevance score (the survey's alternative, selected by
+     score_mode = 1): each head's scores are first normalised by a softmax over the kernels
+     visible at the query's position, and the group sum is taken over those probabilities
+     (section 2.1.2 names a relevance score without fixing its form).  -> kernel_scores_softmax
   7. sliding-window attention, the second attention workload the pages name (csdn summary,
      section 4.1.3: the speculative draft model uses it): causal softmax attention over the
      `window` most recent tokens, the query's own included.          -> window_attention
@@ -176,14 +180,41 @@ def kernel_scores(q_rows: np.ndarray, kernels: np.ndarray, num_kv_heads: int,
     return u
 
 
+def kernel_scores_softmax(q_rows: np.ndarray, positions: np.ndarray, kernels: np.ndarray,
+                          p) -> np.ndarray:
+    """Score mode 1: u[n, g, c] = sum over the heads h of group g of P_h[c], where P_h is the
+    softmax, over the kernels visible at the query's position, of scale * q[n, h] . kernel[c, g]
+    (0 for kernels not visible; a row that sees no kernel has u = 0 everywhere)."""
+    n, Hq, d = q_rows.shape
+    G = Hq // p.num_kv_heads
+    C = kernels.shape[0]
+    vis = kernel_visible(np.arange(C)[None, :], np.asarray(positions)[:, None], p.kernel_size,
+                         p.kernel_stride)                                  # [n, C]
+    u = np.zeros((n, p.num_kv_heads, C), dtype=np.float64)
+    for g in range(p.num_kv_heads):
+        kg = kernels[:, g, :].astype(np.float64)
+        for h in range(g * G, (g + 1) * G):
+            z = p.scale * (q_rows[:, h, :].astype(np.float64) @ kg.T)        # [n, C]
+            z = np.where(vis, z, NEG_INF)
+            m = z.max(axis=1, keepdims=True)
+            m = np.where(np.isfinite(m), m, 0.0)
+            e = np.where(vis, np.exp(z - m), 0.0)
+            den = e.sum(axis=1, keepdims=True)
+            u[:, g, :] += np.divide(e, den, out=np.zeros_like(e), where=den > 0)
+    return u
+
+
 def block_scores(q_rows: np.ndarray, positions: np.ndarray, kernels: np.ndarray,
                  p, num_blocks: int) -> np.ndarray:
     """S[n, g, b] = max of u[n, g, c] over the kernels c that overlap block b and are visible
     at the query's position; -inf where no such kernel exists or b lies after the query's
-    own block."""
+    own block.  u is kernel_scores (score_mode 0) or kernel_scores_softmax (score_mode 1)."""
     positions = np.asarray(positions, dtype=np.int64)
     C = kernels.shape[0]
-    u = kernel_scores(q_rows, kernels, p.num_kv_heads, p.scale)
+    if getattr(p, "score_mode", 0) == 1:
+        u = kernel_scores_softmax(q_rows, positions, kernels, p)
+    else:
+        u = kernel_scores(q_rows, kernels, p.num_kv_heads, p.scale)
     vis = kernel_visible(np.arange(C)[None, :], positions[:, None], p.kernel_size, p.kernel_stride)
     u = np.where(vis[:, None, :], u, NEG_INF)
     S = np.full((len(positions), p.num_kv_heads, num_blocks), NEG_INF)

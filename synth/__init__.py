@@ -59,6 +59,7 @@ class Params:
     num_local_blocks: int = 2
     dtype: str = "bf16"          # "bf16" or "f32"
     softmax_scale: float = 0.0   # <= 0 means 1/sqrt(head_dim)
+    score_mode: int = 0          # 0: group sum of scaled dot products; 1: of per-head softmaxes
 
     @property
     def group(self) -> int:

@@ -15,7 +15,7 @@ ORIG = {name: getattr(orc, name) for name in (
     "round_to_storage", "exact_window_means", "compress_kernels", "kernel_visible",
     "kernels_of_block", "kernel_scores", "block_scores", "forced_blocks", "select_blocks",
     "attended_keys", "sparse_attention", "attended_key_count", "lse_merge",
-    "sparse_attention_backward", "window_attention")}
+    "sparse_attention_backward", "window_attention", "kernel_scores_softmax")}
 
 # cheapest first; each entry is a pin from test_oracle_pins with its arguments bound
 PINS = [
@@ -42,6 +42,9 @@ PINS = [
     ("backward_fd", pins.test_backward_matches_finite_differences),
     ("backward_autograd", pins.test_backward_dense_reduction_equals_autograd),
     ("window_one", pins.test_window_of_one_returns_own_value),
+    ("softmax_scipy", pins.test_softmax_scores_against_scipy_softmax),
+    ("softmax_brute", lambda: pins.test_softmax_scores_equal_brute_force(
+        dict(p=pins.small_params(score_mode=1), L=150, seed=91))),
     ("window_sdpa", lambda: pins.test_window_attention_matches_banded_sdpa(64)),
 ]
 
@@ -235,6 +238,32 @@ def m_window(q_rows, positions, keys, values, window, p, variant):
     return O, lse
 
 
+def m_softmax(q_rows, positions, kernels, p, variant):
+    n, Hq, d = q_rows.shape
+    G = Hq // p.num_kv_heads
+    C = kernels.shape[0]
+    vis = orc.kernel_visible(np.arange(C)[None, :], np.asarray(positions)[:, None],
+                             p.kernel_size, p.kernel_stride)
+    if variant == "all_kernels":
+        vis = np.ones_like(vis)
+    u = np.zeros((n, p.num_kv_heads, C))
+    for g in range(p.num_kv_heads):
+        z = np.stack([p.scale * (q_rows[:, h, :] @ kernels[:, g, :].T)
+                      for h in range(g * G, (g + 1) * G)])                  # [G, n, C]
+        z = np.where(vis[None], z, -np.inf)
+        if variant == "group_softmax":                 # one softmax over heads and kernels
+            m = z.max(axis=(0, 2), keepdims=True)
+            e = np.where(vis[None], np.exp(z - np.where(np.isfinite(m), m, 0)), 0)
+            den = e.sum(axis=(0, 2), keepdims=True)
+            u[:, g, :] = (G * e / np.where(den > 0, den, 1)).sum(axis=0)
+        else:
+            m = z.max(axis=2, keepdims=True)
+            e = np.where(vis[None], np.exp(z - np.where(np.isfinite(m), m, 0)), 0)
+            den = e.sum(axis=2, keepdims=True)
+            u[:, g, :] = (e / np.where(den > 0, den, 1)).sum(axis=0)
+    return u
+
+
 MUTATIONS = {
     "rounding truncates": ("round_to_storage", m_round_truncates),
     "window mean divides by w-1": ("exact_window_means", m_window_divisor),
@@ -264,6 +293,10 @@ MUTATIONS = {
         "sparse_attention_backward", lambda *a: _backward(*a, variant="dk_unscaled")),
     "backward dV on the wrong KV head": (
         "sparse_attention_backward", lambda *a: _backward(*a, variant="dv_transposed_heads")),
+    "softmax over invisible kernels too": (
+        "kernel_scores_softmax", lambda *a: m_softmax(*a, variant="all_kernels")),
+    "one softmax across the group's heads": (
+        "kernel_scores_softmax", lambda *a: m_softmax(*a, variant="group_softmax")),
     "window one token too long": ("window_attention", lambda *a: m_window(*a, variant="one_more")),
     "window leaves out the query's own token": (
         "window_attention", lambda *a: m_window(*a, variant="no_self")),

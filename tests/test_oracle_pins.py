@@ -436,3 +436,54 @@ def test_window_covering_the_past_is_sparse_attention_over_all_blocks():
     O2, L2 = orc.sparse_attention(wl.q, pos, wl.k, wl.v, idx, p)
     np.testing.assert_allclose(O1, O2, rtol=0, atol=1e-13)
     np.testing.assert_allclose(L1, L2, rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------------------- score mode 1
+
+@pytest.mark.parametrize("case", [
+    dict(p=small_params(score_mode=1), L=150, seed=91),
+    dict(p=small_params(dtype="f32", topk=3, num_local_blocks=2, num_init_blocks=0,
+                        score_mode=1), L=133, seed=92),
+])
+def test_softmax_scores_equal_brute_force(case):
+    """P4 for score mode 1: the pure-Python statement (per-head exps over an fsum, explicit
+    token sets) gives the same scores and selections."""
+    p, L = case["p"], case["L"]
+    wl = synth.make_prefill("b", p, [L], seed=case["seed"])
+    res = orc.run_sequence(wl.q, wl.k, wl.v, p)
+    kern, S, I, O, LSE = brute.run(to_nested(wl.q), to_nested(wl.k), to_nested(wl.v),
+                                   p.num_kv_heads, p.block_size, p.kernel_size, p.kernel_stride,
+                                   p.topk, p.num_init_blocks, p.num_local_blocks, p.dtype, p.scale,
+                                   score_mode=1)
+    S = np.array(S)
+    fin = np.isfinite(S)
+    assert np.array_equal(fin, np.isfinite(res.scores))
+    np.testing.assert_allclose(res.scores[fin], S[fin], rtol=1e-12, atol=1e-14)
+    assert np.array_equal(res.idx, np.array(I, dtype=np.int32))
+    np.testing.assert_allclose(res.out, np.array(O), rtol=0, atol=1e-12)
+
+
+def test_softmax_scores_against_scipy_softmax():
+    """The per-head normalisation is scipy's softmax over the visible kernels; the group's
+    probabilities sum to G per row; a row that sees exactly one kernel scores G on it."""
+    from scipy.special import softmax
+    p = small_params(score_mode=1)
+    wl = synth.make_prefill("s", p, [90], seed=93)
+    kern = orc.compress_kernels(wl.k, p.kernel_size, p.kernel_stride, p.dtype)
+    pos = np.arange(90)
+    u = orc.kernel_scores_softmax(wl.q, pos, kern, p)
+    C = kern.shape[0]
+    G = p.group
+    for r in range(90):
+        vis = [c for c in range(C) if p.kernel_stride * c + p.kernel_size - 1 <= r]
+        for g in range(p.num_kv_heads):
+            want = np.zeros(C)
+            for h in range(g * G, (g + 1) * G):
+                if vis:
+                    z = p.scale * wl.q[r, h].astype(np.float64) @ kern[vis, g].astype(np.float64).T
+                    want[vis] += softmax(z)
+            np.testing.assert_allclose(u[r, g], want, rtol=1e-12, atol=1e-15)
+            if vis:
+                assert math.isclose(u[r, g].sum(), G, rel_tol=1e-12)
+            if len(vis) == 1:
+                assert math.isclose(u[r, g, vis[0]], G, rel_tol=1e-14)
