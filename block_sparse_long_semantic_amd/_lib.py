@@ -38,7 +38,7 @@ class _CParams(ctypes.Structure):
                 ("kernel_size", ctypes.c_int32), ("kernel_stride", ctypes.c_int32),
                 ("topk", ctypes.c_int32), ("num_init_blocks", ctypes.c_int32),
                 ("num_local_blocks", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("score_mode", ctypes.c_int32)]
 
 
 _I64P = ctypes.POINTER(ctypes.c_int64)
@@ -122,6 +122,7 @@ class Params:
     num_local_blocks: int = 2
     softmax_scale: float = 0.0
     dtype: int = BF16
+    score_mode: int = 0
 
     @staticmethod
     def from_any(p) -> "Params":
@@ -132,7 +133,8 @@ class Params:
             dt = {"bf16": BF16, "f32": F32}[dt]
         return Params(p.num_q_heads, p.num_kv_heads, p.head_dim, p.block_size, p.kernel_size,
                       p.kernel_stride, p.topk, p.num_init_blocks, p.num_local_blocks,
-                      float(getattr(p, "softmax_scale", 0.0)), int(dt))
+                      float(getattr(p, "softmax_scale", 0.0)), int(dt),
+                      int(getattr(p, "score_mode", 0)))
 
     @property
     def scale(self) -> float:
@@ -141,7 +143,7 @@ class Params:
     def c(self) -> _CParams:
         return _CParams(self.num_q_heads, self.num_kv_heads, self.head_dim, self.block_size,
                         self.kernel_size, self.kernel_stride, self.topk, self.num_init_blocks,
-                        self.num_local_blocks, self.softmax_scale, self.dtype)
+                        self.num_local_blocks, self.softmax_scale, self.dtype, self.score_mode)
 
 
 class Seqs:

@@ -89,6 +89,9 @@ infllm2_status check_params(const infllm2_params* p, Geom* g) {
   g->n_local = p->num_local_blocks;
   g->scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / sqrtf(static_cast<float>(d));
   g->window = 0;
+  if (p->score_mode != 0 && p->score_mode != 1)
+    return fail(INFLLM2_ERR_SHAPE, "score_mode %d is neither 0 nor 1", p->score_mode);
+  g->score_mode = p->score_mode;
   return INFLLM2_OK;
 }
 
@@ -216,6 +219,31 @@ infllm2_status infllm2_block_scores(const infllm2_params* params, const infllm2_
   const int need = max_reachable_blocks(t, g.B);
   if (nb_stride < need)
     return fail(INFLLM2_ERR_SHAPE, "nb_stride %d below the %d reachable blocks", nb_stride, need);
+  if (g.score_mode == 1) {
+    if (!infllm2::scores_softmax_mfma_supported(g, params->dtype)) {
+      rows_prefix(&t);
+      return hip_status(infllm2::launch_scores_softmax(g, params->dtype, t, q, kernels, scores,
+                                                       nb_stride, false,
+                                                       static_cast<hipStream_t>(stream)),
+                        "block_scores launch");
+    }
+    // few rows (decoding): every workgroup splits the kernels over its waves
+    long long tiles = 0;
+    const int full_rows = infllm2::scores_softmax_rows(g, false);
+    for (int b = 0; b < t.n; ++b) tiles += (t.q_len[b] + full_rows - 1) / full_rows;
+    const bool split = tiles * g.Hkv < 128;
+    const int rows_per = infllm2::scores_softmax_rows(g, split);
+    int acc = 0;
+    for (int b = 0; b < t.n; ++b) {
+      t.work_prefix[b] = acc;
+      acc += (t.q_len[b] + rows_per - 1) / rows_per;
+    }
+    t.work_prefix[t.n] = acc;
+    return hip_status(infllm2::launch_scores_softmax(g, params->dtype, t, q, kernels, scores,
+                                                     nb_stride, split,
+                                                     static_cast<hipStream_t>(stream)),
+                      "block_scores launch");
+  }
   const bool mfma = params->dtype == INFLLM2_BF16 && g.B == 64 && g.w == 32 && g.s == 16 &&
                     (g.d == 64 || g.d == 128);
   int range_tiles = 0;

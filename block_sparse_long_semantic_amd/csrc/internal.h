@@ -31,6 +31,7 @@ struct Geom {
   int32_t topk, n_init, n_local;
   float scale;
   int32_t window;       // sliding-window attention: keys pos - window < j <= pos (0 = unused)
+  int32_t score_mode;   // 0: group sum of scaled dot products; 1: of per-head softmaxes
 };
 
 // Sequence owning work item `item` (linear scan; at most kMaxSeqs entries).
@@ -61,6 +62,12 @@ hipError_t launch_compress(const Geom& g, int dtype, const SeqTable& t, const vo
 hipError_t launch_scores(const Geom& g, int dtype, const SeqTable& t, const void* q,
                          const void* kernels, float* scores, int nb_stride, int range_tiles,
                          hipStream_t stream);
+// Score mode 1 (per-head softmax over the visible kernels before the group sum).
+bool scores_softmax_mfma_supported(const Geom& g, int dtype);
+int scores_softmax_rows(const Geom& g, bool split);
+hipError_t launch_scores_softmax(const Geom& g, int dtype, const SeqTable& t, const void* q,
+                                 const void* kernels, float* scores, int nb_stride, bool split,
+                                 hipStream_t stream);
 hipError_t launch_topk(const Geom& g, const SeqTable& t, const float* scores, int nb_stride,
                        int max_blocks, int32_t* idx, hipStream_t stream);
 // Attention over blocks idx[row, g, k0 .. k1) for split `sp` of `splits`.  With splits == 1

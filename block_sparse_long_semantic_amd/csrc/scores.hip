@@ -11,6 +11,13 @@
 //                  is exactly one block's four contained kernels for one query row; the
 //                  fifth (halo) kernel 4b-1 comes from the neighbouring lane group.
 //   * scores_simple any dtype and geometry, plain float32 dot products.
+// Score mode 1 (the softmax-normalised reading of the same passage): each head's scaled dot
+// products are turned into a softmax over the kernels the query can see before the group sum,
+//   u[c] = sum_{h in g} exp(scale q[h] . kernel[c] - lse_h),  lse_h over the visible kernels,
+// and S[b] is the max of u over the visible kernels overlapping b.  Per-head products cannot be
+// pre-summed, so this runs as two passes over the kernels (lse, then u):
+//   * scores_softmax_mfma  bf16, 64 / 32 / 16, d in {64, 128}, G in {8, 16}
+//   * scores_softmax_simple any dtype and geometry.
 #include <algorithm>
 
 #include "internal.h"
@@ -309,7 +316,326 @@ scores_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q,
   }
 }
 
+
+// ------------------------------------------------------------------------------ score mode 1
+constexpr float kLog2eS = 1.4426950408889634f;
+constexpr float kLazyS = 8.f;        // log2 headroom before a running max is moved
+
+// One workgroup per (query row, KV head); work_prefix counts query rows.  Thread-strided over
+// the visible kernels: per head, a block-wide max and sum give lse; then every thread takes
+// whole blocks and sums the heads' probabilities of their overlapping kernels.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+scores_softmax_simple(Geom g, SeqTable t, const T* __restrict__ q, const T* __restrict__ kern,
+                      float* __restrict__ scores, int nb_stride) {
+  __shared__ float qh[16][256];
+  __shared__ float lse[16];
+  __shared__ float red[kThreads / 64];
+  const int vrow = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = find_seq(t, vrow);
+  const int j = vrow - t.work_prefix[b];
+  const int row = t.q_start[b] + j;
+  const int pos = t.q_pos0[b] + j;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int e = tid; e < g.G * g.d; e += kThreads)
+    qh[e / g.d][e % g.d] = load_elem(q, (static_cast<size_t>(row) * g.Hq + kvh * g.G) * g.d + e);
+  __syncthreads();
+  const int C = num_kernels(t.kv_len[b], g.w, g.s);
+  const int nvis = pos - g.w + 1 < 0 ? 0 : min(C, (pos - g.w + 1) / g.s + 1);
+  const size_t kbase = static_cast<size_t>(t.kc_start[b]) * g.Hkv * g.d + static_cast<size_t>(kvh) * g.d;
+  auto dot = [&](int h, int c) {
+    float acc = 0.f;
+    const size_t base = kbase + static_cast<size_t>(c) * g.Hkv * g.d;
+    for (int e = 0; e < g.d; ++e) acc += qh[h][e] * load_elem(kern, base + e);
+    return acc * g.scale;
+  };
+  for (int h = 0; h < g.G; ++h) {
+    float m = -INFINITY;
+    for (int c = tid; c < nvis; c += kThreads) m = fmaxf(m, dot(h, c));
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (lane == 0) red[w] = m;
+    __syncthreads();
+    m = red[0];
+    for (int ww = 1; ww < kThreads / 64; ++ww) m = fmaxf(m, red[ww]);
+    __syncthreads();
+    float sum = 0.f;
+    for (int c = tid; c < nvis; c += kThreads) sum += expf(dot(h, c) - m);
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    if (lane == 0) red[w] = sum;
+    __syncthreads();
+    if (tid == 0) {
+      float tot = 0.f;
+      for (int ww = 0; ww < kThreads / 64; ++ww) tot += red[ww];
+      lse[h] = m + logf(tot);
+    }
+    __syncthreads();
+  }
+  const int nb = pos / g.B + 1;
+  float* out = scores + (static_cast<size_t>(row) * g.Hkv + kvh) * nb_stride;
+  for (int blk = tid; blk < nb; blk += kThreads) {
+    const int lo_num = g.B * blk - g.w + 1;
+    const int lo = lo_num <= 0 ? 0 : (lo_num + g.s - 1) / g.s;
+    const int hi = min(nvis, (g.B * (blk + 1) + g.s - 1) / g.s);
+    float best = -INFINITY;
+    for (int c = lo; c < hi; ++c) {
+      float u = 0.f;
+      for (int h = 0; h < g.G; ++h) u += expf(dot(h, c) - lse[h]);
+      best = fmaxf(best, u);
+    }
+    out[blk] = best;
+  }
+}
+
+// Work item = rows of one sequence x one KV head.  A wave holds NCT column tiles of 16
+// (row, head) columns as MFMA A operands (its queries, 16 heads of one row or 8 heads of two)
+// and streams kernel tiles of 16 as B operands from L2 (v_mfma_f32_16x16x32_bf16), so a lane's
+// accumulator holds 4 heads of one row against one kernel.  Pass 1 keeps, per column, a running
+// max (moved lazily, by ballot) and sum of exp2; the 16 kernel lanes are then merged, giving
+// each head's lse.  Pass 2 recomputes the products, turns them into probabilities, sums the
+// group's heads (4 in the lane, the rest by shuffles) and max-pools kernels onto blocks (a block
+// is the 4 kernels of a lane quad plus the one before, from the neighbouring lane or the previous
+// tile).  SPLIT (few rows, e.g. decoding): every wave holds the same columns and takes a
+// quarter of the kernel tiles; the waves' partial maxima and sums are merged through LDS.
+template <int D, int G, bool SPLIT>
+__global__ void __launch_bounds__(kThreads)
+scores_softmax_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
+                    const uint16_t* __restrict__ kern, float* __restrict__ scores,
+                    int nb_stride) {
+  constexpr int KS = D / 32;
+  constexpr int NCT = 4;                          // column tiles per wave
+  constexpr int RPC = 16 / G;                     // rows per column tile
+  constexpr int RPW = NCT * RPC;                  // rows per wave
+  constexpr int ROWS = SPLIT ? RPW : 4 * RPW;     // rows per work item
+  __shared__ float xm[4][NCT][4][4][2];           // SPLIT: [wave][ct][q4][i][m, l]
+  const int total = t.work_prefix[t.n];
+  const int item = total - 1 - static_cast<int>(blockIdx.x);   // latest rows first
+  const int kvh = blockIdx.y;
+  const int b = find_seq(t, item);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c16 = lane & 15;
+  const int q4 = lane >> 4;
+  const int q_len = t.q_len[b];
+  const int r0 = (item - t.work_prefix[b]) * ROWS;
+  const int r_last = min(r0 + ROWS - 1, q_len - 1);
+  const int own_last = (t.q_pos0[b] + r_last) / 64;
+  const int nt = (own_last + 1 + 3) / 4;                        // kernel tiles (4 blocks each)
+  const int C = num_kernels(t.kv_len[b], g.w, g.s);
+  const size_t kbase = static_cast<size_t>(t.kc_start[b]) * g.Hkv * D + static_cast<size_t>(kvh) * D;
+  const float qscale = g.scale * kLog2eS;
+  const int wrow0 = r0 + (SPLIT ? 0 : wave * RPW);              // first row of the wave
+
+  // A operands: column c16 of tile ct = row wrow0 + ct*RPC + c16/G, head c16 % G
+  bf16x8 aq[NCT][KS];
+  int pos_l[NCT];          // position of the row of the lane's accumulator columns (4q4..4q4+3)
+  bool row_ok[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int ra = wrow0 + ct * RPC + c16 / G;
+    const size_t rowa = static_cast<size_t>(t.q_start[b]) + min(ra, q_len - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      aq[ct][ks] = *reinterpret_cast<const bf16x8*>(
+          q + (rowa * g.Hq + kvh * G + c16 % G) * D + 32 * ks + 8 * q4);
+    const int rc = wrow0 + ct * RPC + (4 * q4) / G;
+    row_ok[ct] = rc < q_len;
+    pos_l[ct] = t.q_pos0[b] + min(rc, q_len - 1);
+  }
+  int t_begin = 0, t_end = nt;
+  if constexpr (SPLIT) {
+    const int per = (nt + 3) / 4;
+    t_begin = min(nt, wave * per);
+    t_end = min(nt, t_begin + per);
+  }
+  auto load_b = [&](int tt, bf16x8 (&kb)[KS]) {
+    const int c = min(16 * tt + c16, C > 0 ? C - 1 : 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kb[ks] = C > 0 ? *reinterpret_cast<const bf16x8*>(kern + kbase + static_cast<size_t>(c) * g.Hkv * D +
+                                                       32 * ks + 8 * q4)
+                     : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+  };
+  auto visible = [&](int c, int pos) { return c < C && g.s * c + g.w - 1 <= pos; };
+
+  // ---- pass 1: per column, max and sum of exp2 over the visible kernels
+  float m[NCT][4], l[NCT][4];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m[ct][i] = -INFINITY;
+      l[ct][i] = 0.f;
+    }
+  if (t_begin < t_end) {
+    bf16x8 kb[KS];
+    load_b(t_begin, kb);
+    for (int tt = t_begin; tt < t_end; ++tt) {
+      bf16x8 kn[KS];
+      load_b(min(tt + 1, t_end - 1), kn);
+      const int c = 16 * tt + c16;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[ct][ks], kb[ks], acc, 0, 0, 0);
+        const bool vis = visible(c, pos_l[ct]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = vis ? acc[i] * qscale : -INFINITY;
+          if (__ballot(x > m[ct][i] + kLazyS) != 0ull) {
+            const float mn = fmaxf(m[ct][i], x);
+            l[ct][i] *= mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[ct][i] - mn);
+            m[ct][i] = mn;
+          }
+          if (vis) l[ct][i] += __builtin_amdgcn_exp2f(x - m[ct][i]);
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kb[ks] = kn[ks];
+    }
+  }
+  // merge the 16 kernel lanes of every column (and, SPLIT, the 4 waves)
+  auto merge = [](float& ma, float& la, float mb, float lb) {
+    const float mn = fmaxf(ma, mb);
+    if (mn == -INFINITY) return;
+    la = la * __builtin_amdgcn_exp2f(ma - mn) + lb * __builtin_amdgcn_exp2f(mb - mn);
+    ma = mn;
+  };
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        const float mo = __shfl_xor(m[ct][i], off);
+        const float lo = __shfl_xor(l[ct][i], off);
+        merge(m[ct][i], l[ct][i], mo, lo);
+      }
+  if constexpr (SPLIT) {
+    if (c16 == 0) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xm[wave][ct][q4][i][0] = m[ct][i];
+          xm[wave][ct][q4][i][1] = l[ct][i];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float mm = -INFINITY, ll = 0.f;
+        for (int ww = 0; ww < 4; ++ww) merge(mm, ll, xm[ww][ct][q4][i][0], xm[ww][ct][q4][i][1]);
+        m[ct][i] = mm;
+        l[ct][i] = ll;
+      }
+  }
+  float lse2[NCT][4];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lse2[ct][i] = l[ct][i] > 0.f ? m[ct][i] + log2f(l[ct][i]) : INFINITY;
+
+  // ---- pass 2: probabilities, group sum, block max-pool
+  // with SPLIT a wave starts one tile early (not written) for its first block's halo kernel
+  const int t_first = (SPLIT && t_begin > 0) ? t_begin - 1 : t_begin;
+  if (t_first >= t_end) return;
+  float carry[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) carry[ct] = -INFINITY;
+  const int src_prev = (lane & 48) | ((c16 + 15) & 15);          // lane c16 - 1 of the group
+  const int src_last = (lane & 48) | 15;
+  bf16x8 kb[KS];
+  load_b(t_first, kb);
+  for (int tt = t_first; tt < t_end; ++tt) {
+    bf16x8 kn[KS];
+    load_b(min(tt + 1, t_end - 1), kn);
+    const int c = 16 * tt + c16;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[ct][ks], kb[ks], acc, 0, 0, 0);
+      const bool vis = visible(c, pos_l[ct]);
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sum += vis ? __builtin_amdgcn_exp2f(acc[i] * qscale - lse2[ct][i]) : 0.f;
+      sum += __shfl_xor(sum, 16);                                 // heads of 8 (G = 8: a row)
+      if constexpr (G == 16) sum += __shfl_xor(sum, 32);          // all 16 heads
+      const float u = vis ? sum : -INFINITY;
+      float qm = fmaxf(u, __shfl_xor(u, 1));
+      qm = fmaxf(qm, __shfl_xor(qm, 2));
+      const float prev = __shfl(u, src_prev);
+      const float last = __shfl(u, src_last);
+      const float best = fmaxf(qm, c16 == 0 ? carry[ct] : prev);
+      carry[ct] = last;
+      const int blk = 4 * tt + c16 / 4;
+      const bool writer = (c16 & 3) == 0 && (G == 16 ? q4 == 0 : (q4 & 1) == 0);
+      if (writer && tt >= t_begin && row_ok[ct] && blk <= pos_l[ct] / 64) {
+        const int rc = wrow0 + ct * RPC + (4 * q4) / G;
+        scores[(static_cast<size_t>(t.q_start[b]) + rc) * g.Hkv * nb_stride +
+               static_cast<size_t>(kvh) * nb_stride + blk] = best;
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kb[ks] = kn[ks];
+  }
+}
+
 }  // namespace
+
+bool scores_softmax_mfma_supported(const Geom& g, int dtype) {
+  return dtype == INFLLM2_BF16 && g.B == 64 && g.w == 32 && g.s == 16 && (g.d == 64 || g.d == 128) &&
+         (g.G == 8 || g.G == 16);
+}
+
+int scores_softmax_rows(const Geom& g, bool split) { return (split ? 64 : 256) / g.G; }
+
+// Score mode 1.  work_prefix counts query rows (simple path) or tiles of
+// scores_softmax_rows(g, split) rows (MFMA path).
+hipError_t launch_scores_softmax(const Geom& g, int dtype, const SeqTable& t, const void* q,
+                                 const void* kernels, float* scores, int nb_stride, bool split,
+                                 hipStream_t stream) {
+  const int items = t.work_prefix[t.n];
+  if (items == 0) return hipSuccess;
+  const dim3 grid(items, g.Hkv);
+  if (!scores_softmax_mfma_supported(g, dtype)) {
+    if (g.G > 16 || g.d > 256) return hipErrorInvalidValue;
+    if (dtype == INFLLM2_BF16)
+      hipLaunchKernelGGL(scores_softmax_simple<uint16_t>, grid, dim3(kThreads), 0, stream, g, t,
+                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kernels),
+                         scores, nb_stride);
+    else
+      hipLaunchKernelGGL(scores_softmax_simple<float>, grid, dim3(kThreads), 0, stream, g, t,
+                         static_cast<const float*>(q), static_cast<const float*>(kernels), scores,
+                         nb_stride);
+    return hipGetLastError();
+  }
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(kernels);
+#define INFLLM2_SOFTMAX_CASE(DD, GG)                                                            \
+  if (g.d == DD && g.G == GG) {                                                                 \
+    if (split)                                                                                  \
+      hipLaunchKernelGGL((scores_softmax_mfma<DD, GG, true>), grid, dim3(kThreads), 0, stream, g, \
+                         t, qq, kk, scores, nb_stride);                                         \
+    else                                                                                        \
+      hipLaunchKernelGGL((scores_softmax_mfma<DD, GG, false>), grid, dim3(kThreads), 0, stream,   \
+                         g, t, qq, kk, scores, nb_stride);                                      \
+    return hipGetLastError();                                                                   \
+  }
+  INFLLM2_SOFTMAX_CASE(128, 16)
+  INFLLM2_SOFTMAX_CASE(128, 8)
+  INFLLM2_SOFTMAX_CASE(64, 16)
+  INFLLM2_SOFTMAX_CASE(64, 8)
+#undef INFLLM2_SOFTMAX_CASE
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_scores(const Geom& g, int dtype, const SeqTable& t, const void* q,
                          const void* kernels, float* scores, int nb_stride, int range_tiles,

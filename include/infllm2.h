@@ -79,6 +79,9 @@ typedef struct {
   int32_t num_local_blocks; /* blocks ending at the query's own block always selected (>= 1) */
   float softmax_scale;      /* <= 0 selects 1/sqrt(head_dim) */
   int32_t dtype;            /* infllm2_dtype of Q, K, V, O and the kernels */
+  int32_t score_mode;       /* relevance score of infllm2_block_scores: 0 = group sum of scaled
+                               dot products, 1 = group sum of per-head softmax probabilities
+                               over the visible kernels (see there) */
 } infllm2_params;
 
 #define INFLLM2_MAX_SEQS 64
@@ -114,7 +117,12 @@ infllm2_status infllm2_compress_kernels(const infllm2_params* params, const infl
  * written for blocks b = 0 .. floor(i/B) at scores[row, g, b]; entries after floor(i/B) are
  * not written.  nb_stride >= floor((q_pos0+q_len-1)/B)+1 for every sequence.  bf16 scores use
  * the group-summed query in float32 split into two bf16 parts on the matrix cores (relative
- * error about 2^-16 of sum |q . kernel|); f32 scores use float32 arithmetic. */
+ * error about 2^-16 of sum |q . kernel|); f32 scores use float32 arithmetic.
+ * params->score_mode = 1 takes the other reading of the same passage: each head's scores are
+ * normalised first, u[c] = sum over h of exp(scale q[h] . kernel[c, g] - lse_h), lse_h the
+ * log-sum-exp of that head's scores over the visible kernels, so u[c] lies in [0, G] and sums
+ * to G over the visible kernels; S[b] as above.  Computed in float32 from the exact bf16
+ * products (two passes over the kernels). */
 infllm2_status infllm2_block_scores(const infllm2_params* params, const infllm2_seqs* seqs,
                                     const void* q, const void* kernels, float* scores,
                                     int32_t nb_stride, void* stream);

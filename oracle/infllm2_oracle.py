@@ -191,6 +191,8 @@ def kernel_scores_softmax(q_rows: np.ndarray, positions: np.ndarray, kernels: np
     vis = kernel_visible(np.arange(C)[None, :], np.asarray(positions)[:, None], p.kernel_size,
                          p.kernel_stride)                                  # [n, C]
     u = np.zeros((n, p.num_kv_heads, C), dtype=np.float64)
+    if C == 0:                     # shorter than one window: no kernel, every score is -inf
+        return u
     for g in range(p.num_kv_heads):
         kg = kernels[:, g, :].astype(np.float64)
         for h in range(g * G, (g + 1) * G):

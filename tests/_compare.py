@@ -14,6 +14,7 @@ Parity rules:
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass
 
 import numpy as np
@@ -161,3 +162,48 @@ def check_gradient(name: str, gpu: np.ndarray, ref: np.ndarray, mag: np.ndarray)
         raise AssertionError(f"{name}: error beyond bound at {i}: {gpu[i]} vs {ref[i]} "
                              f"(bound {lim[i]}, {int(bad.sum())} elements)")
     return ratio
+
+
+def softmax_score_rel_bound(q_rows, kernels, positions, p) -> np.ndarray:
+    """Relative error bound [n, Hkv] of score-mode-1 block scores computed in float32.
+
+    Each probability is exp2(x - lse2) with x = log2(e) scale q . kernel: the float32 dot
+    product of exact bf16 products errs by at most d 2^-24 sum |q k| (a = max of scale sum |q k|
+    over the row's heads and visible kernels), lse2 adds the float32 sum of up to n_vis terms
+    (n_vis 2^-24 relative) and that x's error again through the max; exp2, log2 and the group sum
+    add a few float32 ulps.  So |dP / P| <= ln2 (2 log2(e) d 2^-24 a + n_vis 2^-24) + 2^-21, and
+    the block score (a max of sums of such P) has the same relative bound."""
+    positions = np.asarray(positions)
+    n, Hq, d = q_rows.shape
+    G = p.group
+    C = kernels.shape[0]
+    out = np.zeros((n, p.num_kv_heads))
+    for r in range(n):
+        nvis = 0 if positions[r] < p.kernel_size - 1 else min(
+            C, (int(positions[r]) - p.kernel_size + 1) // p.kernel_stride + 1)
+        if nvis == 0:
+            continue
+        for g in range(p.num_kv_heads):
+            aq = np.abs(q_rows[r, g * G:(g + 1) * G, :].astype(np.float64))
+            a = p.scale * (aq @ np.abs(kernels[:nvis, g, :].astype(np.float64)).T).max()
+            out[r, g] = (math.log(2) * (2 * 1.4426950408889634 * d * 2.0 ** -24 * a
+                                        + nvis * 2.0 ** -24) + 2.0 ** -21)
+    return out
+
+
+def check_softmax_scores(gpu, ref, rel, positions, p) -> float:
+    """Identical -inf pattern on reachable blocks; |gpu - ref| <= rel[row, g] * ref elsewhere.
+    Returns the largest error / bound."""
+    own = np.asarray(positions) // p.block_size
+    worst = 0.0
+    for r in range(len(own)):
+        nb = int(own[r]) + 1
+        g_s, r_s = gpu[r, :, :nb].astype(np.float64), ref[r, :, :nb]
+        assert np.array_equal(np.isneginf(g_s), np.isneginf(r_s)), f"-inf pattern differs, row {r}"
+        fin = np.isfinite(r_s)
+        lim = (rel[r][:, None] * np.abs(r_s) + 1e-30)[fin]
+        d = np.abs(g_s[fin] - r_s[fin])
+        if d.size:
+            worst = max(worst, float((d / lim).max()))
+        assert np.all(d <= lim), f"score error beyond bound, row {r}: {(d / lim).max()}"
+    return worst

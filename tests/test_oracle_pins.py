@@ -487,3 +487,14 @@ def test_softmax_scores_against_scipy_softmax():
                 assert math.isclose(u[r, g].sum(), G, rel_tol=1e-12)
             if len(vis) == 1:
                 assert math.isclose(u[r, g, vis[0]], G, rel_tol=1e-14)
+
+
+def test_softmax_scores_without_kernels():
+    """A sequence shorter than one kernel window has no kernels: every block score is -inf in
+    both score modes (windows complete only; kernel visible only once its last token is seen)."""
+    for mode in (0, 1):
+        p = small_params(score_mode=mode)
+        wl = synth.make_prefill("s", p, [p.kernel_size - 1], seed=94)
+        res = orc.run_sequence(wl.q, wl.k, wl.v, p)
+        assert res.kernels.shape[0] == 0
+        assert np.all(np.isneginf(res.scores))
