@@ -128,13 +128,49 @@ def run_prefill(args, torch, pkg, synth):
                    "scores": bytes_scores / (stage["scores"] * 1e-3) / 1e9,
                    "topk": bytes_topk / (stage["topk"] * 1e-3) / 1e9},
         wl=wl, kernels_gpu=bufs["kernels"])
-    if args.no_backward and args.no_window:
+    if args.no_backward and args.no_window and args.no_score_mode1:
         del q, k, v, bufs
     else:
         result["device"] = dict(q=q, k=k, v=v, seqs=seqs, idx=bufs["idx"], out=bufs["out"],
-                                lse=bufs["lse"])
+                                lse=bufs["lse"], scores=bufs["scores"])
         del bufs
     return result
+
+
+def run_score_mode1(args, torch, pkg, pre):
+    """Block scores in score mode 1 (per-head softmax over the visible kernels before the group
+    sum) on the same layer and kernels; algorithmic work = the per-head products once."""
+    from dataclasses import replace
+    p = replace(pkg.Params.from_any(pre["p"]), score_mode=1)
+    dv_ = pre["device"]
+    stream = torch.cuda.current_stream()
+
+    def call():
+        pkg.block_scores(p, dv_["seqs"], dv_["q"], pre["kernels_gpu"], dv_["scores"], stream=stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        call()
+        ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    vis = 0
+    for L in pre["seq_lens"]:
+        i = np.arange(L, dtype=np.int64)
+        C = 0 if L < p.kernel_size else (L - p.kernel_size) // p.kernel_stride + 1
+        vis += int(np.clip((i - p.kernel_size + 1) // p.kernel_stride + 1, 0, C).sum())
+    flops = 2.0 * p.head_dim * p.num_q_heads * vis
+    tflops = flops / (ms * 1e-3) / 1e12
+    return dict(ms_per_call=ms, visible_kernels=vis, flops_per_call=flops,
+                note="two passes over the kernels (lse, then probabilities); flops count the "
+                     "per-head products once",
+                roofline={"kernel": "scores_softmax_mfma", "bound": "mfma", "achieved": tflops,
+                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                          "frac": tflops / PEAK_BF16_TFLOPS})
 
 
 def run_window(args, torch, pkg, pre):
@@ -513,6 +549,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-window", action="store_true")
+    ap.add_argument("--no-score-mode1", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -572,6 +609,9 @@ def main():
         line["roofline"]["traffic_split"] = {"fetch": tr["fetch_bytes_per_call"],
                                              "write": tr["write_bytes_per_call"],
                                              "unit": "bytes per call"}
+    if not args.no_score_mode1:
+        line["score_mode1"] = run_score_mode1(args, torch, pkg, pre)
+        log(f"score mode 1: {line['score_mode1']['ms_per_call']:.2f} ms/call")
     if not args.no_window:
         line["window"] = run_window(args, torch, pkg, pre)
         log(f"window: {line['window']['ms_per_call']:.2f} ms/call")

@@ -201,7 +201,7 @@ def check_softmax_scores(gpu, ref, rel, positions, p) -> float:
         g_s, r_s = gpu[r, :, :nb].astype(np.float64), ref[r, :, :nb]
         assert np.array_equal(np.isneginf(g_s), np.isneginf(r_s)), f"-inf pattern differs, row {r}"
         fin = np.isfinite(r_s)
-        lim = (rel[r][:, None] * np.abs(r_s) + 1e-30)[fin]
+        lim = np.broadcast_to(rel[r][:, None], r_s.shape)[fin] * np.abs(r_s[fin]) + 1e-30
         d = np.abs(g_s[fin] - r_s[fin])
         if d.size:
             worst = max(worst, float((d / lim).max()))
