@@ -169,6 +169,15 @@ __device__ __forceinline__ void lds_store(int* p, int x) {
   __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
+// Chunk swizzle of row-major K rows: for the 16 rows of one A-operand read (8(c16/4) + c16%4
+// plus a multiple of 4) it is distinct per row parity class, so the 16 lanes of a read hit
+// distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  if constexpr (D == 128) return ((row >> 1) & 12) | (row & 3);
+  else return ((row >> 2) & 6) | ((row >> 1) & 1);
+}
+
 // Number of TPW-bit token groups (waves) with any bit set in a 16-bit token mask.
 template <int TPW>
 __device__ __forceinline__ int count_wave_groups(uint32_t m) {
@@ -288,8 +297,11 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
 
   // ---- staging.  global_load_lds writes lane l's 16 bytes at LDS unit base+l, and each lane
   // picks its own source, so both matrices are stored in the order their readers want:
-  //   K: unit 64*J + lane holds the A-operand chunk that lane reads for MFMA step J, i.e.
-  //      J = (2s + tp)*KS + ks, row 32s + 8(c16/4) + 4tp + c16%4, chunk 4ks + q4;
+  //   K (forward): row-major, load J covering rows RPI*J .. RPI*J + RPI-1 whole (full-row
+  //      reads stream several times faster than short segments), row r's chunk c stored at
+  //      position c ^ kswz(r), which spreads the 16 rows of one A-operand read over all banks;
+  //   K (gradient form): unit 64*J + lane holds the A-operand chunk that lane reads for MFMA
+  //      step J, i.e. J = (2s + tp)*KS + ks, row 32s + 8(c16/4) + 4tp + c16%4, chunk 4ks + q4;
   //   V: unit 32*((s*NT + n)*2 + h) + 8q + 2j + a1 holds row 32s + 8q + 4h + j, chunk 2n + a1,
   //      so every transposing read of (s, n, h) covers 512 contiguous bytes.
   // Both offsets split into a lane part (VGPR) and a part that depends only on the load J.
@@ -305,6 +317,10 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   // so no per-load address arithmetic.  The ragged last block clamps rows per lane instead.
   const int k_lane_bytes = 2 * k_lane_off;
   const int v_lane_bytes = 2 * v_lane_off;
+  constexpr bool KROW = !BWD;
+  constexpr int RPI = 64 / CPR;                                 // K rows per load (row-major)
+  const int kr_lane = lane / CPR;
+  const int kp_lane = lane % CPR;
   auto produce = [&](int u, int slot, int j0, int dj) {
     const int key0 = __builtin_amdgcn_readfirstlane(static_cast<int>(ulist[u] >> 16)) * 64;
     const bool tail = key0 + 64 > kv_len;
@@ -321,8 +337,15 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
         const int vrow0 = 32 * (J / NT);
         const int ks_off = (krow0 * rowstride + 32 * (J % KS)) * 2;
         const int vs_off = (vrow0 * rowstride + 16 * (J % NT)) * 2;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(&ring[slot][0][J * 1024]), 16,
-                                                 k_lane_bytes, ks_off, 0, 0);
+        if constexpr (KROW) {
+          const int c = kp_lane ^ kswz<D>(RPI * J + kr_lane);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(&ring[slot][0][J * 1024]), 16,
+                                                   (kr_lane * rowstride + 8 * c) * 2,
+                                                   RPI * J * rowstride * 2, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(&ring[slot][0][J * 1024]), 16,
+                                                   k_lane_bytes, ks_off, 0, 0);
+        }
         if constexpr (BWD) {       // V in A-operand order
           __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(&ring[slot][1][J * 1024]), 16,
                                                    k_lane_bytes, ks_off, 0, 0);
@@ -342,6 +365,10 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
       const int kr = krow0 + k_lrow, vr = vrow0 + v_lrow;
       ko += ((kr < last ? kr : last) - kr) * rowstride;
       vo += ((vr < last ? vr : last) - vr) * rowstride;
+      if constexpr (KROW) {
+        const int row = RPI * J + kr_lane;
+        ko = (row < last ? row : last) * rowstride + 8 * (kp_lane ^ kswz<D>(row));
+      }
       __builtin_amdgcn_global_load_lds(kb + ko, (lds_void*)(&ring[slot][0][J * 1024]), 16, 0, 0);
       if constexpr (BWD) {
         __builtin_amdgcn_global_load_lds(vb + ko, (lds_void*)(&ring[slot][1][J * 1024]), 16, 0, 0);
@@ -395,6 +422,13 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   const float qscale = g.scale * kLog2e;
   const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&ring[0][0][0]));
   const uint32_t k_lane = ring_lds + 16 * lane;                                 // + slot, + 1KB*J
+  // row-major K: lane's A-operand chunk for k-step ks of row 8(c16/4) + c16%4 (+ 32s + 4tp)
+  uint32_t kofs[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int krl = 8 * (c16 >> 2) + (c16 & 3);
+    kofs[ks] = ring_lds + static_cast<uint32_t>(krl * 2 * D + 16 * ((4 * ks + q4) ^ kswz<D>(krl)));
+  }
   // Transposing reads: forward, V (matrix 1, stored for them); backward, K (matrix 0, stored in
   // A-operand order).  In K's order, keys 32s + 8q + 4h + (0..3), dims 16n + 4c .. 4c+3 sit in
   // unit 64((2s + h)KS + n/2) + 16(2(n%2) + c/2) + 4q + (0..3), half c%2, so a lane's reads of
@@ -514,7 +548,8 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
 #pragma unroll
           for (int tp = 0; tp < 2; ++tp)
             acc4[s][tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                Kp[((2 * s + tp) * KS + ks) * 64], qf[tt][ks], acc4[s][tp], 0, 0, 0);
+                *(const lds_bf16x8*)(uintptr_t)(kofs[ks] + slot_off + (32 * s + 4 * tp) * 2 * D),
+                qf[tt][ks], acc4[s][tp], 0, 0, 0);
       float sv[2][2][4];
 #pragma unroll
       for (int s = 0; s < 2; ++s)
