@@ -301,7 +301,8 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   //      reads stream several times faster than short segments), row r's chunk c stored at
   //      position c ^ kswz(r), which spreads the 16 rows of one A-operand read over all banks;
   //   K (gradient form): unit 64*J + lane holds the A-operand chunk that lane reads for MFMA
-  //      step J, i.e. J = (2s + tp)*KS + ks, row 32s + 8(c16/4) + 4tp + c16%4, chunk 4ks + q4;
+  //      step J, i.e. J = (2s + tp)*KS + ks, row 32s + 8(c16/4) + 4tp + c16%4, chunk 4ks + q4
+  //      (its transposing reads for dQ rely on this order); V then is row-major like K above;
   //   V: unit 32*((s*NT + n)*2 + h) + 8q + 2j + a1 holds row 32s + 8q + 4h + j, chunk 2n + a1,
   //      so every transposing read of (s, n, h) covers 512 contiguous bytes.
   // Both offsets split into a lane part (VGPR) and a part that depends only on the load J.
@@ -346,9 +347,11 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
           __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(&ring[slot][0][J * 1024]), 16,
                                                    k_lane_bytes, ks_off, 0, 0);
         }
-        if constexpr (BWD) {       // V in A-operand order
+        if constexpr (BWD) {       // V row-major like the forward's K (it is an A operand here)
+          const int c = kp_lane ^ kswz<D>(RPI * J + kr_lane);
           __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(&ring[slot][1][J * 1024]), 16,
-                                                   k_lane_bytes, ks_off, 0, 0);
+                                                   (kr_lane * rowstride + 8 * c) * 2,
+                                                   RPI * J * rowstride * 2, 0, 0);
         } else {
           __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(&ring[slot][1][J * 1024]), 16,
                                                    v_lane_bytes, vs_off, 0, 0);
@@ -371,7 +374,9 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
       }
       __builtin_amdgcn_global_load_lds(kb + ko, (lds_void*)(&ring[slot][0][J * 1024]), 16, 0, 0);
       if constexpr (BWD) {
-        __builtin_amdgcn_global_load_lds(vb + ko, (lds_void*)(&ring[slot][1][J * 1024]), 16, 0, 0);
+        const int row = RPI * J + kr_lane;
+        const int vo_r = (row < last ? row : last) * rowstride + 8 * (kp_lane ^ kswz<D>(row));
+        __builtin_amdgcn_global_load_lds(vb + vo_r, (lds_void*)(&ring[slot][1][J * 1024]), 16, 0, 0);
       } else {
         __builtin_amdgcn_global_load_lds(vb + vo, (lds_void*)(&ring[slot][1][J * 1024]), 16, 0, 0);
       }
@@ -480,7 +485,6 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
       if constexpr (BWD) {
         // S^T = K Q^T and dP^T = V dO^T in the same key order; P = exp(S*scale - lse) from the
         // forward's statistics (no running max), dS = P (dP - delta), dQ += dS K.
-        const lds_bf16x8* Vp = (const lds_bf16x8*)(uintptr_t)(k_lane + slot_off + MAT);
         f32x4 sa[2][2], pa4[2][2];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
@@ -497,7 +501,9 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
             for (int tp = 0; tp < 2; ++tp) {
               const int J = ((2 * s + tp) * KS + ks) * 64;
               sa[s][tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kp[J], qf[tt][ks], sa[s][tp], 0, 0, 0);
-              pa4[s][tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Vp[J], dof[tt][ks], pa4[s][tp], 0, 0, 0);
+              pa4[s][tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  *(const lds_bf16x8*)(uintptr_t)(kofs[ks] + slot_off + MAT + (32 * s + 4 * tp) * 2 * D),
+                  dof[tt][ks], pa4[s][tp], 0, 0, 0);
             }
         const int lim = (key0 + 63 > pos || key0 + 64 > kv_len) ? min(pos, kv_len - 1) - key0 : 63;
         const float nl = -lse2[tt];
