@@ -436,6 +436,8 @@ static infllm2_status bwd_common(const infllm2_params* params, const infllm2_seq
   if (nb * g->Hkv > lim || static_cast<long long>(t->work_prefix[t->n]) * g->Hkv * g->topk > lim)
     return fail(INFLLM2_ERR_SHAPE, "backward index beyond 2^31 entries");
   *n_blocks = static_cast<int>(nb);
+  if (infllm2::bwd_segments(*g, *t, *n_blocks) > lim)
+    return fail(INFLLM2_ERR_SHAPE, "backward index beyond 2^31 segments");
   *q_rows = static_cast<int>(qr);
   return INFLLM2_OK;
 }

@@ -29,6 +29,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kChunk = 512;       // query rows per dK/dV work item (one KV block's list slice)
 constexpr int kRows = 32;         // (token, head) rows per step: two 16-row MFMA tiles
 constexpr int kSlots = 4;         // LDS ring depth of the dK/dV kernel
+// The reverse index is split into windows of query rows whose q and dO together take about
+// this many bytes, processed one window after the other, so that the rows a window's blocks
+// stream stay in the last-level cache instead of being fetched from HBM once per block.
+constexpr long long kWindowBytes = 64LL << 20;
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -279,7 +283,7 @@ __global__ void __launch_bounds__(256) bwd_prep(Geom g, SeqTable t, const uint16
                                                 const uint16_t* __restrict__ dout,
                                                 const int32_t* __restrict__ idx,
                                                 float* __restrict__ delta, int* __restrict__ cnt,
-                                                int n_blocks) {
+                                                int n_blocks, int win_rows) {
   const int r = blockIdx.x;
   const int b = find_seq(t, r);
   const int row = t.q_start[b] + (r - t.work_prefix[b]);
@@ -305,7 +309,8 @@ __global__ void __launch_bounds__(256) bwd_prep(Geom g, SeqTable t, const uint16
   const int nb = (t.kv_len[b] + 63) / 64;      // entries outside the sequence are ignored
   for (int e = threadIdx.x; e < per_row; e += 256) {
     const int blk = idx[static_cast<size_t>(row) * per_row + e];
-    if (blk >= 0 && blk < nb) atomicAdd(&cnt[(e / g.topk) * n_blocks + t.aux[b] + blk], 1);
+    if (blk >= 0 && blk < nb)
+      atomicAdd(&cnt[((r / win_rows) * g.Hkv + e / g.topk) * n_blocks + t.aux[b] + blk], 1);
   }
 }
 
@@ -360,7 +365,8 @@ __global__ void __launch_bounds__(1024) bwd_scan(int* __restrict__ cnt, int* __r
 __global__ void __launch_bounds__(256) bwd_scatter(Geom g, SeqTable t, const int32_t* __restrict__ idx,
                                                    int* __restrict__ fill,
                                                    const int* __restrict__ seg_off,
-                                                   int* __restrict__ list, int n_blocks) {
+                                                   int* __restrict__ list, int n_blocks,
+                                                   int win_rows) {
   const int r = blockIdx.x;
   const int b = find_seq(t, r);
   const int row = t.q_start[b] + (r - t.work_prefix[b]);
@@ -369,7 +375,7 @@ __global__ void __launch_bounds__(256) bwd_scatter(Geom g, SeqTable t, const int
   for (int e = threadIdx.x; e < per_row; e += 256) {
     const int blk = idx[static_cast<size_t>(row) * per_row + e];
     if (blk >= 0 && blk < nb) {
-      const int seg = (e / g.topk) * n_blocks + t.aux[b] + blk;
+      const int seg = ((r / win_rows) * g.Hkv + e / g.topk) * n_blocks + t.aux[b] + blk;
       list[seg_off[seg] + atomicAdd(&fill[seg], 1)] = row;
     }
   }
@@ -438,8 +444,8 @@ bwd_dkv(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __re
       else hi = mid;
     }
     const int seg = lo;
-    const int kvh = seg / n_blocks;
-    const int gb = seg - kvh * n_blocks;
+    const int kvh = (seg / n_blocks) % Hkv;       // segment = (row window, KV head, block)
+    const int gb = seg % n_blocks;
     const int b = seq_of_block(t, gb);
     const int key0 = 64 * (gb - t.aux[b]);
     const int e0 = seg_off[seg] + (item - item_off[seg]) * kChunk;
@@ -607,9 +613,21 @@ bwd_dkv(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __re
 
 }  // namespace
 
+// Query rows per window of the reverse index (at least 1024).
+int bwd_window_rows(const Geom& g) {
+  const long long per_row = 2LL * g.Hq * g.d * 2;          // q and dO, bf16
+  return static_cast<int>(std::max<long long>(1024, kWindowBytes / per_row));
+}
+
+long long bwd_segments(const Geom& g, const SeqTable& t, int n_blocks) {
+  const int w = bwd_window_rows(g);
+  const long long n_win = std::max(1, (t.work_prefix[t.n] + w - 1) / w);
+  return n_win * g.Hkv * n_blocks;
+}
+
 size_t bwd_workspace(const Geom& g, const SeqTable& t, int n_blocks, int q_rows) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  const size_t n_seg = static_cast<size_t>(g.Hkv) * n_blocks;
+  const size_t n_seg = static_cast<size_t>(bwd_segments(g, t, n_blocks));
   const size_t entries = static_cast<size_t>(t.work_prefix[t.n]) * g.Hkv * g.topk;
   return al(static_cast<size_t>(q_rows) * g.Hq * 4) + al(n_seg * 4) + 2 * al((n_seg + 1) * 4) +
          al(std::max<size_t>(entries, 1) * 4);
@@ -622,7 +640,8 @@ hipError_t launch_attn_bwd(const Geom& g, const SeqTable& t, int n_blocks, int q
                            const void* out, const float* lse, const void* dout, float* dq,
                            float* dk, float* dv, void* workspace, hipStream_t stream) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  const int n_seg = g.Hkv * n_blocks;
+  const int n_seg = static_cast<int>(bwd_segments(g, t, n_blocks));
+  const int win_rows = bwd_window_rows(g);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   float* delta = reinterpret_cast<float*>(ws);
   ws += al(static_cast<size_t>(q_rows) * g.Hq * 4);
@@ -657,16 +676,16 @@ hipError_t launch_attn_bwd(const Geom& g, const SeqTable& t, int n_blocks, int q
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (g.d == 128) {
     hipLaunchKernelGGL(bwd_prep<128>, dim3(rows), dim3(256), 0, stream, g, t, oo, dd, idx,
-                       delta, cnt, n_blocks);
+                       delta, cnt, n_blocks, win_rows);
   } else {
     hipLaunchKernelGGL(bwd_prep<64>, dim3(rows), dim3(256), 0, stream, g, t, oo, dd, idx,
-                       delta, cnt, n_blocks);
+                       delta, cnt, n_blocks, win_rows);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_scan, dim3(1), dim3(1024), 0, stream, cnt, seg_off, item_off, n_seg);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_scatter, dim3(rows), dim3(256), 0, stream, g, t, idx, cnt, seg_off,
-                     list, n_blocks);
+                     list, n_blocks, win_rows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   // dQ: the forward's tile kernel in its gradient form (tiles of 16 rows)

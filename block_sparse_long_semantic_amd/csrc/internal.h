@@ -94,6 +94,7 @@ hipError_t launch_attn_tile_dq(const Geom& g, const SeqTable& t, const void* q, 
 // Whole backward (dq, dk, dv as float32).  t: work_prefix over query rows, aux[b] the first
 // global KV block of sequence b, n_blocks their total; q_rows bounds every row index + 1.
 size_t bwd_workspace(const Geom& g, const SeqTable& t, int n_blocks, int q_rows);
+long long bwd_segments(const Geom& g, const SeqTable& t, int n_blocks);
 hipError_t launch_attn_bwd(const Geom& g, const SeqTable& t, int n_blocks, int q_rows,
                            const void* q, const void* k, const void* v, const int32_t* idx,
                            const void* out, const float* lse, const void* dout, float* dq,

@@ -167,10 +167,10 @@ def call_bwd(so, p, s, lse=FAKE, dq=FAKE, ws=FAKE, ws_bytes=1 << 30):
 
 def test_backward_workspace_and_checks(so):
     p, s = params(), seqs()
-    # delta (rows x Hq float32), then per (KV head, block) segment a count, two offset tables
+    # delta (rows x Hq float32), then per (row window, KV head, block) segment a count, two offset tables
     # with a final total each, and the row list (rows x Hkv x topk int32), each 256-byte aligned
     al = lambda x: (x + 255) // 256 * 256
-    n_seg = 2 * 2                                     # 100 keys -> 2 blocks, 2 KV heads
+    n_seg = 1 * 2 * 2                   # one row window (100 rows), 2 KV heads, 100 keys -> 2 blocks
     want = al(100 * 32 * 4) + al(n_seg * 4) + 2 * al((n_seg + 1) * 4) + al(100 * 2 * 96 * 4)
     assert lib.backward_workspace_size(p, s) == want
     assert call_bwd(so, p, s, ws_bytes=want - 1) == WS and "workspace" in last(so)
