@@ -5,10 +5,11 @@ A step is one pass of the whole prefill path over the 128K-token MiniCPM4-8B-sha
 initial + 2 local blocks): compress_kernels -> block_scores -> topk_select ->
 sparse_attn_prefill, inputs resident in HBM.  `value` is prefill tokens/s of that pass.
 The line also carries the decode measurement (batch 8 x 128K cache, one token each, 16
-consecutive steps with incremental kernel updates), the backward of the attention on the same
-layer (dQ, dK, dV for a seeded upstream gradient, the forward's selection held fixed), the
-roofline of the dominant kernel (from HIP events on the launch stream) and the CPU oracle
-timed on a bounded sample.
+consecutive steps with incremental kernel updates), a chunked prefill (the last 16K tokens
+against a 112K cache), block scores in score mode 1, sliding-window attention (window 6144),
+the backward of the attention on the same layer (dQ, dK, dV for a seeded upstream gradient, the
+forward's selection held fixed), the roofline of the dominant kernel (from HIP events on the
+launch stream) and the CPU oracle timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--workload prefill128k|prefill32k|varlen]
 """
@@ -34,6 +35,7 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 TILE_TOKENS = 16          # query tokens per attention work item
 WINDOW = 6144             # sliding-window leg: 96 blocks x 64 tokens
+CHUNK = 16384             # chunked-prefill leg: the last 16K tokens against a 112K cache
 SPIN_CYCLES = 24_000_000  # GPU spin before the timed decode steps (about 10 ms at 2.4 GHz)
 SPIN_SECONDS = 0.008      # enqueueing must finish well inside the spin
 ATTN_SOURCES = ["block_sparse_long_semantic_amd/csrc/attn_tile.hip",
@@ -128,13 +130,70 @@ def run_prefill(args, torch, pkg, synth):
                    "scores": bytes_scores / (stage["scores"] * 1e-3) / 1e9,
                    "topk": bytes_topk / (stage["topk"] * 1e-3) / 1e9},
         wl=wl, kernels_gpu=bufs["kernels"])
-    if args.no_backward and args.no_window and args.no_score_mode1:
+    if args.no_backward and args.no_window and args.no_score_mode1 and args.no_chunk:
         del q, k, v, bufs
     else:
         result["device"] = dict(q=q, k=k, v=v, seqs=seqs, idx=bufs["idx"], out=bufs["out"],
                                 lse=bufs["lse"], scores=bufs["scores"])
         del bufs
     return result
+
+
+def run_chunk(args, torch, pkg, pre):
+    """Chunked prefill: the last CHUNK tokens of the 128K sequence arrive as a chunk against a
+    cache holding the earlier ones (q_pos0 > 0): incremental kernels, scores, top-k and
+    attention for the chunk's rows, timed per stage like the full prefill."""
+    p, dv_ = pre["p"], pre["device"]
+    L = pre["seq_lens"][0]
+    C = min(CHUNK, L)
+    q = dv_["q"][L - C:]
+    k, v = dv_["k"], dv_["v"]
+    seqs = pkg.Seqs(np.array([0]), np.array([C]), np.array([L - C]), np.array([0]), np.array([L]),
+                    np.array([0]))
+    prev = np.array([L - C], np.int32)
+    nb = (L - 1) // p.block_size + 1
+    dt = q.dtype
+    scores = torch.empty((C, p.num_kv_heads, nb), dtype=torch.float32, device="cuda")
+    idx = torch.empty((C, p.num_kv_heads, p.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((C, p.num_q_heads), dtype=torch.float32, device="cuda")
+    kern = pre["kernels_gpu"]
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        pkg.compress_kernels(p, seqs, k, kern, prev_kv_len=prev, stream=stream)
+        if ev: ev[1].record(stream)
+        pkg.block_scores(p, seqs, q, kern, scores, stream=stream)
+        if ev: ev[2].record(stream)
+        pkg.topk_select(p, seqs, scores, idx, stream=stream)
+        if ev: ev[3].record(stream)
+        pkg.sparse_attn_prefill(p, seqs, q, k, v, idx, out, lse, stream=stream)
+        if ev: ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for st in range(args.steps):
+        step(evs[st])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    names = ["compress", "scores", "topk", "attention"]
+    stage = {n: float(np.mean([evs[st][i].elapsed_time(evs[st][i + 1]) for st in range(args.steps)]))
+             for i, n in enumerate(names)}
+    i = np.arange(L - C, L, dtype=np.int64)
+    keys = int(np.where((i // p.block_size) + 1 <= p.topk, i + 1,
+                        (p.topk - 1) * p.block_size + (i % p.block_size) + 1).sum())
+    flops = 4.0 * p.head_dim * p.num_q_heads * keys
+    tflops = flops / (stage["attention"] * 1e-3) / 1e12
+    del scores, idx, out, lse
+    return dict(chunk_tokens=C, cache_tokens=L - C, ms_per_chunk=wall * 1e3,
+                tokens_per_s=C / wall, stages_ms=stage,
+                roofline={"kernel": "attn_tile (sparse_attn_prefill, q_pos0 > 0)", "bound": "mfma",
+                          "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                          "frac": tflops / PEAK_BF16_TFLOPS, "flops_per_call": flops})
 
 
 def run_score_mode1(args, torch, pkg, pre):
@@ -550,6 +609,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-window", action="store_true")
     ap.add_argument("--no-score-mode1", action="store_true")
+    ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -609,6 +669,9 @@ def main():
         line["roofline"]["traffic_split"] = {"fetch": tr["fetch_bytes_per_call"],
                                              "write": tr["write_bytes_per_call"],
                                              "unit": "bytes per call"}
+    if not args.no_chunk:
+        line["chunk"] = run_chunk(args, torch, pkg, pre)
+        log(f"chunk: {line['chunk']['ms_per_chunk']:.2f} ms per {line['chunk']['chunk_tokens']} tokens")
     if not args.no_score_mode1:
         line["score_mode1"] = run_score_mode1(args, torch, pkg, pre)
         log(f"score mode 1: {line['score_mode1']['ms_per_call']:.2f} ms/call")

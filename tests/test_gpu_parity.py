@@ -258,6 +258,26 @@ def test_full_size_prefill_sampled(name):
         assert np.all(nsel[rows] == expect[:, None])
 
 
+def test_full_size_chunk_sampled():
+    """Chunked prefill at the measured size: the last 16K tokens of the 128K sequence as queries
+    (q_pos0 = 112K) against the whole cache; sampled rows, and every needle query in the chunk
+    finds its needle."""
+    full = synth.make("prefill128k")
+    p = full.params
+    L, C = 131072, 16384
+    wl = synth.Workload("chunk16k", p, full.q[L - C:], full.k, full.v, np.array([0]),
+                        np.array([C], np.int32), np.array([L - C], np.int32), np.array([0]),
+                        np.array([L], np.int32))
+    log("case full chunk 16K of 128K")
+    res = run_prefill_stages(wl)
+    for nd in full.needles:
+        qp = nd.query_positions[nd.query_positions >= L - C] - (L - C)
+        if len(qp):
+            assert np.all(np.any(res["idx"][qp, nd.kv_head, :] == nd.block, axis=1))
+    rows = np.array(sorted(set(range(0, C, 997)) | set(range(C - 3, C))))
+    check_sequence(wl, res, 0, rows=rows, label="full chunk")
+
+
 def test_full_size_decode():
     wl = synth.make("decode128k", steps=2)
     log("case full decode128k")
