@@ -395,11 +395,9 @@ def run_decode(args, torch, pkg, synth):
     seqs = [pkg.Seqs.decode(kv0 + st + 1, Lmax, Ck) for st in range(args.decode_steps)]
     prevs = [(kv0 + st).astype(np.int32) for st in range(args.decode_steps)]
 
-    def all_steps(ev=None):
+    def all_steps():
         for st in range(args.decode_steps):
-            if ev: ev[st][0].record(stream)
             pkg.decode_step(p, seqs[st], qs[st], k, v, kern, prevs[st], bufs, stream=stream)
-            if ev: ev[st][1].record(stream)
 
     for _ in range(max(1, args.warmup)):
         pkg.compress_kernels(p, s0, k, kern, stream=stream)
@@ -411,16 +409,22 @@ def run_decode(args, torch, pkg, synth):
     all_steps()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # GPU time per step: the GPU spins (about 10 ms) while the host enqueues all steps, so the
-    # events bracket device work only, not the binding's per-call host overhead
-    pkg.compress_kernels(p, s0, k, kern, stream=stream)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.decode_steps)]
-    torch.cuda.synchronize()
-    torch.cuda._sleep(SPIN_CYCLES)
-    t1 = time.perf_counter()
-    all_steps(ev)
-    enqueue = time.perf_counter() - t1
-    torch.cuda.synchronize()
+    # GPU time per step: the GPU spins (about 10 ms) while the host enqueues all steps, so two
+    # events bracket the steps' device work back to back, not the binding's per-call host
+    # overhead (an event between every two steps would add its own cost to each); 4 sweeps
+    sweeps = []
+    for _ in range(4):
+        pkg.compress_kernels(p, s0, k, kern, stream=stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        torch.cuda._sleep(SPIN_CYCLES)
+        t1 = time.perf_counter()
+        ev[0].record(stream)
+        all_steps()
+        ev[1].record(stream)
+        enqueue = time.perf_counter() - t1
+        torch.cuda.synchronize()
+        sweeps.append(ev[0].elapsed_time(ev[1]) * 1e3 / args.decode_steps)
     # the same steps as separate calls, events between the stages (breakdown; the second of two
     # passes is kept, each interval includes one event's own cost)
     for _ in range(2):
@@ -445,7 +449,6 @@ def run_decode(args, torch, pkg, synth):
     stage_us = {n: float(np.mean([sev[st][i].elapsed_time(sev[st][i + 1]) * 1e3
                                   for st in range(args.decode_steps)]))
                 for i, n in enumerate(["compress", "scores", "topk", "attention"])}
-    per = [ev[st][0].elapsed_time(ev[st][1]) * 1e3 for st in range(args.decode_steps)]
     # bytes a step must move: the kernel cache read for scoring, the selected K/V blocks, q/out
     kv_len = kv0 + args.decode_steps
     C = np.array([pkg.num_kernels(int(L), p.kernel_size, p.kernel_stride) for L in kv_len])
@@ -455,8 +458,9 @@ def run_decode(args, torch, pkg, synth):
     bytes_kv = keys * p.num_kv_heads * p.head_dim * 2 * 2
     bytes_q = B * p.num_q_heads * p.head_dim * 2 * 2
     total = bytes_kern + bytes_kv + bytes_q
-    us = float(np.mean(per))
-    out = dict(us_per_step=us, us_per_step_wall=wall * 1e6 / args.decode_steps,
+    us = float(np.median(sweeps))
+    out = dict(us_per_step=us, us_per_step_sweeps=[round(x, 2) for x in sweeps],
+               us_per_step_wall=wall * 1e6 / args.decode_steps,
                host_enqueue_us_per_step=enqueue * 1e6 / args.decode_steps,
                gpu_busy_while_enqueueing=bool(enqueue < SPIN_SECONDS), stages_us=stage_us,
                tokens_per_s=B / (us * 1e-6), batch=B, cache_len=int(Lmax),

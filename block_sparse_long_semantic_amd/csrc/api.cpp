@@ -369,17 +369,14 @@ static int decode_splits(const Geom& g, int dtype, int rows, int num_splits) {
   return auto_splits(g, rows);
 }
 
-static size_t decode_ws_bytes(const Geom& g, int rows, int splits) {
-  // partials (m, l, O[d]) per (row, query head, split), then one counter per (row, kv head)
-  return static_cast<size_t>(rows) * g.Hq * splits * (2 + g.d) * sizeof(float) +
-         static_cast<size_t>(rows) * g.Hkv * sizeof(int);
-}
-
 size_t infllm2_decode_workspace_size(const infllm2_params* params, int32_t total_q_rows,
                                      int32_t num_splits) {
   Geom g;
   if (check_params(params, &g) != INFLLM2_OK || total_q_rows < 0 || num_splits < 0) return 0;
-  return decode_ws_bytes(g, total_q_rows, decode_splits(g, params->dtype, total_q_rows, num_splits));
+  // enough for infllm2_sparse_attn_decode and for the fused form of infllm2_decode_step
+  const int fused = num_splits > 0 ? num_splits : infllm2::decode_fused_splits(g);
+  const int splits = std::max(decode_splits(g, params->dtype, total_q_rows, num_splits), fused);
+  return infllm2::decode_workspace(g, total_q_rows, splits);
 }
 
 infllm2_status infllm2_sparse_attn_decode(const infllm2_params* params, const infllm2_seqs* seqs,
@@ -395,7 +392,7 @@ infllm2_status infllm2_sparse_attn_decode(const infllm2_params* params, const in
     return fail(INFLLM2_ERR_SHAPE, "num_splits %d outside 0..topk", num_splits);
   const int rows = t.work_prefix[t.n];
   const int splits = decode_splits(g, params->dtype, rows, num_splits);
-  const size_t need = decode_ws_bytes(g, rows, splits);
+  const size_t need = infllm2::decode_workspace(g, rows, splits);
   if (splits > 1) {
     if (workspace == nullptr) return fail(INFLLM2_ERR_NULL, "workspace is NULL");
     if (!aligned16(workspace)) return fail(INFLLM2_ERR_ALIGN, "workspace must be 16-byte aligned");
@@ -407,11 +404,14 @@ infllm2_status infllm2_sparse_attn_decode(const infllm2_params* params, const in
     return hip_status(infllm2::launch_attn_decode(g, t, q, k, v, block_idx, splits, workspace, out,
                                                   lse, s),
                       "sparse_attn_decode launch");
+  // generic kernels: partials after the counter area of the common layout
+  float* part = splits > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                      infllm2::decode_layout(rows * g.Hkv).part)
+                           : nullptr;
   hipError_t e = infllm2::launch_attn(g, params->dtype, t, q, k, v, block_idx, splits, out, lse,
-                                      static_cast<float*>(workspace), s);
+                                      part, s);
   if (e != hipSuccess || splits == 1) return hip_status(e, "sparse_attn_decode launch");
-  return hip_status(infllm2::launch_attn_combine(g, params->dtype, t, splits,
-                                                 static_cast<const float*>(workspace), out, lse, s),
+  return hip_status(infllm2::launch_attn_combine(g, params->dtype, t, splits, part, out, lse, s),
                     "sparse_attn_decode combine launch");
 }
 
@@ -481,14 +481,51 @@ infllm2_status infllm2_decode_step(const infllm2_params* params, const infllm2_s
                                   int32_t nb_stride, int32_t* block_idx, int32_t num_splits,
                                   void* workspace, size_t workspace_bytes, void* out, float* lse,
                                   void* stream) {
-  infllm2_status st = infllm2_compress_kernels(params, seqs, k_cache, prev_kv_len, kernels, stream);
+  Geom g;
+  SeqTable t;
+  infllm2_status st = check_params(params, &g);
   if (st != INFLLM2_OK) return st;
-  st = infllm2_block_scores(params, seqs, q, kernels, scores, nb_stride, stream);
+  if ((st = build_table(seqs, g, true, &t)) != INFLLM2_OK) return st;
+  if (!infllm2::decode_fused_supported(g, params->dtype, t)) {
+    st = infllm2_compress_kernels(params, seqs, k_cache, prev_kv_len, kernels, stream);
+    if (st != INFLLM2_OK) return st;
+    st = infllm2_block_scores(params, seqs, q, kernels, scores, nb_stride, stream);
+    if (st != INFLLM2_OK) return st;
+    st = infllm2_topk_select(params, seqs, scores, nb_stride, block_idx, stream);
+    if (st != INFLLM2_OK) return st;
+    return infllm2_sparse_attn_decode(params, seqs, q, k_cache, v_cache, block_idx, num_splits,
+                                      workspace, workspace_bytes, out, lse, stream);
+  }
+  // Fused form: the arguments are checked as the separate calls check them, then the kernels
+  // completed since prev_kv_len are compressed, one launch does scores and top-k, and one the
+  // attention.
+  if (!q || !k_cache || !v_cache || !kernels || !scores || !block_idx || !out)
+    return fail(INFLLM2_ERR_NULL, "q, k_cache, v_cache, kernels, scores, block_idx or out is NULL");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(kernels) ||
+      !aligned16(scores) || !aligned16(block_idx) || !aligned16(out) || (lse && !aligned16(lse)))
+    return fail(INFLLM2_ERR_ALIGN, "decode step buffers must be 16-byte aligned");
+  const int need_nb = max_reachable_blocks(t, g.B);
+  if (nb_stride < need_nb)
+    return fail(INFLLM2_ERR_SHAPE, "nb_stride %d below the %d reachable blocks", nb_stride, need_nb);
+  if (need_nb > 4096)
+    return fail(INFLLM2_ERR_UNSUPPORTED, "%d reachable blocks exceed 4096", need_nb);
+  if (num_splits < 0 || num_splits > g.topk)
+    return fail(INFLLM2_ERR_SHAPE, "num_splits %d outside 0..topk", num_splits);
+  SeqTable tr = t;
+  rows_prefix(&tr);
+  const int rows = tr.work_prefix[tr.n];
+  const int splits = num_splits > 0 ? num_splits : infllm2::decode_fused_splits(g);
+  const size_t need = infllm2::decode_workspace(g, rows, splits);
+  if (workspace == nullptr) return fail(INFLLM2_ERR_NULL, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(INFLLM2_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(INFLLM2_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  st = infllm2_compress_kernels(params, seqs, k_cache, prev_kv_len, kernels, stream);
   if (st != INFLLM2_OK) return st;
-  st = infllm2_topk_select(params, seqs, scores, nb_stride, block_idx, stream);
-  if (st != INFLLM2_OK) return st;
-  return infllm2_sparse_attn_decode(params, seqs, q, k_cache, v_cache, block_idx, num_splits,
-                                    workspace, workspace_bytes, out, lse, stream);
+  return hip_status(infllm2::launch_decode_fused(g, tr, q, kernels, k_cache, v_cache, scores,
+                                                 nb_stride, block_idx, splits, workspace, out,
+                                                 lse, static_cast<hipStream_t>(stream)),
+                    "decode_step launch");
 }
 
 }  // extern "C"

@@ -701,12 +701,7 @@ hipError_t launch_attn_bwd(const Geom& g, const SeqTable& t, int n_blocks, int q
 
   // dK, dV: persistent grid over the work items (their count is known on the device only)
   const long long bound = static_cast<long long>(rows) * g.Hkv * g.topk / kChunk + n_seg;
-  int cus = 256;
-  {
-    int dev = 0;
-    if (hipGetDevice(&dev) == hipSuccess)
-      (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  }
+  const int cus = device_cus();
   const int grid = static_cast<int>(std::max<long long>(1, std::min<long long>(bound, 2LL * cus)));
 #define INFLLM2_DKV_CASE(DD, GG)                                                                \
   if (g.d == DD && g.G == GG) {                                                                 \

@@ -1,18 +1,36 @@
-// Split-KV block-sparse attention for decoding (arXiv abstract of MiniCPM4: the sparse
-// attention accelerates decoding as well as prefilling; paper summary section 2.1.3).
+// Decoding (arXiv abstract of MiniCPM4: the sparse attention accelerates decoding as well as
+// prefilling), in two forms that share the per-block arithmetic:
 //
-// A decoding batch has one (or a few) query rows per sequence, so the selected blocks of a
-// row are spread over many workgroups: workgroup (row, kv head, split) owns a contiguous range
-// of the row's block list, and each of its 4 waves takes every 4th block of that range.  A wave
+// attn_decode -- split-KV block-sparse attention over a given selection (paper summary, section
+// 2.1.3).  A decoding batch has one (or a few) query rows per sequence, so the selected blocks of
+// a row are spread over many workgroups: workgroup (row, kv head, split) owns a contiguous range
+// of the row's block list, and each of its waves takes every NW-th block of that range.  A wave
 // loads its block's K straight into registers, already in MFMA A-operand order (16 bytes per
 // lane per step), and its block's V into its own LDS slot with global_load_lds, in the order the
 // transposing LDS reads need; it folds the block into a running (max, sum, output) for the 16
-// stacked heads of the group.  The 4 waves then merge through LDS, and the workgroup writes its
-// partial.  The last workgroup of a
-// (row, kv head) to finish -- counted with an agent-scope atomic in the workspace -- merges all
-// partials by log-sum-exp and writes the output, so no separate combine launch is needed.  It
-// resets the counter, leaving the workspace ready for the next call.
+// stacked heads of the group.  The waves then merge through LDS, and the workgroup writes its
+// partial.  The last workgroup of a (row, kv head) to finish -- counted with an agent-scope
+// atomic in the workspace -- merges all partials by log-sum-exp and writes the output, so no
+// separate combine launch is needed.  It resets the counter, leaving the workspace ready for the
+// next call.
+//
+// decode_select -- block scores (section 2.1.2: the group-summed query against every semantic
+// kernel, max-pooled onto blocks) and the group-shared top-k (2.1.1-2.1.2) of a decoding step in
+// one launch: one workgroup per chunk of 128 blocks of a (row, kv head) computes the chunk's
+// scores; the workgroup that completes the last chunk of the pair -- counted with an agent-scope
+// atomic in the workspace -- selects its blocks right away (a radix select over the
+// order-preserving score keys, in LDS) and zeroes the counter for the next call.  No workgroup
+// ever waits for another, so the launch needs no co-residency.  The attention over the
+// selection is the next launch (attn_decode).
+//
+// Data crossing workgroups (scores, selections, partials, counters) moves through agent-scope
+// atomic stores and loads, which are coherent across the XCDs' separate L2s by themselves; a
+// fence would instead write back and invalidate a whole L2.
+#include <algorithm>
+
+#include "dpp.h"
 #include "internal.h"
+#include "select.h"
 
 namespace infllm2 {
 namespace {
@@ -22,11 +40,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kWaves = 4;
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -56,62 +73,352 @@ __device__ __forceinline__ uint64_t pack2(float a, float b) {
 }
 __device__ __forceinline__ float lo_f32(uint64_t v) { return __uint_as_float(static_cast<uint32_t>(v)); }
 __device__ __forceinline__ float hi_f32(uint64_t v) { return __uint_as_float(static_cast<uint32_t>(v >> 32)); }
-__device__ __forceinline__ void agent_store(uint64_t* p, uint64_t v) {
+template <typename T>
+__device__ __forceinline__ void agent_store(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint64_t agent_load(const uint64_t* p) {
-  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+template <typename T>
+__device__ __forceinline__ T agent_load(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int agent_add(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Workspace: partial outputs O[d] per (row, kv head, split, head of group), then the partial
-// (max, sum) pairs in the same order, then one counter per (row, kv head).
-struct DecodeWs {
-  float* part_o;
-  float* part_ml;
-  int* count;
+// Query row `vrow` of a launch whose work_prefix counts query rows.
+struct DecRow {
+  int row, pos, kv0, kv_len, b;
+};
+__device__ __forceinline__ DecRow dec_row(const SeqTable& t, int vrow) {
+  DecRow r;
+  r.b = find_seq(t, vrow);
+  const int j = vrow - t.work_prefix[r.b];
+  r.row = t.q_start[r.b] + j;
+  r.pos = t.q_pos0[r.b] + j;
+  r.kv0 = t.kv_start[r.b];
+  r.kv_len = t.kv_len[r.b];
+  return r;
+}
+
+// ------------------------------------------------------------------ attention over selected blocks
+// A wave's running state for the 16 stacked heads of a group: O (accumulator tiles, head = row
+// 4*(lane/16) + i of tile n), the running max (log2 domain) and this lane's partial sum, both
+// for head lane % 16.
+template <int D>
+struct WaveAcc {
+  f32x4 o[D / 16];
+  float m, l;
 };
 
-__device__ __forceinline__ DecodeWs ws_of(void* ws, int rows, int Hkv, int nsplit, int G, int D) {
-  DecodeWs w;
-  const size_t n = static_cast<size_t>(rows) * Hkv * nsplit * G;
-  w.part_o = static_cast<float*>(ws);
-  w.part_ml = w.part_o + n * D;
-  w.count = reinterpret_cast<int*>(w.part_ml + n * 2);
-  return w;
-}
+// Per-lane constants of a wave's block fold for one (row, kv head).
+template <int D, int G>
+struct FoldCtx {
+  bf16x8 qf[D / 32];
+  const uint16_t* kbase;
+  const uint16_t* vbase;
+  int rowstride, k_lane_off, v_lane_off, k_lrow, v_lrow, pos, kv_len;
+  uint32_t vaddr;
+  lds_u8* slot;
+  float qscale;
+};
 
 template <int D, int G>
-__global__ void __launch_bounds__(64 * kWaves)
-attn_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-            const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, int nsplit,
-            void* __restrict__ workspace, uint16_t* __restrict__ out, float* __restrict__ lse) {
+__device__ __forceinline__ void fold_init(FoldCtx<D, G>& c, WaveAcc<D>& a, const Geom& g,
+                                          const uint16_t* q, const uint16_t* k,
+                                          const uint16_t* v, const DecRow& r, int kvh,
+                                          lds_u8* slot, int lane) {
+  constexpr int KS = D / 32;
+  const int c16 = lane & 15;
+  const int q4 = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (c16 < G)
+      c.qf[ks] = *reinterpret_cast<const bf16x8*>(
+          q + (static_cast<size_t>(r.row) * g.Hq + kvh * G + c16) * D + 32 * ks + 8 * q4);
+    else
+      c.qf[ks] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+  }
+  c.rowstride = g.Hkv * D;
+  c.k_lrow = 8 * (c16 >> 2) + (c16 & 3);
+  c.v_lrow = 8 * ((lane & 31) >> 3) + 4 * (lane >> 5) + ((lane >> 1) & 3);
+  c.k_lane_off = c.k_lrow * c.rowstride + 8 * q4;
+  c.v_lane_off = c.v_lrow * c.rowstride + 8 * (lane & 1);
+  c.kbase = k + static_cast<size_t>(r.kv0) * c.rowstride + static_cast<size_t>(kvh) * D;
+  c.vbase = v + static_cast<size_t>(r.kv0) * c.rowstride + static_cast<size_t>(kvh) * D;
+  c.slot = slot;
+  c.vaddr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(slot)) +
+            16 * (8 * q4 + 2 * (c16 >> 2) + ((c16 & 3) >> 1)) + 8 * (c16 & 1);
+  c.pos = r.pos;
+  c.kv_len = r.kv_len;
+  c.qscale = g.scale * kLog2e;
+#pragma unroll
+  for (int n = 0; n < D / 16; ++n) a.o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  a.m = -INFINITY;
+  a.l = 0.f;
+}
+
+// Folds the block starting at key key0 into the wave's state: S^T = K Q^T (keys as rows, in the
+// permuted order that makes the accumulator the P operand), keys past the query position or the
+// cache end masked, online softmax in the exp2 domain, O += P V.
+template <int D, int G>
+__device__ __forceinline__ void fold_block(const FoldCtx<D, G>& c, WaveAcc<D>& a, int key0,
+                                           int lane) {
   constexpr int KS = D / 32;
   constexpr int NT = D / 16;
   constexpr int CPR = D / 8;
+  const int q4 = lane >> 4;
+  const bool tail = key0 + 64 > c.kv_len;
+  const int last = c.kv_len - 1 - key0;
+  const uint16_t* kb = c.kbase + static_cast<size_t>(key0) * c.rowstride;
+  const uint16_t* vb = c.vbase + static_cast<size_t>(key0) * c.rowstride;
+  bf16x8 kr[CPR];                 // A operand of MFMA step J = (2s + tp) * KS + ks
+#pragma unroll
+  for (int J = 0; J < CPR; ++J) {
+    const int krow0 = 32 * (J / (2 * KS)) + 4 * ((J / KS) % 2);
+    const int vrow0 = 32 * (J / NT);
+    int ko = c.k_lane_off + krow0 * c.rowstride + 32 * (J % KS);
+    int vo = c.v_lane_off + vrow0 * c.rowstride + 16 * (J % NT);
+    if (tail) {                   // rows past the cache end repeat its last row (masked)
+      const int kr0 = krow0 + c.k_lrow, vr = vrow0 + c.v_lrow;
+      ko += ((kr0 < last ? kr0 : last) - kr0) * c.rowstride;
+      vo += ((vr < last ? vr : last) - vr) * c.rowstride;
+    }
+    kr[J] = *reinterpret_cast<const bf16x8*>(kb + ko);
+    __builtin_amdgcn_global_load_lds(vb + vo, (lds_void*)(c.slot + J * 1024), 16, 0, 0);
+  }
+  wait_vmcnt<0>();
+  asm volatile("" ::: "memory");
+  float sv[2][2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[(2 * s + tp) * KS + ks], c.qf[ks], acc,
+                                                      0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[s][tp][i] = acc[i];
+    }
+  }
+  if (key0 + 63 > c.pos || tail) {
+    const int lim = min(c.pos, c.kv_len - 1) - key0;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (32 * s + 8 * q4 + 4 * tp + i > lim) sv[s][tp][i] = -INFINITY;
+  }
+  float mx = sv[0][0][0];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sv[s][tp][i]);
+  mx *= c.qscale;
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(a.m, mx);
+  const float alpha = __builtin_amdgcn_exp2f(a.m - m_new);
+  a.l *= alpha;
+  a.m = m_new;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a_i = __shfl(alpha, 4 * q4 + i);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) a.o[n][i] *= a_i;
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sv[s][tp][i], c.qscale, -a.m));
+        sv[s][tp][i] = p;
+        a.l += p;
+      }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const bf16x2 pp[4] = {__builtin_convertvector((f32x2){sv[s][0][0], sv[s][0][1]}, bf16x2),
+                          __builtin_convertvector((f32x2){sv[s][0][2], sv[s][0][3]}, bf16x2),
+                          __builtin_convertvector((f32x2){sv[s][1][0], sv[s][1][1]}, bf16x2),
+                          __builtin_convertvector((f32x2){sv[s][1][2], sv[s][1][3]}, bf16x2)};
+    const bf16x8 pa = __builtin_bit_cast(bf16x8, pp);
+#pragma unroll
+    for (int hh = 0; hh < NT / 4; ++hh) {
+      uint64_t vt[4][2];
+      read_v8(c.vaddr + 512u * (2 * NT * s + 8 * hh), vt);
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const uint64_t both[2] = {vt[n][0], vt[n][1]};
+        a.o[hh * 4 + n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            pa, __builtin_bit_cast(bf16x8, both), a.o[hh * 4 + n], 0, 0, 0);
+      }
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slot reads done before its refill
+}
+
+// Merges the NW waves' states through LDS (`ring`, whose slots are free by now; every thread
+// must call it).  Thread tid ends with head h = tid / (T/16) and DPT = 16 D / T consecutive
+// dims from d0: unnormalised sums acc[], the workgroup max M (log2 domain) and sum L of head h.
+template <int D, int NW>
+__device__ __forceinline__ void merge_waves(const WaveAcc<D>& a, unsigned char* ring,
+                                            float (*wm_s)[16], float (*wl_s)[16], int tid,
+                                            float (&acc)[16 * D / (64 * NW)], float& M,
+                                            float& L) {
+  constexpr int NT = D / 16;
+  constexpr int T = 64 * NW;
+  constexpr int DPT = 16 * D / T;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int c16 = lane & 15;
+  const int q4 = lane >> 4;
+  float l = a.l;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (q4 == 0) {
+    wm_s[w][c16] = a.m;
+    wl_s[w][c16] = l;
+  }
+  __syncthreads();
+  float* obuf = reinterpret_cast<float*>(ring);               // [wave][16][D] floats
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * q4 + i;
+    float Mh = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) Mh = fmaxf(Mh, wm_s[ww][h]);
+    const float scale = wm_s[w][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(wm_s[w][h] - Mh);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) obuf[(w * 16 + h) * D + 16 * n + c16] = a.o[n][i] * scale;
+  }
+  __syncthreads();
+  const int h = tid / (T / 16);
+  const int d0 = (tid % (T / 16)) * DPT;
+  M = -INFINITY;
+  L = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wm_s[ww][h]);
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww)
+    if (wm_s[ww][h] != -INFINITY) L += wl_s[ww][h] * __builtin_amdgcn_exp2f(wm_s[ww][h] - M);
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww)
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) acc[e] += obuf[(ww * 16 + h) * D + d0 + e];
+}
+
+// Writes the merged workgroup result of (row, kv head) straight to the output (single split),
+// or its partial; then the last split of the pair to finish merges all partials by log-sum-exp
+// and writes the output.  Every thread must call it (thread mapping of merge_waves).
+template <int D, int G, int NW>
+__device__ __forceinline__ void finish_split(const Geom& g, int row, int kvh, int pair, int sp,
+                                             int nsplit, const float (&acc)[16 * D / (64 * NW)],
+                                             float M, float L, int* split_done, float* part,
+                                             int pairs, int tid, int* s_last,
+                                             uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int T = 64 * NW;
+  constexpr int DPT = 16 * D / T;
+  constexpr int NP = DPT / 2;                 // 8-byte pieces per thread
+  constexpr int R = DPT >= 8 ? 8 : 16;        // partials merged per round of loads
+  const int h = tid / (T / 16);
+  const int d0 = (tid % (T / 16)) * DPT;
+  const int Hq = g.Hq;
+  if (nsplit == 1) {
+    if (h < G) {
+      uint16_t* op = out + (static_cast<size_t>(row) * Hq + kvh * G + h) * D + d0;
+      const float inv = 1.f / L;
+#pragma unroll
+      for (int e = 0; e < DPT; ++e) op[e] = f32_to_bf16(acc[e] * inv);
+      if (lse != nullptr && d0 == 0) lse[static_cast<size_t>(row) * Hq + kvh * G + h] = (M + log2f(L)) * kLn2;
+    }
+    return;
+  }
+  const size_t n_ent = static_cast<size_t>(pairs) * nsplit * G;
+  float* part_o = part;
+  float* part_ml = part + n_ent * D;
+  const size_t ebase = static_cast<size_t>(pair) * nsplit * G;        // entry of split 0
+  if (h < G) {
+    const size_t e = ebase + static_cast<size_t>(sp) * G + h;
+    uint64_t* po = reinterpret_cast<uint64_t*>(part_o + e * D + d0);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) agent_store(po + i, pack2(acc[2 * i], acc[2 * i + 1]));
+    if (d0 == 0) agent_store(reinterpret_cast<uint64_t*>(part_ml + e * 2), pack2(M, L));
+  }
+  wait_vmcnt<0>();                                   // this wave's stores are complete
+  __syncthreads();
+  if (tid == 0) *s_last = agent_add(split_done + pair, 1) == nsplit - 1;
+  __syncthreads();
+  if (!*s_last) return;
+  if (h < G) {
+    // online log-sum-exp merge; the loads of R splits are issued before any is used
+    float MM = -INFINITY, LL = 0.f;
+    float a2[DPT];
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) a2[e] = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += R) {
+      uint64_t ml[R], ov[R][NP];
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const size_t e = ebase + static_cast<size_t>(min(s0 + u, nsplit - 1)) * G + h;
+        ml[u] = agent_load(reinterpret_cast<const uint64_t*>(part_ml + e * 2));
+        const uint64_t* po = reinterpret_cast<const uint64_t*>(part_o + e * D + d0);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) ov[u][i] = agent_load(po + i);
+      }
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const float ms = lo_f32(ml[u]);
+        if (s0 + u >= nsplit || ms == -INFINITY) continue;      // duplicate or empty split
+        const float Mn = fmaxf(MM, ms);
+        const float fo = __builtin_amdgcn_exp2f(MM - Mn);
+        const float fn = __builtin_amdgcn_exp2f(ms - Mn);
+        LL = LL * fo + hi_f32(ml[u]) * fn;
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          a2[2 * i] = a2[2 * i] * fo + lo_f32(ov[u][i]) * fn;
+          a2[2 * i + 1] = a2[2 * i + 1] * fo + hi_f32(ov[u][i]) * fn;
+        }
+        MM = Mn;
+      }
+    }
+    uint16_t* op = out + (static_cast<size_t>(row) * Hq + kvh * G + h) * D + d0;
+    const float inv = 1.f / LL;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) op[e] = f32_to_bf16(a2[e] * inv);
+    if (lse != nullptr && d0 == 0) lse[static_cast<size_t>(row) * Hq + kvh * G + h] = (MM + log2f(LL)) * kLn2;
+  }
+  if (tid == 0) agent_store(split_done + pair, 0);   // ready for the next call
+}
+
+template <int D, int G, int NW>
+__global__ void __launch_bounds__(64 * NW)
+attn_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+            const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, int nsplit,
+            void* __restrict__ workspace, uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int MAT = 64 * D * 2;                          // one block of V
-  __shared__ __attribute__((aligned(16))) unsigned char ring[kWaves][MAT];
-  __shared__ float wm_s[kWaves][16], wl_s[kWaves][16];
+  __shared__ __attribute__((aligned(16))) unsigned char ring[NW][MAT];
+  __shared__ float wm_s[NW][16], wl_s[NW][16];
   __shared__ int s_last;
 
   const int vrow = blockIdx.x;
   const int kvh = blockIdx.y;
   const int sp = blockIdx.z;
   const int rows = t.work_prefix[t.n];
-  const int b = find_seq(t, vrow);
-  const int j = vrow - t.work_prefix[b];
-  const int row = t.q_start[b] + j;
-  const int pos = t.q_pos0[b] + j;
-  const int kv0 = t.kv_start[b];
-  const int kv_len = t.kv_len[b];
+  const DecRow r = dec_row(t, vrow);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int c16 = lane & 15;
-  const int q4 = lane >> 4;
-  const int Hq = g.Hq, Hkv = g.Hkv;
-  const int rowstride = Hkv * D;
 
-  const int32_t* sel = idx + (static_cast<size_t>(row) * Hkv + kvh) * g.topk;
+  const int32_t* sel = idx + (static_cast<size_t>(r.row) * g.Hkv + kvh) * g.topk;
   // the valid entries form a prefix (ascending, then -1): count them with ballots
   int nsel = 0;
   for (int base = 0; base < g.topk; base += 128) {
@@ -126,242 +433,335 @@ attn_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* 
   const int k_begin = min(nsel, sp * per);
   const int k_end = min(nsel, k_begin + per);
 
-  bf16x8 qf[KS];
+  FoldCtx<D, G> c;
+  WaveAcc<D> a;
+  fold_init(c, a, g, q, k, v, r, kvh, (lds_u8*)&ring[w][0], lane);
+  const int own = r.pos / 64;                       // indices past the row's own block: clamped
+  for (int kk = k_begin + w; kk < k_end; kk += NW)
+    fold_block(c, a, max(0, min(sel[kk], own)) * 64, lane);
+
+  float acc[16 * D / (64 * NW)], M, L;
+  merge_waves<D, NW>(a, &ring[0][0], wm_s, wl_s, tid, acc, M, L);
+  const int pairs = rows * g.Hkv;
+  const DecodeLayout lay = decode_layout(pairs);
+  char* ws = static_cast<char*>(workspace);
+  finish_split<D, G, NW>(g, r.row, kvh, vrow * g.Hkv + kvh, sp, nsplit, acc, M, L,
+                         reinterpret_cast<int*>(ws + lay.split_done),
+                         reinterpret_cast<float*>(ws + lay.part), pairs, tid, &s_last, out, lse);
+}
+
+// waves of the attention workgroups: alone (given indices), and after decode_select
+constexpr int kSplitWaves = 4;
+constexpr int kStepWaves = 8;
+
+// ------------------------------------------------------------------------- scores + selection
+constexpr int kFusedWaves = 8;
+constexpr int kFusedThreads = 64 * kFusedWaves;
+constexpr int kChunkBlocks = 128;               // blocks per score work item
+constexpr int kMaxKeysPerThread = 8;            // selection over at most 8 * 512 blocks
+
+// Block scores of one chunk: blocks blk0 .. blk0+127 (those <= own) of query row `r`, kv head
+// kvh, from kernels 4*blk0-1 .. 4*blk0+511 (the first one is the halo of block blk0).  The
+// group-summed query stays in float32; each kernel row is read by D/8 lanes (16 bytes each),
+// dotted with float32 FMAs and reduced across the lanes by DPP moves; every kernel load is
+// issued before the query sum.  Kernel scores go to LDS, then 128 threads max-pool them onto the blocks.
+template <int D, int G>
+__device__ __forceinline__ void score_chunk(const Geom& g, const SeqTable& t, const DecRow& r,
+                                            int kvh, int blk0, int own,
+                                            const uint16_t* __restrict__ q,
+                                            const uint16_t* __restrict__ kern, float* srow,
+                                            float* qs, float* u, int tid) {
+  constexpr int LPR = D / 8;              // lanes per kernel row
+  constexpr int RPI = 64 / LPR;           // rows per wave instruction
+  constexpr int NROW = 4 * kChunkBlocks + 1;
+  constexpr int NIT = (NROW + RPI - 1) / RPI;
+  constexpr int NW = kFusedWaves;
+  constexpr int PER = (NIT + NW - 1) / NW;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int C = num_kernels(r.kv_len, g.w, g.s);
+  const int c0 = 4 * blk0;
+  const int col = (lane % LPR) * 8;
+  const size_t kbase = static_cast<size_t>(t.kc_start[r.b]) * g.Hkv * D + static_cast<size_t>(kvh) * D;
+  uint4 kv[PER];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    if (c16 < G)
-      qf[ks] = *reinterpret_cast<const bf16x8*>(
-          q + (static_cast<size_t>(row) * Hq + kvh * G + c16) * D + 32 * ks + 8 * q4);
-    else
-      qf[ks] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+  for (int i = 0; i < PER; ++i) {
+    const int it = w + NW * i;
+    const int rr = it * RPI + lane / LPR;
+    const int cc = c0 - 1 + rr;
+    const bool ok = it < NIT && rr < NROW && cc >= 0 && cc < C && 16 * cc + 31 <= r.pos;
+    kv[i] = ok ? *reinterpret_cast<const uint4*>(kern + kbase + static_cast<size_t>(cc) * g.Hkv * D + col)
+               : make_uint4(0u, 0u, 0u, 0u);
   }
-  f32x4 o[NT];
+  for (int e = tid; e < D; e += kFusedThreads) {
+    float qh[G];                                        // all heads' loads in flight at once
 #pragma unroll
-  for (int n = 0; n < NT; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;   // head c16; l_run is this lane's partial sum
-  const float qscale = g.scale * kLog2e;
-
-  const int k_lrow = 8 * (c16 >> 2) + (c16 & 3);
-  const int v_lrow = 8 * ((lane & 31) >> 3) + 4 * (lane >> 5) + ((lane >> 1) & 3);
-  const int k_lane_off = k_lrow * rowstride + 8 * q4;
-  const int v_lane_off = v_lrow * rowstride + 8 * (lane & 1);
-  const uint16_t* kbase = k + static_cast<size_t>(kv0) * rowstride + static_cast<size_t>(kvh) * D;
-  const uint16_t* vbase = v + static_cast<size_t>(kv0) * rowstride + static_cast<size_t>(kvh) * D;
-  const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&ring[w][0]));
-  const uint32_t vaddr = ring_lds + 16 * (8 * q4 + 2 * (c16 >> 2) + ((c16 & 3) >> 1)) + 8 * (c16 & 1);
-
-  for (int kk = k_begin + w; kk < k_end; kk += kWaves) {
-    const int key0 = sel[kk] * 64;
-    const bool tail = key0 + 64 > kv_len;
-    const int last = kv_len - 1 - key0;
-    const uint16_t* kb = kbase + static_cast<size_t>(key0) * rowstride;
-    const uint16_t* vb = vbase + static_cast<size_t>(key0) * rowstride;
-    bf16x8 kr[CPR];                 // A operand of MFMA step J = (2s + tp) * KS + ks
+    for (int h = 0; h < G; ++h) qh[h] = bf16_to_f32(q[(static_cast<size_t>(r.row) * g.Hq + kvh * G + h) * D + e]);
+    float s = 0.f;
 #pragma unroll
-    for (int J = 0; J < CPR; ++J) {
-      const int krow0 = 32 * (J / (2 * KS)) + 4 * ((J / KS) % 2);
-      const int vrow0 = 32 * (J / NT);
-      int ko = k_lane_off + krow0 * rowstride + 32 * (J % KS);
-      int vo = v_lane_off + vrow0 * rowstride + 16 * (J % NT);
-      if (tail) {                   // rows past the cache end repeat its last row (masked)
-        const int kr0 = krow0 + k_lrow, vr = vrow0 + v_lrow;
-        ko += ((kr0 < last ? kr0 : last) - kr0) * rowstride;
-        vo += ((vr < last ? vr : last) - vr) * rowstride;
-      }
-      const uint16_t* gv = vb + vo;
-      kr[J] = *reinterpret_cast<const bf16x8*>(kb + ko);
-      __builtin_amdgcn_global_load_lds(gv, (lds_void*)(&ring[w][J * 1024]), 16, 0, 0);
-    }
-    wait_vmcnt<0>();
-    asm volatile("" ::: "memory");
-    float sv[2][2][4];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int tp = 0; tp < 2; ++tp) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[(2 * s + tp) * KS + ks], qf[ks], acc,
-                                                        0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sv[s][tp][i] = acc[i];
-      }
-    }
-    if (key0 + 63 > pos || tail) {
-      const int lim = min(pos, kv_len - 1) - key0;
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (32 * s + 8 * q4 + 4 * tp + i > lim) sv[s][tp][i] = -INFINITY;
-    }
-    float mx = sv[0][0][0];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sv[s][tp][i]);
-    mx *= qscale;
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    l_run *= alpha;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a_i = __shfl(alpha, 4 * q4 + i);
-#pragma unroll
-      for (int n = 0; n < NT; ++n) o[n][i] *= a_i;
-    }
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int tp = 0; tp < 2; ++tp)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sv[s][tp][i], qscale, -m_run));
-          sv[s][tp][i] = p;
-          l_run += p;
-        }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const bf16x2 pp[4] = {__builtin_convertvector((f32x2){sv[s][0][0], sv[s][0][1]}, bf16x2),
-                            __builtin_convertvector((f32x2){sv[s][0][2], sv[s][0][3]}, bf16x2),
-                            __builtin_convertvector((f32x2){sv[s][1][0], sv[s][1][1]}, bf16x2),
-                            __builtin_convertvector((f32x2){sv[s][1][2], sv[s][1][3]}, bf16x2)};
-      const bf16x8 pa = __builtin_bit_cast(bf16x8, pp);
-#pragma unroll
-      for (int hh = 0; hh < NT / 4; ++hh) {
-        uint64_t vt[4][2];
-        read_v8(vaddr + 512u * (2 * NT * s + 8 * hh), vt);
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          const uint64_t both[2] = {vt[n][0], vt[n][1]};
-          o[hh * 4 + n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              pa, __builtin_bit_cast(bf16x8, both), o[hh * 4 + n], 0, 0, 0);
-        }
-      }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slot reads done before its refill
-  }
-
-  // ---- merge the 4 waves through LDS (their slots are free now)
-  float l = l_run;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (q4 == 0) {
-    wm_s[w][c16] = m_run;
-    wl_s[w][c16] = l;
+    for (int h = 0; h < G; ++h) s += qh[h];
+    qs[e] = s;
   }
   __syncthreads();
-  float* obuf = reinterpret_cast<float*>(&ring[0][0]);               // [wave][16][D] floats
+  float qv[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * q4 + i;
-    float M = -INFINITY;
+  for (int e = 0; e < 8; ++e) qv[e] = qs[col + e];
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, wm_s[ww][h]);
-    const float scale = wm_s[w][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(wm_s[w][h] - M);
+  for (int i = 0; i < PER; ++i) {
+    const int it = w + NW * i;
+    const int rr = it * RPI + lane / LPR;
+    const int cc = c0 - 1 + rr;
+    const bool ok = it < NIT && rr < NROW && cc >= 0 && cc < C && 16 * cc + 31 <= r.pos;
+    const uint32_t w4[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
+    float dot = 0.f;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) obuf[(w * 16 + h) * D + 16 * n + c16] = o[n][i] * scale;
+    for (int e = 0; e < 4; ++e) {
+      dot = fmaf(__uint_as_float(w4[e] << 16), qv[2 * e], dot);
+      dot = fmaf(__uint_as_float(w4[e] & 0xFFFF0000u), qv[2 * e + 1], dot);
+    }
+    dot = group_sum<LPR>(dot);
+    if (lane % LPR == 0 && it < NIT && rr < NROW) u[rr] = ok ? dot : -INFINITY;
   }
   __syncthreads();
-  // thread -> (head h, 8 dims); 256 threads cover 16 heads x 128 dims (d = 64: half idle)
-  const int h = tid >> 4;
-  const int d0 = (tid & 15) * 8;
-  float M = -INFINITY, L = 0.f;
+  if (tid < kChunkBlocks) {
+    const int blk = blk0 + tid;
+    if (blk <= own) {
+      // block blk's kernels 4blk-1 .. 4blk+3 sit at u[4*tid .. 4*tid+4]
+      float best = u[4 * tid];
 #pragma unroll
-  for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, wm_s[ww][h]);
-#pragma unroll
-  for (int ww = 0; ww < kWaves; ++ww)
-    if (wm_s[ww][h] != -INFINITY) L += wl_s[ww][h] * __builtin_amdgcn_exp2f(wm_s[ww][h] - M);
-  float acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  if (d0 < D) {
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += obuf[(ww * 16 + h) * D + d0 + e];
-  }
-
-  if (nsplit == 1) {
-    if (h < G && d0 < D) {
-      uint16_t* op = out + (static_cast<size_t>(row) * Hq + kvh * G + h) * D + d0;
-      const float inv = 1.f / L;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) op[e] = f32_to_bf16(acc[e] * inv);
-      if (lse != nullptr && d0 == 0) lse[static_cast<size_t>(row) * Hq + kvh * G + h] = (M + log2f(L)) * kLn2;
+      for (int e = 1; e < 5; ++e) best = fmaxf(best, u[4 * tid + e]);
+      agent_store(srow + blk, best * g.scale);
     }
+  }
+}
+
+// LDS of the fused kernel's selection.
+struct SelLds {
+  int hist[2][256];
+  int wsum[kFusedWaves][2];
+  uint32_t wmin[kFusedWaves], wmax[kFusedWaves];
+  uint32_t bin_key[64];
+  int bin_blk[64];
+  int nbin;
+  int digit, above, count;
+};
+
+// Group-shared top-k of one (row, kv head) from its stored block scores srow[0 .. own] (section
+// 2.1.1: highest relevance first; reading: forced first n_init and last n_local blocks, ties to
+// the lower index, ascending output).  The (topk - forced)-th largest order-preserving key
+// among the other blocks is located by a radix select over the keys' actual range: the first
+// pass bins (key - min) >> s into 256 bins (s the smallest shift that fits max - min), each
+// later pass splits the chosen bin 256 ways.  It stops when every key of the chosen bin is
+// wanted, or the bin holds a single key value (taken in block order), or the bin holds at most
+// 64 keys: then one wave ranks those keys exactly (key descending, block ascending) and marks
+// the wanted ones.  `keys` holds one key per block in LDS for the ordered output.
+__device__ __forceinline__ void select_blocks(const Geom& g, int own, const float* srow,
+                                              int32_t* out_idx, uint32_t* keys, SelLds& sm,
+                                              int tid) {
+  constexpr int T = kFusedThreads;
+  constexpr int NW = kFusedWaves;
+  constexpr uint32_t kTaken = 0xFFFFFFFFu;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int nb = own + 1;
+  if (nb <= g.topk) {
+    for (int e = tid; e < g.topk; e += T) agent_store(out_idx + e, e < nb ? e : -1);
     return;
   }
-
-  // ---- partial of this split, then the last split of (row, kv head) merges all of them
-  DecodeWs ws = ws_of(workspace, rows, Hkv, nsplit, G, D);
-  const size_t ebase = (static_cast<size_t>(vrow) * Hkv + kvh) * nsplit * G;   // entry of split 0
-  // Partials cross workgroups (and XCDs, whose L2s are not coherent with each other) through
-  // agent-scope atomic stores and loads, which are coherent at that scope by themselves; a
-  // fence would instead write back and invalidate the whole L2 of the XCD.
-  if (h < G && d0 < D) {
-    const size_t e = ebase + static_cast<size_t>(sp) * G + h;
-    uint64_t* po = reinterpret_cast<uint64_t*>(ws.part_o + e * D + d0);
+  const int local_lo = max(0, own - g.n_local + 1);
+  const int init_end = min(g.n_init, nb);
+  const int n_forced = init_end + (own - local_lo + 1) - max(0, init_end - local_lo);
+  const int npt = (nb + T - 1) / T;
+  // every score load is issued before any is used
+  float sc[kMaxKeysPerThread];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      agent_store(po + i, pack2(acc[2 * i], acc[2 * i + 1]));
-    if (d0 == 0) agent_store(reinterpret_cast<uint64_t*>(ws.part_ml + e * 2), pack2(M, L));
+  for (int e = 0; e < kMaxKeysPerThread; ++e)
+    sc[e] = e < npt ? __uint_as_float(agent_load(reinterpret_cast<const uint32_t*>(srow) +
+                                                 min(e * T + tid, nb - 1)))
+                    : 0.f;
+  uint32_t kr[kMaxKeysPerThread];
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int e = 0; e < kMaxKeysPerThread; ++e) {
+    const int blk = e * T + tid;
+    const bool forced = blk < g.n_init || blk >= local_lo;
+    kr[e] = (e < npt && blk < nb && !forced) ? order_key(sc[e]) : 0u;   // 0: not a candidate
+    if (e < npt && blk < nb) keys[blk] = kr[e];
+    if (kr[e] != 0u) {
+      kmin = min(kmin, kr[e]);
+      kmax = max(kmax, kr[e]);
+    }
   }
-  wait_vmcnt<0>();                                   // this wave's stores are complete
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) {
+    sm.wmin[w] = kmin;
+    sm.wmax[w] = kmax;
+  }
+  if (tid < 256) {
+    sm.hist[0][tid] = 0;
+    sm.hist[1][tid] = 0;
+  }
+  if (tid == 0) sm.nbin = 0;
   __syncthreads();
-  int* cnt = ws.count + static_cast<size_t>(vrow) * Hkv + kvh;
-  if (tid == 0)
-    s_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             nsplit - 1;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) {
+    kmin = min(kmin, sm.wmin[ww]);
+    kmax = max(kmax, sm.wmax[ww]);
+  }
+  int want = g.topk - n_forced;                         // still wanted in the current bin
+  // keys >= hi are taken, keys in [lo, hi) in block order until `want` are (want == 0: none)
+  uint64_t lo = uint64_t{1} << 32, hi = uint64_t{1} << 32;
+  if (want > 0) {
+    uint32_t blo = kmin;                                // the current bin is [blo, bin_hi)
+    uint64_t bin_hi = static_cast<uint64_t>(kmax) + 1;
+    const uint32_t span = kmax - kmin;
+    int s = span == 0u ? 0 : max(0, 32 - __clz(static_cast<int>(span)) - 8);
+    const uint64_t above_lane = ~((2ull << lane) - 1);  // lanes over this one (none for 63)
+    for (int pass = 0;; ++pass) {
+      int* hist = sm.hist[pass & 1];
+#pragma unroll
+      for (int e = 0; e < kMaxKeysPerThread; ++e) {
+        const uint32_t key = kr[e];
+        if (key != 0u && key >= blo && key < bin_hi) atomicAdd(&hist[(key - blo) >> s], 1);
+      }
+      __syncthreads();
+      if (w == 0) {
+        // lane L holds bins 4L .. 4L+3 (zeroed again for the pass after next); the count over
+        // them is summed from the lanes above by one ballot per bit (counts < 2^13)
+        int c[4], tot = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          c[j] = hist[4 * lane + j];
+          hist[4 * lane + j] = 0;
+          tot += c[j];
+        }
+        int above = masked_count<13>(tot, above_lane);
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+          if (above < want && above + c[j] >= want) {
+            sm.digit = 4 * lane + j;
+            sm.above = above;
+            sm.count = c[j];
+          }
+          above += c[j];
+        }
+      }
+      __syncthreads();
+      blo += static_cast<uint32_t>(sm.digit) << s;
+      bin_hi = static_cast<uint64_t>(blo) + (uint64_t{1} << s);
+      want -= sm.above;
+      const int count = sm.count;
+      lo = blo;
+      hi = bin_hi;
+      if (count == want || s == 0) break;               // the whole bin is wanted, or one value
+      if (count <= 64) {
+        // rank the bin's keys in one wave and mark the wanted ones taken, the others dropped
+#pragma unroll
+        for (int e = 0; e < kMaxKeysPerThread; ++e) {
+          const uint32_t key = kr[e];
+          if (key != 0u && key >= blo && key < bin_hi) {
+            const int slot = atomicAdd(&sm.nbin, 1);
+            sm.bin_key[slot] = key;
+            sm.bin_blk[slot] = e * T + tid;
+          }
+        }
+        __syncthreads();
+        if (w == 0) {
+          const uint32_t ki = lane < count ? sm.bin_key[lane] : 0u;
+          const int bi = lane < count ? sm.bin_blk[lane] : 0x7FFFFFFF;
+          int rank = 0;
+          for (int j = 0; j < count; ++j) {
+            const uint32_t kj = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ki), j));
+            const int bj = __builtin_amdgcn_readlane(bi, j);
+            rank += (kj > ki || (kj == ki && bj < bi)) ? 1 : 0;
+          }
+          if (lane < count) keys[bi] = rank < want ? kTaken : 0u;
+        }
+        __syncthreads();
+        want = 0;                                       // the bin is decided: marks only
+        hi = min(bin_hi, static_cast<uint64_t>(kTaken));
+        lo = hi;
+        break;
+      }
+      s = max(0, s - 8);
+    }
+  }
+  // over the bin: taken; in the bin: taken in block order until `want` are.  Thread tid
+  // writes blocks npt*tid .. npt*tid + npt - 1.
+  const int blk_lo = npt * tid;
+  const int blk_hi = min(nb, blk_lo + npt);
+  int fixed = 0, eq = 0;
+  for (int blk = blk_lo; blk < blk_hi; ++blk) {
+    const uint32_t key = keys[blk];
+    const bool forced = blk < g.n_init || blk >= local_lo;
+    fixed += (forced || (key != 0u && key >= hi)) ? 1 : 0;
+    eq += (!forced && key != 0u && key >= lo && key < hi) ? 1 : 0;
+  }
+  // exclusive prefix counts over the workgroup: bit ballots within the wave, then wave totals
+  const uint64_t below = (1ull << lane) - 1;
+  int fixed_before = masked_count<4>(fixed, below);
+  int eq_before = masked_count<4>(eq, below);
+  const int fixed_wave = masked_count<4>(fixed, ~0ull);    // ballots: the whole wave takes part
+  const int eq_wave = masked_count<4>(eq, ~0ull);
+  if (lane == 0) {
+    sm.wsum[w][0] = fixed_wave;
+    sm.wsum[w][1] = eq_wave;
+  }
+  __syncthreads();
+  for (int ww = 0; ww < w; ++ww) {
+    fixed_before += sm.wsum[ww][0];
+    eq_before += sm.wsum[ww][1];
+  }
+  int eq_seen = eq_before;
+  int p = fixed_before + min(eq_seen, want);
+  for (int blk = blk_lo; blk < blk_hi; ++blk) {
+    const uint32_t key = keys[blk];
+    const bool forced = blk < g.n_init || blk >= local_lo;
+    bool take = forced || (key != 0u && key >= hi);
+    if (!take && key != 0u && key >= lo && key < hi) {
+      take = eq_seen < want;
+      ++eq_seen;
+    }
+    if (take && p < g.topk) agent_store(out_idx + p, blk);   // p < topk unless keys are NaN
+    p += take ? 1 : 0;
+  }
+}
+
+template <int D, int G>
+__global__ void __launch_bounds__(kFusedThreads)
+decode_select(Geom g, SeqTable t, const uint16_t* __restrict__ q,
+              const uint16_t* __restrict__ kern, float* __restrict__ scores, int nb_stride,
+              int32_t* __restrict__ idx, void* __restrict__ workspace) {
+  __shared__ __attribute__((aligned(16))) uint32_t stage[kMaxKeysPerThread * kFusedThreads];
+  __shared__ float qs[D];
+  __shared__ SelLds sm;
+  __shared__ int s_last;
+  static_assert(kMaxKeysPerThread * kFusedThreads >= 4 * kChunkBlocks + 4, "score staging fits");
+
+  const int tid = threadIdx.x;
+  const int chunk = blockIdx.x;
+  const int pair = blockIdx.y;
+  const int kvh = pair % g.Hkv;
+  const DecRow r = dec_row(t, pair / g.Hkv);
+  const int own = r.pos / 64;
+  const int n_chunks = own / kChunkBlocks + 1;
+  if (chunk >= n_chunks) return;                       // whole workgroup
+  const int pairs = t.work_prefix[t.n] * g.Hkv;
+  int* score_done = reinterpret_cast<int*>(static_cast<char*>(workspace) +
+                                           decode_layout(pairs).score_done);
+  float* srow = scores + (static_cast<size_t>(r.row) * g.Hkv + kvh) * nb_stride;
+  score_chunk<D, G>(g, t, r, kvh, chunk * kChunkBlocks, own, q, kern, srow, qs,
+                    reinterpret_cast<float*>(stage), tid);
+  wait_vmcnt<0>();                                     // this wave's scores are stored
+  __syncthreads();
+  if (tid == 0) s_last = agent_add(score_done + pair, 1) == n_chunks - 1;
   __syncthreads();
   if (!s_last) return;
-  if (h < G && d0 < D) {
-    // online log-sum-exp merge; the loads of 8 splits are issued before any is used
-    float MM = -INFINITY, LL = 0.f;
-    float a2[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) a2[e] = 0.f;
-    for (int s0 = 0; s0 < nsplit; s0 += 8) {
-      uint64_t ml[8], ov[8][4];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const size_t e = ebase + static_cast<size_t>(min(s0 + u, nsplit - 1)) * G + h;
-        ml[u] = agent_load(reinterpret_cast<const uint64_t*>(ws.part_ml + e * 2));
-        const uint64_t* po = reinterpret_cast<const uint64_t*>(ws.part_o + e * D + d0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ov[u][i] = agent_load(po + i);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float ms = lo_f32(ml[u]);
-        if (s0 + u >= nsplit || ms == -INFINITY) continue;      // duplicate or empty split
-        const float Mn = fmaxf(MM, ms);
-        const float fo = __builtin_amdgcn_exp2f(MM - Mn);
-        const float fn = __builtin_amdgcn_exp2f(ms - Mn);
-        LL = LL * fo + hi_f32(ml[u]) * fn;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          a2[2 * i] = a2[2 * i] * fo + lo_f32(ov[u][i]) * fn;
-          a2[2 * i + 1] = a2[2 * i + 1] * fo + hi_f32(ov[u][i]) * fn;
-        }
-        MM = Mn;
-      }
-    }
-    uint16_t* op = out + (static_cast<size_t>(row) * Hq + kvh * G + h) * D + d0;
-    const float inv = 1.f / LL;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) op[e] = f32_to_bf16(a2[e] * inv);
-    if (lse != nullptr && d0 == 0) lse[static_cast<size_t>(row) * Hq + kvh * G + h] = (MM + log2f(LL)) * kLn2;
-  }
-  if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
+  // the pair's last chunk: select, and zero the counter for the next call (its last user)
+  select_blocks(g, own, srow, idx + (static_cast<size_t>(r.row) * g.Hkv + kvh) * g.topk, stage,
+                sm, tid);
+  if (tid == 0) agent_store(score_done + pair, 0);
 }
 
 }  // namespace
@@ -370,15 +770,30 @@ bool attn_decode_supported(const Geom& g, int dtype) {
   return dtype == INFLLM2_BF16 && g.B == 64 && (g.d == 64 || g.d == 128) && (g.G == 8 || g.G == 16);
 }
 
-size_t attn_decode_workspace(const Geom& g, int rows, int nsplit) {
-  return static_cast<size_t>(rows) * g.Hkv * nsplit * g.G * (g.d + 2) * sizeof(float) +
-         static_cast<size_t>(rows) * g.Hkv * sizeof(int);
+size_t decode_workspace(const Geom& g, int rows, int nsplit) {
+  const int pairs = rows * g.Hkv;
+  return decode_layout(pairs).part +
+         static_cast<size_t>(pairs) * nsplit * g.G * (g.d + 2) * sizeof(float);
 }
 
-// work_prefix of `t` counts query rows.
-hipError_t launch_attn_decode(const Geom& g, const SeqTable& t, const void* q, const void* k,
-                              const void* v, const int32_t* idx, int nsplit, void* workspace,
-                              void* out, float* lse, hipStream_t stream) {
+int decode_fused_splits(const Geom& g) { return (g.topk + kStepWaves - 1) / kStepWaves; }
+
+bool decode_fused_supported(const Geom& g, int dtype, const SeqTable& t) {
+  if (!attn_decode_supported(g, dtype) || g.w != 32 || g.s != 16 || g.score_mode != 0) return false;
+  long long rows = 0;
+  for (int b = 0; b < t.n; ++b) rows += t.q_len[b];
+  if (rows * g.Hkv > 65535) return false;               // one grid row per (row, KV head)
+  for (int b = 0; b < t.n; ++b)
+    if (t.q_len[b] > 0 && (t.q_pos0[b] + t.q_len[b] - 1) / 64 + 1 > kMaxKeysPerThread * kFusedThreads)
+      return false;
+  return true;
+}
+
+template <int NW>
+static hipError_t launch_split_attention(const Geom& g, const SeqTable& t, const void* q,
+                                         const void* k, const void* v, const int32_t* idx,
+                                         int nsplit, void* workspace, void* out, float* lse,
+                                         hipStream_t stream) {
   const int rows = t.work_prefix[t.n];
   if (rows == 0) return hipSuccess;
   if (nsplit < 1 || nsplit > 65535 || g.Hkv > 65535) return hipErrorInvalidValue;
@@ -389,7 +804,7 @@ hipError_t launch_attn_decode(const Geom& g, const SeqTable& t, const void* q, c
   uint16_t* oo = static_cast<uint16_t*>(out);
 #define INFLLM2_DEC_CASE(DD, GG)                                                                \
   if (g.d == DD && g.G == GG) {                                                                 \
-    hipLaunchKernelGGL((attn_decode<DD, GG>), grid, dim3(64 * kWaves), 0, stream, g, t, qq, kk, \
+    hipLaunchKernelGGL((attn_decode<DD, GG, NW>), grid, dim3(64 * NW), 0, stream, g, t, qq, kk, \
                        vv, idx, nsplit, workspace, oo, lse);                                    \
     return hipGetLastError();                                                                   \
   }
@@ -399,6 +814,48 @@ hipError_t launch_attn_decode(const Geom& g, const SeqTable& t, const void* q, c
   INFLLM2_DEC_CASE(64, 8)
 #undef INFLLM2_DEC_CASE
   return hipErrorInvalidValue;
+}
+
+// work_prefix of `t` counts query rows.
+hipError_t launch_attn_decode(const Geom& g, const SeqTable& t, const void* q, const void* k,
+                              const void* v, const int32_t* idx, int nsplit, void* workspace,
+                              void* out, float* lse, hipStream_t stream) {
+  return launch_split_attention<kSplitWaves>(g, t, q, k, v, idx, nsplit, workspace, out, lse,
+                                             stream);
+}
+
+// work_prefix of `t` counts query rows; kernels must already hold every complete kernel.
+hipError_t launch_decode_fused(const Geom& g, const SeqTable& t, const void* q,
+                               const void* kernels, const void* k, const void* v, float* scores,
+                               int nb_stride, int32_t* idx, int nsplit, void* workspace,
+                               void* out, float* lse, hipStream_t stream) {
+  const int rows = t.work_prefix[t.n];
+  if (rows == 0) return hipSuccess;
+  int max_blocks = 1;
+  for (int b = 0; b < t.n; ++b)
+    if (t.q_len[b] > 0) max_blocks = std::max(max_blocks, (t.q_pos0[b] + t.q_len[b] - 1) / 64 + 1);
+  const int max_chunks = (max_blocks + kChunkBlocks - 1) / kChunkBlocks;
+  if (static_cast<long long>(rows) * g.Hkv > 65535) return hipErrorInvalidValue;
+  const dim3 grid(max_chunks, rows * g.Hkv);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kc = static_cast<const uint16_t*>(kernels);
+  bool launched = false;
+#define INFLLM2_SEL_CASE(DD, GG)                                                                \
+  if (!launched && g.d == DD && g.G == GG) {                                                    \
+    hipLaunchKernelGGL((decode_select<DD, GG>), grid, dim3(kFusedThreads), 0, stream, g, t, qq, \
+                       kc, scores, nb_stride, idx, workspace);                                  \
+    launched = true;                                                                            \
+  }
+  INFLLM2_SEL_CASE(128, 16)
+  INFLLM2_SEL_CASE(128, 8)
+  INFLLM2_SEL_CASE(64, 16)
+  INFLLM2_SEL_CASE(64, 8)
+#undef INFLLM2_SEL_CASE
+  if (!launched) return hipErrorInvalidValue;
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_split_attention<kStepWaves>(g, t, q, k, v, idx, nsplit, workspace, out, lse,
+                                            stream);
 }
 
 }  // namespace infllm2

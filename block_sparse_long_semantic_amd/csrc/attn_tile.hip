@@ -716,8 +716,7 @@ bool attn_tile_supported(const Geom& g, int dtype, const SeqTable& t) {
   return true;
 }
 
-// Number of compute units of the current device (cached per device).
-static int device_cus() {
+int device_cus() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

@@ -56,6 +56,25 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Number of compute units of the current device (cached per device; 256 if the query fails).
+int device_cus();
+
+// Decode workspace, shared by the split-KV decode attention and the decoding step: two int
+// arrays over the (row, KV head) pairs (completed attention splits, completed score chunks),
+// each padded to 256 bytes, then the float32 partials: outputs [pair][split][G][d], then
+// (max, sum) [pair][split][G][2].  Byte offsets:
+struct DecodeLayout {
+  size_t split_done, score_done, part;
+};
+__host__ __device__ inline DecodeLayout decode_layout(int pairs) {
+  const size_t arr = (static_cast<size_t>(pairs) * 4 + 255) / 256 * 256;
+  DecodeLayout L;
+  L.split_done = 0;
+  L.score_done = arr;
+  L.part = 2 * arr;
+  return L;
+}
+
 // Launch entry points (one per translation unit).  All return hipSuccess or the launch error.
 hipError_t launch_compress(const Geom& g, int dtype, const SeqTable& t, const void* k,
                            void* kernels, hipStream_t stream);
@@ -99,12 +118,21 @@ hipError_t launch_attn_bwd(const Geom& g, const SeqTable& t, int n_blocks, int q
                            const void* q, const void* k, const void* v, const int32_t* idx,
                            const void* out, const float* lse, const void* dout, float* dq,
                            float* dk, float* dv, void* workspace, hipStream_t stream);
-// Split-KV decoding attention with the merge done by the last workgroup of each (row, kv head).
+// Split-KV decoding attention with the merge done by the last workgroup of each (row, kv head);
+// its workspace follows decode_layout.
 bool attn_decode_supported(const Geom& g, int dtype);
-size_t attn_decode_workspace(const Geom& g, int rows, int nsplit);
+size_t decode_workspace(const Geom& g, int rows, int nsplit);
 hipError_t launch_attn_decode(const Geom& g, const SeqTable& t, const void* q, const void* k,
                               const void* v, const int32_t* idx, int nsplit, void* workspace,
                               void* out, float* lse, hipStream_t stream);
+// One decoding step after the kernels are compressed: block scores and top-k in one launch
+// (decode_select), then the split-KV attention; work_prefix of `t` counts query rows.
+bool decode_fused_supported(const Geom& g, int dtype, const SeqTable& t);
+int decode_fused_splits(const Geom& g);
+hipError_t launch_decode_fused(const Geom& g, const SeqTable& t, const void* q,
+                               const void* kernels, const void* k, const void* v, float* scores,
+                               int nb_stride, int32_t* idx, int nsplit, void* workspace,
+                               void* out, float* lse, hipStream_t stream);
 hipError_t launch_attn_combine(const Geom& g, int dtype, const SeqTable& t, int splits,
                                const float* part, void* out, float* lse, hipStream_t stream);
 

@@ -20,6 +20,7 @@
 //   * scores_softmax_simple any dtype and geometry.
 #include <algorithm>
 
+#include "dpp.h"
 #include "internal.h"
 
 namespace infllm2 {
@@ -233,8 +234,8 @@ scores_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
 // Few query rows (decoding): the work is streaming every semantic kernel of the sequence once,
 // so it is spread over chunks of 64 blocks (256 kernels + the halo kernel before them) per
 // workgroup.  The group-summed query stays in float32; each kernel row is read by D/8 lanes
-// (16 bytes each, one coalesced row per lane group), dotted with float32 FMAs and reduced with
-// lane shuffles.  Kernel scores go to LDS, then 64 threads max-pool them onto the chunk's
+// (16 bytes each, one coalesced row per lane group), dotted with float32 FMAs and reduced across
+// the lanes by DPP moves.  Kernel scores go to LDS, then 64 threads max-pool them onto the chunk's
 // blocks and write one coalesced row segment.
 template <int D>
 __global__ void __launch_bounds__(kThreads)
@@ -278,8 +279,15 @@ scores_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q,
   }
   for (int e = tid; e < D; e += kThreads) {
     float acc = 0.f;
-    for (int h = 0; h < g.G; ++h)
-      acc += bf16_to_f32(q[(static_cast<size_t>(row) * g.Hq + kvh * g.G + h) * D + e]);
+    for (int h0 = 0; h0 < g.G; h0 += 16) {
+      float qh[16];                                     // 16 heads' loads in flight at once
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        qh[j] = bf16_to_f32(q[(static_cast<size_t>(row) * g.Hq + kvh * g.G + min(h0 + j, g.G - 1)) * D + e]);
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (h0 + j < g.G) acc += qh[j];
+    }
     qs[e] = acc;
   }
   __syncthreads();
@@ -299,8 +307,7 @@ scores_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q,
       dot = fmaf(__uint_as_float(w4[e] << 16), qv[2 * e], dot);
       dot = fmaf(__uint_as_float(w4[e] & 0xFFFF0000u), qv[2 * e + 1], dot);
     }
-#pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
+    dot = group_sum<LPR>(dot);
     if (lane % LPR == 0 && it < NIT && r < NROW) u[r] = ok ? dot : -INFINITY;
   }
   __syncthreads();

@@ -192,10 +192,12 @@ infllm2_status infllm2_sparse_attn_backward(const infllm2_params* params,
                                             float* dk, float* dv, void* workspace,
                                             size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace infllm2_sparse_attn_decode needs for `total_q_rows` query rows
- * (sum of q_len) split `num_splits` ways (0 = the automatic choice).  The workspace holds the
- * per-split partial results and one completion counter per (row, KV head): it must be
- * zero-filled before its first use, and every call leaves it zero-filled again. */
+/* Bytes of device workspace infllm2_sparse_attn_decode and infllm2_decode_step need for
+ * `total_q_rows` query rows (sum of q_len) split `num_splits` ways (0 = the automatic choice of
+ * each call).  The workspace holds per-(row, KV head) counters, then the per-split partial
+ * results: it must be zero-filled before its first use, and every call leaves the counters
+ * zero again.  Calls that share a workspace must not overlap
+ * (enqueue them on one stream). */
 size_t infllm2_decode_workspace_size(const infllm2_params* params, int32_t total_q_rows,
                                      int32_t num_splits);
 
@@ -209,11 +211,16 @@ infllm2_status infllm2_sparse_attn_decode(const infllm2_params* params, const in
                                           void* workspace, size_t workspace_bytes, void* out,
                                           float* lse, void* stream);
 
-/* One decoding step, the calls above chained on `stream` in the method's order: semantic
- * kernels completed since prev_kv_len (host array, may be NULL), block scores into `scores`
- * (nb_stride floats per (row, KV head)), top-k into block_idx, then split-KV attention.
- * Arguments mean what they mean in those calls; the first failing call's status is returned
- * and nothing after it is enqueued. */
+/* One decoding step in the method's order (csdn summary 2.1.1-2.1.3): semantic kernels
+ * completed since prev_kv_len (host array, may be NULL), block scores into `scores` (nb_stride
+ * floats per (row, KV head)), top-k into block_idx, then split-KV attention.  Arguments mean
+ * what they mean in the separate calls, and the same checks apply; `workspace` is always
+ * required here.  For bf16, block 64, kernels 32/16, d 64 or 128, groups of 8 or 16 and score
+ * mode 0, the scores and the top-k run as one launch (the last workgroup to finish a (row, KV
+ * head)'s scores selects its blocks) and the attention as a second; the results equal those of
+ * the separate calls (scores and indices exactly, outputs to float32 rounding).  Otherwise the
+ * separate calls are chained on `stream`; the first failing call's status is returned and
+ * nothing after it is enqueued. */
 infllm2_status infllm2_decode_step(const infllm2_params* params, const infllm2_seqs* seqs,
                                   const void* q, const void* k_cache, const void* v_cache,
                                   void* kernels, const int32_t* prev_kv_len, float* scores,

@@ -143,12 +143,13 @@ def test_incremental_range_checked(so):
 def test_decode_workspace(so):
     p = params()
     d = p.head_dim
-    # per (row, query head, split): running max, denominator and d partial outputs (float32),
-    # then one int32 completion counter per (row, KV head)
-    counters = 8 * p.num_kv_heads * 4
+    # two int32 counter arrays over the (row, KV head) pairs, each padded to 256 bytes, then
+    # per (row, query head, split) the running max, denominator and d partial outputs (float32)
+    al = lambda x: (x + 255) // 256 * 256
+    counters = 2 * al(8 * p.num_kv_heads * 4)
     assert lib.decode_workspace_size(p, 8, 12) == 8 * 32 * 12 * (2 + d) * 4 + counters
-    auto = lib.decode_workspace_size(p, 8, 0)
-    assert auto > counters and (auto - counters) % (8 * 32 * (2 + d) * 4) == 0
+    # automatic splits: one block per wave of 4 (96 / 4)
+    assert lib.decode_workspace_size(p, 8, 0) == 8 * 32 * 24 * (2 + d) * 4 + counters
     cp, cs = p.c(), seqs(q_len=[1], q_pos0=[99]).c()
     st = so.infllm2_sparse_attn_decode(ctypes.byref(cp), ctypes.byref(cs), FAKE, FAKE, FAKE, FAKE,
                                        4, FAKE, 16, FAKE, None, None)
@@ -156,6 +157,24 @@ def test_decode_workspace(so):
     st = so.infllm2_sparse_attn_decode(ctypes.byref(cp), ctypes.byref(cs), FAKE, FAKE, FAKE, FAKE,
                                        97, FAKE, 1 << 30, FAKE, None, None)
     assert st == SHAPE
+
+
+def test_decode_step_checks(so):
+    """The single-launch decode step (bf16, d 128, G 16) checks every argument before anything
+    is enqueued; each call below breaks exactly one of them."""
+    p = params()
+    s = seqs(q_len=[1], q_pos0=[99])
+    cp, cs = p.c(), s.c()
+
+    def call(ws=FAKE, ws_bytes=1 << 30, nb=2, scores=FAKE, splits=0):
+        return so.infllm2_decode_step(ctypes.byref(cp), ctypes.byref(cs), FAKE, FAKE, FAKE, FAKE,
+                                      None, scores, nb, FAKE, splits, ws, ws_bytes, FAKE, None,
+                                      None)
+    assert call(ws=None) == NULL and "workspace" in last(so)
+    assert call(ws_bytes=16) == WS
+    assert call(nb=1) == SHAPE and "nb_stride" in last(so)
+    assert call(scores=MISALIGNED) == ALIGN
+    assert call(splits=97) == SHAPE
 
 
 def call_bwd(so, p, s, lse=FAKE, dq=FAKE, ws=FAKE, ws_bytes=1 << 30):

@@ -145,6 +145,27 @@ def test_results_are_deterministic():
 
 # ------------------------------------------------------------------------- decode
 
+def check_decode_seq(p, ks, vs, q_rows, gk, scores, idx, out, lse, label):
+    """One sequence of a decode step against the oracle: q_rows [n, Hq, d] are its new tokens
+    (positions L-n .. L-1 of its L cached tokens); the other arguments are the GPU's kernels
+    and the rows' scores, indices, outputs and LSE."""
+    L = ks.shape[0]
+    n = q_rows.shape[0]
+    kern_ref = orc.compress_kernels(ks, p.kernel_size, p.kernel_stride, p.dtype)
+    assert np.array_equal(gk[:kern_ref.shape[0]], kern_ref), f"{label}: kernels differ"
+    ref = orc.run_sequence(q_rows, ks, vs, p, q_pos0=L - n, kernels=kern_ref,
+                           with_attention=False)
+    NB = ref.scores.shape[2]
+    gs = scores[:, :, :NB]
+    bound = cmp.score_bound(q_rows.astype(np.float64), kern_ref, ref.positions, p, NB)
+    cmp.check_scores(gs, ref.scores, bound, ref.positions, p)
+    assert np.array_equal(idx, orc.select_all(gs.astype(np.float64), ref.positions, p)), \
+        f"{label}: top-k differs on the GPU's own scores"
+    cmp.check_indices(idx, ref.idx, ref.scores, ref.positions, p)
+    O, Ls = orc.sparse_attention(q_rows.astype(np.float64), ref.positions, ks, vs, idx, p)
+    cmp.check_attention(out, lse, O, Ls, p.dtype)
+
+
 def run_decode(wl, steps, num_splits=0, check=True, label="decode", step_fn=None):
     step_fn = step_fn or lib.decode_step
     p = wl.params
@@ -173,25 +194,11 @@ def run_decode(wl, steps, num_splits=0, check=True, label="decode", step_fn=None
         if check:
             for b in range(B):
                 L = int(kv[b])
-                ks, vs = wl.k[b, :L], wl.v[b, :L]
-                kern_ref = orc.compress_kernels(ks, p.kernel_size, p.kernel_stride, p.dtype)
-                C = kern_ref.shape[0]
-                gk = host(kern[b * Ck:b * Ck + C])
-                assert np.array_equal(gk, kern_ref), f"{label}: kernels differ seq {b} step {st}"
-                ref = orc.run_sequence(wl.q_steps[st][b:b + 1], ks, vs, p, q_pos0=L - 1,
-                                       kernels=kern_ref, with_attention=False)
-                NB = ref.scores.shape[2]
-                gs = outs[-1]["scores"][b:b + 1, :, :NB]
-                bound = cmp.score_bound(wl.q_steps[st][b:b + 1].astype(np.float64), kern_ref,
-                                        ref.positions, p, NB)
-                cmp.check_scores(gs, ref.scores, bound, ref.positions, p)
-                gidx = outs[-1]["idx"][b:b + 1]
-                assert np.array_equal(gidx, orc.select_all(gs.astype(np.float64), ref.positions, p))
-                cmp.check_indices(gidx, ref.idx, ref.scores, ref.positions, p)
-                O, Ls = orc.sparse_attention(wl.q_steps[st][b:b + 1].astype(np.float64),
-                                             ref.positions, ks, vs, gidx, p)
-                cmp.check_attention(outs[-1]["out"][b:b + 1], outs[-1]["lse"][b:b + 1], O, Ls,
-                                    p.dtype)
+                o = outs[-1]
+                check_decode_seq(p, wl.k[b, :L], wl.v[b, :L], wl.q_steps[st][b:b + 1],
+                                 host(kern[b * Ck:(b + 1) * Ck]), o["scores"][b:b + 1],
+                                 o["idx"][b:b + 1], o["out"][b:b + 1], o["lse"][b:b + 1],
+                                 f"{label} seq {b} step {st}")
     return outs
 
 
@@ -285,15 +292,116 @@ def test_full_size_decode():
 
 
 def test_decode_fused_call_matches_staged_calls():
+    """infllm2_decode_step (scores and top-k in one launch, then the attention) against the four
+    separate calls: both checked against the oracle, scores and indices identical, outputs
+    equal to float32 rounding (the step may split the blocks over other workgroup shapes)."""
     p = synth.config_params("decode128k")
     wl = synth.make_decode("dec-fused", p, batch=4, max_len=4096, steps=2, seed=44,
                            kv_len0=[4000, 2500, 1000, 64])
     log("case decode fused vs staged")
-    fused = run_decode(wl, 2, check=False)
-    staged = run_decode(wl, 2, check=False, step_fn=lib.pipeline.decode_step_staged)
+    fused = run_decode(wl, 2, label="step")
+    staged = run_decode(wl, 2, step_fn=lib.pipeline.decode_step_staged, label="staged")
     for st, (a, b) in enumerate(zip(fused, staged)):
-        for n in ("idx", "out", "lse"):
-            assert np.array_equal(a[n], b[n]), n
+        assert np.array_equal(a["idx"], b["idx"])
         for r in range(wl.batch):   # scores past the query's own block are left unwritten
             nb = (int(wl.kv_len0[r]) + st) // p.block_size + 1
             assert np.array_equal(a["scores"][r, :, :nb], b["scores"][r, :, :nb])
+        assert np.abs(a["out"] - b["out"]).max() <= 1e-2
+        assert np.abs(a["lse"] - b["lse"]).max() <= 1e-4
+
+
+def test_decode_forced_blocks_only():
+    """top-k equal to the forced blocks (1 first + 2 local): nothing is left to choose once a
+    row sees more than 3 blocks."""
+    p = replace(synth.config_params("decode128k"), topk=3)
+    wl = synth.make_decode("dec-forced", p, batch=3, max_len=3000, steps=2, seed=45,
+                           kv_len0=[2990, 900, 100])
+    log("case decode forced only")
+    run_decode(wl, 2)
+
+
+def test_decode_tied_scores():
+    """Every key equal, so every kernel and every block score ties: the lowest block indices
+    win, and attention over equal keys is the mean of the selected values."""
+    p = synth.config_params("decode128k")
+    wl = synth.make_decode("dec-ties", p, batch=2, max_len=8192, steps=2, seed=46,
+                           kv_len0=[8000, 7000])
+    wl.k[:] = wl.k[:, :1]
+    log("case decode ties")
+    outs = run_decode(wl, 2)
+    for st, o in enumerate(outs):
+        for b in range(wl.batch):
+            own = (int(wl.kv_len0[b]) + st) // p.block_size
+            chosen = o["idx"][b, 0]
+            assert chosen[0] == 0 and chosen[-2] == own - 1 and chosen[-1] == own
+            assert np.array_equal(chosen[1:-2], np.arange(1, p.topk - 2))
+
+
+def test_decode_several_rows_per_sequence():
+    """Three new tokens per sequence in one step (positions L-3 .. L-1), each row with its own
+    scores, selection and attention; one sequence with a single row."""
+    p = synth.config_params("decode128k")
+    lens, nq, Lmax = [3000, 2100, 700], [3, 3, 1], 3072
+    B = len(lens)
+    wl = synth.make_decode("dec-rows", p, batch=B, max_len=Lmax, steps=1, seed=47)
+    rng = np.random.default_rng(48)
+    qs = [synth.make_upstream_grad((n, p.num_q_heads, p.head_dim), int(rng.integers(1 << 30)))
+          for n in nq]
+    Ck = orc.num_kernels(Lmax, p.kernel_size, p.kernel_stride)
+    k = dev(wl.k.reshape(B * Lmax, p.num_kv_heads, p.head_dim), p.dtype)
+    v = dev(wl.v.reshape(B * Lmax, p.num_kv_heads, p.head_dim), p.dtype)
+    kern = torch.zeros((B * Ck, p.num_kv_heads, p.head_dim), dtype=k.dtype, device="cuda")
+    q_start = np.concatenate([[0], np.cumsum(nq)[:-1]])
+    seqs = lib.Seqs(q_start, nq, np.array(lens) - np.array(nq), np.arange(B) * Lmax, lens,
+                    np.arange(B) * Ck)
+    bufs = lib.pipeline.decode_buffers(p, sum(nq), (Lmax + 63) // 64, 0, "cuda")
+    log("case decode several rows")
+    lib.decode_step(p, seqs, dev(np.concatenate(qs), p.dtype), k, v, kern, None, bufs)
+    torch.cuda.synchronize()
+    res = {n: host(bufs[n]) for n in ("scores", "idx", "out", "lse")}
+    for b in range(B):
+        r = slice(int(q_start[b]), int(q_start[b]) + nq[b])
+        check_decode_seq(p, wl.k[b, :lens[b]], wl.v[b, :lens[b]], qs[b],
+                         host(kern[b * Ck:(b + 1) * Ck]), res["scores"][r], res["idx"][r],
+                         res["out"][r], res["lse"][r], f"rows seq {b}")
+
+
+def test_decode_longest_cache():
+    """A 262144-token cache: 4096 blocks, the most a selection takes."""
+    p = synth.config_params("decode128k")
+    wl = synth.make_decode("dec-256k", p, batch=1, max_len=262144, steps=1, seed=49)
+    log("case decode 256K")
+    run_decode(wl, 1, label="256K decode")
+
+
+def decode_counters_bytes(rows, p):
+    al = lambda x: (x + 255) // 256 * 256
+    return 2 * al(rows * p.num_kv_heads * 4)
+
+
+def test_decode_leaves_workspace_counters_zero():
+    """Each decode step zeroes the workspace counters it used (score chunks, attention splits),
+    so consecutive steps share one workspace; every step checked against the oracle."""
+    p = synth.config_params("decode128k")
+    B, Lmax = 3, 4096
+    wl = synth.make_decode("dec-ws", p, batch=B, max_len=Lmax, steps=3, seed=50,
+                           kv_len0=[4000, 3000, 2000])
+    Ck = orc.num_kernels(Lmax, p.kernel_size, p.kernel_stride)
+    k = dev(wl.k.reshape(B * Lmax, p.num_kv_heads, p.head_dim), p.dtype)
+    v = dev(wl.v.reshape(B * Lmax, p.num_kv_heads, p.head_dim), p.dtype)
+    kern = torch.zeros((B * Ck, p.num_kv_heads, p.head_dim), dtype=k.dtype, device="cuda")
+    bufs = lib.pipeline.decode_buffers(p, B, Lmax // 64, 0, "cuda")
+    n_cnt = decode_counters_bytes(B, p) // 4
+    for st in range(3):
+        kv = wl.kv_len0.astype(np.int64) + st + 1
+        seqs = lib.Seqs.decode(kv, Lmax, Ck)
+        log(f"case decode workspace step {st}")
+        lib.decode_step(p, seqs, dev(wl.q_steps[st], p.dtype), k, v, kern, None, bufs)
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(bufs["workspace"].view(torch.int32)[:n_cnt])) == 0
+        for b in range(B):
+            L = int(kv[b])
+            check_decode_seq(p, wl.k[b, :L], wl.v[b, :L], wl.q_steps[st][b:b + 1],
+                             host(kern[b * Ck:(b + 1) * Ck]), host(bufs["scores"])[b:b + 1],
+                             host(bufs["idx"])[b:b + 1], host(bufs["out"])[b:b + 1],
+                             host(bufs["lse"])[b:b + 1], f"ws step {st} seq {b}")
