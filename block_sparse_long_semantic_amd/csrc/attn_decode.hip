@@ -68,6 +68,30 @@ __device__ __forceinline__ void read_v8(uint32_t addr, uint64_t (&vt)[4][2]) {
       : "memory");
 }
 
+// Row-major V slot (d = 128): 4 x 2 transposing reads, tile n from its own address a_n, the two
+// 4-key halves at +0 and +1024 bytes (+8192 for the second 32-key half of the block); waited
+// for inside the statement.
+#define INFLLM2_TR4X2(NAME, O0, O1)                                                            \
+  __device__ __forceinline__ void NAME(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,    \
+                                       uint64_t(&vt)[4][2]) {                                 \
+    asm volatile("ds_read_b64_tr_b16 %0, %8 offset:" #O0 "\n"                                 \
+                 "ds_read_b64_tr_b16 %1, %8 offset:" #O1 "\n"                                 \
+                 "ds_read_b64_tr_b16 %2, %9 offset:" #O0 "\n"                                 \
+                 "ds_read_b64_tr_b16 %3, %9 offset:" #O1 "\n"                                 \
+                 "ds_read_b64_tr_b16 %4, %10 offset:" #O0 "\n"                                \
+                 "ds_read_b64_tr_b16 %5, %10 offset:" #O1 "\n"                                \
+                 "ds_read_b64_tr_b16 %6, %11 offset:" #O0 "\n"                                \
+                 "ds_read_b64_tr_b16 %7, %11 offset:" #O1 "\n"                                \
+                 "s_waitcnt lgkmcnt(0)"                                                        \
+                 : "=&v"(vt[0][0]), "=&v"(vt[0][1]), "=&v"(vt[1][0]), "=&v"(vt[1][1]),         \
+                   "=&v"(vt[2][0]), "=&v"(vt[2][1]), "=&v"(vt[3][0]), "=&v"(vt[3][1])          \
+                 : "v"(a0), "v"(a1), "v"(a2), "v"(a3)                                          \
+                 : "memory");                                                                  \
+  }
+INFLLM2_TR4X2(read_tr_half0, 0, 1024)
+INFLLM2_TR4X2(read_tr_half1, 8192, 9216)
+#undef INFLLM2_TR4X2
+
 __device__ __forceinline__ uint64_t pack2(float a, float b) {
   return static_cast<uint64_t>(__float_as_uint(a)) | (static_cast<uint64_t>(__float_as_uint(b)) << 32);
 }
@@ -110,14 +134,21 @@ struct WaveAcc {
   float m, l;
 };
 
-// Per-lane constants of a wave's block fold for one (row, kv head).
+// Per-lane constants of a wave's block fold for one (row, kv head).  d = 128: V goes to the
+// wave's LDS slot as whole rows (4 rows of 256 bytes per load instruction), row r's 16-byte
+// chunk c stored at position c ^ vswz(r), vswz(r) = 2 ((r & 3) + 4 ((r >> 3) & 1)), which
+// spreads every transposing read over all 64 banks (each chunk position read by 2 of its 16
+// rows); lane addresses of the 8 column tiles in vt_addr.  d = 64: V in the order of the
+// transposing reads (one base address, immediate offsets).
 template <int D, int G>
 struct FoldCtx {
   bf16x8 qf[D / 32];
   const uint16_t* kbase;
   const uint16_t* vbase;
   int rowstride, k_lane_off, v_lane_off, k_lrow, v_lrow, pos, kv_len;
+  int v_col0, v_col1;
   uint32_t vaddr;
+  uint32_t vt_addr[D == 128 ? 8 : 1];
   lds_u8* slot;
   float qscale;
 };
@@ -146,8 +177,25 @@ __device__ __forceinline__ void fold_init(FoldCtx<D, G>& c, WaveAcc<D>& a, const
   c.kbase = k + static_cast<size_t>(r.kv0) * c.rowstride + static_cast<size_t>(kvh) * D;
   c.vbase = v + static_cast<size_t>(r.kv0) * c.rowstride + static_cast<size_t>(kvh) * D;
   c.slot = slot;
-  c.vaddr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(slot)) +
-            16 * (8 * q4 + 2 * (c16 >> 2) + ((c16 & 3) >> 1)) + 8 * (c16 & 1);
+  const uint32_t slot_addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(slot));
+  c.vaddr = slot_addr + 16 * (8 * q4 + 2 * (c16 >> 2) + ((c16 & 3) >> 1)) + 8 * (c16 & 1);
+  if constexpr (D == 128) {
+    // load instruction J: lane -> row 4J + lane/16, global chunk (lane % 16) ^ vswz(row), where
+    // vswz(row) = 2 (lane/16) + 8 ((J >> 1) & 1)
+    c.v_col0 = 8 * ((lane & 15) ^ (2 * (lane >> 4)));
+    c.v_col1 = c.v_col0 ^ 64;
+    // transposing reads: lane (L = lane % 16, kq = lane / 16) addresses row 8 kq + L/4 (+4 for
+    // the second 4-key half), columns 16 n + 4 (L % 4) .. + 3
+    const int L = lane & 15;
+    const int sw = 2 * ((L >> 2) + 4 * (q4 & 1));
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+      c.vt_addr[n] = slot_addr + (8 * q4 + (L >> 2)) * 256 + (((2 * n) ^ sw) + ((L & 3) >> 1)) * 16 +
+                     8 * (L & 1);
+  } else {
+    c.v_col0 = c.v_col1 = 0;
+    c.vt_addr[0] = 0;
+  }
   c.pos = r.pos;
   c.kv_len = r.kv_len;
   c.qscale = g.scale * kLog2e;
@@ -177,11 +225,20 @@ __device__ __forceinline__ void fold_block(const FoldCtx<D, G>& c, WaveAcc<D>& a
     const int krow0 = 32 * (J / (2 * KS)) + 4 * ((J / KS) % 2);
     const int vrow0 = 32 * (J / NT);
     int ko = c.k_lane_off + krow0 * c.rowstride + 32 * (J % KS);
-    int vo = c.v_lane_off + vrow0 * c.rowstride + 16 * (J % NT);
+    int vo;
+    if constexpr (D == 128) {
+      const int vr = 4 * J + (lane >> 4);
+      vo = (tail && vr > last ? last : vr) * c.rowstride + (((J >> 1) & 1) ? c.v_col1 : c.v_col0);
+    } else {
+      vo = c.v_lane_off + vrow0 * c.rowstride + 16 * (J % NT);
+      if (tail) {
+        const int vr = vrow0 + c.v_lrow;
+        vo += ((vr < last ? vr : last) - vr) * c.rowstride;
+      }
+    }
     if (tail) {                   // rows past the cache end repeat its last row (masked)
-      const int kr0 = krow0 + c.k_lrow, vr = vrow0 + c.v_lrow;
+      const int kr0 = krow0 + c.k_lrow;
       ko += ((kr0 < last ? kr0 : last) - kr0) * c.rowstride;
-      vo += ((vr < last ? vr : last) - vr) * c.rowstride;
     }
     kr[J] = *reinterpret_cast<const bf16x8*>(kb + ko);
     __builtin_amdgcn_global_load_lds(vb + vo, (lds_void*)(c.slot + J * 1024), 16, 0, 0);
@@ -252,7 +309,16 @@ __device__ __forceinline__ void fold_block(const FoldCtx<D, G>& c, WaveAcc<D>& a
 #pragma unroll
     for (int hh = 0; hh < NT / 4; ++hh) {
       uint64_t vt[4][2];
-      read_v8(c.vaddr + 512u * (2 * NT * s + 8 * hh), vt);
+      if constexpr (D == 128) {
+        if (s == 0)
+          read_tr_half0(c.vt_addr[4 * hh], c.vt_addr[4 * hh + 1], c.vt_addr[4 * hh + 2],
+                        c.vt_addr[4 * hh + 3], vt);
+        else
+          read_tr_half1(c.vt_addr[4 * hh], c.vt_addr[4 * hh + 1], c.vt_addr[4 * hh + 2],
+                        c.vt_addr[4 * hh + 3], vt);
+      } else {
+        read_v8(c.vaddr + 512u * (2 * NT * s + 8 * hh), vt);
+      }
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const uint64_t both[2] = {vt[n][0], vt[n][1]};
