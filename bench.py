@@ -129,7 +129,8 @@ def run_prefill(args, torch, pkg, synth):
         stage_gbs={"compress": bytes_compress / (stage["compress"] * 1e-3) / 1e9,
                    "scores": bytes_scores / (stage["scores"] * 1e-3) / 1e9,
                    "topk": bytes_topk / (stage["topk"] * 1e-3) / 1e9},
-        wl=wl, kernels_gpu=bufs["kernels"])
+        wl=wl, kernels_gpu=bufs["kernels"],
+        gather=gather_bound(p, bufs["idx"].cpu().numpy(), lens, flops, stage["attention"]))
     if args.no_backward and args.no_window and args.no_score_mode1 and args.no_chunk:
         del q, k, v, bufs
     else:
@@ -194,6 +195,37 @@ def run_chunk(args, torch, pkg, pre):
                 roofline={"kernel": "attn_tile (sparse_attn_prefill, q_pos0 > 0)", "bound": "mfma",
                           "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                           "frac": tflops / PEAK_BF16_TFLOPS, "flops_per_call": flops})
+
+
+def gather_bound(p, idx, seq_lens, flops, ms_attention):
+    """The prefill attention's gather: K/V bytes of every (token, KV head)'s selected blocks
+    (idx: host array [rows, Hkv, topk] of one packed prefill) against the bytes the tile kernel
+    stages (each 16-token tile loads the union of its tokens' selected blocks once), the reuse
+    factor and the staging rate achieved."""
+    block_bytes = 2 * p.block_size * p.head_dim * 2                 # K and V, bf16
+    selected = int((idx >= 0).sum()) * block_bytes
+    staged_blocks = 0
+    start = 0
+    for L in seq_lens:
+        sel = idx[start:start + L]
+        start += L
+        pad = (-L) % 16
+        if pad:
+            sel = np.concatenate([sel, np.full((pad,) + sel.shape[1:], -1, sel.dtype)])
+        t = np.sort(sel.reshape(-1, 16, sel.shape[1], sel.shape[2]).transpose(0, 2, 1, 3)
+                    .reshape(-1, 16 * sel.shape[2]), axis=1)
+        new = np.ones(t.shape, bool)
+        new[:, 1:] = t[:, 1:] != t[:, :-1]
+        staged_blocks += int((new & (t >= 0)).sum())
+    staged = staged_blocks * block_bytes
+    rate = staged / (ms_attention * 1e-3)
+    return {"selected_bytes": selected, "staged_bytes": staged,
+            "reuse_tokens_per_staged_block": selected / staged,
+            "flop_per_staged_byte": flops / staged,
+            "staging_rate_gbs": rate / 1e9,
+            "staging_bytes_per_clk_per_cu": rate / 256 / 2.4e9,
+            "note": "16-token tiles; each tile stages the union of its tokens' selected blocks "
+                    "(K and V) from L2 into LDS once"}
 
 
 def run_score_mode1(args, torch, pkg, pre):
@@ -667,6 +699,7 @@ def main():
                      "launches_per_call": pre["launches"],
                      "avg_launch_us": st["attention"] * 1e3 / pre["launches"]},
     }
+    line["roofline"]["gather"] = pre["gather"]
     tr = measured_traffic(pre["workload"])
     if tr is not None:
         line["roofline"]["traffic"] = tr["fetch_bytes_per_call"] + tr["write_bytes_per_call"]
