@@ -620,7 +620,8 @@ struct SelLds {
 // later pass splits the chosen bin 256 ways.  It stops when every key of the chosen bin is
 // wanted, or the bin holds a single key value (taken in block order), or the bin holds at most
 // 64 keys: then one wave ranks those keys exactly (key descending, block ascending) and marks
-// the wanted ones.  `keys` holds one key per block in LDS for the ordered output.
+// the wanted ones.  `keys` holds one key per block in LDS for the ordered output.  The indices
+// are written with plain stores: only the next launch reads them.
 __device__ __forceinline__ void select_blocks(const Geom& g, int own, const float* srow,
                                               int32_t* out_idx, uint32_t* keys, SelLds& sm,
                                               int tid) {
@@ -631,7 +632,7 @@ __device__ __forceinline__ void select_blocks(const Geom& g, int own, const floa
   const int w = tid >> 6;
   const int nb = own + 1;
   if (nb <= g.topk) {
-    for (int e = tid; e < g.topk; e += T) agent_store(out_idx + e, e < nb ? e : -1);
+    for (int e = tid; e < g.topk; e += T) out_idx[e] = e < nb ? e : -1;
     return;
   }
   const int local_lo = max(0, own - g.n_local + 1);
@@ -789,7 +790,7 @@ __device__ __forceinline__ void select_blocks(const Geom& g, int own, const floa
       take = eq_seen < want;
       ++eq_seen;
     }
-    if (take && p < g.topk) agent_store(out_idx + p, blk);   // p < topk unless keys are NaN
+    if (take && p < g.topk) out_idx[p] = blk;           // p < topk unless keys are NaN
     p += take ? 1 : 0;
   }
 }
