@@ -224,6 +224,17 @@ def test_decode_split_invariance(splits):
         assert np.abs(a["lse"] - b["lse"]).max() <= 1e-4
 
 
+@pytest.mark.parametrize("Hq,d", [(32, 128), (16, 128), (32, 64), (16, 64)])
+def test_decode_step_geometries(Hq, d):
+    """The decode step's kernels for each (head_dim, group) pair (G = Hq / 2), checked against
+    the oracle; ragged cache lengths, two steps."""
+    p = replace(synth.config_params("decode128k"), num_q_heads=Hq, head_dim=d)
+    wl = synth.make_decode(f"dec-geo-{Hq}-{d}", p, batch=3, max_len=9000, steps=2, seed=51,
+                           kv_len0=[8990, 5000, 700])
+    log(f"case decode step Hq={Hq} d={d}")
+    run_decode(wl, 2, label=f"geo {Hq}/{d}")
+
+
 def test_decode_f32_tiny_shape():
     p = synth.config_params("tiny")
     wl = synth.make_decode("dec-f32", p, batch=2, max_len=512, steps=3, seed=43,
