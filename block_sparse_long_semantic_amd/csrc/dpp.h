@@ -24,6 +24,22 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
       __builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, false));
 }
 
+constexpr int kDppRowRor1 = 0x121;       // lane i of a 16-lane row takes lane (i - 1) mod 16
+
+// Sums of lanes l and l ^ 16 (rows 0+1 and 2+3), and of lanes l and l ^ 32 (the two halves), by
+// the gfx950 row swaps: swapping a value with itself and adding the two results pairs every lane
+// with its partner; both partners get the same sum (the operands in the same order).
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum over aligned groups of N = 4, 8 or 16 lanes; every lane of a group gets the same value
 // (the same additions in a commuted order).
 template <int N>

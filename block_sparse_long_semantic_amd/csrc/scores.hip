@@ -400,8 +400,9 @@ scores_softmax_simple(Geom g, SeqTable t, const T* __restrict__ q, const T* __re
 // accumulator holds 4 heads of one row against one kernel.  Pass 1 keeps, per column, a running
 // max (moved lazily, by ballot) and sum of exp2; the 16 kernel lanes are then merged, giving
 // each head's lse.  Pass 2 recomputes the products, turns them into probabilities, sums the
-// group's heads (4 in the lane, the rest by shuffles) and max-pools kernels onto blocks (a block
-// is the 4 kernels of a lane quad plus the one before, from the neighbouring lane or the previous
+// group's heads (4 in the lane, the rest across the 16-lane rows by the gfx950 row swaps) and
+// max-pools kernels onto blocks (a block is the 4 kernels of a lane quad, by DPP quad moves,
+// plus the one before, from the neighbouring lane by a DPP row rotation or from the previous
 // tile).  SPLIT (few rows, e.g. decoding): every wave holds the same columns and takes a
 // quarter of the kernel tiles; the waves' partial maxima and sums are merged through LDS.
 template <int D, int G, bool SPLIT>
@@ -554,8 +555,6 @@ scores_softmax_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
   float carry[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) carry[ct] = -INFINITY;
-  const int src_prev = (lane & 48) | ((c16 + 15) & 15);          // lane c16 - 1 of the group
-  const int src_last = (lane & 48) | 15;
   bf16x8 kb[KS];
   load_b(t_first, kb);
   for (int tt = t_first; tt < t_end; ++tt) {
@@ -573,15 +572,16 @@ scores_softmax_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         sum += vis ? __builtin_amdgcn_exp2f(acc[i] * qscale - lse2[ct][i]) : 0.f;
-      sum += __shfl_xor(sum, 16);                                 // heads of 8 (G = 8: a row)
-      if constexpr (G == 16) sum += __shfl_xor(sum, 32);          // all 16 heads
+      sum = xor16_sum(sum);                                       // heads of 8 (G = 8: a row)
+      if constexpr (G == 16) sum = xor32_sum(sum);                // all 16 heads
       const float u = vis ? sum : -INFINITY;
-      float qm = fmaxf(u, __shfl_xor(u, 1));
-      qm = fmaxf(qm, __shfl_xor(qm, 2));
-      const float prev = __shfl(u, src_prev);
-      const float last = __shfl(u, src_last);
+      float qm = fmaxf(u, dpp_f32<kDppXor1>(u));
+      qm = fmaxf(qm, dpp_f32<kDppXor2>(qm));
+      // lane c16 takes kernel c16 - 1 of the tile; lane 0 gets kernel 15 of this tile, which is
+      // its previous kernel in the next tile (carried)
+      const float prev = dpp_f32<kDppRowRor1>(u);
       const float best = fmaxf(qm, c16 == 0 ? carry[ct] : prev);
-      carry[ct] = last;
+      carry[ct] = prev;
       const int blk = 4 * tt + c16 / 4;
       const bool writer = (c16 & 3) == 0 && (G == 16 ? q4 == 0 : (q4 & 1) == 0);
       if (writer && tt >= t_begin && row_ok[ct] && blk <= pos_l[ct] / 64) {
