@@ -374,7 +374,7 @@ size_t infllm2_decode_workspace_size(const infllm2_params* params, int32_t total
   Geom g;
   if (check_params(params, &g) != INFLLM2_OK || total_q_rows < 0 || num_splits < 0) return 0;
   // enough for infllm2_sparse_attn_decode and for the fused form of infllm2_decode_step
-  const int fused = num_splits > 0 ? num_splits : infllm2::decode_fused_splits(g);
+  const int fused = num_splits > 0 ? num_splits : infllm2::decode_step_splits(g);
   const int splits = std::max(decode_splits(g, params->dtype, total_q_rows, num_splits), fused);
   return infllm2::decode_workspace(g, total_q_rows, splits);
 }
@@ -486,7 +486,7 @@ infllm2_status infllm2_decode_step(const infllm2_params* params, const infllm2_s
   infllm2_status st = check_params(params, &g);
   if (st != INFLLM2_OK) return st;
   if ((st = build_table(seqs, g, true, &t)) != INFLLM2_OK) return st;
-  if (!infllm2::decode_fused_supported(g, params->dtype, t)) {
+  if (!infllm2::decode_step_supported(g, params->dtype, t)) {
     st = infllm2_compress_kernels(params, seqs, k_cache, prev_kv_len, kernels, stream);
     if (st != INFLLM2_OK) return st;
     st = infllm2_block_scores(params, seqs, q, kernels, scores, nb_stride, stream);
@@ -514,7 +514,7 @@ infllm2_status infllm2_decode_step(const infllm2_params* params, const infllm2_s
   SeqTable tr = t;
   rows_prefix(&tr);
   const int rows = tr.work_prefix[tr.n];
-  const int splits = num_splits > 0 ? num_splits : infllm2::decode_fused_splits(g);
+  const int splits = num_splits > 0 ? num_splits : infllm2::decode_step_splits(g);
   const size_t need = infllm2::decode_workspace(g, rows, splits);
   if (workspace == nullptr) return fail(INFLLM2_ERR_NULL, "workspace is NULL");
   if (!aligned16(workspace)) return fail(INFLLM2_ERR_ALIGN, "workspace must be 16-byte aligned");
@@ -522,7 +522,7 @@ infllm2_status infllm2_decode_step(const infllm2_params* params, const infllm2_s
     return fail(INFLLM2_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
   st = infllm2_compress_kernels(params, seqs, k_cache, prev_kv_len, kernels, stream);
   if (st != INFLLM2_OK) return st;
-  return hip_status(infllm2::launch_decode_fused(g, tr, q, kernels, k_cache, v_cache, scores,
+  return hip_status(infllm2::launch_decode_step(g, tr, q, kernels, k_cache, v_cache, scores,
                                                  nb_stride, block_idx, splits, workspace, out,
                                                  lse, static_cast<hipStream_t>(stream)),
                     "decode_step launch");

@@ -843,9 +843,9 @@ size_t decode_workspace(const Geom& g, int rows, int nsplit) {
          static_cast<size_t>(pairs) * nsplit * g.G * (g.d + 2) * sizeof(float);
 }
 
-int decode_fused_splits(const Geom& g) { return (g.topk + kStepWaves - 1) / kStepWaves; }
+int decode_step_splits(const Geom& g) { return (g.topk + kStepWaves - 1) / kStepWaves; }
 
-bool decode_fused_supported(const Geom& g, int dtype, const SeqTable& t) {
+bool decode_step_supported(const Geom& g, int dtype, const SeqTable& t) {
   if (!attn_decode_supported(g, dtype) || g.w != 32 || g.s != 16 || g.score_mode != 0) return false;
   long long rows = 0;
   for (int b = 0; b < t.n; ++b) rows += t.q_len[b];
@@ -892,7 +892,7 @@ hipError_t launch_attn_decode(const Geom& g, const SeqTable& t, const void* q, c
 }
 
 // work_prefix of `t` counts query rows; kernels must already hold every complete kernel.
-hipError_t launch_decode_fused(const Geom& g, const SeqTable& t, const void* q,
+hipError_t launch_decode_step(const Geom& g, const SeqTable& t, const void* q,
                                const void* kernels, const void* k, const void* v, float* scores,
                                int nb_stride, int32_t* idx, int nsplit, void* workspace,
                                void* out, float* lse, hipStream_t stream) {

@@ -127,9 +127,9 @@ hipError_t launch_attn_decode(const Geom& g, const SeqTable& t, const void* q, c
                               void* out, float* lse, hipStream_t stream);
 // One decoding step after the kernels are compressed: block scores and top-k in one launch
 // (decode_select), then the split-KV attention; work_prefix of `t` counts query rows.
-bool decode_fused_supported(const Geom& g, int dtype, const SeqTable& t);
-int decode_fused_splits(const Geom& g);
-hipError_t launch_decode_fused(const Geom& g, const SeqTable& t, const void* q,
+bool decode_step_supported(const Geom& g, int dtype, const SeqTable& t);
+int decode_step_splits(const Geom& g);
+hipError_t launch_decode_step(const Geom& g, const SeqTable& t, const void* q,
                                const void* kernels, const void* k, const void* v, float* scores,
                                int nb_stride, int32_t* idx, int nsplit, void* workspace,
                                void* out, float* lse, hipStream_t stream);
