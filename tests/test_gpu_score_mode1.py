@@ -107,3 +107,42 @@ def test_mode1_full_size_sampled():
                            set(range(L - 3, L)) |
                            {int(r) for nd in wl.needles[:4] for r in nd.query_positions[:2]}))
     check_mode1(wl, res, 0, rows=rows, label="mode1 full")
+
+
+def test_mode1_decode_steps():
+    """Two decode steps (infllm2_decode_step) in score mode 1: the step chains the separate
+    calls for this mode; scores within the float32 bound, the top-k equal to the oracle's
+    selection on the GPU's scores, attention on the GPU's indices."""
+    p = replace(synth.config_params("decode128k"), score_mode=1)
+    B, Lmax = 3, 6000
+    wl = synth.make_decode("m1-dec", p, batch=B, max_len=Lmax, steps=2, seed=104,
+                           kv_len0=[5990, 3000, 800])
+    Ck = orc.num_kernels(Lmax, p.kernel_size, p.kernel_stride)
+    k = dev(wl.k.reshape(B * Lmax, p.num_kv_heads, p.head_dim), p.dtype)
+    v = dev(wl.v.reshape(B * Lmax, p.num_kv_heads, p.head_dim), p.dtype)
+    kern = torch.zeros((B * Ck, p.num_kv_heads, p.head_dim), dtype=k.dtype, device="cuda")
+    bufs = lib.pipeline.decode_buffers(p, B, (Lmax + 63) // 64, 0, "cuda")
+    for st in range(2):
+        kv = wl.kv_len0.astype(np.int64) + st + 1
+        seqs = lib.Seqs.decode(kv, Lmax, Ck)
+        log(f"case mode1 decode step {st}")
+        lib.decode_step(p, seqs, dev(wl.q_steps[st], p.dtype), k, v, kern, None, bufs)
+        torch.cuda.synchronize()
+        scores, idx = host(bufs["scores"]), host(bufs["idx"])
+        out, lse = host(bufs["out"]), host(bufs["lse"])
+        for b in range(B):
+            L = int(kv[b])
+            ks, vs = wl.k[b, :L], wl.v[b, :L]
+            qr = wl.q_steps[st][b:b + 1]
+            kern_ref = orc.compress_kernels(ks, p.kernel_size, p.kernel_stride, p.dtype)
+            ref = orc.run_sequence(qr, ks, vs, p, q_pos0=L - 1, kernels=kern_ref,
+                                   with_attention=False)
+            NB = ref.scores.shape[2]
+            gs = scores[b:b + 1, :, :NB]
+            rel = cmp.softmax_score_rel_bound(qr, kern_ref, ref.positions, p)
+            cmp.check_softmax_scores(gs, ref.scores, rel, ref.positions, p)
+            gidx = idx[b:b + 1]
+            assert np.array_equal(gidx, orc.select_all(gs.astype(np.float64), ref.positions, p))
+            cmp.check_indices(gidx, ref.idx, ref.scores, ref.positions, p)
+            O, Ls = orc.sparse_attention(qr.astype(np.float64), ref.positions, ks, vs, gidx, p)
+            cmp.check_attention(out[b:b + 1], lse[b:b + 1], O, Ls, p.dtype)
