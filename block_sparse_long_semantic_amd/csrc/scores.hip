@@ -87,10 +87,11 @@ scores_simple(Geom g, SeqTable t, const T* __restrict__ q, const T* __restrict__
 // a quarter of the kernel tiles the rows can see (a kernel tile is 16 kernels = 4 blocks), so
 // each kernel fragment it loads feeds 8 MFMAs.  Block scores are max-pooled in registers: a lane
 // holds 4 consecutive kernels of one row, and the kernel before them (shared with the previous
-// block) comes from the lane 16 below, or from the previous tile.  Scores are collected per wave
-// in LDS for 16 kernel tiles (64 blocks) and written out as whole row segments.
+// block) comes from the lane 16 below, or from the previous tile.  Each kernel tile's fragment
+// is loaded while the previous tile's MFMAs run.  Scores are collected per wave in LDS for 16
+// kernel tiles (64 blocks) and written out four blocks per lane, four rows per instruction.
 constexpr int kChunkTiles = 16;                  // kernel tiles per staged chunk (64 blocks)
-constexpr int kStageRow = 4 * kChunkTiles + 1;   // floats per staged row (+1: bank offset)
+constexpr int kStageRow = 4 * kChunkTiles + 4;   // floats per staged row (16-byte rows)
 
 template <int D>
 __global__ void __launch_bounds__(kThreads)
@@ -123,31 +124,47 @@ scores_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
     const int r = r0 + 16 * wave + c16;
     const size_t row = static_cast<size_t>(t.q_start[b]) + (r < q_len ? r : q_len - 1);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      float acc[8];
+    for (int ks2 = 0; ks2 < KS; ks2 += 2) {
+      // every head of the group (at most 16) over two dimension slices is loaded before the
+      // first addition, so a slice pair waits for one round trip; indices past the group repeat
+      // its last head and are not added (the sum runs over the heads in order)
+      const uint16_t* qrow = q + (row * g.Hq + kvh * g.G) * D + 32 * ks2 + 8 * q4;
+      uint4 v[2][16];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-      for (int h = 0; h < g.G; ++h) {
-        const uint4 v = *reinterpret_cast<const uint4*>(
-            q + (row * g.Hq + kvh * g.G + h) * D + 32 * ks + 8 * q4);
-        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int h = 0; h < 16; ++h)
+          v[j][h] = *reinterpret_cast<const uint4*>(qrow + 32 * j +
+                                                    static_cast<size_t>(min(h, g.G - 1)) * D);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int ks = ks2 + j;
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+        for (int h = 0; h < 16; ++h) {
+          const uint32_t w4[4] = {v[j][h].x, v[j][h].y, v[j][h].z, v[j][h].w};
+          if (h < g.G) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[2 * e] += __uint_as_float(w4[e] << 16);
+              acc[2 * e + 1] += __uint_as_float(w4[e] & 0xFFFF0000u);
+            }
+          }
+        }
+        uint32_t hi4[4], lo4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += __uint_as_float(w4[e] << 16);
-          acc[2 * e + 1] += __uint_as_float(w4[e] & 0xFFFF0000u);
+          const uint16_t h0 = f32_to_bf16(acc[2 * e]), h1 = f32_to_bf16(acc[2 * e + 1]);
+          const uint16_t l0 = f32_to_bf16(acc[2 * e] - bf16_to_f32(h0));
+          const uint16_t l1 = f32_to_bf16(acc[2 * e + 1] - bf16_to_f32(h1));
+          hi4[e] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+          lo4[e] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
         }
+        qop[((wave * KS + ks) * 2 + 0) * 64 + lane] = make_uint4(hi4[0], hi4[1], hi4[2], hi4[3]);
+        qop[((wave * KS + ks) * 2 + 1) * 64 + lane] = make_uint4(lo4[0], lo4[1], lo4[2], lo4[3]);
       }
-      uint32_t hi4[4], lo4[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint16_t h0 = f32_to_bf16(acc[2 * e]), h1 = f32_to_bf16(acc[2 * e + 1]);
-        const uint16_t l0 = f32_to_bf16(acc[2 * e] - bf16_to_f32(h0));
-        const uint16_t l1 = f32_to_bf16(acc[2 * e + 1] - bf16_to_f32(h1));
-        hi4[e] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-        lo4[e] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
-      }
-      qop[((wave * KS + ks) * 2 + 0) * 64 + lane] = make_uint4(hi4[0], hi4[1], hi4[2], hi4[3]);
-      qop[((wave * KS + ks) * 2 + 1) * 64 + lane] = make_uint4(lo4[0], lo4[1], lo4[2], lo4[3]);
     }
   }
   __syncthreads();
@@ -172,22 +189,31 @@ scores_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
   const int C = num_kernels(t.kv_len[b], g.w, g.s);
   const size_t kbase = static_cast<size_t>(t.kc_start[b]) * g.Hkv * D + static_cast<size_t>(kvh) * D;
   const unsigned src_lane = static_cast<unsigned>((lane + 48) & 63);   // lane - 16 (mod 64)
+  // whole float4 stores need 16-byte aligned output rows
+  const bool vec_out = (nb_stride & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
   float carry[RG];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) carry[rg] = -INFINITY;
+  // A operands of kernel tile tt (16 kernels x D dims; kernel index clamped into the sequence)
+  auto load_tile = [&](int tt, bf16x8 (&a)[KS]) {
+    const int ck_c = min(16 * tt + c16, C - 1 > 0 ? C - 1 : 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      a[ks] = C > 0 ? *reinterpret_cast<const bf16x8*>(kern + kbase +
+                                                      static_cast<size_t>(ck_c) * g.Hkv * D +
+                                                      32 * ks + 8 * q4)
+                    : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+  };
+  bf16x8 a_next[KS];                     // the next tile's operands, loaded one tile ahead
+  load_tile(t_begin > 0 ? t_begin - 1 : t_begin, a_next);
   for (int c0 = t_begin; c0 < t_end; c0 += kChunkTiles) {
     const int c1 = min(t_end, c0 + kChunkTiles);
     // the first chunk starts one tile early (not staged) for the halo kernel of its first block
     for (int tt = (c0 == t_begin && t_begin > 0) ? t_begin - 1 : c0; tt < c1; ++tt) {
-      const int ck = 16 * tt + c16;                               // A row: kernel
-      const int ck_c = min(ck, C - 1 > 0 ? C - 1 : 0);
       bf16x8 a[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        a[ks] = C > 0 ? *reinterpret_cast<const bf16x8*>(kern + kbase +
-                                                        static_cast<size_t>(ck_c) * g.Hkv * D +
-                                                        32 * ks + 8 * q4)
-                      : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+      for (int ks = 0; ks < KS; ++ks) a[ks] = a_next[ks];
+      if (tt + 1 < t_end) load_tile(tt + 1, a_next);
       f32x4 acc[RG];
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) acc[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -215,15 +241,27 @@ scores_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
       }
     }
     asm volatile("" ::: "memory");
-    // write the chunk: one row per instruction, blocks 4*c0 .. 4*c1 - 1 up to the row's own block
-    const int blk = 4 * c0 + lane;
-    for (int rr = 0; rr < 64; ++rr) {
+    // write the chunk: four rows per instruction, four consecutive blocks per lane (blocks
+    // 4*c0 .. 4*c1 - 1, up to the row's own block)
+    const int j4 = 4 * c16;
+    const int blk = 4 * c0 + j4;
+    for (int rr0 = 0; rr0 < 64 && r0 + rr0 < q_len; rr0 += 4) {
+      const int rr = rr0 + q4;
       const int r = r0 + rr;
-      if (r >= q_len) break;
       const int own = (t.q_pos0[b] + r) / 64;
-      if (lane < 4 * (c1 - c0) && blk <= own)
-        scores[(static_cast<size_t>(t.q_start[b]) + r) * g.Hkv * nb_stride +
-               static_cast<size_t>(kvh) * nb_stride + blk] = stage[rr * kStageRow + lane];
+      if (r < q_len && j4 < 4 * (c1 - c0) && blk <= own) {
+        const float4 s4 = *reinterpret_cast<const float4*>(stage + rr * kStageRow + j4);
+        float* dst = scores + (static_cast<size_t>(t.q_start[b]) + r) * g.Hkv * nb_stride +
+                     static_cast<size_t>(kvh) * nb_stride + blk;
+        if (vec_out && blk + 3 <= own) {
+          *reinterpret_cast<float4*>(dst) = s4;
+        } else {
+          dst[0] = s4.x;
+          if (blk + 1 <= own) dst[1] = s4.y;
+          if (blk + 2 <= own) dst[2] = s4.z;
+          if (blk + 3 <= own) dst[3] = s4.w;
+        }
+      }
     }
     asm volatile("" ::: "memory");
   }
