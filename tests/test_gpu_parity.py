@@ -120,6 +120,28 @@ def test_chunked_prefill_against_cache():
     check_sequence(wl, res, 0, label="chunk")
 
 
+def test_prefill_tied_scores():
+    """Every key equal, so every candidate block of a row scores the same (a single key value in
+    the selection): besides the forced blocks the lowest block indices win."""
+    p = synth.config_params("prefill32k")
+    wl = synth.make_prefill("ties", p, [9000], seed=47)
+    wl.k[:] = wl.k[:1]
+    log("case prefill ties")
+    res = run_prefill_stages(wl)
+    rows = np.array(sorted(set(range(0, 9000, 97)) | set(range(8930, 9000))))
+    check_sequence(wl, res, 0, rows=rows, label="ties")
+    n_plain = p.topk - p.num_init_blocks - p.num_local_blocks
+    for r in rows:
+        own = int(r) // p.block_size
+        if own + 1 <= p.topk:
+            continue
+        for h in range(p.num_kv_heads):
+            chosen = res["idx"][r, h]
+            assert np.array_equal(chosen[:p.num_init_blocks + n_plain],
+                                  np.arange(p.num_init_blocks + n_plain))
+            assert chosen[-2] == own - 1 and chosen[-1] == own
+
+
 @pytest.mark.parametrize("name,lens", [("prefill32k", [20000, 13001, 77]),
                                        ("varlen", [16421, 9000, 30])])
 def test_mfma_scores_ragged_tiles(name, lens):
