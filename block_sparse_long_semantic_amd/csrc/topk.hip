@@ -7,7 +7,7 @@
 //     range: the first pass bins (key - min) >> s into 256 LDS counters (s the smallest shift
 //     that fits max - min), later passes split the chosen bin 256 ways; it stops when the
 //     whole bin is wanted, or the bin holds one key value, or at most 64 keys, which are then
-//     gathered in block order and ranked exactly;
+//     gathered one per lane and finished by a bitwise search over their offsets in the bin;
 //   * keys above the threshold are taken, keys equal to it in ascending block order (ties ->
 //     lower index) as far as wanted; the selection is written ascending with ballot prefix
 //     counts.
@@ -55,16 +55,14 @@ topk_kernel(Geom g, SeqTable t, const float* __restrict__ scores, int nb_stride,
 #pragma unroll
   for (int e = 0; e < NPL; ++e) sc[e] = srow[min(64 * e + lane, nb - 1)];
   uint32_t key[NPL];
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  uint32_t kmin1 = 0xFFFFFFFFu, kmax = 0u;                 // kmin1: smallest key - 1
 #pragma unroll
   for (int e = 0; e < NPL; ++e) {
     const int blk = 64 * e + lane;
     const bool forced = blk < g.n_init || blk >= local_lo;
     key[e] = (blk < nb && !forced) ? order_key(sc[e]) : 0u;     // 0: not a candidate
-    if (key[e] != 0u) {
-      kmin = min(kmin, key[e]);
-      kmax = max(kmax, key[e]);
-    }
+    kmin1 = min(kmin1, key[e] - 1u);                             // 0 wraps past every key
+    kmax = max(kmax, key[e]);
   }
 
   // Threshold: keys above thr are taken; of the keys equal to it, the first n_eq in block order
@@ -72,13 +70,14 @@ topk_kernel(Geom g, SeqTable t, const float* __restrict__ scores, int nb_stride,
   uint32_t thr = 0xFFFFFFFFu;
   int n_eq = 0;
   if (want > 0) {
-    kmin = wave_min_u32(kmin);
+    const uint32_t kmin = wave_min_u32(kmin1) + 1u;
     kmax = wave_max_u32(kmax);
 #pragma unroll
     for (int i = 0; i < 4; ++i) sm.hist[4 * lane + i] = 0;
-    uint32_t blo = kmin;                                 // the current bin is [blo, bin_hi)
-    uint64_t bin_hi = static_cast<uint64_t>(kmax) + 1;
-    const uint32_t span = kmax - kmin;
+    // the current bin is [blo, blo + span]; since blo >= kmin > 0, the single unsigned test
+    // (k - blo) <= span also rejects the non-candidates (k = 0 wraps past it)
+    uint32_t blo = kmin;
+    uint32_t span = kmax - kmin;
     int s = span == 0u ? 0 : max(0, 32 - __clz(static_cast<int>(span)) - 8);
     const uint64_t above_lane = ~((2ull << lane) - 1);   // lanes over this one (none for 63)
     int w = want;                                        // still wanted within the bin
@@ -86,8 +85,8 @@ topk_kernel(Geom g, SeqTable t, const float* __restrict__ scores, int nb_stride,
       __syncthreads();
 #pragma unroll
       for (int e = 0; e < NPL; ++e) {
-        const uint32_t k = key[e];
-        if (k != 0u && k >= blo && k < bin_hi) atomicAdd(&sm.hist[(k - blo) >> s], 1);
+        const uint32_t r = key[e] - blo;
+        if (r <= span) atomicAdd(&sm.hist[r >> s], 1);
       }
       __syncthreads();
       // lane L holds bins 4L .. 4L+3 (zeroed again for the next pass); the count of the bins
@@ -115,7 +114,7 @@ topk_kernel(Geom g, SeqTable t, const float* __restrict__ scores, int nb_stride,
       d_above = __builtin_amdgcn_readlane(d_above, src);
       d_count = __builtin_amdgcn_readlane(d_count, src);
       blo += static_cast<uint32_t>(digit) << s;
-      bin_hi = static_cast<uint64_t>(blo) + (uint64_t{1} << s);
+      span = (1u << s) - 1u;                             // s <= 24
       w -= d_above;
       if (d_count == w) {                                // every key of the bin is wanted
         thr = blo;
@@ -128,31 +127,33 @@ topk_kernel(Geom g, SeqTable t, const float* __restrict__ scores, int nb_stride,
         break;
       }
       if (d_count <= 64) {
-        // gather the bin's keys in block order, rank them: thr is the key with fewer than w
-        // keys above it and at least w at or above it
+        // gather the bin's keys (one per lane, as offsets from blo) and finish with a bitwise
+        // search over the s offset bits: t is the largest offset with at least w keys at or
+        // above it (lanes past the bin hold 0, never counted: every candidate offset is > 0)
         int base = 0;
 #pragma unroll
         for (int e = 0; e < NPL; ++e) {
-          const uint32_t k = key[e];
-          const bool in = k != 0u && k >= blo && k < bin_hi;
+          const uint32_t r = key[e] - blo;
+          const bool in = r <= span;
           const unsigned long long m = __ballot(in);
-          if (in) sm.bin_key[base + prefix_count(m)] = k;
+          if (in) sm.bin_key[base + prefix_count(m)] = r;
           base += __popcll(m);
         }
         __syncthreads();
-        const uint32_t ki = lane < d_count ? sm.bin_key[lane] : 0u;
-        int gt = 0, ge = 0;
-        for (int jj = 0; jj < d_count; ++jj) {
-          const uint32_t kj = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ki), jj));
-          gt += kj > ki ? 1 : 0;
-          ge += kj >= ki ? 1 : 0;
+        const uint32_t ri = lane < d_count ? sm.bin_key[lane] : 0u;
+        uint32_t t = 0u;
+        int n_ge = d_count;
+        for (int bit = s - 1; bit >= 0; --bit) {
+          const uint32_t cand = t | (1u << bit);
+          const int c = __popcll(__ballot(ri >= cand));
+          if (c >= w) {
+            t = cand;
+            n_ge = c;
+            if (c == w) break;
+          }
         }
-        const bool is_thr = lane < d_count && gt < w && w <= ge;
-        const int t_src = __ffsll(static_cast<unsigned long long>(__ballot(is_thr))) - 1;
-        thr = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ki), t_src));
-        const int t_gt = __builtin_amdgcn_readlane(gt, t_src);
-        const int t_ge = __builtin_amdgcn_readlane(ge, t_src);
-        n_eq = (t_ge == w) ? -1 : w - t_gt;
+        thr = blo + t;
+        n_eq = n_ge == w ? -1 : w - __popcll(__ballot(lane < d_count && ri > t));
         break;
       }
       s = max(0, s - 8);
