@@ -373,9 +373,9 @@ size_t infllm2_decode_workspace_size(const infllm2_params* params, int32_t total
                                      int32_t num_splits) {
   Geom g;
   if (check_params(params, &g) != INFLLM2_OK || total_q_rows < 0 || num_splits < 0) return 0;
-  // enough for infllm2_sparse_attn_decode and for the fused form of infllm2_decode_step
-  const int fused = num_splits > 0 ? num_splits : infllm2::decode_step_splits(g);
-  const int splits = std::max(decode_splits(g, params->dtype, total_q_rows, num_splits), fused);
+  // enough for infllm2_sparse_attn_decode and for the two-launch form of infllm2_decode_step
+  const int step = num_splits > 0 ? num_splits : infllm2::decode_step_splits(g);
+  const int splits = std::max(decode_splits(g, params->dtype, total_q_rows, num_splits), step);
   return infllm2::decode_workspace(g, total_q_rows, splits);
 }
 

@@ -521,8 +521,8 @@ constexpr int kSplitWaves = 4;
 constexpr int kStepWaves = 8;
 
 // ------------------------------------------------------------------------- scores + selection
-constexpr int kFusedWaves = 8;
-constexpr int kFusedThreads = 64 * kFusedWaves;
+constexpr int kSelectWaves = 8;
+constexpr int kSelectThreads = 64 * kSelectWaves;
 constexpr int kChunkBlocks = 128;               // blocks per score work item
 constexpr int kMaxKeysPerThread = 8;            // selection over at most 8 * 512 blocks
 
@@ -541,7 +541,7 @@ __device__ __forceinline__ void score_chunk(const Geom& g, const SeqTable& t, co
   constexpr int RPI = 64 / LPR;           // rows per wave instruction
   constexpr int NROW = 4 * kChunkBlocks + 1;
   constexpr int NIT = (NROW + RPI - 1) / RPI;
-  constexpr int NW = kFusedWaves;
+  constexpr int NW = kSelectWaves;
   constexpr int PER = (NIT + NW - 1) / NW;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -559,7 +559,7 @@ __device__ __forceinline__ void score_chunk(const Geom& g, const SeqTable& t, co
     kv[i] = ok ? *reinterpret_cast<const uint4*>(kern + kbase + static_cast<size_t>(cc) * g.Hkv * D + col)
                : make_uint4(0u, 0u, 0u, 0u);
   }
-  for (int e = tid; e < D; e += kFusedThreads) {
+  for (int e = tid; e < D; e += kSelectThreads) {
     float qh[G];                                        // all heads' loads in flight at once
 #pragma unroll
     for (int h = 0; h < G; ++h) qh[h] = bf16_to_f32(q[(static_cast<size_t>(r.row) * g.Hq + kvh * G + h) * D + e]);
@@ -601,11 +601,11 @@ __device__ __forceinline__ void score_chunk(const Geom& g, const SeqTable& t, co
   }
 }
 
-// LDS of the fused kernel's selection.
+// LDS of the decode step's selection (decode_select).
 struct SelLds {
   int hist[2][256];
-  int wsum[kFusedWaves][2];
-  uint32_t wmin[kFusedWaves], wmax[kFusedWaves];
+  int wsum[kSelectWaves][2];
+  uint32_t wmin[kSelectWaves], wmax[kSelectWaves];
   uint32_t bin_key[64];
   int bin_blk[64];
   int nbin;
@@ -625,8 +625,8 @@ struct SelLds {
 __device__ __forceinline__ void select_blocks(const Geom& g, int own, const float* srow,
                                               int32_t* out_idx, uint32_t* keys, SelLds& sm,
                                               int tid) {
-  constexpr int T = kFusedThreads;
-  constexpr int NW = kFusedWaves;
+  constexpr int T = kSelectThreads;
+  constexpr int NW = kSelectWaves;
   constexpr uint32_t kTaken = 0xFFFFFFFFu;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -796,15 +796,15 @@ __device__ __forceinline__ void select_blocks(const Geom& g, int own, const floa
 }
 
 template <int D, int G>
-__global__ void __launch_bounds__(kFusedThreads)
+__global__ void __launch_bounds__(kSelectThreads)
 decode_select(Geom g, SeqTable t, const uint16_t* __restrict__ q,
               const uint16_t* __restrict__ kern, float* __restrict__ scores, int nb_stride,
               int32_t* __restrict__ idx, void* __restrict__ workspace) {
-  __shared__ __attribute__((aligned(16))) uint32_t stage[kMaxKeysPerThread * kFusedThreads];
+  __shared__ __attribute__((aligned(16))) uint32_t stage[kMaxKeysPerThread * kSelectThreads];
   __shared__ float qs[D];
   __shared__ SelLds sm;
   __shared__ int s_last;
-  static_assert(kMaxKeysPerThread * kFusedThreads >= 4 * kChunkBlocks + 4, "score staging fits");
+  static_assert(kMaxKeysPerThread * kSelectThreads >= 4 * kChunkBlocks + 4, "score staging fits");
 
   const int tid = threadIdx.x;
   const int chunk = blockIdx.x;
@@ -851,7 +851,7 @@ bool decode_step_supported(const Geom& g, int dtype, const SeqTable& t) {
   for (int b = 0; b < t.n; ++b) rows += t.q_len[b];
   if (rows * g.Hkv > 65535) return false;               // one grid row per (row, KV head)
   for (int b = 0; b < t.n; ++b)
-    if (t.q_len[b] > 0 && (t.q_pos0[b] + t.q_len[b] - 1) / 64 + 1 > kMaxKeysPerThread * kFusedThreads)
+    if (t.q_len[b] > 0 && (t.q_pos0[b] + t.q_len[b] - 1) / 64 + 1 > kMaxKeysPerThread * kSelectThreads)
       return false;
   return true;
 }
@@ -909,7 +909,7 @@ hipError_t launch_decode_step(const Geom& g, const SeqTable& t, const void* q,
   bool launched = false;
 #define INFLLM2_SEL_CASE(DD, GG)                                                                \
   if (!launched && g.d == DD && g.G == GG) {                                                    \
-    hipLaunchKernelGGL((decode_select<DD, GG>), grid, dim3(kFusedThreads), 0, stream, g, t, qq, \
+    hipLaunchKernelGGL((decode_select<DD, GG>), grid, dim3(kSelectThreads), 0, stream, g, t, qq, \
                        kc, scores, nb_stride, idx, workspace);                                  \
     launched = true;                                                                            \
   }

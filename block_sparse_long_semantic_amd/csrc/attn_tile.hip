@@ -2,26 +2,29 @@
 // each token attends only to its most relevant KV blocks; FlashAttention-style online
 // softmax).
 //
-// Design (one workgroup = 4 waves = one tile of T = 16 consecutive query tokens of one
+// Design (one workgroup = 8 waves = one tile of T = 16 consecutive query tokens of one
 // sequence and one KV head):
 //   * Union: the tile's 16 selected-block lists are OR-ed into a per-block 16-bit token mask in
 //     LDS and compacted into an ascending list of (block, mask).  Each union block's K and V
 //     (64 keys x d, bf16) are staged into LDS once for all tokens that chose it.
 //   * Staging: global_load_lds (16 B per lane, straight to LDS, no registers) into a ring of
-//     NSLOT slots; the next block's loads are in flight while the current one is consumed.
-//     Waits are explicit vmcnt counts and raw s_barrier (a fenced __syncthreads would drain
-//     every in-flight load).  Rows are stored row-major with an XOR swizzle of the 16-byte
-//     chunks so that the MFMA operand reads below hit distinct LDS banks.
-//   * Compute: wave w owns tokens 4w..4w+3 (registers: Q operand, O accumulator, running max
-//     and sum).  For every union block it processes only its tokens whose mask bit is set:
+//     NS slots, block u in slot u % NS.  K is stored row-major with the 16-byte chunks of row r
+//     XOR-swizzled by kswz(r), so that an A-operand read spans all banks; V in the unit order
+//     its transposing reads want.  The last wave to finish with a slot (an LDS counter against
+//     the number of waves whose tokens chose the block) refills it with block u + NS and
+//     raises the slot's ready word once the loads have landed; waits poll that word, bounded.
+//   * Compute: wave w owns tokens 2w and 2w + 1 (registers: Q operand, O accumulator, running
+//     max and sum).  For every union block it processes only its tokens whose mask bit is set:
 //       S^T = K Q^T   16 keys x 16 heads per v_mfma_f32_16x16x32_bf16 (A = K from LDS)
-//       online softmax over the 64 keys (exp2, running max/sum per head)
+//       online softmax over the 64 keys (exp2; the running max moves only when a block's max
+//                     exceeds it by more than kLazy, decided for the whole wave)
 //       O  += P V     16 heads x 16 dims per MFMA; B = V read with ds_read_b64_tr_b16, which
 //                     transposes 4x16 bf16 tiles across each 16-lane group, so V needs no
 //                     transposed copy.  The key order inside each 32-key step makes the
 //                     S^T fragment a lane holds exactly its P operand.
-//   * Scheduling: work items are laid out so that each XCD (blockIdx % 8) runs consecutive
-//     tiles of one KV head, which select from the same blocks and share that XCD's L2.
+//   * Scheduling: work items go in rounds of one workgroup per compute unit, laid out so that
+//     each XCD (blockIdx % 8) runs consecutive tiles of one KV head, which select from the
+//     same blocks and share that XCD's L2.
 #include <algorithm>
 
 #include "internal.h"
@@ -46,12 +49,6 @@ constexpr int kMaxUnion = 2048;   // reachable blocks per tile handled by this k
 constexpr float kLazy = 8.f;      // log2 headroom before the running max is moved
 constexpr int kSpinLimit = 1 << 20;  // bounded waits (about 30 ms): a protocol error never hangs
 constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3 for gfx9-family raw buffers
-
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 template <int N>
