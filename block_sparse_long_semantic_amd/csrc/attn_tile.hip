@@ -26,6 +26,7 @@
 //     each XCD (blockIdx % 8) runs consecutive tiles of one KV head, which select from the
 //     same blocks and share that XCD's L2.
 #include <algorithm>
+#include <atomic>
 
 #include "internal.h"
 
@@ -713,17 +714,19 @@ bool attn_tile_supported(const Geom& g, int dtype, const SeqTable& t) {
   return true;
 }
 
+// Compute units of the current device, looked up once per device.  The cache is shared by every
+// calling thread: relaxed atomics (racing first calls store the same value).
 int device_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];                 // static storage: starts at 0
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // work_prefix of `t` must count tiles of 16 query rows per sequence.  Items are launched in
