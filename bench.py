@@ -382,6 +382,39 @@ def copy_calibration(torch, mib: int):
     del src, dst
 
 
+def measured_peaks(torch):
+    """Achievable rates of this GPU, reported beside the datasheet peaks for context: a streaming
+    kernel (out = -in over 1 GiB of bf16: 2 GiB moved per call) and a large bf16 matrix product
+    (8192^3, the vendor GEMM behind torch.mm), each timed with events on the current stream."""
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+    n = (1 << 30) // 2
+    src = torch.randn(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: torch.neg(src, out=dst), 10)
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+    c = torch.empty(m, m, dtype=torch.bfloat16, device="cuda")
+    t_mm = timed(lambda: torch.mm(a, b, out=c), 10)
+    del a, b, c
+    return {"hbm_stream_gbs": 2.0 * (n * 2) / t_copy / 1e9,
+            "bf16_gemm_tflops": 2.0 * m ** 3 / t_mm / 1e12,
+            "note": "out = -in over 1 GiB bf16 (2 GiB moved per call); torch.mm of two "
+                    "8192 x 8192 bf16 matrices; context for the datasheet peaks "
+                    f"({PEAK_HBM_GBS:.0f} GB/s, {PEAK_BF16_TFLOPS:.0f} TFLOP/s), which the "
+                    "roofline fractions use"}
+
+
 def source_digest(paths) -> str:
     h = hashlib.sha256()
     for rel in paths:
@@ -647,6 +680,8 @@ def main():
     ap.add_argument("--no-score-mode1", action="store_true")
     ap.add_argument("--no-chunk", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the streaming-copy and GEMM rate measurements")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a streaming copy of MIB MiB (counter calibration)")
@@ -721,6 +756,11 @@ def main():
     if not args.no_decode:
         line["decode"] = run_decode(args, torch, pkg, synth)
         log(f"decode: {line['decode']['us_per_step']:.1f} us/step")
+    if not args.no_peaks:
+        line["measured_peaks"] = measured_peaks(torch)
+        mp = line["measured_peaks"]
+        log(f"measured peaks: stream {mp['hbm_stream_gbs']:.0f} GB/s, bf16 GEMM "
+            f"{mp['bf16_gemm_tflops']:.0f} TFLOP/s")
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()
         line["cpu_baseline"] = cpu_baseline(pre, args.cpu_budget)
