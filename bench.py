@@ -567,11 +567,23 @@ def cpu_baseline(pre, budget_s: float):
     per_row = t_rows / max(done, 1)
     tok_s = L / (t_comp + per_row * L)
     return {"value": tok_s, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "sample": f"{args_workload_name(pre)}: full kernel compression ({t_comp:.1f} s) + "
                       f"block scores, top-k and attention for {done} of {L} query rows spread evenly "
                       f"over the sequence ({t_rows:.1f} s on {workers} single-threaded "
                       f"processes), float64 numpy; tokens/s = L / (compression + L x mean "
                       f"time per row)"}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def args_workload_name(pre):
