@@ -20,7 +20,6 @@ import csv
 import glob
 import hashlib
 import json
-import math
 import os
 import sys
 import time

@@ -44,10 +44,9 @@ clarity, not speed; large workloads are checked on sampled query rows.
 """
 from __future__ import annotations
 
-import math
 from dataclasses import dataclass
 from fractions import Fraction
-from typing import Dict, Optional, Sequence
+from typing import Optional, Sequence
 
 import numpy as np
 
