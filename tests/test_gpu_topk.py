@@ -1,5 +1,5 @@
 """The top-k selection alone, on synthetic score rows written straight into the scores buffer:
-rows that reach up to 4096 blocks (a 256K-token sequence), rows around the all-blocks limit,
+rows that reach 100 to 4096 blocks (up to a 256K-token sequence), rows around the all-blocks limit,
 and score distributions that stress the selection (heavy ties, a single value, both signs with
 +-0, a wide exponent range, -inf entries).  The indices must equal the oracle's selection
 exactly."""
@@ -36,19 +36,20 @@ def score_rows(kind: str, shape, rng) -> np.ndarray:
 
 
 @pytest.mark.parametrize("kind", ["normal", "ties", "one-value", "signs", "wide", "neg-inf"])
-@pytest.mark.parametrize("kv_len", [131072, 262144])
+@pytest.mark.parametrize("kv_len", [6400, 16384, 65536, 131072, 262144])
 def test_topk_on_given_scores(kind, kv_len):
     p = synth.config_params("prefill128k")
     H = p.num_kv_heads
-    # sequence 0: its last 600 positions (2048 or 4096 reachable blocks); sequence 1: positions
-    # whose reachable block counts run from 93 to 99 across topk = 96
+    # sequence 0: its last 600 positions (100 to 4096 reachable blocks: 1 to 64 keys per lane of
+    # the one-wave selection); sequence 1: positions whose reachable block counts run from 93 to
+    # 99 across topk = 96
     seqs = lib.Seqs(q_start=[0, 600], q_len=[600, 400], q_pos0=[kv_len - 600, 5900],
                     kv_start=[0, kv_len], kv_len=[kv_len, 6300], kc_start=[0, 0])
     pos = np.concatenate([kv_len - 600 + np.arange(600), 5900 + np.arange(400)])
     nb = kv_len // p.block_size
     assert len(pos) * H > 1024                # the one-wave-per-row selection, not the wide one
     kinds = ["normal", "ties", "one-value", "signs", "wide", "neg-inf"]
-    rng = np.random.default_rng(500 + 10 * kinds.index(kind) + kv_len // 131072)
+    rng = np.random.default_rng(500 + 10 * kinds.index(kind) + kv_len // 6400)
     S = score_rows(kind, (len(pos), H, nb), rng)
     log(f"case topk on given scores {kind} kv_len={kv_len}")
     scores = torch.from_numpy(S).cuda()
