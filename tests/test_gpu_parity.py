@@ -107,6 +107,20 @@ def test_edge_sequences():
         check_sequence(wl, res, b, label="edge")
 
 
+def test_sixty_four_sequences_packed():
+    """The largest sequence table (64 packed sequences) with seeded lengths from 0 to 1500,
+    among them empty, single-token and shorter-than-a-window ones: every row of every sequence."""
+    p = synth.config_params("prefill32k")
+    rng = np.random.default_rng(48)
+    lens = [int(x) for x in rng.integers(0, 1500, 64)]
+    lens[:4] = [0, 1, 31, 64]
+    wl = synth.make_prefill("sixty-four", p, lens, seed=48)
+    log("case 64 packed sequences")
+    res = run_prefill_stages(wl)
+    for b in range(wl.num_seqs):
+        check_sequence(wl, res, b, label="64 seqs")
+
+
 def test_chunked_prefill_against_cache():
     """Queries for the last tokens only (q_pos0 > 0) attend to the whole cached sequence."""
     p = synth.config_params("prefill32k")
