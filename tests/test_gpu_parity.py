@@ -246,6 +246,18 @@ def test_decode_small_ragged_lengths():
     run_decode(wl, 6)
 
 
+def test_decode_sixty_four_sequences():
+    """A decoding batch at the largest sequence table: 64 caches of seeded lengths (among them
+    1 token and less than one kernel window), two steps."""
+    p = synth.config_params("decode128k")
+    rng = np.random.default_rng(49)
+    kv0 = [int(x) for x in rng.integers(1, 5990, 64)]
+    kv0[:3] = [1, 20, 63]
+    wl = synth.make_decode("dec-64", p, batch=64, max_len=6000, steps=2, seed=49, kv_len0=kv0)
+    log("case decode 64 sequences")
+    run_decode(wl, 2)
+
+
 @pytest.mark.parametrize("splits", [1, 3, 7])
 def test_decode_split_invariance(splits):
     p = synth.config_params("decode128k")
