@@ -601,200 +601,6 @@ __device__ __forceinline__ void score_chunk(const Geom& g, const SeqTable& t, co
   }
 }
 
-// LDS of the decode step's selection (decode_select).
-struct SelLds {
-  int hist[2][256];
-  int wsum[kSelectWaves][2];
-  uint32_t wmin[kSelectWaves], wmax[kSelectWaves];
-  uint32_t bin_key[64];
-  int bin_blk[64];
-  int nbin;
-  int digit, above, count;
-};
-
-// Group-shared top-k of one (row, kv head) from its stored block scores srow[0 .. own] (section
-// 2.1.1: highest relevance first; reading: forced first n_init and last n_local blocks, ties to
-// the lower index, ascending output).  The (topk - forced)-th largest order-preserving key
-// among the other blocks is located by a radix select over the keys' actual range: the first
-// pass bins (key - min) >> s into 256 bins (s the smallest shift that fits max - min), each
-// later pass splits the chosen bin 256 ways.  It stops when every key of the chosen bin is
-// wanted, or the bin holds a single key value (taken in block order), or the bin holds at most
-// 64 keys: then one wave ranks those keys exactly (key descending, block ascending) and marks
-// the wanted ones.  `keys` holds one key per block in LDS for the ordered output.  The indices
-// are written with plain stores: only the next launch reads them.
-__device__ __forceinline__ void select_blocks(const Geom& g, int own, const float* srow,
-                                              int32_t* out_idx, uint32_t* keys, SelLds& sm,
-                                              int tid) {
-  constexpr int T = kSelectThreads;
-  constexpr int NW = kSelectWaves;
-  constexpr uint32_t kTaken = 0xFFFFFFFFu;
-  const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int nb = own + 1;
-  if (nb <= g.topk) {
-    for (int e = tid; e < g.topk; e += T) out_idx[e] = e < nb ? e : -1;
-    return;
-  }
-  const int local_lo = max(0, own - g.n_local + 1);
-  const int init_end = min(g.n_init, nb);
-  const int n_forced = init_end + (own - local_lo + 1) - max(0, init_end - local_lo);
-  const int npt = (nb + T - 1) / T;
-  // every score load is issued before any is used
-  float sc[kMaxKeysPerThread];
-#pragma unroll
-  for (int e = 0; e < kMaxKeysPerThread; ++e)
-    sc[e] = e < npt ? __uint_as_float(agent_load(reinterpret_cast<const uint32_t*>(srow) +
-                                                 min(e * T + tid, nb - 1)))
-                    : 0.f;
-  uint32_t kr[kMaxKeysPerThread];
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll
-  for (int e = 0; e < kMaxKeysPerThread; ++e) {
-    const int blk = e * T + tid;
-    const bool forced = blk < g.n_init || blk >= local_lo;
-    kr[e] = (e < npt && blk < nb && !forced) ? order_key(sc[e]) : 0u;   // 0: not a candidate
-    if (e < npt && blk < nb) keys[blk] = kr[e];
-    if (kr[e] != 0u) {
-      kmin = min(kmin, kr[e]);
-      kmax = max(kmax, kr[e]);
-    }
-  }
-  kmin = wave_min_u32(kmin);
-  kmax = wave_max_u32(kmax);
-  if (lane == 0) {
-    sm.wmin[w] = kmin;
-    sm.wmax[w] = kmax;
-  }
-  if (tid < 256) {
-    sm.hist[0][tid] = 0;
-    sm.hist[1][tid] = 0;
-  }
-  if (tid == 0) sm.nbin = 0;
-  __syncthreads();
-#pragma unroll
-  for (int ww = 0; ww < NW; ++ww) {
-    kmin = min(kmin, sm.wmin[ww]);
-    kmax = max(kmax, sm.wmax[ww]);
-  }
-  int want = g.topk - n_forced;                         // still wanted in the current bin
-  // keys >= hi are taken, keys in [lo, hi) in block order until `want` are (want == 0: none)
-  uint64_t lo = uint64_t{1} << 32, hi = uint64_t{1} << 32;
-  if (want > 0) {
-    uint32_t blo = kmin;                                // the current bin is [blo, bin_hi)
-    uint64_t bin_hi = static_cast<uint64_t>(kmax) + 1;
-    const uint32_t span = kmax - kmin;
-    int s = span == 0u ? 0 : max(0, 32 - __clz(static_cast<int>(span)) - 8);
-    const uint64_t above_lane = ~((2ull << lane) - 1);  // lanes over this one (none for 63)
-    for (int pass = 0;; ++pass) {
-      int* hist = sm.hist[pass & 1];
-#pragma unroll
-      for (int e = 0; e < kMaxKeysPerThread; ++e) {
-        const uint32_t key = kr[e];
-        if (key != 0u && key >= blo && key < bin_hi) atomicAdd(&hist[(key - blo) >> s], 1);
-      }
-      __syncthreads();
-      if (w == 0) {
-        // lane L holds bins 4L .. 4L+3 (zeroed again for the pass after next); the count over
-        // them is summed from the lanes above by one ballot per bit (counts < 2^13)
-        int c[4], tot = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          c[j] = hist[4 * lane + j];
-          hist[4 * lane + j] = 0;
-          tot += c[j];
-        }
-        int above = masked_count<13>(tot, above_lane);
-#pragma unroll
-        for (int j = 3; j >= 0; --j) {
-          if (above < want && above + c[j] >= want) {
-            sm.digit = 4 * lane + j;
-            sm.above = above;
-            sm.count = c[j];
-          }
-          above += c[j];
-        }
-      }
-      __syncthreads();
-      blo += static_cast<uint32_t>(sm.digit) << s;
-      bin_hi = static_cast<uint64_t>(blo) + (uint64_t{1} << s);
-      want -= sm.above;
-      const int count = sm.count;
-      lo = blo;
-      hi = bin_hi;
-      if (count == want || s == 0) break;               // the whole bin is wanted, or one value
-      if (count <= 64) {
-        // rank the bin's keys in one wave and mark the wanted ones taken, the others dropped
-#pragma unroll
-        for (int e = 0; e < kMaxKeysPerThread; ++e) {
-          const uint32_t key = kr[e];
-          if (key != 0u && key >= blo && key < bin_hi) {
-            const int slot = atomicAdd(&sm.nbin, 1);
-            sm.bin_key[slot] = key;
-            sm.bin_blk[slot] = e * T + tid;
-          }
-        }
-        __syncthreads();
-        if (w == 0) {
-          const uint32_t ki = lane < count ? sm.bin_key[lane] : 0u;
-          const int bi = lane < count ? sm.bin_blk[lane] : 0x7FFFFFFF;
-          int rank = 0;
-          for (int j = 0; j < count; ++j) {
-            const uint32_t kj = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ki), j));
-            const int bj = __builtin_amdgcn_readlane(bi, j);
-            rank += (kj > ki || (kj == ki && bj < bi)) ? 1 : 0;
-          }
-          if (lane < count) keys[bi] = rank < want ? kTaken : 0u;
-        }
-        __syncthreads();
-        want = 0;                                       // the bin is decided: marks only
-        hi = min(bin_hi, static_cast<uint64_t>(kTaken));
-        lo = hi;
-        break;
-      }
-      s = max(0, s - 8);
-    }
-  }
-  // over the bin: taken; in the bin: taken in block order until `want` are.  Thread tid
-  // writes blocks npt*tid .. npt*tid + npt - 1.
-  const int blk_lo = npt * tid;
-  const int blk_hi = min(nb, blk_lo + npt);
-  int fixed = 0, eq = 0;
-  for (int blk = blk_lo; blk < blk_hi; ++blk) {
-    const uint32_t key = keys[blk];
-    const bool forced = blk < g.n_init || blk >= local_lo;
-    fixed += (forced || (key != 0u && key >= hi)) ? 1 : 0;
-    eq += (!forced && key != 0u && key >= lo && key < hi) ? 1 : 0;
-  }
-  // exclusive prefix counts over the workgroup: bit ballots within the wave, then wave totals
-  const uint64_t below = (1ull << lane) - 1;
-  int fixed_before = masked_count<4>(fixed, below);
-  int eq_before = masked_count<4>(eq, below);
-  const int fixed_wave = masked_count<4>(fixed, ~0ull);    // ballots: the whole wave takes part
-  const int eq_wave = masked_count<4>(eq, ~0ull);
-  if (lane == 0) {
-    sm.wsum[w][0] = fixed_wave;
-    sm.wsum[w][1] = eq_wave;
-  }
-  __syncthreads();
-  for (int ww = 0; ww < w; ++ww) {
-    fixed_before += sm.wsum[ww][0];
-    eq_before += sm.wsum[ww][1];
-  }
-  int eq_seen = eq_before;
-  int p = fixed_before + min(eq_seen, want);
-  for (int blk = blk_lo; blk < blk_hi; ++blk) {
-    const uint32_t key = keys[blk];
-    const bool forced = blk < g.n_init || blk >= local_lo;
-    bool take = forced || (key != 0u && key >= hi);
-    if (!take && key != 0u && key >= lo && key < hi) {
-      take = eq_seen < want;
-      ++eq_seen;
-    }
-    if (take && p < g.topk) out_idx[p] = blk;           // p < topk unless keys are NaN
-    p += take ? 1 : 0;
-  }
-}
-
 template <int D, int G>
 __global__ void __launch_bounds__(kSelectThreads)
 decode_select(Geom g, SeqTable t, const uint16_t* __restrict__ q,
@@ -802,7 +608,7 @@ decode_select(Geom g, SeqTable t, const uint16_t* __restrict__ q,
               int32_t* __restrict__ idx, void* __restrict__ workspace) {
   __shared__ __attribute__((aligned(16))) uint32_t stage[kMaxKeysPerThread * kSelectThreads];
   __shared__ float qs[D];
-  __shared__ SelLds sm;
+  __shared__ WgSelectLds<kSelectWaves> sm;
   __shared__ int s_last;
   static_assert(kMaxKeysPerThread * kSelectThreads >= 4 * kChunkBlocks + 4, "score staging fits");
 
@@ -826,8 +632,8 @@ decode_select(Geom g, SeqTable t, const uint16_t* __restrict__ q,
   __syncthreads();
   if (!s_last) return;
   // the pair's last chunk: select, and zero the counter for the next call (its last user)
-  select_blocks(g, own, srow, idx + (static_cast<size_t>(r.row) * g.Hkv + kvh) * g.topk, stage,
-                sm, tid);
+  wg_select<kSelectWaves, kMaxKeysPerThread>(
+      g, own, srow, idx + (static_cast<size_t>(r.row) * g.Hkv + kvh) * g.topk, stage, sm, tid);
   if (tid == 0) agent_store(score_done + pair, 0);
 }
 

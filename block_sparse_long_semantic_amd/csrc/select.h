@@ -1,15 +1,15 @@
 // Group-shared top-k selection of one (query row, KV head) by a whole workgroup (MiniCPM4 paper
 // summary, section 2.1.1: each query token selects its most relevant KV blocks; section 2.1.2:
-// one selection per query-head group).  Used where few rows are selected at once (decoding).
+// one selection per query-head group), for launches with few rows (decoding): the selection
+// kernel's small-batch form and the decode step's scoring launch.
 //
 // Scores map to order-preserving unsigned keys (-0 ranks as +0).  Forced blocks (the first
-// n_init and the n_local ending at the query's own block) are set aside; the (topk - forced)-th
-// largest key among the others is found by a bitwise search (each thread counts its keys at or
-// above the candidate, waves sum with bit ballots, the workgroup through LDS); keys equal to
-// the threshold are taken in ascending block order; the selection is written ascending,
-// padded with -1.
+// n_init and the n_local ending at the query's own block) are always taken; among the others
+// the best by (score descending, block ascending) fill the rest of topk; the selection is
+// written ascending, padded with -1.
 #pragma once
 
+#include "dpp.h"
 #include "internal.h"
 
 namespace infllm2 {
@@ -25,93 +25,205 @@ __device__ __forceinline__ int prefix_count(unsigned long long mask) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
 }
 
-// Sum over the wave of a small per-lane count (< 128): one ballot per bit of the count.
-__device__ __forceinline__ int wave_count(int c) {
-  int tot = 0;
-#pragma unroll
-  for (int bit = 0; bit < 7; ++bit) tot += __popcll(__ballot((c >> bit) & 1)) << bit;
-  return tot;
+// Relaxed agent-scope load: coherent across the XCDs' L2s without a fence.
+__device__ __forceinline__ uint32_t coherent_load(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Workgroup total of a per-wave value through LDS slot `slot` (one barrier); *before receives
-// the sum over the waves below this one.
+// LDS of wg_select.
 template <int NW>
-__device__ __forceinline__ int wg_sum(int (*buf)[NW], int slot, int w, int lane, int v,
-                                      int* before) {
-  if (lane == 0) buf[slot][w] = v;
-  __syncthreads();
-  int tot = 0, pre = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const int c = buf[slot][i];
-    tot += c;
-    pre += i < w ? c : 0;
-  }
-  if (before) *before = pre;
-  return tot;
-}
-
-// LDS scratch of wg_select.
-template <int NW, int NPT>
-struct SelectScratch {
-  int cnt[2 + 2 * NPT][NW];
+struct WgSelectLds {
+  int hist[2][256];
+  int wsum[NW][2];
+  uint32_t wmin[NW], wmax[NW];
+  uint32_t bin_key[64];
+  int bin_blk[64];
+  int nbin;
+  int digit, above, count;
 };
 
-// Selects among blocks 0 .. own (own = query position / B) with keys in registers: thread tid of
-// the NW-wave workgroup holds block 64*NW*e + tid in key[e] (0 for forced blocks and for blocks
-// past own, non-zero otherwise).  Writes topk entries of `out`.  Every thread must call it.
-template <int NW, int NPT>
-__device__ void wg_select(const uint32_t (&key)[NPT], int own, int topk, int n_init, int n_local,
-                          int32_t* __restrict__ out, SelectScratch<NW, NPT>& sm) {
-  constexpr int NT = 64 * NW;
-  const int tid = threadIdx.x;
+// Group-shared top-k of one (row, kv head) by a workgroup of NW waves, from its stored block
+// scores srow[0 .. own] (up to KPT per thread).  The (topk - forced)-th largest order-preserving
+// key among the non-forced blocks is located by a radix select over the keys' actual range: the
+// first pass bins (key - min) >> s into 256 LDS counters (s the smallest shift that fits
+// max - min), each later pass splits the chosen bin 256 ways.  It stops when every key of the
+// chosen bin is wanted, or the bin holds a single key value (taken in block order), or the bin
+// holds at most 64 keys: then one wave ranks those keys exactly (key descending, block
+// ascending) and marks the wanted ones.  `keys` (LDS, one word per block) holds the keys for the
+// ordered output.  Scores are read with agent-scope loads, so they may come from other
+// workgroups of the same launch; the indices are written with plain stores (the next launch
+// reads them).  Every thread of the workgroup must call it.
+template <int NW, int KPT>
+__device__ __forceinline__ void wg_select(const Geom& g, int own, const float* srow,
+                                          int32_t* out_idx, uint32_t* keys, WgSelectLds<NW>& sm,
+                                          int tid) {
+  constexpr int T = 64 * NW;
+  constexpr uint32_t kTaken = 0xFFFFFFFFu;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int nb = own + 1;
-  const int local_lo = max(0, own - n_local + 1);
-  const int init_end = min(n_init, nb);
+  if (nb <= g.topk) {
+    for (int e = tid; e < g.topk; e += T) out_idx[e] = e < nb ? e : -1;
+    return;
+  }
+  const int local_lo = max(0, own - g.n_local + 1);
+  const int init_end = min(g.n_init, nb);
   const int n_forced = init_end + (own - local_lo + 1) - max(0, init_end - local_lo);
-  const int want = topk - n_forced;
-
-  // bitwise search for the threshold; buffers alternate so one barrier per step suffices
-  uint32_t thr = 0u;
-  int step = 0;
-  for (int bit = 31; bit >= 0; --bit, ++step) {
-    const uint32_t cand = thr | (1u << bit);
-    int c = 0;
+  const int npt = (nb + T - 1) / T;
+  // every score load is issued before any is used
+  float sc[KPT];
 #pragma unroll
-    for (int e = 0; e < NPT; ++e) c += key[e] >= cand ? 1 : 0;
-    const int tot = wg_sum<NW>(sm.cnt, step & 1, w, lane, wave_count(c), nullptr);
-    if (tot >= want) {
-      thr = cand;
-      if (tot == want) break;                              // same decision in every wave
+  for (int e = 0; e < KPT; ++e)
+    sc[e] = e < npt ? __uint_as_float(coherent_load(reinterpret_cast<const uint32_t*>(srow) +
+                                                 min(e * T + tid, nb - 1)))
+                    : 0.f;
+  uint32_t kr[KPT];
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) {
+    const int blk = e * T + tid;
+    const bool forced = blk < g.n_init || blk >= local_lo;
+    kr[e] = (e < npt && blk < nb && !forced) ? order_key(sc[e]) : 0u;   // 0: not a candidate
+    if (e < npt && blk < nb) keys[blk] = kr[e];
+    if (kr[e] != 0u) {
+      kmin = min(kmin, kr[e]);
+      kmax = max(kmax, kr[e]);
     }
   }
-  __syncthreads();                                         // the last step's counts are read
-  int c_gt = 0;
-#pragma unroll
-  for (int e = 0; e < NPT; ++e) c_gt += key[e] > thr ? 1 : 0;
-  const int need_eq = want - wg_sum<NW>(sm.cnt, 0, w, lane, wave_count(c_gt), nullptr);
-
-  int base_eq = 0, base = 0;
-#pragma unroll
-  for (int e = 0; e < NPT; ++e) {
-    const int blk = NT * e + tid;
-    const bool eq = key[e] == thr && key[e] != 0u;
-    const unsigned long long meq = __ballot(eq);
-    int eq_before;
-    const int eq_tot = wg_sum<NW>(sm.cnt, 2 + 2 * e, w, lane, __popcll(meq), &eq_before);
-    const bool take_eq = eq && (base_eq + eq_before + prefix_count(meq)) < need_eq;
-    base_eq += eq_tot;
-    const bool forced = blk < nb && (blk < n_init || blk >= local_lo);
-    const bool sel = forced || key[e] > thr || take_eq;
-    const unsigned long long ms = __ballot(sel);
-    int sel_before;
-    const int sel_tot = wg_sum<NW>(sm.cnt, 3 + 2 * e, w, lane, __popcll(ms), &sel_before);
-    if (sel) out[base + sel_before + prefix_count(ms)] = blk;
-    base += sel_tot;
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) {
+    sm.wmin[w] = kmin;
+    sm.wmax[w] = kmax;
   }
-  for (int p = base + tid; p < topk; p += NT) out[p] = -1;
+  if (tid < 256) {
+    sm.hist[0][tid] = 0;
+    sm.hist[1][tid] = 0;
+  }
+  if (tid == 0) sm.nbin = 0;
+  __syncthreads();
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) {
+    kmin = min(kmin, sm.wmin[ww]);
+    kmax = max(kmax, sm.wmax[ww]);
+  }
+  int want = g.topk - n_forced;                         // still wanted in the current bin
+  // keys >= hi are taken, keys in [lo, hi) in block order until `want` are (want == 0: none)
+  uint64_t lo = uint64_t{1} << 32, hi = uint64_t{1} << 32;
+  if (want > 0) {
+    uint32_t blo = kmin;                                // the current bin is [blo, bin_hi)
+    uint64_t bin_hi = static_cast<uint64_t>(kmax) + 1;
+    const uint32_t span = kmax - kmin;
+    int s = span == 0u ? 0 : max(0, 32 - __clz(static_cast<int>(span)) - 8);
+    const uint64_t above_lane = ~((2ull << lane) - 1);  // lanes over this one (none for 63)
+    for (int pass = 0;; ++pass) {
+      int* hist = sm.hist[pass & 1];
+#pragma unroll
+      for (int e = 0; e < KPT; ++e) {
+        const uint32_t key = kr[e];
+        if (key != 0u && key >= blo && key < bin_hi) atomicAdd(&hist[(key - blo) >> s], 1);
+      }
+      __syncthreads();
+      if (w == 0) {
+        // lane L holds bins 4L .. 4L+3 (zeroed again for the pass after next); the count over
+        // them is summed from the lanes above by one ballot per bit (counts < 2^13)
+        int c[4], tot = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          c[j] = hist[4 * lane + j];
+          hist[4 * lane + j] = 0;
+          tot += c[j];
+        }
+        int above = masked_count<13>(tot, above_lane);
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+          if (above < want && above + c[j] >= want) {
+            sm.digit = 4 * lane + j;
+            sm.above = above;
+            sm.count = c[j];
+          }
+          above += c[j];
+        }
+      }
+      __syncthreads();
+      blo += static_cast<uint32_t>(sm.digit) << s;
+      bin_hi = static_cast<uint64_t>(blo) + (uint64_t{1} << s);
+      want -= sm.above;
+      const int count = sm.count;
+      lo = blo;
+      hi = bin_hi;
+      if (count == want || s == 0) break;               // the whole bin is wanted, or one value
+      if (count <= 64) {
+        // rank the bin's keys in one wave and mark the wanted ones taken, the others dropped
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+          const uint32_t key = kr[e];
+          if (key != 0u && key >= blo && key < bin_hi) {
+            const int slot = atomicAdd(&sm.nbin, 1);
+            sm.bin_key[slot] = key;
+            sm.bin_blk[slot] = e * T + tid;
+          }
+        }
+        __syncthreads();
+        if (w == 0) {
+          const uint32_t ki = lane < count ? sm.bin_key[lane] : 0u;
+          const int bi = lane < count ? sm.bin_blk[lane] : 0x7FFFFFFF;
+          int rank = 0;
+          for (int j = 0; j < count; ++j) {
+            const uint32_t kj = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ki), j));
+            const int bj = __builtin_amdgcn_readlane(bi, j);
+            rank += (kj > ki || (kj == ki && bj < bi)) ? 1 : 0;
+          }
+          if (lane < count) keys[bi] = rank < want ? kTaken : 0u;
+        }
+        __syncthreads();
+        want = 0;                                       // the bin is decided: marks only
+        hi = min(bin_hi, static_cast<uint64_t>(kTaken));
+        lo = hi;
+        break;
+      }
+      s = max(0, s - 8);
+    }
+  }
+  // over the bin: taken; in the bin: taken in block order until `want` are.  Thread tid
+  // writes blocks npt*tid .. npt*tid + npt - 1.
+  const int blk_lo = npt * tid;
+  const int blk_hi = min(nb, blk_lo + npt);
+  int fixed = 0, eq = 0;
+  for (int blk = blk_lo; blk < blk_hi; ++blk) {
+    const uint32_t key = keys[blk];
+    const bool forced = blk < g.n_init || blk >= local_lo;
+    fixed += (forced || (key != 0u && key >= hi)) ? 1 : 0;
+    eq += (!forced && key != 0u && key >= lo && key < hi) ? 1 : 0;
+  }
+  // exclusive prefix counts over the workgroup: bit ballots within the wave, then wave totals
+  const uint64_t below = (1ull << lane) - 1;
+  int fixed_before = masked_count<4>(fixed, below);
+  int eq_before = masked_count<4>(eq, below);
+  const int fixed_wave = masked_count<4>(fixed, ~0ull);    // ballots: the whole wave takes part
+  const int eq_wave = masked_count<4>(eq, ~0ull);
+  if (lane == 0) {
+    sm.wsum[w][0] = fixed_wave;
+    sm.wsum[w][1] = eq_wave;
+  }
+  __syncthreads();
+  for (int ww = 0; ww < w; ++ww) {
+    fixed_before += sm.wsum[ww][0];
+    eq_before += sm.wsum[ww][1];
+  }
+  int eq_seen = eq_before;
+  int p = fixed_before + min(eq_seen, want);
+  for (int blk = blk_lo; blk < blk_hi; ++blk) {
+    const uint32_t key = keys[blk];
+    const bool forced = blk < g.n_init || blk >= local_lo;
+    bool take = forced || (key != 0u && key >= hi);
+    if (!take && key != 0u && key >= lo && key < hi) {
+      take = eq_seen < want;
+      ++eq_seen;
+    }
+    if (take && p < g.topk) out_idx[p] = blk;           // p < topk unless keys are NaN
+    p += take ? 1 : 0;
+  }
 }
 
 }  // namespace infllm2

@@ -199,17 +199,17 @@ topk_kernel(Geom g, SeqTable t, const float* __restrict__ scores, int nb_stride,
   for (int p = base + lane; p < g.topk; p += 64) out[p] = -1;
 }
 
-// The same selection with one workgroup of 16 waves per (query row, KV head), for launches
-// with few rows (decoding): block b = 1024*e + thread.
-constexpr int kWideWaves = 16;
+// The same selection by one workgroup of 8 waves per (query row, KV head), for launches with
+// few rows (decoding): the radix select of select.h, up to 8 blocks per thread.
+constexpr int kWideWaves = 8;
 constexpr int kWideThreads = 64 * kWideWaves;
+constexpr int kWideKeys = 8;
 
-template <int NPT>
 __global__ void __launch_bounds__(kWideThreads)
 topk_wide(Geom g, SeqTable t, const float* __restrict__ scores, int nb_stride,
           int32_t* __restrict__ idx) {
-  __shared__ SelectScratch<kWideWaves, NPT> sm;
-  const int tid = threadIdx.x;
+  __shared__ uint32_t keys[kWideKeys * kWideThreads];
+  __shared__ WgSelectLds<kWideWaves> sm;
   const int item = blockIdx.x;
   const int vrow = item / g.Hkv;
   const int kvh = item % g.Hkv;
@@ -217,24 +217,9 @@ topk_wide(Geom g, SeqTable t, const float* __restrict__ scores, int nb_stride,
   const int j = vrow - t.work_prefix[b];
   const int row = t.q_start[b] + j;
   const int pos = t.q_pos0[b] + j;
-  const int own = pos / g.B;
-  const int nb = own + 1;
-  int32_t* out = idx + (static_cast<size_t>(row) * g.Hkv + kvh) * g.topk;
-  if (nb <= g.topk) {                                       // uniform over the workgroup
-    for (int e = tid; e < g.topk; e += kWideThreads) out[e] = e < nb ? e : -1;
-    return;
-  }
-  const float* srow = scores + (static_cast<size_t>(row) * g.Hkv + kvh) * nb_stride;
-  const int local_lo = max(0, own - g.n_local + 1);
-  uint32_t key[NPT];
-#pragma unroll
-  for (int e = 0; e < NPT; ++e) {
-    const int blk = kWideThreads * e + tid;
-    const float sc = srow[min(blk, nb - 1)];
-    const bool forced = blk < g.n_init || blk >= local_lo;
-    key[e] = (blk < nb && !forced) ? order_key(sc) : 0u;
-  }
-  wg_select<kWideWaves, NPT>(key, own, g.topk, g.n_init, g.n_local, out, sm);
+  const size_t pair = static_cast<size_t>(row) * g.Hkv + kvh;
+  wg_select<kWideWaves, kWideKeys>(g, pos / g.B, scores + pair * nb_stride, idx + pair * g.topk,
+                                   keys, sm, static_cast<int>(threadIdx.x));
 }
 
 }  // namespace
@@ -243,18 +228,10 @@ hipError_t launch_topk(const Geom& g, const SeqTable& t, const float* scores, in
                        int max_blocks, int32_t* idx, hipStream_t stream) {
   const int items = t.work_prefix[t.n] * g.Hkv;
   if (items == 0) return hipSuccess;
-  if (items <= 1024 && max_blocks <= 4 * kWideThreads) {
-    const int npt = (max_blocks + kWideThreads - 1) / kWideThreads;
-#define INFLLM2_TOPK_WIDE(N)                                                                  \
-    if (npt <= N) {                                                                           \
-      hipLaunchKernelGGL(topk_wide<N>, dim3(items), dim3(kWideThreads), 0, stream, g, t,     \
-                         scores, nb_stride, idx);                                             \
-      return hipGetLastError();                                                               \
-    }
-    INFLLM2_TOPK_WIDE(1)
-    INFLLM2_TOPK_WIDE(2)
-    INFLLM2_TOPK_WIDE(4)
-#undef INFLLM2_TOPK_WIDE
+  if (items <= 1024 && max_blocks <= kWideKeys * kWideThreads) {
+    hipLaunchKernelGGL(topk_wide, dim3(items), dim3(kWideThreads), 0, stream, g, t, scores,
+                       nb_stride, idx);
+    return hipGetLastError();
   }
   const dim3 grid(items);
   const dim3 block(64);

@@ -59,3 +59,27 @@ def test_topk_on_given_scores(kind, kv_len):
     want = orc.select_all(S, pos, p)
     bad = np.nonzero(np.any(got != want, axis=2))
     assert bad[0].size == 0, f"{kind}: rows {bad[0][:5]} heads {bad[1][:5]} differ"
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "one-value", "signs", "wide", "neg-inf"])
+@pytest.mark.parametrize("kv_len", [6400, 65536, 262144])
+def test_topk_few_rows_on_given_scores(kind, kv_len):
+    """At most 1024 (row, KV head) pairs: the workgroup-wide form of the selection."""
+    p = synth.config_params("prefill128k")
+    H = p.num_kv_heads
+    seqs = lib.Seqs(q_start=[0, 200], q_len=[200, 100], q_pos0=[kv_len - 200, 5950],
+                    kv_start=[0, kv_len], kv_len=[kv_len, 6050], kc_start=[0, 0])
+    pos = np.concatenate([kv_len - 200 + np.arange(200), 5950 + np.arange(100)])
+    nb = kv_len // p.block_size
+    assert len(pos) * H <= 1024
+    kinds = ["normal", "ties", "one-value", "signs", "wide", "neg-inf"]
+    rng = np.random.default_rng(700 + 10 * kinds.index(kind) + kv_len // 6400)
+    S = score_rows(kind, (len(pos), H, nb), rng)
+    log(f"case topk few rows on given scores {kind} kv_len={kv_len}")
+    scores = torch.from_numpy(S).cuda()
+    idx = torch.full((len(pos), H, p.topk), -7, dtype=torch.int32, device="cuda")
+    lib.topk_select(p, seqs, scores, idx)
+    got = host(idx)
+    want = orc.select_all(S, pos, p)
+    bad = np.nonzero(np.any(got != want, axis=2))
+    assert bad[0].size == 0, f"{kind}: rows {bad[0][:5]} heads {bad[1][:5]} differ"
