@@ -29,7 +29,7 @@ abstract for the prefill and decode use):
      Architecture"; arXiv abstract; paper summary section 2.1): with the selected blocks held
      fixed -- the selection is piecewise constant in Q and K, so its derivative is zero almost
      everywhere -- dQ, dK and dV of step 5 for an upstream gradient dO.     -> sparse_attention_backward
-  3'. a second reading of step 3's relevance score (the survey's alternative, selected by
+  3'. a second reading of step 3's relevance score (the other plain reading, selected by
      score_mode = 1): each head's scores are first normalised by a softmax over the kernels
      visible at the query's position, and the group sum is taken over those probabilities
      (section 2.1.2 names a relevance score without fixing its form).  -> kernel_scores_softmax
