@@ -3,9 +3,11 @@
 // block).  HBM-bound: every key row is read once per window containing it (w/s = 2 times for
 // the measured geometry; the second read hits L2) and each kernel row is written once.
 //
-// Exactness: window sums are accumulated in float64.  For bf16 (8 significant bits) or f32
-// inputs of ordinary magnitude these sums are exact, so the single rounding to the storage
-// dtype below (to nearest even, straight from float64) reproduces the exact mean's rounding.
+// Exactness: window sums are accumulated in float64.  With p significant bits per input (8 for
+// bf16, 24 for f32) and w terms, no partial sum rounds while the window's nonzero inputs span at
+// most 53 - p - ceil(log2 w) binary exponents (40 for bf16 at w = 32); then the single rounding
+// to the storage dtype below (to nearest even, straight from float64) is the exact mean's
+// rounding.  Wider windows may round in the sum (at most one unit in the last place off).
 #include "internal.h"
 
 namespace infllm2 {

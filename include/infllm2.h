@@ -100,7 +100,11 @@ typedef struct {
 
 /* Semantic kernels (paper summary section 2.1.2: fine-grained semantic kernels represent each
  * KV block).  Kernel c of a sequence is the mean of the keys of its tokens s*c .. s*c+w-1,
- * accumulated exactly in float64 and rounded once, to nearest even, to the key dtype.
+ * summed in float64 and rounded once, to nearest even, to the key dtype.  The float64 sum is
+ * exact, so the kernel is the exactly rounded mean, whenever the window's nonzero keys differ in
+ * binary exponent by at most 53 - p - ceil(log2 w) (p = 8 significant bits for bf16, 24 for
+ * float32: 40 and 24 binades for w = 32), which keys of ordinary magnitude always meet; a window
+ * spread wider may round once more in the sum and land one unit in the last place away.
  * prev_kv_len (host array, may be NULL = all zeros) makes the call incremental: only kernels
  * with prev_kv_len[b] < s*c + w <= kv_len[b] are written; other rows of `kernels` are left
  * untouched.  Reads k, writes kernels. */

@@ -171,6 +171,46 @@ def test_mfma_scores_ragged_tiles(name, lens):
         check_sequence(wl, res, b, rows=np.array(rows), label=f"mfma-ragged {name} seq {b}")
 
 
+def test_compress_exactness_condition_wide_exponents():
+    """Keys spread over 2^-60 .. 2^60 in some windows: a window's float64 sum is exact when its
+    nonzero keys differ in binary exponent by at most 40 (8 significant bits each, at most 32
+    terms), and the kernel then equals the exactly rounded mean bit for bit; other windows may
+    round once more, and stay within one bf16 unit of the exact result."""
+    p = synth.config_params("prefill32k")
+    L = 4096
+    rng = np.random.default_rng(71)
+    k = rng.standard_normal((L, p.num_kv_heads, p.head_dim)).astype(np.float64)
+    e = rng.integers(-15, 16, k.shape)
+    wide = (np.arange(L) // 512) % 2 == 1
+    e[wide] = rng.integers(-60, 61, (int(wide.sum()), p.num_kv_heads, p.head_dim))
+    k = synth.round_to_bf16((k * 2.0 ** e).astype(np.float32))
+    C = orc.num_kernels(L, p.kernel_size, p.kernel_stride)
+    seqs = lib.Seqs([0], [0], [0], [0], [L], [0])
+    kd = dev(k, "bf16")
+    kern = torch.zeros((C, p.num_kv_heads, p.head_dim), dtype=torch.bfloat16, device="cuda")
+    log("case compress wide exponents")
+    lib.compress_kernels(p, seqs, kd, kern)
+    torch.cuda.synchronize()
+    got = host(kern)
+    ref = orc.compress_kernels(k, p.kernel_size, p.kernel_stride, p.dtype)
+    ex = np.frexp(k.astype(np.float64))[1].astype(np.int64)
+    big = np.where(k != 0, ex, np.iinfo(np.int64).min)
+    small = np.where(k != 0, ex, np.iinfo(np.int64).max)
+    exact_ok = np.zeros(got.shape, bool)
+    for c in range(C):
+        sl = slice(p.kernel_stride * c, p.kernel_stride * c + p.kernel_size)
+        hi, lo = big[sl].max(axis=0), small[sl].min(axis=0)
+        exact_ok[c] = (hi == np.iinfo(np.int64).min) | (hi - lo <= 40)
+    assert np.array_equal(got[exact_ok], ref[exact_ok]), "kernel differs where the sum is exact"
+    gb = got.view(np.uint32) >> 16
+    rb = ref.astype(np.float32).view(np.uint32) >> 16
+    diff = np.abs(gb.astype(np.int64) - rb.astype(np.int64))
+    same_sign = np.sign(got) == np.sign(ref)
+    assert np.all((diff <= 1) & (same_sign | (diff == 0)) | (got == ref)), "beyond one bf16 unit"
+    log(f"compress wide: {int(exact_ok.sum())} exact-condition entries, "
+        f"{int((~exact_ok).sum())} others, {int((diff[~exact_ok] > 0).sum())} of them off by one unit")
+
+
 def test_results_are_deterministic():
     wl = synth.make("varlen", length_scale=1 / 32)
     a = run_prefill_stages(wl)
@@ -293,12 +333,29 @@ def test_decode_f32_tiny_shape():
 
 # ------------------------------------------------------------------------- full sizes
 
-def sample_rows(wl, b, extra=()):
+def whole_tiles(L, n_windows=8, needle_rows=()):
+    """Every row of n_windows windows of 96 consecutive rows aligned to 96 (whole tiles of 16,
+    24 or 32 query rows): spread over the sequence, the last window, and one holding a needle
+    query (when there is one)."""
+    W = 96
+    last = max(0, (L - 1) // W)
+    starts = {int(x) for x in np.linspace(0, last, n_windows - 1).round()} | {last}
+    if len(needle_rows):
+        starts.add(int(needle_rows[0]) // W)
+    rows = set()
+    for st in starts:
+        rows |= set(range(st * W, min(L, st * W + W)))
+    return rows
+
+
+def sample_rows(wl, b, extra=(), tiles=False):
     p = wl.params
     L = int(wl.q_len[b])
     dense = min(L, p.topk * p.block_size)
     rows = set(range(0, dense, 97)) | set(range(max(0, L - 5), L)) | set(range(dense, L, 1777))
     rows |= {r for r in extra if 0 <= r < L}
+    if tiles:
+        rows |= whole_tiles(L, needle_rows=[r for r in extra if 0 <= r < L])
     return np.array(sorted(rows))
 
 
@@ -313,7 +370,8 @@ def test_full_size_prefill_sampled(name):
         assert np.all(np.any(res["idx"][rows, nd.kv_head, :] == nd.block, axis=1))
     for b in range(wl.num_seqs):
         extra = [int(r) for nd in wl.needles if nd.seq == b for r in nd.query_positions[:4]]
-        check_sequence(wl, res, b, rows=sample_rows(wl, b, extra), label=f"full {name}")
+        check_sequence(wl, res, b, rows=sample_rows(wl, b, extra, tiles=True),
+                       label=f"full {name}")
     # sparsity: selected-token fraction per row follows the configured top-k
     p = wl.params
     nsel = (res["idx"] >= 0).sum(axis=2)

@@ -3,6 +3,8 @@ rows that reach 100 to 4096 blocks (up to a 256K-token sequence), rows around th
 and score distributions that stress the selection (heavy ties, a single value, both signs with
 +-0, a wide exponent range, -inf entries).  The indices must equal the oracle's selection
 exactly."""
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -76,6 +78,36 @@ def test_topk_few_rows_on_given_scores(kind, kv_len):
     rng = np.random.default_rng(700 + 10 * kinds.index(kind) + kv_len // 6400)
     S = score_rows(kind, (len(pos), H, nb), rng)
     log(f"case topk few rows on given scores {kind} kv_len={kv_len}")
+    scores = torch.from_numpy(S).cuda()
+    idx = torch.full((len(pos), H, p.topk), -7, dtype=torch.int32, device="cuda")
+    lib.topk_select(p, seqs, scores, idx)
+    got = host(idx)
+    want = orc.select_all(S, pos, p)
+    bad = np.nonzero(np.any(got != want, axis=2))
+    assert bad[0].size == 0, f"{kind}: rows {bad[0][:5]} heads {bad[1][:5]} differ"
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "one-value", "signs", "wide", "neg-inf"])
+@pytest.mark.parametrize("topk", [256, 1024])
+@pytest.mark.parametrize("form", ["many-rows", "few-rows"])
+def test_topk_large_k_on_given_scores(kind, topk, form):
+    """top-k beyond 128 non-forced blocks: the one-wave form then starts its first radix pass at
+    the smallest key instead of the lanes' lower bound.  Rows at the end of a 128K sequence and
+    rows whose reachable block counts cross topk; both forms of the selection."""
+    p = replace(synth.config_params("prefill128k"), topk=topk)
+    H = p.num_kv_heads
+    kv_len = 131072
+    lim = topk * p.block_size
+    n0, n1 = (600, 400) if form == "many-rows" else (200, 100)
+    seqs = lib.Seqs(q_start=[0, n0], q_len=[n0, n1], q_pos0=[kv_len - n0, lim - n1 // 2],
+                    kv_start=[0, kv_len], kv_len=[kv_len, lim + n1], kc_start=[0, 0])
+    pos = np.concatenate([kv_len - n0 + np.arange(n0), lim - n1 // 2 + np.arange(n1)])
+    nb = kv_len // p.block_size
+    assert (len(pos) * H > 1024) == (form == "many-rows")
+    kinds = ["normal", "ties", "one-value", "signs", "wide", "neg-inf"]
+    rng = np.random.default_rng(900 + 10 * kinds.index(kind) + topk // 256 + 5 * (form == "few-rows"))
+    S = score_rows(kind, (len(pos), H, nb), rng)
+    log(f"case topk k={topk} {form} {kind}")
     scores = torch.from_numpy(S).cuda()
     idx = torch.full((len(pos), H, p.topk), -7, dtype=torch.int32, device="cuda")
     lib.topk_select(p, seqs, scores, idx)
