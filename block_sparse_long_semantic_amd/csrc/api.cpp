@@ -319,12 +319,6 @@ infllm2_status infllm2_sparse_attn_prefill(const infllm2_params* params,
   infllm2_status st = attn_common(params, seqs, q, k, v, block_idx, out, lse, &g, &t);
   if (st != INFLLM2_OK) return st;
   if (infllm2::attn_tile_supported(g, params->dtype, t)) {
-    int acc = 0;
-    for (int b = 0; b < t.n; ++b) {
-      t.work_prefix[b] = acc;
-      acc += (t.q_len[b] + 15) / 16;
-    }
-    t.work_prefix[t.n] = acc;
     return hip_status(infllm2::launch_attn_tile(g, t, q, k, v, block_idx, out, lse,
                                                 static_cast<hipStream_t>(stream)),
                       "sparse_attn_prefill launch");
@@ -352,12 +346,7 @@ infllm2_status infllm2_sliding_window_attn(const infllm2_params* params,
                 "sliding-window attention needs bf16, block_size 64, head_dim 64 or 128, group "
                 "size 8 or 16 and queries at positions below 2048 * 64");
   g.window = window;
-  int acc = 0;
-  for (int b = 0; b < t.n; ++b) {
-    t.work_prefix[b] = acc;
-    acc += (t.q_len[b] + 15) / 16;
-  }
-  t.work_prefix[t.n] = acc;
+  rows_prefix(&t);
   return hip_status(infllm2::launch_attn_tile_window(g, t, q, k, v, out, lse,
                                                      static_cast<hipStream_t>(stream)),
                     "sliding_window_attn launch");

@@ -688,15 +688,8 @@ hipError_t launch_attn_bwd(const Geom& g, const SeqTable& t, int n_blocks, int q
                      list, n_blocks, win_rows);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  // dQ: the forward's tile kernel in its gradient form (tiles of 16 rows)
-  SeqTable tt = t;
-  int acc = 0;
-  for (int b = 0; b < tt.n; ++b) {
-    tt.work_prefix[b] = acc;
-    acc += (tt.q_len[b] + 15) / 16;
-  }
-  tt.work_prefix[tt.n] = acc;
-  if ((e = launch_attn_tile_dq(g, tt, q, k, v, idx, dout, lse, delta, dq, stream)) != hipSuccess)
+  // dQ: the forward's tile kernel in its gradient form (it forms its own tiles from the rows)
+  if ((e = launch_attn_tile_dq(g, t, q, k, v, idx, dout, lse, delta, dq, stream)) != hipSuccess)
     return e;
 
   // dK, dV: persistent grid over the work items (their count is known on the device only)

@@ -5,8 +5,12 @@
 // Design (one workgroup = 8 waves = one tile of T = 16 consecutive query tokens of one
 // sequence and one KV head):
 //   * Union: the tile's 16 selected-block lists are OR-ed into a per-block 16-bit token mask in
-//     LDS and compacted into an ascending list of (block, mask).  Each union block's K and V
-//     (64 keys x d, bf16) are staged into LDS once for all tokens that chose it.
+//     LDS and compacted into a list of (block, mask).  Each union block's K and V (64 keys x d,
+//     bf16) are staged into LDS once for all tokens that chose it.  The forward and gradient
+//     forms stream the list in the order of the waves' progress (each wave's needed blocks,
+//     ranked r = 0 .. n_w - 1, get the key (r + 1/2) / n_w; an entry takes its waves' largest
+//     key), so that any stretch of the stream holds about equal work for every wave and fewer
+//     waves idle at the head of the ring; the order stays close to ascending block order.
 //   * Staging: global_load_lds (16 B per lane, straight to LDS, no registers) into a ring of
 //     NS slots, block u in slot u % NS.  K is stored row-major with the 16-byte chunks of row r
 //     XOR-swizzled by kswz(r), so that an A-operand read spans all banks; V in the unit order
@@ -43,8 +47,10 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kT = 16;            // query tokens per workgroup
-constexpr int kWaves = 8;         // waves per workgroup (tokens per wave = kT / kWaves)
+constexpr int kT = 16;            // query tokens per workgroup of the gradient and window forms
+constexpr int kWaves = 8;         // their waves per workgroup (tokens per wave = kT / kWaves)
+constexpr int kTF = 16;           // query tokens per workgroup of the sparse forward
+constexpr int kWavesF = 8;        // its waves (two per SIMD, 2 tokens each)
 constexpr bool kRounds = true;    // launch items in rounds of one workgroup per CU
 constexpr int kMaxUnion = 2048;   // reachable blocks per tile handled by this kernel
 constexpr float kLazy = 8.f;      // log2 headroom before the running max is moved
@@ -176,19 +182,13 @@ __device__ __forceinline__ int kswz(int row) {
   else return ((row >> 2) & 6) | ((row >> 1) & 1);
 }
 
-// Number of TPW-bit token groups (waves) with any bit set in a 16-bit token mask.
-template <int TPW>
+// Number of waves (groups of TPW consecutive token bits) with any bit set in a token mask.
+template <int TPW, int NW>
 __device__ __forceinline__ int count_wave_groups(uint32_t m) {
-  if constexpr (TPW == 1) {
-    return __builtin_popcount(m);
-  } else if constexpr (TPW == 2) {
-    return __builtin_popcount((m | (m >> 1)) & 0x5555u);
-  } else {
-    static_assert(TPW == 4, "tokens per wave");
-    m |= m >> 1;
-    m |= m >> 2;
-    return __builtin_popcount(m & 0x1111u);
-  }
+  int n = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) n += ((m >> (TPW * w)) & ((1u << TPW) - 1u)) != 0u;
+  return n;
 }
 
 // BWD = false: the attention itself (writes out, lse).  BWD = true: dQ for upstream gradient
@@ -196,7 +196,9 @@ __device__ __forceinline__ int count_wave_groups(uint32_t m) {
 // holds V in the same A-operand order as K, and K's transposing reads come from K's own copy.
 // WIN = true (forward only): sliding-window attention over keys pos - g.window < j <= pos; the
 // blocks come from the positions instead of idx.
-template <int D, int G, int NS, int NW, int TPW, bool BWD, bool WIN = false>
+// ORD: stream the union in the order of the waves' normalised progress instead of ascending
+// block order.
+template <int D, int G, int NS, int NW, int TPW, bool BWD, bool WIN = false, bool ORD = false>
 __global__ void __launch_bounds__(64 * NW, 1)
 attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
           const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
@@ -208,10 +210,14 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int MAT = 64 * D * 2;            // bytes of one 64-key matrix
   constexpr int NTHR = 64 * NW;
-  static_assert(TPW * NW == kT, "tile = waves x tokens per wave");
+  constexpr int T = NW * TPW;                // query tokens of the tile
+  static_assert(T <= 32 && 32 % T != 1, "tile of at most 32 tokens");
+  constexpr int MPW = (T & (T - 1)) == 0 ? 32 / T : 1;  // token masks per bitmap word
+  constexpr uint32_t TMASK = T == 32 ? 0xFFFFFFFFu : (1u << T) - 1u;
   __shared__ __attribute__((aligned(16))) unsigned char ring[NS][2][MAT];
-  __shared__ uint32_t bitmap[kMaxUnion / 2];
-  __shared__ uint32_t ulist[kMaxUnion];
+  __shared__ uint32_t bitmap[kMaxUnion / MPW];
+  __shared__ uint32_t umask[kMaxUnion];      // union list: token mask of entry u
+  __shared__ uint16_t ublk[kMaxUnion];       //             its block index
   __shared__ int wave_tot[NW];
   __shared__ int ready[NS];
   __shared__ int done[NS];
@@ -225,8 +231,8 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   const int kvh = item / n_tiles;
   const int tile = item - kvh * n_tiles;
   const int b = find_seq(t, tile);
-  const int r0 = (tile - t.work_prefix[b]) * kT;
-  const int nq = min(kT, t.q_len[b] - r0);
+  const int r0 = (tile - t.work_prefix[b]) * T;
+  const int nq = min(T, t.q_len[b] - r0);
   const int row0 = t.q_start[b] + r0;
   const int pos0 = t.q_pos0[b] + r0;
   const int kv0 = t.kv_start[b];
@@ -241,7 +247,7 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   const int Hq = g.Hq, Hkv = g.Hkv;
 
   // ---- union of the tile's selected blocks
-  for (int e = tid; e < (nbt + 1) / 2; e += NTHR) bitmap[e] = 0u;
+  for (int e = tid; e < (nbt + MPW - 1) / MPW; e += NTHR) bitmap[e] = 0u;
   __syncthreads();
   if constexpr (WIN) {
     // token tok needs the blocks meeting [pos - window + 1, pos]
@@ -252,13 +258,13 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
         const int pos = pos0 + tok;
         if (64 * blk <= pos && 64 * blk + 63 > pos - g.window) m |= 1u << tok;
       }
-      if (m != 0u) atomicOr(&bitmap[blk >> 1], m << (16 * (blk & 1)));
+      if (m != 0u) atomicOr(&bitmap[blk / MPW], m << (T * (blk % MPW)));
     }
   } else {
     for (int e = tid; e < nq * g.topk; e += NTHR) {
       const int tok = e / g.topk;
       const int blk = idx[(static_cast<size_t>(row0 + tok) * Hkv + kvh) * g.topk + (e - tok * g.topk)];
-      if (blk >= 0) atomicOr(&bitmap[blk >> 1], (1u << tok) << (16 * (blk & 1)));
+      if (blk >= 0) atomicOr(&bitmap[blk / MPW], (1u << tok) << (T * (blk % MPW)));
     }
   }
   __syncthreads();
@@ -271,7 +277,7 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
       const int blk = b0 + e;
-      m8[e] = blk < nbt ? (bitmap[blk >> 1] >> (16 * (blk & 1))) & 0xFFFFu : 0u;
+      m8[e] = blk < nbt ? (bitmap[blk / MPW] >> (T * (blk % MPW))) & TMASK : 0u;
       cnt += m8[e] != 0u;
     }
     int incl = cnt;
@@ -286,12 +292,87 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
     for (int ww = 0; ww < w; ++ww) base += wave_tot[ww];
 #pragma unroll
     for (int e = 0; e < KPT; ++e)
-      if (m8[e] != 0u) ulist[base++] = (static_cast<uint32_t>(b0 + e) << 16) | m8[e];
+      if (m8[e] != 0u) {
+        umask[base] = m8[e];
+        ublk[base] = static_cast<uint16_t>(b0 + e);
+        ++base;
+      }
   }
   __syncthreads();
   int n_union = 0;
 #pragma unroll
   for (int ww = 0; ww < NW; ++ww) n_union += wave_tot[ww];
+
+  if constexpr (ORD) {
+    // Stream order: merge the waves' lists of needed blocks by normalised progress, so that
+    // every stretch of the stream holds about as much work for each wave.  Entry u needed by
+    // wave w as its r-th of n_w blocks gets the key (r + 1/2) / n_w; an entry takes the largest
+    // key over its waves, ties by block order.  Sorted (bitonic) in the ring's memory, which is
+    // free until staging starts.
+    uint32_t* skey = reinterpret_cast<uint32_t*>(&ring[0][0][0]);
+    int npow2 = 1;
+    while (npow2 < n_union) npow2 <<= 1;
+    for (int e = tid; e < npow2; e += NTHR) skey[e] = e < n_union ? 0u : 0xFFFFFFFFu;
+    __syncthreads();
+    {
+      const uint32_t wbits = ((1u << TPW) - 1u) << (TPW * w);
+      int n_w = 0;
+      for (int base = 0; base < n_union; base += 64) {
+        const bool nd = base + lane < n_union && (umask[base + lane] & wbits) != 0u;
+        n_w += __builtin_popcountll(__ballot(nd));
+      }
+      int rank = 0;
+      for (int base = 0; base < n_union; base += 64) {
+        const int u = base + lane;
+        const bool nd = u < n_union && (umask[u] & wbits) != 0u;
+        const unsigned long long bal = __ballot(nd);
+        if (nd) {
+          const int r = rank + __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+          const uint32_t key = static_cast<uint32_t>(((2u * r + 1u) << 19) / static_cast<uint32_t>(n_w));
+          atomicMax(&skey[u], (key << 11) | static_cast<uint32_t>(u));
+        }
+        rank += __builtin_popcountll(bal);
+      }
+    }
+    __syncthreads();
+    for (int kk = 2; kk <= npow2; kk <<= 1) {
+      for (int j = kk >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < npow2; i += NTHR) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const uint32_t a = skey[i], c = skey[ixj];
+            if ((a > c) == ((i & kk) == 0)) {
+              skey[i] = c;
+              skey[ixj] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    constexpr int EPT = kMaxUnion / NTHR;
+    uint32_t pm[EPT];
+    uint16_t pb[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int i = tid + e * NTHR;
+      if (i < n_union) {
+        const int u = static_cast<int>(skey[i] & 2047u);
+        pm[e] = umask[u];
+        pb[e] = ublk[u];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int i = tid + e * NTHR;
+      if (i < n_union) {
+        umask[i] = pm[e];
+        ublk[i] = pb[e];
+      }
+    }
+    __syncthreads();
+  }
 
   // ---- staging.  global_load_lds writes lane l's 16 bytes at LDS unit base+l, and each lane
   // picks its own source, so both matrices are stored in the order their readers want:
@@ -321,7 +402,7 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   const int kr_lane = lane / CPR;
   const int kp_lane = lane % CPR;
   auto produce = [&](int u, int slot, int j0, int dj) {
-    const int key0 = __builtin_amdgcn_readfirstlane(static_cast<int>(ulist[u] >> 16)) * 64;
+    const int key0 = __builtin_amdgcn_readfirstlane(static_cast<int>(ublk[u])) * 64;
     const bool tail = key0 + 64 > kv_len;
     const uint16_t* kb = kbase + static_cast<size_t>(key0) * rowstride;
     const uint16_t* vb = vbase + static_cast<size_t>(key0) * rowstride;
@@ -440,16 +521,17 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
       BWD ? ring_lds + 256 * ((c16 & 3) >> 1) + 64 * q4 + 16 * (c16 >> 2) + 8 * (c16 & 1)
           : ring_lds + MAT + 16 * (8 * q4 + 2 * (c16 >> 2) + ((c16 & 3) >> 1)) + 8 * (c16 & 1);
 
-  // ---- main loop.  Each wave walks the union list in order and works only on blocks its tokens
-  // chose.  Slot u % NS holds block u once ready[slot] == u.  The last wave to finish a block
+  // ---- main loop.  Each wave walks the union list in stream order and works only on blocks
+  // its tokens chose.  Slot u % NS holds stream entry u once ready[slot] == u.  The last wave to finish a block
   // (counted in done[slot] against the number of waves that need it) refills the slot with block
   // u + NS and publishes it after its loads have landed: right away if it is about to wait for a
   // block itself, otherwise after its next block of work.  Every wait is bounded.
-  int pending = -1;
+  int pending = -1;       // stream entry this wave loaded and has not published yet
   bool stalled = false;
   // The wave reads 64 list entries at a time and jumps straight to the blocks its tokens chose.
   for (int ubase = 0; ubase < n_union && !stalled; ubase += 64) {
-    const uint32_t chunk = ubase + lane < n_union ? ulist[ubase + lane] : 0u;
+    const uint32_t chunk = ubase + lane < n_union ? umask[ubase + lane] : 0u;
+    const int chunk_blk = ubase + lane < n_union ? static_cast<int>(ublk[ubase + lane]) : 0;
     unsigned long long todo = __ballot(((chunk >> (TPW * w)) & ((1u << TPW) - 1u)) != 0u);
    while (todo != 0ull) {
     const int bit = __builtin_ctzll(todo);
@@ -472,7 +554,7 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
       if (stalled) break;
     }
     asm volatile("" ::: "memory");
-    const int key0 = static_cast<int>(ent >> 16) * 64;
+    const int key0 = __builtin_amdgcn_readlane(chunk_blk, bit) * 64;
     const uint32_t slot_off = static_cast<uint32_t>(slot) * (2 * MAT);
     const lds_bf16x8* Kp = (const lds_bf16x8*)(uintptr_t)(k_lane + slot_off);
     const uint32_t vaddr = v_lane + slot_off;
@@ -639,8 +721,8 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
       pending = -1;
     }
     // done accounting; the last of the block's waves refills the slot
-    const uint32_t mk = ent & 0xFFFFu;
-    const int needers = count_wave_groups<TPW>(mk);
+    const uint32_t mk = ent;
+    const int needers = count_wave_groups<TPW, NW>(mk);
     int old = 0;
     if (lane == 0) old = atomicAdd(&done[slot], 1);
     old = __shfl(old, 0);
@@ -729,13 +811,25 @@ int device_cus() {
   return n;
 }
 
-// work_prefix of `t` must count tiles of 16 query rows per sequence.  Items are launched in
-// rounds of one workgroup per compute unit, so that the workgroups sharing an XCD start
-// together on neighbouring tiles and walk the same KV blocks at the same time (their L2 then
-// serves each block to all of them).
-hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, const void* k,
+// The table with work_prefix over tiles of `rows` query rows per sequence.
+SeqTable tile_table(const SeqTable& t, int rows) {
+  SeqTable r = t;
+  int acc = 0;
+  for (int b = 0; b < t.n; ++b) {
+    r.work_prefix[b] = acc;
+    acc += (t.q_len[b] + rows - 1) / rows;
+  }
+  r.work_prefix[t.n] = acc;
+  return r;
+}
+
+// Items are launched in rounds of one workgroup per compute unit, so that the workgroups
+// sharing an XCD start together on neighbouring tiles and walk the same KV blocks at the same
+// time (their L2 then serves each block to all of them).  The forward runs tiles of kTF rows.
+hipError_t launch_attn_tile(const Geom& g, const SeqTable& t_rows, const void* q, const void* k,
                             const void* v, const int32_t* idx, void* out, float* lse,
                             hipStream_t stream) {
+  const SeqTable t = tile_table(t_rows, kTF);
   const int n_items = t.work_prefix[t.n] * g.Hkv;
   if (n_items == 0) return hipSuccess;
   const int round = kRounds ? (device_cus() / 8) * 8 : (n_items + 7) / 8 * 8;
@@ -747,8 +841,9 @@ hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, con
     const int grid = std::min(round, (n_items - base + 7) / 8 * 8);
 #define INFLLM2_TILE_CASE(DD, GG, NS)                                                         \
   if (g.d == DD && g.G == GG) {                                                               \
-    hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWaves, kT / kWaves, false>), dim3(grid),       \
-                       dim3(64 * kWaves), 0, stream, g, t, qq, kk, vv, idx, oo, lse, n_items, \
+    hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWavesF, kTF / kWavesF, false, false, true>),   \
+                       dim3(grid),                                                            \
+                       dim3(64 * kWavesF), 0, stream, g, t, qq, kk, vv, idx, oo, lse, n_items,\
                        base, nullptr, nullptr, nullptr, nullptr);                             \
     const hipError_t e = hipGetLastError();                                                   \
     if (e != hipSuccess) return e;                                                            \
@@ -764,13 +859,14 @@ hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, con
   return hipSuccess;
 }
 
-// Gradient of the queries for the same tiles (work_prefix counts tiles of 16 rows): dout is the
+// Gradient of the queries (tiles of kT rows; `t_rows` counts query rows): dout is the
 // upstream gradient of out, lse the forward's natural-log statistics and delta[row, head] =
 // dout . out.  Writes dq (fp32, [row, Hq, d]) for every row of every sequence.
-hipError_t launch_attn_tile_dq(const Geom& g, const SeqTable& t, const void* q, const void* k,
+hipError_t launch_attn_tile_dq(const Geom& g, const SeqTable& t_rows, const void* q, const void* k,
                                const void* v, const int32_t* idx, const void* dout,
                                const float* lse, const float* delta, float* dq,
                                hipStream_t stream) {
+  const SeqTable t = tile_table(t_rows, kT);
   const int n_items = t.work_prefix[t.n] * g.Hkv;
   if (n_items == 0) return hipSuccess;
   const int round = kRounds ? (device_cus() / 8) * 8 : (n_items + 7) / 8 * 8;
@@ -782,7 +878,8 @@ hipError_t launch_attn_tile_dq(const Geom& g, const SeqTable& t, const void* q, 
     const int grid = std::min(round, (n_items - base + 7) / 8 * 8);
 #define INFLLM2_DQ_CASE(DD, GG, NS)                                                           \
   if (g.d == DD && g.G == GG) {                                                               \
-    hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWaves, kT / kWaves, true>), dim3(grid),        \
+    hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWaves, kT / kWaves, true, false, true>),       \
+                       dim3(grid),                                                            \
                        dim3(64 * kWaves), 0, stream, g, t, qq, kk, vv, idx, nullptr, nullptr, \
                        n_items, base, dd, lse, delta, dq);                                    \
     const hipError_t e = hipGetLastError();                                                   \
@@ -799,8 +896,10 @@ hipError_t launch_attn_tile_dq(const Geom& g, const SeqTable& t, const void* q, 
   return hipSuccess;
 }
 
-hipError_t launch_attn_tile_window(const Geom& g, const SeqTable& t, const void* q, const void* k,
-                                   const void* v, void* out, float* lse, hipStream_t stream) {
+hipError_t launch_attn_tile_window(const Geom& g, const SeqTable& t_rows, const void* q,
+                                   const void* k, const void* v, void* out, float* lse,
+                                   hipStream_t stream) {
+  const SeqTable t = tile_table(t_rows, kT);
   const int n_items = t.work_prefix[t.n] * g.Hkv;
   if (n_items == 0) return hipSuccess;
   const int round = kRounds ? (device_cus() / 8) * 8 : (n_items + 7) / 8 * 8;

@@ -95,16 +95,17 @@ hipError_t launch_topk(const Geom& g, const SeqTable& t, const float* scores, in
 hipError_t launch_attn(const Geom& g, int dtype, const SeqTable& t, const void* q,
                        const void* k, const void* v, const int32_t* idx, int splits,
                        void* out, float* lse, float* part, hipStream_t stream);
-// Tiled prefill attention (tiles of 16 query rows sharing staged K/V blocks).
+// Tiled prefill attention (tiles of consecutive query rows sharing staged K/V blocks).  The
+// three tile launchers take work_prefix over query rows and form their own tiles.
 bool attn_tile_supported(const Geom& g, int dtype, const SeqTable& t);
 hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, const void* k,
                             const void* v, const int32_t* idx, void* out, float* lse,
                             hipStream_t stream);
-// Sliding-window attention by the tile kernel (work_prefix over tiles of 16 rows; g.window >= 1):
+// Sliding-window attention by the tile kernel (g.window >= 1):
 // the blocks each tile needs follow from the positions, no index array.
 hipError_t launch_attn_tile_window(const Geom& g, const SeqTable& t, const void* q, const void* k,
                                    const void* v, void* out, float* lse, hipStream_t stream);
-// Gradient of the queries by the tile kernel (work_prefix over tiles of 16 rows); delta[row, h]
+// Gradient of the queries by the tile kernel; delta[row, h]
 // = dout . out.  Writes dq as float32 [row, Hq, d].
 hipError_t launch_attn_tile_dq(const Geom& g, const SeqTable& t, const void* q, const void* k,
                                const void* v, const int32_t* idx, const void* dout,
