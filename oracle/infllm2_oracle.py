@@ -86,9 +86,30 @@ def num_kernels(length: int, kernel_size: int, kernel_stride: int) -> int:
     return (length - kernel_size) // kernel_stride + 1
 
 
+def _storage_midpoint(x: float, dtype: str) -> bool:
+    """Whether x lies exactly halfway between two neighbouring values of the storage format."""
+    if x == 0.0 or not np.isfinite(x):
+        return False
+    m, e = np.frexp(x)
+    t = m * 2.0 ** (_significand_bits(dtype) + 1)     # exact: a power-of-two scaling
+    return float(t).is_integer() and int(t) % 2 == 1
+
+
+def _toward(x: float, exact: Fraction, dtype: str) -> float:
+    """x, the float64 nearest to `exact`, moved one float64 step toward `exact` when x is a
+    storage midpoint that `exact` is not: rounding the result to the storage format then gives
+    the rounding of `exact` itself, not of x (no double rounding)."""
+    if _storage_midpoint(x, dtype) and Fraction(x) != exact:
+        return float(np.nextafter(x, np.inf if exact > x else -np.inf))
+    return x
+
+
 def exact_window_means(keys: np.ndarray, kernel_size: int, kernel_stride: int,
                        c_lo: int, c_hi: int, dtype: str) -> np.ndarray:
-    """Exact mean of keys[s*c : s*c+w] for c in [c_lo, c_hi), as float64.
+    """Mean of keys[s*c : s*c+w] for c in [c_lo, c_hi), as the float64 nearest to the exact
+    mean, except that a float64 landing exactly halfway between two storage values that the
+    exact mean is not is moved one float64 step toward it (so that one rounding of the result
+    to the storage format is the rounding of the exact mean).
 
     The window sum is taken with numpy in float64 and certified exact: every value is a
     multiple of 2**(e_min - p) (p = significand bits of the input format, e_min the smallest
@@ -112,13 +133,23 @@ def exact_window_means(keys: np.ndarray, kernel_size: int, kernel_stride: int,
         _, ex = np.frexp(np.where(win == 0.0, np.inf, win))
         ex = np.where(win == 0.0, 10_000, ex).min(axis=1)   # smallest exponent per window
         unit_ok = (absum == 0.0) | (np.log2(np.maximum(absum, 1e-300)) < 52 + ex - p)
+        means = sums / w
+        # a mean that lands on a storage midpoint: settle the side with the exact value (the
+        # division by w may have rounded onto it)
+        mant, _ = np.frexp(means)
+        t = mant * 2.0 ** (_significand_bits(dtype) + 1)
+        on_mid = unit_ok & (means != 0.0) & (t == np.floor(t)) & (np.mod(t, 2.0) == 1.0)
+        for idx in np.argwhere(on_mid):
+            key = tuple(int(x) for x in idx)
+            means[key] = _toward(float(means[key]), Fraction(float(sums[key])) / w, dtype)
         if not np.all(unit_ok):
             bad = np.argwhere(~unit_ok)
             for idx in bad:
                 c = int(idx[0]); rem = tuple(int(t) for t in idx[1:])
                 vals = [Fraction(float(win[(c,) + (t,) + rem])) for t in range(w)]
-                sums[(c,) + rem] = float(sum(vals, Fraction(0)))
-        out[a - c_lo:b - c_lo] = sums / w
+                exact = sum(vals, Fraction(0)) / w
+                means[(c,) + rem] = _toward(float(exact), exact, dtype)
+        out[a - c_lo:b - c_lo] = means
     return out
 
 

@@ -84,6 +84,27 @@ def test_window_sum_certificate_falls_back_to_exact_sum():
     assert m[0, 0, 0] == 2.0 ** -40 / 32
 
 
+def test_window_mean_rounds_once_from_the_exact_value():
+    """Rounding the exact mean, not a float64 approximation of it.  Window of w = 32 with keys
+    1, 2^-8 and 2^-80 (all bf16 values) and zeros: the exact mean (1 + 2^-8 + 2^-80) / 32 lies
+    just above the bf16 midpoint (1 + 2^-8) / 32 of its neighbours 2^-5 and (1 + 2^-7) 2^-5, so
+    it rounds up, while its nearest float64 is the midpoint itself and would round to the even
+    neighbour 2^-5.  Likewise for w = 6, where the division itself rounds: keys 4, 2, 2^-6,
+    2^-7, 2^-58, 2^-59 have the exact mean 1 + 2^-8 + 2^-60 (just above a midpoint: up), and with
+    the last two keys negated 1 + 2^-8 - 2^-60 (just below: down)."""
+    K = np.zeros((32, 1, 1))
+    K[0], K[1], K[2] = 1.0, 2.0 ** -8, 2.0 ** -80
+    got = orc.compress_kernels(K, 32, 16, "bf16")
+    assert got[0, 0, 0] == (1 + 2.0 ** -7) * 2.0 ** -5
+    K6 = np.array([4.0, 2.0, 2.0 ** -6, 2.0 ** -7, 2.0 ** -58, 2.0 ** -59]).reshape(6, 1, 1)
+    assert orc.compress_kernels(K6, 6, 6, "bf16")[0, 0, 0] == 1 + 2.0 ** -7
+    K6[4:] *= -1
+    assert orc.compress_kernels(K6, 6, 6, "bf16")[0, 0, 0] == 1.0
+    # a mean that is exactly a midpoint still ties to even
+    K6 = np.array([4.0, 2.0, 2.0 ** -6, 2.0 ** -7, 0.0, 0.0]).reshape(6, 1, 1)
+    assert orc.compress_kernels(K6, 6, 6, "bf16")[0, 0, 0] == 1.0
+
+
 def test_incremental_kernels_equal_full_compress():
     """P9: appending tokens one at a time creates exactly the kernels of the full pass."""
     p = synth.config_params("varlen")
