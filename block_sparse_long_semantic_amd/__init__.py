@@ -1,7 +1,7 @@
 """InfLLM v2 block-sparse attention on MI355X (gfx950): thin Python binding of libinfllm2.
 
 Every compute step runs in the HIP library; this package only marshals arguments (device
-pointers of torch tensors, the current HIP stream, host-side sequence metadata).  Importing
+pointers of torch tensors, the current HIP stream, the sequence metadata's device copy).  Importing
 it loads the shared library and fails loudly if it has not been built
 (`python -m block_sparse_long_semantic_amd.build`).
 """

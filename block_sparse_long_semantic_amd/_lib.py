@@ -46,8 +46,11 @@ _I32P = ctypes.POINTER(ctypes.c_int32)
 
 
 class _CSeqs(ctypes.Structure):
-    _fields_ = [("num_seqs", ctypes.c_int32), ("q_start", _I64P), ("q_len", _I32P),
-                ("q_pos0", _I32P), ("kv_start", _I64P), ("kv_len", _I32P), ("kc_start", _I64P)]
+    _fields_ = [("num_seqs", ctypes.c_int32), ("max_q_len", ctypes.c_int32),
+                ("max_kv_len", ctypes.c_int32), ("q_rows", ctypes.c_int32),
+                ("q_start", ctypes.c_void_p), ("q_len", ctypes.c_void_p),
+                ("q_pos0", ctypes.c_void_p), ("kv_start", ctypes.c_void_p),
+                ("kv_len", ctypes.c_void_p), ("kc_start", ctypes.c_void_p)]
 
 
 _lib = None
@@ -57,14 +60,14 @@ def _declare(lib):
     P, S = ctypes.POINTER(_CParams), ctypes.POINTER(_CSeqs)
     vp, st = ctypes.c_void_p, ctypes.c_int
     sig = {
-        "infllm2_compress_kernels": (st, [P, S, vp, _I32P, vp, vp]),
+        "infllm2_compress_kernels": (st, [P, S, vp, vp, vp, vp]),
         "infllm2_block_scores": (st, [P, S, vp, vp, vp, ctypes.c_int32, vp]),
         "infllm2_topk_select": (st, [P, S, vp, ctypes.c_int32, vp, vp]),
         "infllm2_sparse_attn_prefill": (st, [P, S, vp, vp, vp, vp, vp, vp, vp]),
         "infllm2_decode_workspace_size": (ctypes.c_size_t, [P, ctypes.c_int32, ctypes.c_int32]),
         "infllm2_sparse_attn_decode": (st, [P, S, vp, vp, vp, vp, ctypes.c_int32, vp,
                                             ctypes.c_size_t, vp, vp, vp]),
-        "infllm2_decode_step": (st, [P, S, vp, vp, vp, vp, _I32P, vp, ctypes.c_int32, vp,
+        "infllm2_decode_step": (st, [P, S, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp,
                                      ctypes.c_int32, vp, ctypes.c_size_t, vp, vp, vp]),
         "infllm2_sliding_window_attn": (st, [P, S, ctypes.c_int32, vp, vp, vp, vp, vp, vp]),
         "infllm2_backward_workspace_size": (ctypes.c_size_t, [P, S]),
@@ -147,9 +150,16 @@ class Params:
 
 
 class Seqs:
-    """Host-side sequence metadata (see the header for the meaning of every field)."""
+    """Sequence metadata (the header gives every field's meaning): the per-sequence arrays, kept
+    on the host and copied to the device (one packed buffer per device) where the library's
+    kernels read them, and the host bounds num_seqs, max_q_len, max_kv_len and q_rows, which
+    default to the arrays' own maxima.  Seqs.on_device() wraps arrays that already live on the
+    device (no host copy): the caller may rewrite them there between calls, e.g. for the next
+    decoding step of a captured graph, within the bounds."""
 
-    def __init__(self, q_start, q_len, q_pos0, kv_start, kv_len, kc_start=None):
+    def __init__(self, q_start, q_len, q_pos0, kv_start, kv_len, kc_start=None, *,
+                 max_q_len: Optional[int] = None, max_kv_len: Optional[int] = None,
+                 q_rows: Optional[int] = None):
         self.q_start = np.ascontiguousarray(q_start, dtype=np.int64)
         self.q_len = np.ascontiguousarray(q_len, dtype=np.int32)
         self.q_pos0 = np.ascontiguousarray(q_pos0, dtype=np.int32)
@@ -160,14 +170,46 @@ class Seqs:
         for a in (self.q_start, self.q_pos0, self.kv_start, self.kv_len):
             if len(a) != n:
                 raise ValueError("sequence metadata arrays differ in length")
+        if self.kc_start is not None and len(self.kc_start) != n:
+            raise ValueError("sequence metadata arrays differ in length")
+        self.max_q_len = int(self.q_len.max()) if max_q_len is None and n else int(max_q_len or 0)
+        self.max_kv_len = int(self.kv_len.max()) if max_kv_len is None and n else int(max_kv_len or 0)
+        self.q_rows = (int((self.q_start + self.q_len).max()) if q_rows is None and n
+                       else int(q_rows or 0))
+        self._n = n
+        self._dev = {}          # device -> (packed buffer, pointers)
+        self._device_arrays = None
+
+    @staticmethod
+    def on_device(q_start, q_len, q_pos0, kv_start, kv_len, kc_start, *, max_q_len: int,
+                  max_kv_len: int, q_rows: int) -> "Seqs":
+        """Metadata given as device tensors (int64 starts, int32 lengths and positions; kc_start
+        may be None) with explicit host bounds."""
+        torch = _torch()
+        want = [(q_start, torch.int64), (q_len, torch.int32), (q_pos0, torch.int32),
+                (kv_start, torch.int64), (kv_len, torch.int32)]
+        if kc_start is not None:
+            want.append((kc_start, torch.int64))
+        n = int(q_len.numel())
+        for t, dt in want:
+            if t.device.type != "cuda" or t.dtype != dt or not t.is_contiguous() or t.numel() != n:
+                raise ValueError("device metadata must be contiguous device tensors of num_seqs "
+                                 "entries (int64 starts, int32 lengths and positions)")
+        obj = Seqs.__new__(Seqs)
+        obj.q_start = obj.q_len = obj.q_pos0 = obj.kv_start = obj.kv_len = obj.kc_start = None
+        obj.max_q_len, obj.max_kv_len, obj.q_rows = int(max_q_len), int(max_kv_len), int(q_rows)
+        obj._n = n
+        obj._dev = {}
+        obj._device_arrays = (q_start, q_len, q_pos0, kv_start, kv_len, kc_start)
+        return obj
 
     @property
     def num_seqs(self) -> int:
-        return int(len(self.q_len))
+        return int(self._n)
 
     @property
     def total_q_rows(self) -> int:
-        return int(self.q_len.sum())
+        return int(self.q_rows)
 
     @staticmethod
     def packed_prefill(seq_lens: Sequence[int], kc_start: Optional[Sequence[int]] = None,
@@ -187,13 +229,53 @@ class Seqs:
         return Seqs(np.arange(n), np.ones(n), kv - 1, np.arange(n) * max_len, kv,
                     np.arange(n) * max_kernels)
 
-    def c(self) -> _CSeqs:
-        kc = self.kc_start
-        return _CSeqs(self.num_seqs,
-                      self.q_start.ctypes.data_as(_I64P), self.q_len.ctypes.data_as(_I32P),
-                      self.q_pos0.ctypes.data_as(_I32P), self.kv_start.ctypes.data_as(_I64P),
-                      self.kv_len.ctypes.data_as(_I32P),
-                      kc.ctypes.data_as(_I64P) if kc is not None else ctypes.cast(None, _I64P))
+    def _device_pointers(self, device):
+        if self._device_arrays is not None:
+            return [None if t is None else t.data_ptr() for t in self._device_arrays]
+        key = str(device)
+        if key not in self._dev:
+            torch = _torch()
+            n = self._n
+            parts = [self.q_start, self.kv_start,
+                     self.kc_start if self.kc_start is not None else np.zeros(n, np.int64),
+                     self.q_len, self.q_pos0, self.kv_len]
+            host = np.concatenate([a.view(np.uint8) for a in parts])
+            buf = torch.from_numpy(host).to(device)
+            base = buf.data_ptr()
+            offs = [0, 8 * n, 16 * n, 24 * n, 28 * n, 32 * n]
+            ptrs = [base + o for o in offs]
+            # order of the C struct: q_start, q_len, q_pos0, kv_start, kv_len, kc_start
+            self._dev[key] = (buf, [ptrs[0], ptrs[3], ptrs[4], ptrs[1], ptrs[5],
+                                    ptrs[2] if self.kc_start is not None else None])
+        return self._dev[key][1]
+
+    def c(self, device=None) -> _CSeqs:
+        """The C struct.  With a device: pointers to the device copies (made once per device).
+        Without one, host pointers stand in: only the host bounds may then be used (workspace
+        sizes, argument checks); no launch may be given such a struct."""
+        if device is not None:
+            p = self._device_pointers(device)
+        elif self._device_arrays is not None:
+            p = self._device_pointers(None)
+        else:
+            kc = self.kc_start
+            p = [self.q_start.ctypes.data, self.q_len.ctypes.data, self.q_pos0.ctypes.data,
+                 self.kv_start.ctypes.data, self.kv_len.ctypes.data,
+                 kc.ctypes.data if kc is not None else None]
+        return _CSeqs(self.num_seqs, self.max_q_len, self.max_kv_len, self.q_rows, *p)
+
+
+def _device_ints(a, device, name):
+    """A device int32 array: a device tensor as given, or a host array copied to the device."""
+    if a is None:
+        return None, None
+    torch = _torch()
+    if isinstance(a, torch.Tensor):
+        if a.device.type != "cuda" or a.dtype != torch.int32 or not a.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+        return a, ctypes.c_void_p(a.data_ptr())
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+    return t, ctypes.c_void_p(t.data_ptr())
 
 
 # ----------------------------------------------------------------------------- calls
@@ -240,11 +322,8 @@ def compress_kernels(params, seqs: Seqs, k, kernels, prev_kv_len=None, stream=No
     p = Params.from_any(params)
     lib = load_library()
     dt = _elem_dtype(p)
-    prev = None
-    if prev_kv_len is not None:
-        prev_arr = np.ascontiguousarray(prev_kv_len, dtype=np.int32)
-        prev = prev_arr.ctypes.data_as(_I32P)
-    cp, cs = p.c(), seqs.c()
+    keep, prev = _device_ints(prev_kv_len, k.device, "prev_kv_len")
+    cp, cs = p.c(), seqs.c(k.device)
     _check(lib.infllm2_compress_kernels(ctypes.byref(cp), ctypes.byref(cs), _ptr(k, "k", dt),
                                         prev, _ptr(kernels, "kernels", dt),
                                         _stream(stream, k.device)),
@@ -256,7 +335,7 @@ def block_scores(params, seqs: Seqs, q, kernels, scores, stream=None):
     lib = load_library()
     dt = _elem_dtype(p)
     torch = _torch()
-    cp, cs = p.c(), seqs.c()
+    cp, cs = p.c(), seqs.c(q.device)
     _check(lib.infllm2_block_scores(ctypes.byref(cp), ctypes.byref(cs), _ptr(q, "q", dt),
                                     _ptr(kernels, "kernels", dt),
                                     _ptr(scores, "scores", torch.float32, 3),
@@ -268,7 +347,7 @@ def topk_select(params, seqs: Seqs, scores, block_idx, stream=None):
     p = Params.from_any(params)
     lib = load_library()
     torch = _torch()
-    cp, cs = p.c(), seqs.c()
+    cp, cs = p.c(), seqs.c(scores.device)
     _check(lib.infllm2_topk_select(ctypes.byref(cp), ctypes.byref(cs),
                                    _ptr(scores, "scores", torch.float32, 3), int(scores.shape[2]),
                                    _ptr(block_idx, "block_idx", torch.int32),
@@ -281,7 +360,7 @@ def sparse_attn_prefill(params, seqs: Seqs, q, k, v, block_idx, out, lse=None, s
     lib = load_library()
     dt = _elem_dtype(p)
     torch = _torch()
-    cp, cs = p.c(), seqs.c()
+    cp, cs = p.c(), seqs.c(q.device)
     _check(lib.infllm2_sparse_attn_prefill(
         ctypes.byref(cp), ctypes.byref(cs), _ptr(q, "q", dt), _ptr(k, "k", dt), _ptr(v, "v", dt),
         _ptr(block_idx, "block_idx", torch.int32), _ptr(out, "out", dt),
@@ -302,7 +381,7 @@ def sparse_attn_decode(params, seqs: Seqs, q, k, v, block_idx, out, lse=None, nu
     lib = load_library()
     dt = _elem_dtype(p)
     torch = _torch()
-    cp, cs = p.c(), seqs.c()
+    cp, cs = p.c(), seqs.c(q.device)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr = _ptr(workspace, "workspace")
@@ -321,11 +400,8 @@ def decode_step_fused(params, seqs: Seqs, q, k_cache, v_cache, kernels, prev_kv_
     lib = load_library()
     dt = _elem_dtype(p)
     torch = _torch()
-    prev = None
-    if prev_kv_len is not None:
-        prev_arr = np.ascontiguousarray(prev_kv_len, dtype=np.int32)
-        prev = prev_arr.ctypes.data_as(_I32P)
-    cp, cs = p.c(), seqs.c()
+    keep, prev = _device_ints(prev_kv_len, q.device, "prev_kv_len")
+    cp, cs = p.c(), seqs.c(q.device)
     _check(lib.infllm2_decode_step(
         ctypes.byref(cp), ctypes.byref(cs), _ptr(q, "q", dt), _ptr(k_cache, "k_cache", dt),
         _ptr(v_cache, "v_cache", dt), _ptr(kernels, "kernels", dt), prev,
@@ -351,7 +427,7 @@ def sparse_attn_backward(params, seqs: Seqs, q, k, v, block_idx, out, lse, dout,
     dt = _elem_dtype(p)
     torch = _torch()
     f32 = torch.float32
-    cp, cs = p.c(), seqs.c()
+    cp, cs = p.c(), seqs.c(q.device)
     _check(lib.infllm2_sparse_attn_backward(
         ctypes.byref(cp), ctypes.byref(cs), _ptr(q, "q", dt), _ptr(k, "k", dt), _ptr(v, "v", dt),
         _ptr(block_idx, "block_idx", torch.int32), _ptr(out, "out", dt), _ptr(lse, "lse", f32),
@@ -366,7 +442,7 @@ def sliding_window_attn(params, seqs: Seqs, window: int, q, k, v, out, lse=None,
     lib = load_library()
     dt = _elem_dtype(p)
     torch = _torch()
-    cp, cs = p.c(), seqs.c()
+    cp, cs = p.c(), seqs.c(q.device)
     _check(lib.infllm2_sliding_window_attn(
         ctypes.byref(cp), ctypes.byref(cs), int(window), _ptr(q, "q", dt), _ptr(k, "k", dt),
         _ptr(v, "v", dt), _ptr(out, "out", dt),

@@ -95,54 +95,33 @@ infllm2_status check_params(const infllm2_params* p, Geom* g) {
   return INFLLM2_OK;
 }
 
-// Copies and checks the host sequence metadata.  need_kc: kc_start is required.
+// Checks the host bounds and the presence of the device arrays (their contents are the
+// kernels' to read).  need_kc: kc_start is required.
 infllm2_status build_table(const infllm2_seqs* s, const Geom& g, bool need_kc, SeqTable* t) {
+  (void)g;
   if (s == nullptr) return fail(INFLLM2_ERR_NULL, "seqs is NULL");
-  if (s->num_seqs < 1 || s->num_seqs > infllm2::kMaxSeqs)
-    return fail(INFLLM2_ERR_SHAPE, "num_seqs %d outside 1..%d", s->num_seqs, infllm2::kMaxSeqs);
+  if (s->num_seqs < 1) return fail(INFLLM2_ERR_SHAPE, "num_seqs %d below 1", s->num_seqs);
+  if (s->max_q_len < 0 || s->max_kv_len < 0 || s->q_rows < 0)
+    return fail(INFLLM2_ERR_SHAPE, "negative bound (max_q_len %d, max_kv_len %d, q_rows %d)",
+                s->max_q_len, s->max_kv_len, s->q_rows);
+  if (s->max_q_len > s->max_kv_len)
+    return fail(INFLLM2_ERR_SHAPE, "max_q_len %d exceeds max_kv_len %d (every query sees its own key)",
+                s->max_q_len, s->max_kv_len);
   if (!s->q_start || !s->q_len || !s->q_pos0 || !s->kv_start || !s->kv_len)
     return fail(INFLLM2_ERR_NULL, "a sequence metadata array is NULL");
   if (need_kc && !s->kc_start) return fail(INFLLM2_ERR_NULL, "kc_start is NULL");
-  memset(t, 0, sizeof(*t));
   t->n = s->num_seqs;
-  const int64_t lim = (int64_t{1} << 31) - 1;
-  for (int b = 0; b < s->num_seqs; ++b) {
-    const int64_t qs = s->q_start[b], ks = s->kv_start[b];
-    const int64_t kc = need_kc ? s->kc_start[b] : 0;
-    const int32_t ql = s->q_len[b], kl = s->kv_len[b], p0 = s->q_pos0[b];
-    if (qs < 0 || ks < 0 || kc < 0 || ql < 0 || kl < 0 || p0 < 0)
-      return fail(INFLLM2_ERR_SHAPE, "sequence %d: negative start, length or position", b);
-    if (static_cast<int64_t>(p0) + ql > kl)
-      return fail(INFLLM2_ERR_SHAPE, "sequence %d: q_pos0 (%d) + q_len (%d) exceeds kv_len (%d)",
-                  b, p0, ql, kl);
-    const int64_t nk = infllm2::num_kernels(kl, g.w, g.s);
-    if (qs + ql > lim || ks + kl > lim || kc + nk > lim)
-      return fail(INFLLM2_ERR_SHAPE, "sequence %d: row index beyond 2^31", b);
-    t->q_start[b] = static_cast<int32_t>(qs);
-    t->q_len[b] = ql;
-    t->q_pos0[b] = p0;
-    t->kv_start[b] = static_cast<int32_t>(ks);
-    t->kv_len[b] = kl;
-    t->kc_start[b] = static_cast<int32_t>(kc);
-  }
+  t->max_q_len = s->max_q_len;
+  t->max_kv_len = s->max_kv_len;
+  t->q_rows = s->q_rows;
+  t->q_start = s->q_start;
+  t->q_len = s->q_len;
+  t->q_pos0 = s->q_pos0;
+  t->kv_start = s->kv_start;
+  t->kv_len = s->kv_len;
+  t->kc_start = s->kc_start;
+  t->prev_kv_len = nullptr;
   return INFLLM2_OK;
-}
-
-// work_prefix over query rows
-void rows_prefix(SeqTable* t) {
-  int acc = 0;
-  for (int b = 0; b < t->n; ++b) {
-    t->work_prefix[b] = acc;
-    acc += t->q_len[b];
-  }
-  t->work_prefix[t->n] = acc;
-}
-
-int max_reachable_blocks(const SeqTable& t, int B) {
-  int m = 0;
-  for (int b = 0; b < t.n; ++b)
-    if (t.q_len[b] > 0) m = std::max(m, (t.q_pos0[b] + t.q_len[b] - 1) / B + 1);
-  return m;
 }
 
 int auto_splits(const Geom& g, int rows) {
@@ -186,19 +165,7 @@ infllm2_status infllm2_compress_kernels(const infllm2_params* params, const infl
   if (k == nullptr || kernels == nullptr) return fail(INFLLM2_ERR_NULL, "k or kernels is NULL");
   if (!aligned16(k) || !aligned16(kernels))
     return fail(INFLLM2_ERR_ALIGN, "k and kernels must be 16-byte aligned");
-  int acc = 0;
-  for (int b = 0; b < t.n; ++b) {
-    const int prev = prev_kv_len ? prev_kv_len[b] : 0;
-    if (prev < 0 || prev > t.kv_len[b])
-      return fail(INFLLM2_ERR_SHAPE, "sequence %d: prev_kv_len %d outside 0..kv_len (%d)", b, prev,
-                  t.kv_len[b]);
-    const int lo = infllm2::num_kernels(prev, g.w, g.s);
-    const int hi = infllm2::num_kernels(t.kv_len[b], g.w, g.s);
-    t.aux[b] = lo;
-    t.work_prefix[b] = acc;
-    acc += (hi - lo + 15) / 16;
-  }
-  t.work_prefix[t.n] = acc;
+  t.prev_kv_len = prev_kv_len;
   return hip_status(infllm2::launch_compress(g, params->dtype, t, k, kernels,
                                              static_cast<hipStream_t>(stream)),
                     "compress_kernels launch");
@@ -216,57 +183,15 @@ infllm2_status infllm2_block_scores(const infllm2_params* params, const infllm2_
     return fail(INFLLM2_ERR_NULL, "q, kernels or scores is NULL");
   if (!aligned16(q) || !aligned16(kernels) || !aligned16(scores))
     return fail(INFLLM2_ERR_ALIGN, "q, kernels and scores must be 16-byte aligned");
-  const int need = max_reachable_blocks(t, g.B);
+  const int need = infllm2::bound_blocks(t, g.B);
   if (nb_stride < need)
     return fail(INFLLM2_ERR_SHAPE, "nb_stride %d below the %d reachable blocks", nb_stride, need);
-  if (g.score_mode == 1) {
-    if (!infllm2::scores_softmax_mfma_supported(g, params->dtype)) {
-      rows_prefix(&t);
-      return hip_status(infllm2::launch_scores_softmax(g, params->dtype, t, q, kernels, scores,
-                                                       nb_stride, false,
-                                                       static_cast<hipStream_t>(stream)),
-                        "block_scores launch");
-    }
-    // few rows (decoding): every workgroup splits the kernels over its waves
-    long long tiles = 0;
-    const int full_rows = infllm2::scores_softmax_rows(g, false);
-    for (int b = 0; b < t.n; ++b) tiles += (t.q_len[b] + full_rows - 1) / full_rows;
-    const bool split = tiles * g.Hkv < 128;
-    const int rows_per = infllm2::scores_softmax_rows(g, split);
-    int acc = 0;
-    for (int b = 0; b < t.n; ++b) {
-      t.work_prefix[b] = acc;
-      acc += (t.q_len[b] + rows_per - 1) / rows_per;
-    }
-    t.work_prefix[t.n] = acc;
+  if (g.score_mode == 1)
     return hip_status(infllm2::launch_scores_softmax(g, params->dtype, t, q, kernels, scores,
-                                                     nb_stride, split,
-                                                     static_cast<hipStream_t>(stream)),
+                                                     nb_stride, static_cast<hipStream_t>(stream)),
                       "block_scores launch");
-  }
-  const bool mfma = params->dtype == INFLLM2_BF16 && g.B == 64 && g.w == 32 && g.s == 16 &&
-                    (g.d == 64 || g.d == 128);
-  int range_tiles = 0;
-  if (!mfma) {
-    rows_prefix(&t);
-  } else {
-    long long tiles64 = 0;
-    for (int b = 0; b < t.n; ++b) tiles64 += (t.q_len[b] + 63) / 64;
-    const bool decode_like = tiles64 * g.Hkv < 512;
-    range_tiles = decode_like ? 16 : (1 << 28);
-    if (decode_like) {
-      rows_prefix(&t);
-    } else {
-      int acc = 0;
-      for (int b = 0; b < t.n; ++b) {
-        t.work_prefix[b] = acc;
-        acc += (t.q_len[b] + 63) / 64;
-      }
-      t.work_prefix[t.n] = acc;
-    }
-  }
   return hip_status(infllm2::launch_scores(g, params->dtype, t, q, kernels, scores, nb_stride,
-                                           range_tiles, static_cast<hipStream_t>(stream)),
+                                           static_cast<hipStream_t>(stream)),
                     "block_scores launch");
 }
 
@@ -282,13 +207,12 @@ infllm2_status infllm2_topk_select(const infllm2_params* params, const infllm2_s
     return fail(INFLLM2_ERR_NULL, "scores or block_idx is NULL");
   if (!aligned16(scores) || !aligned16(block_idx))
     return fail(INFLLM2_ERR_ALIGN, "scores and block_idx must be 16-byte aligned");
-  const int need = max_reachable_blocks(t, g.B);
+  const int need = infllm2::bound_blocks(t, g.B);
   if (nb_stride < need)
     return fail(INFLLM2_ERR_SHAPE, "nb_stride %d below the %d reachable blocks", nb_stride, need);
   if (need > 4096)
     return fail(INFLLM2_ERR_UNSUPPORTED, "%d reachable blocks exceed 4096", need);
-  rows_prefix(&t);
-  return hip_status(infllm2::launch_topk(g, t, scores, nb_stride, need, block_idx,
+  return hip_status(infllm2::launch_topk(g, t, scores, nb_stride, block_idx,
                                          static_cast<hipStream_t>(stream)),
                     "topk_select launch");
 }
@@ -305,7 +229,6 @@ static infllm2_status attn_common(const infllm2_params* params, const infllm2_se
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(block_idx) ||
       !aligned16(out) || (lse && !aligned16(lse)))
     return fail(INFLLM2_ERR_ALIGN, "attention buffers must be 16-byte aligned");
-  rows_prefix(t);
   return INFLLM2_OK;
 }
 
@@ -344,9 +267,8 @@ infllm2_status infllm2_sliding_window_attn(const infllm2_params* params,
   if (!infllm2::attn_tile_supported(g, params->dtype, t))
     return fail(INFLLM2_ERR_UNSUPPORTED,
                 "sliding-window attention needs bf16, block_size 64, head_dim 64 or 128, group "
-                "size 8 or 16 and queries at positions below 2048 * 64");
+                "size 8 or 16 and max_kv_len at most 2048 * 64");
   g.window = window;
-  rows_prefix(&t);
   return hip_status(infllm2::launch_attn_tile_window(g, t, q, k, v, out, lse,
                                                      static_cast<hipStream_t>(stream)),
                     "sliding_window_attn launch");
@@ -379,7 +301,7 @@ infllm2_status infllm2_sparse_attn_decode(const infllm2_params* params, const in
   if (st != INFLLM2_OK) return st;
   if (num_splits < 0 || num_splits > g.topk)
     return fail(INFLLM2_ERR_SHAPE, "num_splits %d outside 0..topk", num_splits);
-  const int rows = t.work_prefix[t.n];
+  const int rows = t.q_rows;
   const int splits = decode_splits(g, params->dtype, rows, num_splits);
   const size_t need = infllm2::decode_workspace(g, rows, splits);
   if (splits > 1) {
@@ -404,39 +326,29 @@ infllm2_status infllm2_sparse_attn_decode(const infllm2_params* params, const in
                     "sparse_attn_decode combine launch");
 }
 
-// Backward metadata: work_prefix over rows, aux[b] = first global KV block of sequence b.
 static infllm2_status bwd_common(const infllm2_params* params, const infllm2_seqs* seqs, Geom* g,
-                                 SeqTable* t, int* n_blocks, int* q_rows) {
+                                 SeqTable* t) {
   infllm2_status st = check_params(params, g);
   if (st != INFLLM2_OK) return st;
   if ((st = build_table(seqs, *g, false, t)) != INFLLM2_OK) return st;
-  rows_prefix(t);
   if (!infllm2::attn_tile_supported(*g, params->dtype, *t))
     return fail(INFLLM2_ERR_UNSUPPORTED,
                 "backward needs bf16, block_size 64, head_dim 64 or 128, group size 8 or 16 and "
-                "at most 2048 reachable blocks per sequence");
-  long long nb = 0, qr = 0;
-  for (int b = 0; b < t->n; ++b) {
-    t->aux[b] = static_cast<int32_t>(nb);
-    nb += (t->kv_len[b] + g->B - 1) / g->B;
-    if (t->q_len[b] > 0) qr = std::max<long long>(qr, static_cast<long long>(t->q_start[b]) + t->q_len[b]);
-  }
+                "max_kv_len at most 2048 * 64");
   const long long lim = (1LL << 31) - 1;
-  if (nb * g->Hkv > lim || static_cast<long long>(t->work_prefix[t->n]) * g->Hkv * g->topk > lim)
+  const long long nb = static_cast<long long>(t->n) * infllm2::bound_blocks(*t, 64);
+  if (nb * g->Hkv > lim || static_cast<long long>(infllm2::bound_rows(*t)) * g->Hkv * g->topk > lim)
     return fail(INFLLM2_ERR_SHAPE, "backward index beyond 2^31 entries");
-  *n_blocks = static_cast<int>(nb);
-  if (infllm2::bwd_segments(*g, *t, *n_blocks) > lim)
+  if (infllm2::bwd_segments(*g, *t) > lim)
     return fail(INFLLM2_ERR_SHAPE, "backward index beyond 2^31 segments");
-  *q_rows = static_cast<int>(qr);
   return INFLLM2_OK;
 }
 
 size_t infllm2_backward_workspace_size(const infllm2_params* params, const infllm2_seqs* seqs) {
   Geom g;
   SeqTable t;
-  int nb = 0, qr = 0;
-  if (bwd_common(params, seqs, &g, &t, &nb, &qr) != INFLLM2_OK) return 0;
-  return infllm2::bwd_workspace(g, t, nb, qr);
+  if (bwd_common(params, seqs, &g, &t) != INFLLM2_OK) return 0;
+  return infllm2::bwd_workspace(g, t);
 }
 
 infllm2_status infllm2_sparse_attn_backward(const infllm2_params* params,
@@ -448,19 +360,18 @@ infllm2_status infllm2_sparse_attn_backward(const infllm2_params* params,
                                             size_t workspace_bytes, void* stream) {
   Geom g;
   SeqTable t;
-  int nb = 0, qr = 0;
-  infllm2_status st = bwd_common(params, seqs, &g, &t, &nb, &qr);
+  infllm2_status st = bwd_common(params, seqs, &g, &t);
   if (st != INFLLM2_OK) return st;
   if (!q || !k || !v || !block_idx || !out || !lse || !dout || !dq || !dk || !dv || !workspace)
     return fail(INFLLM2_ERR_NULL, "a backward tensor or the workspace is NULL");
   const void* ptrs[] = {q, k, v, block_idx, out, lse, dout, dq, dk, dv, workspace};
   for (const void* p : ptrs)
     if (!aligned16(p)) return fail(INFLLM2_ERR_ALIGN, "backward buffers must be 16-byte aligned");
-  const size_t need = infllm2::bwd_workspace(g, t, nb, qr);
+  const size_t need = infllm2::bwd_workspace(g, t);
   if (workspace_bytes < need)
     return fail(INFLLM2_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
-  return hip_status(infllm2::launch_attn_bwd(g, t, nb, qr, q, k, v, block_idx, out, lse, dout, dq,
-                                             dk, dv, workspace, static_cast<hipStream_t>(stream)),
+  return hip_status(infllm2::launch_attn_bwd(g, t, q, k, v, block_idx, out, lse, dout, dq, dk, dv,
+                                             workspace, static_cast<hipStream_t>(stream)),
                     "sparse_attn_backward launch");
 }
 
@@ -493,25 +404,22 @@ infllm2_status infllm2_decode_step(const infllm2_params* params, const infllm2_s
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(kernels) ||
       !aligned16(scores) || !aligned16(block_idx) || !aligned16(out) || (lse && !aligned16(lse)))
     return fail(INFLLM2_ERR_ALIGN, "decode step buffers must be 16-byte aligned");
-  const int need_nb = max_reachable_blocks(t, g.B);
+  const int need_nb = infllm2::bound_blocks(t, g.B);
   if (nb_stride < need_nb)
     return fail(INFLLM2_ERR_SHAPE, "nb_stride %d below the %d reachable blocks", nb_stride, need_nb);
   if (need_nb > 4096)
     return fail(INFLLM2_ERR_UNSUPPORTED, "%d reachable blocks exceed 4096", need_nb);
   if (num_splits < 0 || num_splits > g.topk)
     return fail(INFLLM2_ERR_SHAPE, "num_splits %d outside 0..topk", num_splits);
-  SeqTable tr = t;
-  rows_prefix(&tr);
-  const int rows = tr.work_prefix[tr.n];
   const int splits = num_splits > 0 ? num_splits : infllm2::decode_step_splits(g);
-  const size_t need = infllm2::decode_workspace(g, rows, splits);
+  const size_t need = infllm2::decode_workspace(g, t.q_rows, splits);
   if (workspace == nullptr) return fail(INFLLM2_ERR_NULL, "workspace is NULL");
   if (!aligned16(workspace)) return fail(INFLLM2_ERR_ALIGN, "workspace must be 16-byte aligned");
   if (workspace_bytes < need)
     return fail(INFLLM2_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
   st = infllm2_compress_kernels(params, seqs, k_cache, prev_kv_len, kernels, stream);
   if (st != INFLLM2_OK) return st;
-  return hip_status(infllm2::launch_decode_step(g, tr, q, kernels, k_cache, v_cache, scores,
+  return hip_status(infllm2::launch_decode_step(g, t, q, kernels, k_cache, v_cache, scores,
                                                  nb_stride, block_idx, splits, workspace, out,
                                                  lse, static_cast<hipStream_t>(stream)),
                     "decode_step launch");

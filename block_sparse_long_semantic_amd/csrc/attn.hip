@@ -25,20 +25,23 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// The query row of dense work item `item` (query rows counted over the sequences in order);
+// false past the last row.  Every lane of the calling wave must call it.  Split-KV partials are
+// indexed by the query row itself (vrow == row).
 struct RowInfo {
   int vrow, row, pos, kv0, kv_len;
 };
 
-__device__ __forceinline__ RowInfo row_info(const SeqTable& t, int vrow) {
-  const int b = find_seq(t, vrow);
-  const int j = vrow - t.work_prefix[b];
-  RowInfo r;
-  r.vrow = vrow;
-  r.row = t.q_start[b] + j;
-  r.pos = t.q_pos0[b] + j;
-  r.kv0 = t.kv_start[b];
-  r.kv_len = t.kv_len[b];
-  return r;
+__device__ __forceinline__ bool row_info(const SeqTable& t, int item, RowInfo& r) {
+  int b, j;
+  if (!locate(t, item, [&](int s) { return t.q_len[s]; }, b, j)) return false;
+  const Seq sq = load_seq(t, b);
+  r.row = sq.q_start + j;
+  r.vrow = r.row;
+  r.pos = sq.q_pos0 + j;
+  r.kv0 = sq.kv_start;
+  r.kv_len = sq.kv_len;
+  return true;
 }
 
 // Number of valid (non -1) entries of an ascending, -1 padded index row.
@@ -95,7 +98,8 @@ attn_simple(Geom g, SeqTable t, const T* __restrict__ q, const T* __restrict__ k
   __shared__ float qs[4096];
   __shared__ float z[16 * 64];
   __shared__ float m_s[16], l_s[16], a_s[16];
-  const RowInfo ri = row_info(t, blockIdx.x);
+  RowInfo ri;
+  if (!row_info(t, static_cast<int>(blockIdx.x), ri)) return;
   const int kvh = blockIdx.y;
   const int sp = blockIdx.z;
   const int G = g.G, d = g.d;
@@ -174,7 +178,7 @@ attn_simple(Geom g, SeqTable t, const T* __restrict__ q, const T* __restrict__ k
       lse[static_cast<size_t>(ri.row) * g.Hq + kvh * G + threadIdx.x] =
           (m_s[threadIdx.x] + log2f(l_s[threadIdx.x])) * kLn2;
   } else {
-    const Partials pp = partials_of(part, g, t.work_prefix[t.n], splits);
+    const Partials pp = partials_of(part, g, t.q_rows, splits);
 #pragma unroll
     for (int i = 0; i < kSimpleMaxItems; ++i) {
       const int it = threadIdx.x + i * kSimpleThreads;
@@ -208,7 +212,8 @@ attn_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   __shared__ __attribute__((aligned(16))) uint16_t Ks[64 * KP];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
 
-  const RowInfo ri = row_info(t, blockIdx.x);
+  RowInfo ri;
+  if (!row_info(t, static_cast<int>(blockIdx.x), ri)) return;
   const int kvh = blockIdx.y;
   const int sp = blockIdx.z;
   const int lane = threadIdx.x;
@@ -353,7 +358,7 @@ attn_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
     if (lse != nullptr && q4 == 0 && c16 < G)
       lse[static_cast<size_t>(ri.row) * Hq + kvh * G + c16] = (m_run + log2f(l_run)) * kLn2;
   } else {
-    const Partials pp = partials_of(part, g, t.work_prefix[t.n], splits);
+    const Partials pp = partials_of(part, g, t.q_rows, splits);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * q4 + i;
@@ -377,9 +382,10 @@ template <typename T>
 __global__ void __launch_bounds__(256)
 attn_combine(Geom g, SeqTable t, int splits, const float* __restrict__ part, T* __restrict__ out,
              float* __restrict__ lse) {
-  const RowInfo ri = row_info(t, blockIdx.x);
+  RowInfo ri;
+  if (!row_info(t, static_cast<int>(blockIdx.x), ri)) return;
   const int h = blockIdx.y;
-  const Partials pp = partials_of(const_cast<float*>(part), g, t.work_prefix[t.n], splits);
+  const Partials pp = partials_of(const_cast<float*>(part), g, t.q_rows, splits);
   const size_t slot0 = (static_cast<size_t>(ri.vrow) * g.Hq + h) * splits;
   float M = -INFINITY;
   for (int s = 0; s < splits; ++s) M = fmaxf(M, pp.ml[2 * (slot0 + s)]);
@@ -406,7 +412,7 @@ attn_combine(Geom g, SeqTable t, int splits, const float* __restrict__ part, T* 
 hipError_t launch_attn(const Geom& g, int dtype, const SeqTable& t, const void* q,
                        const void* k, const void* v, const int32_t* idx, int splits,
                        void* out, float* lse, float* part, hipStream_t stream) {
-  const int rows = t.work_prefix[t.n];
+  const int rows = bound_rows(t);
   if (rows == 0) return hipSuccess;
   const dim3 grid(rows, g.Hkv, splits);
   const bool mfma = dtype == INFLLM2_BF16 && g.B == 64 && (g.d == 64 || g.d == 128) &&
@@ -443,7 +449,7 @@ hipError_t launch_attn(const Geom& g, int dtype, const SeqTable& t, const void* 
 
 hipError_t launch_attn_combine(const Geom& g, int dtype, const SeqTable& t, int splits,
                                const float* part, void* out, float* lse, hipStream_t stream) {
-  const int rows = t.work_prefix[t.n];
+  const int rows = bound_rows(t);
   if (rows == 0) return hipSuccess;
   const dim3 grid(rows, g.Hq);
   const dim3 block(g.d < 256 ? g.d : 256);

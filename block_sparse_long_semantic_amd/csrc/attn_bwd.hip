@@ -60,12 +60,8 @@ __device__ __forceinline__ void raw_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Sequence owning global KV block gb (t.aux holds the first global block of each sequence).
-__device__ __forceinline__ int seq_of_block(const SeqTable& t, int gb) {
-  int b = 0;
-  while (b + 1 < t.n && t.aux[b + 1] <= gb) ++b;
-  return b;
-}
+// Global KV block numbering: block j of sequence b is b * bound_blocks(t, 64) + j (a slot of
+// the longest sequence's block count per sequence).
 
 // Transposing LDS reads for the B operands of one step: for each 16-dim tile nd, two reads (row
 // tiles u = 0, 1) at addresses a0[nd], a1[nd], waited for in the same statement (the compiler
@@ -256,18 +252,20 @@ __device__ __forceinline__ void read_a<2, 4096>(const uint32_t (&a)[2], bf16x8 (
 }
 
 // ---------------------------------------------------------------------------------------------
-// Fill float32 ranges with zeros: sequence b's KV rows of dk and dv (grid.y = sequence).
+// Fill float32 ranges with zeros: sequence b's KV rows of dk and dv (sequences strided over
+// grid.y).
 __global__ void __launch_bounds__(256) zero_kv_grads(SeqTable t, int row_elems, float* dk,
                                                       float* dv) {
-  const int b = blockIdx.y;
-  const size_t n4 = static_cast<size_t>(t.kv_len[b]) * row_elems / 4;
-  const size_t base4 = static_cast<size_t>(t.kv_start[b]) * row_elems / 4;
-  f32x4* k4 = reinterpret_cast<f32x4*>(dk) + base4;
-  f32x4* v4 = reinterpret_cast<f32x4*>(dv) + base4;
-  for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
-       i += static_cast<size_t>(gridDim.x) * 256) {
-    k4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    v4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = blockIdx.y; b < t.n; b += gridDim.y) {
+    const size_t n4 = static_cast<size_t>(uniform(t.kv_len[b])) * row_elems / 4;
+    const size_t base4 = static_cast<size_t>(uniform(static_cast<int32_t>(t.kv_start[b]))) * row_elems / 4;
+    f32x4* k4 = reinterpret_cast<f32x4*>(dk) + base4;
+    f32x4* v4 = reinterpret_cast<f32x4*>(dv) + base4;
+    for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
+         i += static_cast<size_t>(gridDim.x) * 256) {
+      k4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      v4[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   }
 }
 
@@ -275,7 +273,7 @@ __global__ void __launch_bounds__(256) zero_ints(int* p, int n) {
   for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0;
 }
 
-// One workgroup per query row (work_prefix counts rows): delta[row, h] = dO[row, h] . O[row, h]
+// One workgroup per query row (r = dense row item): delta[row, h] = dO[row, h] . O[row, h]
 // in float32 from the stored bf16 tensors, and the row's selected blocks counted per
 // (KV head, global block) segment.
 template <int D>
@@ -285,8 +283,11 @@ __global__ void __launch_bounds__(256) bwd_prep(Geom g, SeqTable t, const uint16
                                                 float* __restrict__ delta, int* __restrict__ cnt,
                                                 int n_blocks, int win_rows) {
   const int r = blockIdx.x;
-  const int b = find_seq(t, r);
-  const int row = t.q_start[b] + (r - t.work_prefix[b]);
+  int b, j;
+  if (!locate(t, r, [&](int s) { return t.q_len[s]; }, b, j)) return;
+  const Seq sq = load_seq(t, b);
+  const int row = sq.q_start + j;
+  const int gb0 = b * bound_blocks(t, 64);
   constexpr int CPH = D / 8;  // 16-byte chunks per head
   const int n = g.Hq * CPH;   // a multiple of 64: whole waves only
   for (int c = threadIdx.x; c < n; c += 256) {
@@ -306,11 +307,11 @@ __global__ void __launch_bounds__(256) bwd_prep(Geom g, SeqTable t, const uint16
     if ((c & (CPH - 1)) == 0) delta[static_cast<size_t>(row) * g.Hq + c / CPH] = s;
   }
   const int per_row = g.Hkv * g.topk;
-  const int nb = (t.kv_len[b] + 63) / 64;      // entries outside the sequence are ignored
+  const int nb = (sq.kv_len + 63) / 64;      // entries outside the sequence are ignored
   for (int e = threadIdx.x; e < per_row; e += 256) {
     const int blk = idx[static_cast<size_t>(row) * per_row + e];
     if (blk >= 0 && blk < nb)
-      atomicAdd(&cnt[((r / win_rows) * g.Hkv + e / g.topk) * n_blocks + t.aux[b] + blk], 1);
+      atomicAdd(&cnt[((r / win_rows) * g.Hkv + e / g.topk) * n_blocks + gb0 + blk], 1);
   }
 }
 
@@ -368,14 +369,17 @@ __global__ void __launch_bounds__(256) bwd_scatter(Geom g, SeqTable t, const int
                                                    int* __restrict__ list, int n_blocks,
                                                    int win_rows) {
   const int r = blockIdx.x;
-  const int b = find_seq(t, r);
-  const int row = t.q_start[b] + (r - t.work_prefix[b]);
+  int b, j;
+  if (!locate(t, r, [&](int s) { return t.q_len[s]; }, b, j)) return;
+  const Seq sq = load_seq(t, b);
+  const int row = sq.q_start + j;
+  const int gb0 = b * bound_blocks(t, 64);
   const int per_row = g.Hkv * g.topk;
-  const int nb = (t.kv_len[b] + 63) / 64;
+  const int nb = (sq.kv_len + 63) / 64;
   for (int e = threadIdx.x; e < per_row; e += 256) {
     const int blk = idx[static_cast<size_t>(row) * per_row + e];
     if (blk >= 0 && blk < nb) {
-      const int seg = ((r / win_rows) * g.Hkv + e / g.topk) * n_blocks + t.aux[b] + blk;
+      const int seg = ((r / win_rows) * g.Hkv + e / g.topk) * n_blocks + gb0 + blk;
       list[seg_off[seg] + atomicAdd(&fill[seg], 1)] = row;
     }
   }
@@ -446,12 +450,14 @@ bwd_dkv(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __re
     const int seg = lo;
     const int kvh = (seg / n_blocks) % Hkv;       // segment = (row window, KV head, block)
     const int gb = seg % n_blocks;
-    const int b = seq_of_block(t, gb);
-    const int key0 = 64 * (gb - t.aux[b]);
+    const int nbs = bound_blocks(t, 64);
+    const int b = gb / nbs;
+    const Seq sq = load_seq(t, b);
+    const int key0 = 64 * (gb - b * nbs);
     const int e0 = seg_off[seg] + (item - item_off[seg]) * kChunk;
     const int ne = min(kChunk, seg_off[seg + 1] - e0);
-    const int kv_len = t.kv_len[b];
-    const int pos_shift = t.q_pos0[b] - t.q_start[b];   // position = row + pos_shift
+    const int kv_len = sq.kv_len;
+    const int pos_shift = sq.q_pos0 - sq.q_start;   // position = row + pos_shift
 
     __syncthreads();                                     // previous item's reads of ents done
     for (int e = tid; e < ne; e += 256) ents[e] = list[e0 + e];
@@ -460,7 +466,7 @@ bwd_dkv(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __re
     bf16x8 kf[KS], vf[KS];
     {
       const int key = min(key0 + 16 * w + c16, kv_len - 1);
-      const size_t off = (static_cast<size_t>(t.kv_start[b] + key) * Hkv + kvh) * D + 8 * q4;
+      const size_t off = (static_cast<size_t>(sq.kv_start + key) * Hkv + kvh) * D + 8 * q4;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         kf[ks] = *reinterpret_cast<const bf16x8*>(k + off + 32 * ks);
@@ -600,7 +606,7 @@ bwd_dkv(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __re
     for (int i = 0; i < 4; ++i) {
       const int key = key0 + 16 * w + 4 * q4 + i;
       if (key < kv_len) {
-        const size_t off = (static_cast<size_t>(t.kv_start[b] + key) * Hkv + kvh) * D + c16;
+        const size_t off = (static_cast<size_t>(sq.kv_start + key) * Hkv + kvh) * D + c16;
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           unsafeAtomicAdd(dv + off + 16 * n, adv[n][i]);
@@ -619,32 +625,34 @@ int bwd_window_rows(const Geom& g) {
   return static_cast<int>(std::max<long long>(1024, kWindowBytes / per_row));
 }
 
-long long bwd_segments(const Geom& g, const SeqTable& t, int n_blocks) {
+static int bwd_blocks(const SeqTable& t) { return t.n * bound_blocks(t, 64); }
+
+long long bwd_segments(const Geom& g, const SeqTable& t) {
   const int w = bwd_window_rows(g);
-  const long long n_win = std::max(1, (t.work_prefix[t.n] + w - 1) / w);
-  return n_win * g.Hkv * n_blocks;
+  const long long n_win = std::max(1, (bound_rows(t) + w - 1) / w);
+  return n_win * g.Hkv * bwd_blocks(t);
 }
 
-size_t bwd_workspace(const Geom& g, const SeqTable& t, int n_blocks, int q_rows) {
+size_t bwd_workspace(const Geom& g, const SeqTable& t) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  const size_t n_seg = static_cast<size_t>(bwd_segments(g, t, n_blocks));
-  const size_t entries = static_cast<size_t>(t.work_prefix[t.n]) * g.Hkv * g.topk;
-  return al(static_cast<size_t>(q_rows) * g.Hq * 4) + al(n_seg * 4) + 2 * al((n_seg + 1) * 4) +
+  const size_t n_seg = static_cast<size_t>(bwd_segments(g, t));
+  const size_t entries = static_cast<size_t>(bound_rows(t)) * g.Hkv * g.topk;
+  return al(static_cast<size_t>(t.q_rows) * g.Hq * 4) + al(n_seg * 4) + 2 * al((n_seg + 1) * 4) +
          al(std::max<size_t>(entries, 1) * 4);
 }
 
-// t: work_prefix over query rows, aux[b] = first global KV block of sequence b; n_blocks the
-// total.  The workspace must be bwd_workspace() bytes.
-hipError_t launch_attn_bwd(const Geom& g, const SeqTable& t, int n_blocks, int q_rows,
-                           const void* q, const void* k, const void* v, const int32_t* idx,
-                           const void* out, const float* lse, const void* dout, float* dq,
-                           float* dk, float* dv, void* workspace, hipStream_t stream) {
+// The workspace must be bwd_workspace() bytes.
+hipError_t launch_attn_bwd(const Geom& g, const SeqTable& t, const void* q, const void* k,
+                           const void* v, const int32_t* idx, const void* out, const float* lse,
+                           const void* dout, float* dq, float* dk, float* dv, void* workspace,
+                           hipStream_t stream) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
-  const int n_seg = static_cast<int>(bwd_segments(g, t, n_blocks));
+  const int n_blocks = bwd_blocks(t);
+  const int n_seg = static_cast<int>(bwd_segments(g, t));
   const int win_rows = bwd_window_rows(g);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   float* delta = reinterpret_cast<float*>(ws);
-  ws += al(static_cast<size_t>(q_rows) * g.Hq * 4);
+  ws += al(static_cast<size_t>(t.q_rows) * g.Hq * 4);
   int* cnt = reinterpret_cast<int*>(ws);
   ws += al(static_cast<size_t>(n_seg) * 4);
   int* seg_off = reinterpret_cast<int*>(ws);
@@ -653,7 +661,7 @@ hipError_t launch_attn_bwd(const Geom& g, const SeqTable& t, int n_blocks, int q
   ws += al((static_cast<size_t>(n_seg) + 1) * 4);
   int* list = reinterpret_cast<int*>(ws);
 
-  const int rows = t.work_prefix[t.n];
+  const int rows = bound_rows(t);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
@@ -661,13 +669,12 @@ hipError_t launch_attn_bwd(const Geom& g, const SeqTable& t, int n_blocks, int q
   const uint16_t* dd = static_cast<const uint16_t*>(dout);
   hipError_t e;
 
-  int max_kv = 0;
-  for (int b = 0; b < t.n; ++b) max_kv = std::max(max_kv, t.kv_len[b]);
-  if (max_kv > 0) {
+  if (t.max_kv_len > 0) {
     const int row_elems = g.Hkv * g.d;
-    const long long n4 = static_cast<long long>(max_kv) * row_elems / 4;
+    const long long n4 = static_cast<long long>(t.max_kv_len) * row_elems / 4;
     const int gx = static_cast<int>(std::min<long long>((n4 + 255) / 256, 1024));
-    hipLaunchKernelGGL(zero_kv_grads, dim3(gx, t.n), dim3(256), 0, stream, t, row_elems, dk, dv);
+    hipLaunchKernelGGL(zero_kv_grads, dim3(gx, std::min(t.n, 65535)), dim3(256), 0, stream, t,
+                       row_elems, dk, dv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (rows == 0) return hipSuccess;

@@ -109,19 +109,22 @@ __device__ __forceinline__ int agent_add(int* p, int v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Query row `vrow` of a launch whose work_prefix counts query rows.
+// The query row of dense work item `item` (query rows counted over the sequences in order);
+// false past the last row.  Every lane of the calling wave must call it.  Per-(row, KV head)
+// workspace entries are indexed by the query row itself.
 struct DecRow {
-  int row, pos, kv0, kv_len, b;
+  int row, pos, kv0, kv_len, kc0;
 };
-__device__ __forceinline__ DecRow dec_row(const SeqTable& t, int vrow) {
-  DecRow r;
-  r.b = find_seq(t, vrow);
-  const int j = vrow - t.work_prefix[r.b];
-  r.row = t.q_start[r.b] + j;
-  r.pos = t.q_pos0[r.b] + j;
-  r.kv0 = t.kv_start[r.b];
-  r.kv_len = t.kv_len[r.b];
-  return r;
+__device__ __forceinline__ bool dec_row(const SeqTable& t, int item, DecRow& r) {
+  int b, j;
+  if (!locate(t, item, [&](int s) { return t.q_len[s]; }, b, j)) return false;
+  const Seq sq = load_seq(t, b);
+  r.row = sq.q_start + j;
+  r.pos = sq.q_pos0 + j;
+  r.kv0 = sq.kv_start;
+  r.kv_len = sq.kv_len;
+  r.kc0 = sq.kc_start;
+  return true;
 }
 
 // ------------------------------------------------------------------ attention over selected blocks
@@ -475,11 +478,10 @@ attn_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* 
   __shared__ float wm_s[NW][16], wl_s[NW][16];
   __shared__ int s_last;
 
-  const int vrow = blockIdx.x;
   const int kvh = blockIdx.y;
   const int sp = blockIdx.z;
-  const int rows = t.work_prefix[t.n];
-  const DecRow r = dec_row(t, vrow);
+  DecRow r;
+  if (!dec_row(t, static_cast<int>(blockIdx.x), r)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -508,10 +510,10 @@ attn_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* 
 
   float acc[16 * D / (64 * NW)], M, L;
   merge_waves<D, NW>(a, &ring[0][0], wm_s, wl_s, tid, acc, M, L);
-  const int pairs = rows * g.Hkv;
+  const int pairs = t.q_rows * g.Hkv;
   const DecodeLayout lay = decode_layout(pairs);
   char* ws = static_cast<char*>(workspace);
-  finish_split<D, G, NW>(g, r.row, kvh, vrow * g.Hkv + kvh, sp, nsplit, acc, M, L,
+  finish_split<D, G, NW>(g, r.row, kvh, r.row * g.Hkv + kvh, sp, nsplit, acc, M, L,
                          reinterpret_cast<int*>(ws + lay.split_done),
                          reinterpret_cast<float*>(ws + lay.part), pairs, tid, &s_last, out, lse);
 }
@@ -548,7 +550,7 @@ __device__ __forceinline__ void score_chunk(const Geom& g, const SeqTable& t, co
   const int C = num_kernels(r.kv_len, g.w, g.s);
   const int c0 = 4 * blk0;
   const int col = (lane % LPR) * 8;
-  const size_t kbase = static_cast<size_t>(t.kc_start[r.b]) * g.Hkv * D + static_cast<size_t>(kvh) * D;
+  const size_t kbase = static_cast<size_t>(r.kc0) * g.Hkv * D + static_cast<size_t>(kvh) * D;
   uint4 kv[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -614,13 +616,14 @@ decode_select(Geom g, SeqTable t, const uint16_t* __restrict__ q,
 
   const int tid = threadIdx.x;
   const int chunk = blockIdx.x;
-  const int pair = blockIdx.y;
-  const int kvh = pair % g.Hkv;
-  const DecRow r = dec_row(t, pair / g.Hkv);
+  const int kvh = static_cast<int>(blockIdx.y) % g.Hkv;
+  DecRow r;
+  if (!dec_row(t, static_cast<int>(blockIdx.y) / g.Hkv, r)) return;
+  const int pair = r.row * g.Hkv + kvh;
   const int own = r.pos / 64;
   const int n_chunks = own / kChunkBlocks + 1;
   if (chunk >= n_chunks) return;                       // whole workgroup
-  const int pairs = t.work_prefix[t.n] * g.Hkv;
+  const int pairs = t.q_rows * g.Hkv;
   int* score_done = reinterpret_cast<int*>(static_cast<char*>(workspace) +
                                            decode_layout(pairs).score_done);
   float* srow = scores + (static_cast<size_t>(r.row) * g.Hkv + kvh) * nb_stride;
@@ -653,13 +656,8 @@ int decode_step_splits(const Geom& g) { return (g.topk + kStepWaves - 1) / kStep
 
 bool decode_step_supported(const Geom& g, int dtype, const SeqTable& t) {
   if (!attn_decode_supported(g, dtype) || g.w != 32 || g.s != 16 || g.score_mode != 0) return false;
-  long long rows = 0;
-  for (int b = 0; b < t.n; ++b) rows += t.q_len[b];
-  if (rows * g.Hkv > 65535) return false;               // one grid row per (row, KV head)
-  for (int b = 0; b < t.n; ++b)
-    if (t.q_len[b] > 0 && (t.q_pos0[b] + t.q_len[b] - 1) / 64 + 1 > kMaxKeysPerThread * kSelectThreads)
-      return false;
-  return true;
+  if (static_cast<long long>(bound_rows(t)) * g.Hkv > 65535) return false;  // a grid row per pair
+  return bound_blocks(t, 64) <= kMaxKeysPerThread * kSelectThreads;
 }
 
 template <int NW>
@@ -667,7 +665,7 @@ static hipError_t launch_split_attention(const Geom& g, const SeqTable& t, const
                                          const void* k, const void* v, const int32_t* idx,
                                          int nsplit, void* workspace, void* out, float* lse,
                                          hipStream_t stream) {
-  const int rows = t.work_prefix[t.n];
+  const int rows = bound_rows(t);
   if (rows == 0) return hipSuccess;
   if (nsplit < 1 || nsplit > 65535 || g.Hkv > 65535) return hipErrorInvalidValue;
   const dim3 grid(rows, g.Hkv, nsplit);
@@ -689,7 +687,6 @@ static hipError_t launch_split_attention(const Geom& g, const SeqTable& t, const
   return hipErrorInvalidValue;
 }
 
-// work_prefix of `t` counts query rows.
 hipError_t launch_attn_decode(const Geom& g, const SeqTable& t, const void* q, const void* k,
                               const void* v, const int32_t* idx, int nsplit, void* workspace,
                               void* out, float* lse, hipStream_t stream) {
@@ -697,16 +694,14 @@ hipError_t launch_attn_decode(const Geom& g, const SeqTable& t, const void* q, c
                                              stream);
 }
 
-// work_prefix of `t` counts query rows; kernels must already hold every complete kernel.
+// kernels must already hold every complete kernel.
 hipError_t launch_decode_step(const Geom& g, const SeqTable& t, const void* q,
                                const void* kernels, const void* k, const void* v, float* scores,
                                int nb_stride, int32_t* idx, int nsplit, void* workspace,
                                void* out, float* lse, hipStream_t stream) {
-  const int rows = t.work_prefix[t.n];
+  const int rows = bound_rows(t);
   if (rows == 0) return hipSuccess;
-  int max_blocks = 1;
-  for (int b = 0; b < t.n; ++b)
-    if (t.q_len[b] > 0) max_blocks = std::max(max_blocks, (t.q_pos0[b] + t.q_len[b] - 1) / 64 + 1);
+  const int max_blocks = std::max(1, bound_blocks(t, 64));
   const int max_chunks = (max_blocks + kChunkBlocks - 1) / kChunkBlocks;
   if (static_cast<long long>(rows) * g.Hkv > 65535) return hipErrorInvalidValue;
   const dim3 grid(max_chunks, rows * g.Hkv);

@@ -227,16 +227,20 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   const int item =
       item_base + static_cast<int>(blockIdx.x % 8) * per_xcd + static_cast<int>(blockIdx.x / 8);
   if (item >= n_items) return;
-  const int n_tiles = t.work_prefix[t.n];
+  auto tiles_of = [&](int s) { return (t.q_len[s] + T - 1) / T; };
+  const int n_tiles = count_items(t, tiles_of);
+  if (item >= n_tiles * g.Hkv) return;
   const int kvh = item / n_tiles;
   const int tile = item - kvh * n_tiles;
-  const int b = find_seq(t, tile);
-  const int r0 = (tile - t.work_prefix[b]) * T;
-  const int nq = min(T, t.q_len[b] - r0);
-  const int row0 = t.q_start[b] + r0;
-  const int pos0 = t.q_pos0[b] + r0;
-  const int kv0 = t.kv_start[b];
-  const int kv_len = t.kv_len[b];
+  int b, lt;
+  locate(t, tile, tiles_of, b, lt);
+  const Seq sq = load_seq(t, b);
+  const int r0 = lt * T;
+  const int nq = min(T, sq.q_len - r0);
+  const int row0 = sq.q_start + r0;
+  const int pos0 = sq.q_pos0 + r0;
+  const int kv0 = sq.kv_start;
+  const int kv_len = sq.kv_len;
   const int nbt = (pos0 + nq - 1) / 64 + 1;  // reachable blocks of the tile (<= kMaxUnion)
 
   const int tid = threadIdx.x;
@@ -789,11 +793,8 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
 }  // namespace
 
 bool attn_tile_supported(const Geom& g, int dtype, const SeqTable& t) {
-  if (dtype != INFLLM2_BF16 || g.B != 64 || !(g.d == 64 || g.d == 128) || !(g.G == 8 || g.G == 16))
-    return false;
-  for (int b = 0; b < t.n; ++b)
-    if (t.q_len[b] > 0 && (t.q_pos0[b] + t.q_len[b] - 1) / 64 + 1 > kMaxUnion) return false;
-  return true;
+  return dtype == INFLLM2_BF16 && g.B == 64 && (g.d == 64 || g.d == 128) &&
+         (g.G == 8 || g.G == 16) && bound_blocks(t, 64) <= kMaxUnion;
 }
 
 // Compute units of the current device, looked up once per device.  The cache is shared by every
@@ -811,26 +812,13 @@ int device_cus() {
   return n;
 }
 
-// The table with work_prefix over tiles of `rows` query rows per sequence.
-SeqTable tile_table(const SeqTable& t, int rows) {
-  SeqTable r = t;
-  int acc = 0;
-  for (int b = 0; b < t.n; ++b) {
-    r.work_prefix[b] = acc;
-    acc += (t.q_len[b] + rows - 1) / rows;
-  }
-  r.work_prefix[t.n] = acc;
-  return r;
-}
-
 // Items are launched in rounds of one workgroup per compute unit, so that the workgroups
 // sharing an XCD start together on neighbouring tiles and walk the same KV blocks at the same
 // time (their L2 then serves each block to all of them).  The forward runs tiles of kTF rows.
-hipError_t launch_attn_tile(const Geom& g, const SeqTable& t_rows, const void* q, const void* k,
+hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, const void* k,
                             const void* v, const int32_t* idx, void* out, float* lse,
                             hipStream_t stream) {
-  const SeqTable t = tile_table(t_rows, kTF);
-  const int n_items = t.work_prefix[t.n] * g.Hkv;
+  const int n_items = bound_tiles(t, kTF) * g.Hkv;   // a bound: the kernel counts the tiles
   if (n_items == 0) return hipSuccess;
   const int round = kRounds ? (device_cus() / 8) * 8 : (n_items + 7) / 8 * 8;
   const uint16_t* qq = static_cast<const uint16_t*>(q);
@@ -859,15 +847,14 @@ hipError_t launch_attn_tile(const Geom& g, const SeqTable& t_rows, const void* q
   return hipSuccess;
 }
 
-// Gradient of the queries (tiles of kT rows; `t_rows` counts query rows): dout is the
+// Gradient of the queries (tiles of kT rows): dout is the
 // upstream gradient of out, lse the forward's natural-log statistics and delta[row, head] =
 // dout . out.  Writes dq (fp32, [row, Hq, d]) for every row of every sequence.
-hipError_t launch_attn_tile_dq(const Geom& g, const SeqTable& t_rows, const void* q, const void* k,
+hipError_t launch_attn_tile_dq(const Geom& g, const SeqTable& t, const void* q, const void* k,
                                const void* v, const int32_t* idx, const void* dout,
                                const float* lse, const float* delta, float* dq,
                                hipStream_t stream) {
-  const SeqTable t = tile_table(t_rows, kT);
-  const int n_items = t.work_prefix[t.n] * g.Hkv;
+  const int n_items = bound_tiles(t, kT) * g.Hkv;
   if (n_items == 0) return hipSuccess;
   const int round = kRounds ? (device_cus() / 8) * 8 : (n_items + 7) / 8 * 8;
   const uint16_t* qq = static_cast<const uint16_t*>(q);
@@ -896,11 +883,10 @@ hipError_t launch_attn_tile_dq(const Geom& g, const SeqTable& t_rows, const void
   return hipSuccess;
 }
 
-hipError_t launch_attn_tile_window(const Geom& g, const SeqTable& t_rows, const void* q,
+hipError_t launch_attn_tile_window(const Geom& g, const SeqTable& t, const void* q,
                                    const void* k, const void* v, void* out, float* lse,
                                    hipStream_t stream) {
-  const SeqTable t = tile_table(t_rows, kT);
-  const int n_items = t.work_prefix[t.n] * g.Hkv;
+  const int n_items = bound_tiles(t, kT) * g.Hkv;
   if (n_items == 0) return hipSuccess;
   const int round = kRounds ? (device_cus() / 8) * 8 : (n_items + 7) / 8 * 8;
   const uint16_t* qq = static_cast<const uint16_t*>(q);

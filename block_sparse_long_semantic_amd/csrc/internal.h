@@ -8,22 +8,109 @@
 
 namespace infllm2 {
 
-constexpr int kMaxSeqs = INFLLM2_MAX_SEQS;
-
-// Sequence metadata passed by value as a kernel argument (no device-side metadata buffers).
-// work_prefix[b] is the first work item of sequence b for the launch at hand; work_prefix[n]
-// is the total.  Its meaning (tiles, rows, ...) is defined by each launch.
+// Sequence metadata as the kernels see it: the caller's device arrays (read when a kernel runs,
+// never on the host) and the host bounds that size the grids.  Kernels map a dense work item to
+// its sequence with locate() below; what an item is (a query row, a tile of rows, a tile of
+// kernels, ...) is defined by each launch.
 struct SeqTable {
-  int32_t n;
-  int32_t q_start[kMaxSeqs];
-  int32_t q_len[kMaxSeqs];
-  int32_t q_pos0[kMaxSeqs];
-  int32_t kv_start[kMaxSeqs];
-  int32_t kv_len[kMaxSeqs];
-  int32_t kc_start[kMaxSeqs];
-  int32_t aux[kMaxSeqs];          // per-launch extra (e.g. first kernel of an incremental pass)
-  int32_t work_prefix[kMaxSeqs + 1];
+  int32_t n;            // sequences
+  int32_t max_q_len;    // bound on every q_len[b]
+  int32_t max_kv_len;   // bound on every kv_len[b]
+  int32_t q_rows;       // bound on every q_start[b] + q_len[b]
+  const int64_t* q_start;
+  const int32_t* q_len;
+  const int32_t* q_pos0;
+  const int64_t* kv_start;
+  const int32_t* kv_len;
+  const int64_t* kc_start;      // may be null where the call has no kernels
+  const int32_t* prev_kv_len;   // incremental compression only (null: all zeros)
 };
+
+// A wave-uniform value as the compiler should see it (scalar registers): values loaded from the
+// metadata arrays at a uniform index are uniform, but the compiler cannot prove it, and would
+// otherwise build addresses and buffer descriptors from them in vector registers.
+__device__ __forceinline__ int32_t uniform(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// One sequence's metadata, loaded from the device arrays (row indices fit in 32 bits); b must be
+// wave-uniform.
+struct Seq {
+  int32_t q_start, q_len, q_pos0, kv_start, kv_len, kc_start;
+};
+
+__device__ __forceinline__ Seq load_seq(const SeqTable& t, int b) {
+  Seq s;
+  s.q_start = uniform(static_cast<int32_t>(t.q_start[b]));
+  s.q_len = uniform(t.q_len[b]);
+  s.q_pos0 = uniform(t.q_pos0[b]);
+  s.kv_start = uniform(static_cast<int32_t>(t.kv_start[b]));
+  s.kv_len = uniform(t.kv_len[b]);
+  s.kc_start = t.kc_start != nullptr ? uniform(static_cast<int32_t>(t.kc_start[b])) : 0;
+  return s;
+}
+
+// Sequence b owns count(b) consecutive work items, in sequence order.  locate() finds the
+// sequence owning dense item `item` and the item's index within it; false once item is past
+// the last sequence's items.  Every active lane of the calling wave must call it with the same
+// item (a wave-wide prefix sum over as many sequences at a time as the wave has lanes; a
+// partial wave, lanes 0 .. nl-1, works too); the results are wave-uniform.
+template <typename F>
+__device__ __forceinline__ bool locate(const SeqTable& t, int item, F count, int& b, int& local) {
+  const int lane = threadIdx.x & 63;
+  const int nl = 64 - __builtin_clzll(static_cast<unsigned long long>(__ballot(1)));
+  int acc = 0;
+  for (int base = 0; base < t.n; base += nl) {
+    const int c = base + lane < t.n ? count(base + lane) : 0;
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    const int tot = uniform(__shfl(incl, nl - 1));
+    if (item < acc + tot) {
+      const int L = __ffsll(static_cast<unsigned long long>(__ballot(incl > item - acc))) - 1;
+      b = uniform(base + L);
+      local = uniform(item - acc - __shfl(incl - c, L));
+      return true;
+    }
+    acc += tot;
+  }
+  return false;
+}
+
+// Total of count(b) over all sequences (same calling rule as locate).
+template <typename F>
+__device__ __forceinline__ int count_items(const SeqTable& t, F count) {
+  const int lane = threadIdx.x & 63;
+  const int nl = 64 - __builtin_clzll(static_cast<unsigned long long>(__ballot(1)));
+  int acc = 0;
+  for (int base = 0; base < t.n; base += nl) {
+    int c = base + lane < t.n ? count(base + lane) : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(c, off);
+      if (lane >= off) c += y;
+    }
+    acc += uniform(__shfl(c, nl - 1));
+  }
+  return acc;
+}
+
+// Host-side bounds on the number of work items of a launch (the grid), from the host bounds of
+// the table: query rows, and tiles of `rows` query rows per sequence.
+inline int bound_rows(const SeqTable& t) {
+  const long long a = static_cast<long long>(t.n) * t.max_q_len;
+  return static_cast<int>(a < t.q_rows ? a : t.q_rows);
+}
+inline int bound_tiles(const SeqTable& t, int rows) {
+  const long long a = static_cast<long long>(t.n) * ((t.max_q_len + rows - 1) / rows);
+  const long long c = (static_cast<long long>(t.q_rows) + rows - 1) / rows + t.n;
+  return static_cast<int>(a < c ? a : c);
+}
+// Reachable blocks of the longest sequence (query positions are below max_kv_len).
+__host__ __device__ inline int bound_blocks(const SeqTable& t, int B) {
+  return t.max_kv_len > 0 ? (t.max_kv_len - 1) / B + 1 : 0;
+}
 
 struct Geom {
   int32_t Hq, Hkv, G, d;
@@ -33,13 +120,6 @@ struct Geom {
   int32_t window;       // sliding-window attention: keys pos - window < j <= pos (0 = unused)
   int32_t score_mode;   // 0: group sum of scaled dot products; 1: of per-head softmaxes
 };
-
-// Sequence owning work item `item` (linear scan; at most kMaxSeqs entries).
-__device__ __forceinline__ int find_seq(const SeqTable& t, int item) {
-  int b = 0;
-  while (b + 1 < t.n && t.work_prefix[b + 1] <= item) ++b;
-  return b;
-}
 
 __host__ __device__ __forceinline__ int num_kernels(int len, int w, int s) {
   return len < w ? 0 : (len - w) / s + 1;
@@ -79,24 +159,21 @@ __host__ __device__ inline DecodeLayout decode_layout(int pairs) {
 hipError_t launch_compress(const Geom& g, int dtype, const SeqTable& t, const void* k,
                            void* kernels, hipStream_t stream);
 hipError_t launch_scores(const Geom& g, int dtype, const SeqTable& t, const void* q,
-                         const void* kernels, float* scores, int nb_stride, int range_tiles,
-                         hipStream_t stream);
+                         const void* kernels, float* scores, int nb_stride, hipStream_t stream);
 // Score mode 1 (per-head softmax over the visible kernels before the group sum).
 bool scores_softmax_mfma_supported(const Geom& g, int dtype);
-int scores_softmax_rows(const Geom& g, bool split);
 hipError_t launch_scores_softmax(const Geom& g, int dtype, const SeqTable& t, const void* q,
-                                 const void* kernels, float* scores, int nb_stride, bool split,
+                                 const void* kernels, float* scores, int nb_stride,
                                  hipStream_t stream);
 hipError_t launch_topk(const Geom& g, const SeqTable& t, const float* scores, int nb_stride,
-                       int max_blocks, int32_t* idx, hipStream_t stream);
+                       int32_t* idx, hipStream_t stream);
 // Attention over blocks idx[row, g, k0 .. k1) for split `sp` of `splits`.  With splits == 1
 // the kernels write O and lse; otherwise they write partials to `part` and
 // launch_attn_combine merges them.
 hipError_t launch_attn(const Geom& g, int dtype, const SeqTable& t, const void* q,
                        const void* k, const void* v, const int32_t* idx, int splits,
                        void* out, float* lse, float* part, hipStream_t stream);
-// Tiled prefill attention (tiles of consecutive query rows sharing staged K/V blocks).  The
-// three tile launchers take work_prefix over query rows and form their own tiles.
+// Tiled prefill attention (tiles of consecutive query rows sharing staged K/V blocks).
 bool attn_tile_supported(const Geom& g, int dtype, const SeqTable& t);
 hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, const void* k,
                             const void* v, const int32_t* idx, void* out, float* lse,
@@ -111,14 +188,14 @@ hipError_t launch_attn_tile_dq(const Geom& g, const SeqTable& t, const void* q, 
                                const void* v, const int32_t* idx, const void* dout,
                                const float* lse, const float* delta, float* dq,
                                hipStream_t stream);
-// Whole backward (dq, dk, dv as float32).  t: work_prefix over query rows, aux[b] the first
-// global KV block of sequence b, n_blocks their total; q_rows bounds every row index + 1.
-size_t bwd_workspace(const Geom& g, const SeqTable& t, int n_blocks, int q_rows);
-long long bwd_segments(const Geom& g, const SeqTable& t, int n_blocks);
-hipError_t launch_attn_bwd(const Geom& g, const SeqTable& t, int n_blocks, int q_rows,
-                           const void* q, const void* k, const void* v, const int32_t* idx,
-                           const void* out, const float* lse, const void* dout, float* dq,
-                           float* dk, float* dv, void* workspace, hipStream_t stream);
+// Whole backward (dq, dk, dv as float32).  KV blocks are numbered per sequence slot: block j of
+// sequence b is global block b * bound_blocks(t, 64) + j.
+size_t bwd_workspace(const Geom& g, const SeqTable& t);
+long long bwd_segments(const Geom& g, const SeqTable& t);
+hipError_t launch_attn_bwd(const Geom& g, const SeqTable& t, const void* q, const void* k,
+                           const void* v, const int32_t* idx, const void* out, const float* lse,
+                           const void* dout, float* dq, float* dk, float* dv, void* workspace,
+                           hipStream_t stream);
 // Split-KV decoding attention with the merge done by the last workgroup of each (row, kv head);
 // its workspace follows decode_layout.
 bool attn_decode_supported(const Geom& g, int dtype);
@@ -127,7 +204,7 @@ hipError_t launch_attn_decode(const Geom& g, const SeqTable& t, const void* q, c
                               const void* v, const int32_t* idx, int nsplit, void* workspace,
                               void* out, float* lse, hipStream_t stream);
 // One decoding step after the kernels are compressed: block scores and top-k in one launch
-// (decode_select), then the split-KV attention; work_prefix of `t` counts query rows.
+// (decode_select), then the split-KV attention.
 bool decode_step_supported(const Geom& g, int dtype, const SeqTable& t);
 int decode_step_splits(const Geom& g);
 hipError_t launch_decode_step(const Geom& g, const SeqTable& t, const void* q,

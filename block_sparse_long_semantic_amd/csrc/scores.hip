@@ -41,18 +41,18 @@ __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p, size_t i
 }
 
 // ------------------------------------------------------------------------------ simple path
-// One workgroup per (query row, KV head); work_prefix counts query rows.
+// One workgroup per (query row, KV head).
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
 scores_simple(Geom g, SeqTable t, const T* __restrict__ q, const T* __restrict__ kern,
               float* __restrict__ scores, int nb_stride) {
   __shared__ float qs[256];
-  const int vrow = blockIdx.x;
   const int kvh = blockIdx.y;
-  const int b = find_seq(t, vrow);
-  const int j = vrow - t.work_prefix[b];
-  const int row = t.q_start[b] + j;
-  const int pos = t.q_pos0[b] + j;
+  int b, j;
+  if (!locate(t, static_cast<int>(blockIdx.x), [&](int s) { return t.q_len[s]; }, b, j)) return;
+  const Seq sq = load_seq(t, b);
+  const int row = sq.q_start + j;
+  const int pos = sq.q_pos0 + j;
   for (int e = threadIdx.x; e < g.d; e += kThreads) {
     float acc = 0.f;
     for (int h = 0; h < g.G; ++h)
@@ -60,7 +60,7 @@ scores_simple(Geom g, SeqTable t, const T* __restrict__ q, const T* __restrict__
     qs[e] = acc;
   }
   __syncthreads();
-  const int C = num_kernels(t.kv_len[b], g.w, g.s);
+  const int C = num_kernels(sq.kv_len, g.w, g.s);
   const int nb = pos / g.B + 1;
   float* out = scores + (static_cast<size_t>(row) * g.Hkv + kvh) * nb_stride;
   for (int blk = threadIdx.x; blk < nb; blk += kThreads) {
@@ -70,7 +70,7 @@ scores_simple(Geom g, SeqTable t, const T* __restrict__ q, const T* __restrict__
     float best = -INFINITY;
     for (int c = lo; c < hi; ++c) {
       if (g.s * c + g.w - 1 > pos) break;
-      const size_t base = (static_cast<size_t>(t.kc_start[b]) + c) * g.Hkv * g.d +
+      const size_t base = (static_cast<size_t>(sq.kc_start) + c) * g.Hkv * g.d +
                           static_cast<size_t>(kvh) * g.d;
       float dot = 0.f;
       for (int e = 0; e < g.d; ++e) dot += qs[e] * load_elem(kern, base + e);
@@ -102,18 +102,22 @@ scores_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
   constexpr int QOP_BYTES = RG * KS * 2 * 64 * 16;             // exchanged B operands
   constexpr int STAGE_BYTES = 4 * 64 * kStageRow * 4;          // per-wave score staging
   __shared__ __attribute__((aligned(16))) unsigned char smem[QOP_BYTES > STAGE_BYTES ? QOP_BYTES : STAGE_BYTES];
-  const int total = t.work_prefix[t.n];
+  auto tiles64 = [&](int s) { return (t.q_len[s] + 63) / 64; };
+  const int total = count_items(t, tiles64);
   const int item = total - 1 - static_cast<int>(blockIdx.x);   // heaviest (latest) rows first
+  if (item < 0) return;
   const int kvh = blockIdx.y;
-  const int b = find_seq(t, item);
+  int b, lt;
+  locate(t, item, tiles64, b, lt);
+  const Seq sq = load_seq(t, b);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int c16 = lane & 15;
   const int q4 = lane >> 4;
-  const int q_len = t.q_len[b];
-  const int r0 = (item - t.work_prefix[b]) * 64;
+  const int q_len = sq.q_len;
+  const int r0 = lt * 64;
   const int r_last = min(r0 + 63, q_len - 1);
-  const int nbt = ((t.q_pos0[b] + r_last) / 64 + 1 + 3) / 4;  // kernel tiles of the last row
+  const int nbt = ((sq.q_pos0 + r_last) / 64 + 1 + 3) / 4;  // kernel tiles of the last row
   const int per = (nbt + 3) / 4;
   const int t_begin = wave * per;
   const int t_end = min(nbt, t_begin + per);
@@ -122,7 +126,7 @@ scores_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
   uint4* qop = reinterpret_cast<uint4*>(smem);                 // [rg][ks][hi/lo][lane]
   {
     const int r = r0 + 16 * wave + c16;
-    const size_t row = static_cast<size_t>(t.q_start[b]) + (r < q_len ? r : q_len - 1);
+    const size_t row = static_cast<size_t>(sq.q_start) + (r < q_len ? r : q_len - 1);
 #pragma unroll
     for (int ks2 = 0; ks2 < KS; ks2 += 2) {
       // every head of the group (at most 16) over two dimension slices is loaded before the
@@ -175,7 +179,7 @@ scores_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
   for (int rg = 0; rg < RG; ++rg) {
     const int r = r0 + 16 * rg + c16;
     row_ok[rg] = r < q_len;
-    pos[rg] = t.q_pos0[b] + (row_ok[rg] ? r : q_len - 1);
+    pos[rg] = sq.q_pos0 + (row_ok[rg] ? r : q_len - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bhi[rg][ks] = __builtin_bit_cast(bf16x8, qop[((rg * KS + ks) * 2 + 0) * 64 + lane]);
@@ -186,8 +190,8 @@ scores_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
   if (t_begin >= t_end) return;
   float* stage = reinterpret_cast<float*>(smem) + wave * 64 * kStageRow;   // [row][block]
 
-  const int C = num_kernels(t.kv_len[b], g.w, g.s);
-  const size_t kbase = static_cast<size_t>(t.kc_start[b]) * g.Hkv * D + static_cast<size_t>(kvh) * D;
+  const int C = num_kernels(sq.kv_len, g.w, g.s);
+  const size_t kbase = static_cast<size_t>(sq.kc_start) * g.Hkv * D + static_cast<size_t>(kvh) * D;
   const unsigned src_lane = static_cast<unsigned>((lane + 48) & 63);   // lane - 16 (mod 64)
   // whole float4 stores need 16-byte aligned output rows
   const bool vec_out = (nb_stride & 3) == 0 && (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
@@ -248,10 +252,10 @@ scores_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
     for (int rr0 = 0; rr0 < 64 && r0 + rr0 < q_len; rr0 += 4) {
       const int rr = rr0 + q4;
       const int r = r0 + rr;
-      const int own = (t.q_pos0[b] + r) / 64;
+      const int own = (sq.q_pos0 + r) / 64;
       if (r < q_len && j4 < 4 * (c1 - c0) && blk <= own) {
         const float4 s4 = *reinterpret_cast<const float4*>(stage + rr * kStageRow + j4);
-        float* dst = scores + (static_cast<size_t>(t.q_start[b]) + r) * g.Hkv * nb_stride +
+        float* dst = scores + (static_cast<size_t>(sq.q_start) + r) * g.Hkv * nb_stride +
                      static_cast<size_t>(kvh) * nb_stride + blk;
         if (vec_out && blk + 3 <= own) {
           *reinterpret_cast<float4*>(dst) = s4;
@@ -286,21 +290,21 @@ scores_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q,
   __shared__ float u[NROW + 3];
   const int chunk = blockIdx.x;
   const int kvh = blockIdx.y;
-  const int vrow = blockIdx.z;
-  const int b = find_seq(t, vrow);
-  const int j = vrow - t.work_prefix[b];
-  const int row = t.q_start[b] + j;
-  const int pos = t.q_pos0[b] + j;
+  int b, j;
+  if (!locate(t, static_cast<int>(blockIdx.z), [&](int s) { return t.q_len[s]; }, b, j)) return;
+  const Seq sq = load_seq(t, b);
+  const int row = sq.q_start + j;
+  const int pos = sq.q_pos0 + j;
   const int own = pos / 64;
   const int blk0 = chunk * 64;
   if (blk0 > own) return;                 // whole workgroup
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int C = num_kernels(t.kv_len[b], g.w, g.s);
+  const int C = num_kernels(sq.kv_len, g.w, g.s);
   const int c0 = 4 * blk0;
   const int col = (lane % LPR) * 8;
-  const size_t kbase = static_cast<size_t>(t.kc_start[b]) * g.Hkv * D + static_cast<size_t>(kvh) * D;
+  const size_t kbase = static_cast<size_t>(sq.kc_start) * g.Hkv * D + static_cast<size_t>(kvh) * D;
   constexpr int NIT = (NROW + RPI - 1) / RPI;
   constexpr int NW = kThreads / 64;
   constexpr int PER = (NIT + NW - 1) / NW;                // row groups per wave
@@ -366,7 +370,7 @@ scores_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q,
 constexpr float kLog2eS = 1.4426950408889634f;
 constexpr float kLazyS = 8.f;        // log2 headroom before a running max is moved
 
-// One workgroup per (query row, KV head); work_prefix counts query rows.  Thread-strided over
+// One workgroup per (query row, KV head).  Thread-strided over
 // the visible kernels: per head, a block-wide max and sum give lse; then every thread takes
 // whole blocks and sums the heads' probabilities of their overlapping kernels.
 template <typename T>
@@ -376,19 +380,19 @@ scores_softmax_simple(Geom g, SeqTable t, const T* __restrict__ q, const T* __re
   __shared__ float qh[16][256];
   __shared__ float lse[16];
   __shared__ float red[kThreads / 64];
-  const int vrow = blockIdx.x;
   const int kvh = blockIdx.y;
-  const int b = find_seq(t, vrow);
-  const int j = vrow - t.work_prefix[b];
-  const int row = t.q_start[b] + j;
-  const int pos = t.q_pos0[b] + j;
+  int b, j;
+  if (!locate(t, static_cast<int>(blockIdx.x), [&](int s) { return t.q_len[s]; }, b, j)) return;
+  const Seq sq = load_seq(t, b);
+  const int row = sq.q_start + j;
+  const int pos = sq.q_pos0 + j;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   for (int e = tid; e < g.G * g.d; e += kThreads)
     qh[e / g.d][e % g.d] = load_elem(q, (static_cast<size_t>(row) * g.Hq + kvh * g.G) * g.d + e);
   __syncthreads();
-  const int C = num_kernels(t.kv_len[b], g.w, g.s);
+  const int C = num_kernels(sq.kv_len, g.w, g.s);
   const int nvis = pos - g.w + 1 < 0 ? 0 : min(C, (pos - g.w + 1) / g.s + 1);
-  const size_t kbase = static_cast<size_t>(t.kc_start[b]) * g.Hkv * g.d + static_cast<size_t>(kvh) * g.d;
+  const size_t kbase = static_cast<size_t>(sq.kc_start) * g.Hkv * g.d + static_cast<size_t>(kvh) * g.d;
   auto dot = [&](int h, int c) {
     float acc = 0.f;
     const size_t base = kbase + static_cast<size_t>(c) * g.Hkv * g.d;
@@ -454,21 +458,25 @@ scores_softmax_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
   constexpr int RPW = NCT * RPC;                  // rows per wave
   constexpr int ROWS = SPLIT ? RPW : 4 * RPW;     // rows per work item
   __shared__ float xm[4][NCT][4][4][2];           // SPLIT: [wave][ct][q4][i][m, l]
-  const int total = t.work_prefix[t.n];
+  auto tiles_of = [&](int s) { return (t.q_len[s] + ROWS - 1) / ROWS; };
+  const int total = count_items(t, tiles_of);
   const int item = total - 1 - static_cast<int>(blockIdx.x);   // latest rows first
+  if (item < 0) return;
   const int kvh = blockIdx.y;
-  const int b = find_seq(t, item);
+  int b, lt;
+  locate(t, item, tiles_of, b, lt);
+  const Seq sq = load_seq(t, b);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int c16 = lane & 15;
   const int q4 = lane >> 4;
-  const int q_len = t.q_len[b];
-  const int r0 = (item - t.work_prefix[b]) * ROWS;
+  const int q_len = sq.q_len;
+  const int r0 = lt * ROWS;
   const int r_last = min(r0 + ROWS - 1, q_len - 1);
-  const int own_last = (t.q_pos0[b] + r_last) / 64;
+  const int own_last = (sq.q_pos0 + r_last) / 64;
   const int nt = (own_last + 1 + 3) / 4;                        // kernel tiles (4 blocks each)
-  const int C = num_kernels(t.kv_len[b], g.w, g.s);
-  const size_t kbase = static_cast<size_t>(t.kc_start[b]) * g.Hkv * D + static_cast<size_t>(kvh) * D;
+  const int C = num_kernels(sq.kv_len, g.w, g.s);
+  const size_t kbase = static_cast<size_t>(sq.kc_start) * g.Hkv * D + static_cast<size_t>(kvh) * D;
   const float qscale = g.scale * kLog2eS;
   const int wrow0 = r0 + (SPLIT ? 0 : wave * RPW);              // first row of the wave
 
@@ -479,14 +487,14 @@ scores_softmax_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
     const int ra = wrow0 + ct * RPC + c16 / G;
-    const size_t rowa = static_cast<size_t>(t.q_start[b]) + min(ra, q_len - 1);
+    const size_t rowa = static_cast<size_t>(sq.q_start) + min(ra, q_len - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       aq[ct][ks] = *reinterpret_cast<const bf16x8*>(
           q + (rowa * g.Hq + kvh * G + c16 % G) * D + 32 * ks + 8 * q4);
     const int rc = wrow0 + ct * RPC + (4 * q4) / G;
     row_ok[ct] = rc < q_len;
-    pos_l[ct] = t.q_pos0[b] + min(rc, q_len - 1);
+    pos_l[ct] = sq.q_pos0 + min(rc, q_len - 1);
   }
   int t_begin = 0, t_end = nt;
   if constexpr (SPLIT) {
@@ -624,7 +632,7 @@ scores_softmax_mfma(Geom g, SeqTable t, const uint16_t* __restrict__ q,
       const bool writer = (c16 & 3) == 0 && (G == 16 ? q4 == 0 : (q4 & 1) == 0);
       if (writer && tt >= t_begin && row_ok[ct] && blk <= pos_l[ct] / 64) {
         const int rc = wrow0 + ct * RPC + (4 * q4) / G;
-        scores[(static_cast<size_t>(t.q_start[b]) + rc) * g.Hkv * nb_stride +
+        scores[(static_cast<size_t>(sq.q_start) + rc) * g.Hkv * nb_stride +
                static_cast<size_t>(kvh) * nb_stride + blk] = best;
       }
     }
@@ -642,16 +650,17 @@ bool scores_softmax_mfma_supported(const Geom& g, int dtype) {
 
 int scores_softmax_rows(const Geom& g, bool split) { return (split ? 64 : 256) / g.G; }
 
-// Score mode 1.  work_prefix counts query rows (simple path) or tiles of
-// scores_softmax_rows(g, split) rows (MFMA path).
+// Score mode 1: one workgroup per query row (generic path) or per tile of
+// scores_softmax_rows(g, split) rows (matrix cores; the split form when the tiles of the full
+// form would not fill the GPU).
 hipError_t launch_scores_softmax(const Geom& g, int dtype, const SeqTable& t, const void* q,
-                                 const void* kernels, float* scores, int nb_stride, bool split,
+                                 const void* kernels, float* scores, int nb_stride,
                                  hipStream_t stream) {
-  const int items = t.work_prefix[t.n];
-  if (items == 0) return hipSuccess;
-  const dim3 grid(items, g.Hkv);
   if (!scores_softmax_mfma_supported(g, dtype)) {
+    const int rows = bound_rows(t);
+    if (rows == 0) return hipSuccess;
     if (g.G > 16 || g.d > 256) return hipErrorInvalidValue;
+    const dim3 grid(rows, g.Hkv);
     if (dtype == INFLLM2_BF16)
       hipLaunchKernelGGL(scores_softmax_simple<uint16_t>, grid, dim3(kThreads), 0, stream, g, t,
                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kernels),
@@ -662,6 +671,10 @@ hipError_t launch_scores_softmax(const Geom& g, int dtype, const SeqTable& t, co
                          nb_stride);
     return hipGetLastError();
   }
+  const bool split = static_cast<long long>(bound_tiles(t, scores_softmax_rows(g, false))) * g.Hkv < 128;
+  const int items = bound_tiles(t, scores_softmax_rows(g, split));
+  if (items == 0) return hipSuccess;
+  const dim3 grid(items, g.Hkv);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(kernels);
 #define INFLLM2_SOFTMAX_CASE(DD, GG)                                                            \
@@ -682,14 +695,15 @@ hipError_t launch_scores_softmax(const Geom& g, int dtype, const SeqTable& t, co
   return hipErrorInvalidValue;
 }
 
+// Score mode 0: generic path one workgroup per (query row, KV head); matrix cores either per
+// tile of 64 rows, or, when those tiles would not fill the GPU (decoding), per (64-block chunk,
+// KV head, row).
 hipError_t launch_scores(const Geom& g, int dtype, const SeqTable& t, const void* q,
-                         const void* kernels, float* scores, int nb_stride, int range_tiles,
-                         hipStream_t stream) {
+                         const void* kernels, float* scores, int nb_stride, hipStream_t stream) {
   const bool mfma = dtype == INFLLM2_BF16 && g.B == 64 && g.w == 32 && g.s == 16 &&
                     (g.d == 64 || g.d == 128);
   if (!mfma) {
-    // work_prefix must count query rows
-    const int rows = t.work_prefix[t.n];
+    const int rows = bound_rows(t);
     if (rows == 0) return hipSuccess;
     const dim3 grid(rows, g.Hkv);
     if (dtype == INFLLM2_BF16)
@@ -702,15 +716,11 @@ hipError_t launch_scores(const Geom& g, int dtype, const SeqTable& t, const void
                          nb_stride);
     return hipGetLastError();
   }
-  const bool decode_like = range_tiles > 0 && range_tiles < (1 << 28);
-  if (decode_like) {
-    // work_prefix counts query rows; one workgroup per (64-block chunk, kv head, row)
-    const int rows = t.work_prefix[t.n];
-    if (rows == 0) return hipSuccess;
-    int max_blocks = 0;
-    for (int b = 0; b < t.n; ++b)
-      if (t.q_len[b] > 0) max_blocks = std::max(max_blocks, (t.q_pos0[b] + t.q_len[b] - 1) / 64 + 1);
-    const dim3 grid((max_blocks + 63) / 64, g.Hkv, rows);
+  const int items = bound_tiles(t, 64);
+  if (items == 0) return hipSuccess;
+  if (static_cast<long long>(items) * g.Hkv < 512) {
+    const int rows = bound_rows(t);
+    const dim3 grid((bound_blocks(t, 64) + 63) / 64, g.Hkv, rows);
     if (g.d == 128)
       hipLaunchKernelGGL(scores_decode<128>, grid, dim3(kThreads), 0, stream, g, t,
                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kernels),
@@ -721,9 +731,6 @@ hipError_t launch_scores(const Geom& g, int dtype, const SeqTable& t, const void
                          scores, nb_stride);
     return hipGetLastError();
   }
-  // work_prefix counts tiles of 64 query rows, built by the caller for this mode.
-  const int items = t.work_prefix[t.n];
-  if (items == 0) return hipSuccess;
   const dim3 grid(items, g.Hkv);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(kernels);

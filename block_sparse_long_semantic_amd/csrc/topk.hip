@@ -25,7 +25,7 @@ struct WaveSelectLds {
   uint32_t bin_key[64];
 };
 
-// work_prefix counts query rows.
+// One wave per (query row, KV head).
 template <int NPL>
 __global__ void __launch_bounds__(64)
 topk_kernel(Geom g, SeqTable t, const float* __restrict__ scores, int nb_stride,
@@ -33,12 +33,11 @@ topk_kernel(Geom g, SeqTable t, const float* __restrict__ scores, int nb_stride,
   __shared__ WaveSelectLds sm;
   const int lane = threadIdx.x;
   const int item = blockIdx.x;
-  const int vrow = item / g.Hkv;
   const int kvh = item % g.Hkv;
-  const int b = find_seq(t, vrow);
-  const int j = vrow - t.work_prefix[b];
-  const int row = t.q_start[b] + j;
-  const int pos = t.q_pos0[b] + j;
+  int b, j;
+  if (!locate(t, item / g.Hkv, [&](int s) { return t.q_len[s]; }, b, j)) return;
+  const int row = uniform(static_cast<int>(t.q_start[b])) + j;
+  const int pos = uniform(t.q_pos0[b]) + j;
   const int own = pos / g.B;
   const int nb = own + 1;
   int32_t* out = idx + (static_cast<size_t>(row) * g.Hkv + kvh) * g.topk;
@@ -211,12 +210,11 @@ topk_wide(Geom g, SeqTable t, const float* __restrict__ scores, int nb_stride,
   __shared__ uint32_t keys[kWideKeys * kWideThreads];
   __shared__ WgSelectLds<kWideWaves> sm;
   const int item = blockIdx.x;
-  const int vrow = item / g.Hkv;
   const int kvh = item % g.Hkv;
-  const int b = find_seq(t, vrow);
-  const int j = vrow - t.work_prefix[b];
-  const int row = t.q_start[b] + j;
-  const int pos = t.q_pos0[b] + j;
+  int b, j;
+  if (!locate(t, item / g.Hkv, [&](int s) { return t.q_len[s]; }, b, j)) return;
+  const int row = uniform(static_cast<int>(t.q_start[b])) + j;
+  const int pos = uniform(t.q_pos0[b]) + j;
   const size_t pair = static_cast<size_t>(row) * g.Hkv + kvh;
   wg_select<kWideWaves, kWideKeys>(g, pos / g.B, scores + pair * nb_stride, idx + pair * g.topk,
                                    keys, sm, static_cast<int>(threadIdx.x));
@@ -225,8 +223,9 @@ topk_wide(Geom g, SeqTable t, const float* __restrict__ scores, int nb_stride,
 }  // namespace
 
 hipError_t launch_topk(const Geom& g, const SeqTable& t, const float* scores, int nb_stride,
-                       int max_blocks, int32_t* idx, hipStream_t stream) {
-  const int items = t.work_prefix[t.n] * g.Hkv;
+                       int32_t* idx, hipStream_t stream) {
+  const int max_blocks = bound_blocks(t, g.B);
+  const int items = bound_rows(t) * g.Hkv;
   if (items == 0) return hipSuccess;
   if (items <= 1024 && max_blocks <= kWideKeys * kWideThreads) {
     hipLaunchKernelGGL(topk_wide, dim3(items), dim3(kWideThreads), 0, stream, g, t, scores,

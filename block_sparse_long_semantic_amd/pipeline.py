@@ -3,7 +3,8 @@
 prefill:     compress_kernels -> block_scores -> topk_select -> sparse_attn_prefill
 decode_step: compress_kernels (incremental) -> block_scores -> topk_select
              -> sparse_attn_decode
-Buffers are torch tensors; pass `bufs` from a previous call to reuse them.
+Buffers are torch tensors; pass `bufs` from a previous call to reuse them.  The sequence
+metadata reaches the library as device arrays (Seqs copies them once per device).
 """
 from __future__ import annotations
 
@@ -23,11 +24,9 @@ def _dtype(p: Params):
 
 
 def reachable_blocks(p: Params, seqs: Seqs) -> int:
-    m = 0
-    for b in range(seqs.num_seqs):
-        if seqs.q_len[b] > 0:
-            m = max(m, (int(seqs.q_pos0[b]) + int(seqs.q_len[b]) - 1) // p.block_size + 1)
-    return m
+    """Blocks a query of these sequences may reach: the library's bound ceil(max_kv_len / B),
+    the score buffers' least row stride."""
+    return (seqs.max_kv_len + p.block_size - 1) // p.block_size
 
 
 def prefill_buffers(params, seqs: Seqs, q, kv_rows_kernels: int) -> Dict[str, object]:

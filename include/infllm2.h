@@ -28,20 +28,24 @@
  *   lse       [q_rows,  Hq]           float32, natural log of the softmax denominator
  * Query head h reads KV head h / (Hq / Hkv) (contiguous GQA groups).
  *
- * Sequences (infllm2_seqs, HOST arrays, read during the call only): sequence b owns query rows
- * q_start[b] .. q_start[b]+q_len[b]-1, whose positions in the sequence are q_pos0[b]+j; its
- * keys/values are rows kv_start[b] .. kv_start[b]+kv_len[b]-1 (position t at row kv_start+t);
- * its semantic kernels are rows kc_start[b] + c, c < floor((kv_len-w)/s)+1.  A packed prefill
- * uses q_start = kv_start = cu_seqlens and q_pos0 = 0; a decode batch over a padded cache uses
- * kv_start = b*max_len, q_len = 1, q_pos0 = kv_len-1 (the new token's K/V already stored).
- * Every query must see its own key: q_pos0 + q_len <= kv_len.
+ * Sequences (infllm2_seqs): sequence b owns query rows q_start[b] .. q_start[b]+q_len[b]-1,
+ * whose positions in the sequence are q_pos0[b]+j; its keys/values are rows kv_start[b] ..
+ * kv_start[b]+kv_len[b]-1 (position t at row kv_start+t); its semantic kernels are rows
+ * kc_start[b] + c, c < floor((kv_len-w)/s)+1.  A packed prefill uses q_start = kv_start =
+ * cu_seqlens and q_pos0 = 0; a decode batch over a padded cache uses kv_start = b*max_len,
+ * q_len = 1, q_pos0 = kv_len-1 (the new token's K/V already stored).  Every query must see its
+ * own key: q_pos0 + q_len <= kv_len.  The per-sequence arrays live in DEVICE memory and are read
+ * by the kernels when they run; a call reads only the host bounds of the struct.  So a call, or
+ * a captured graph of calls, may be replayed after the caller rewrites the arrays on the device
+ * (the next decoding step's lengths), as long as the host bounds still hold.
  *
  * Ownership and errors: the caller allocates every buffer; the library never allocates,
  * frees or synchronises.  Calls only enqueue kernels on `stream` (a hipStream_t; NULL = the
  * default stream) and return.  Arguments are validated on the host before anything is
  * enqueued; a failed check returns a non-zero status, enqueues nothing and records a message
  * for infllm2_last_error() (thread-local).  A failed launch returns INFLLM2_ERR_HIP.  Device
- * contents (values, indices) are trusted; non-finite inputs give undefined results.
+ * contents (values, indices and the per-sequence arrays) are trusted: metadata that breaks the
+ * rules above or the host bounds, and non-finite inputs, give undefined results.
  */
 #ifndef INFLLM2_H
 #define INFLLM2_H
@@ -84,13 +88,18 @@ typedef struct {
                                over the visible kernels (see there) */
 } infllm2_params;
 
-#define INFLLM2_MAX_SEQS 64
-
-/* Per-sequence metadata, host memory, num_seqs in 1..INFLLM2_MAX_SEQS.  Row indices must be
- * below 2^31. */
+/* Per-sequence metadata.  The host bounds size the launches and are checked on the host; the
+ * six arrays (num_seqs entries each) are DEVICE memory, read only by the kernels and trusted
+ * (every q_len[b] <= max_q_len, kv_len[b] <= max_kv_len, q_start[b] + q_len[b] <= q_rows,
+ * row indices below 2^31).  kc_start may be NULL for calls without semantic kernels (top-k,
+ * attention). */
 typedef struct {
-  int32_t num_seqs;
-  const int64_t* q_start;
+  int32_t num_seqs;        /* host: number of sequences, >= 1 (no upper limit) */
+  int32_t max_q_len;       /* host: bound on every q_len[b] */
+  int32_t max_kv_len;      /* host: bound on every kv_len[b] */
+  int32_t q_rows;          /* host: rows of q / out / scores / block_idx / lse (a bound on
+                              every q_start[b] + q_len[b]) */
+  const int64_t* q_start;  /* device arrays */
   const int32_t* q_len;
   const int32_t* q_pos0;
   const int64_t* kv_start;
@@ -105,9 +114,9 @@ typedef struct {
  * binary exponent by at most 53 - p - ceil(log2 w) (p = 8 significant bits for bf16, 24 for
  * float32: 40 and 24 binades for w = 32), which keys of ordinary magnitude always meet; a window
  * spread wider may round once more in the sum and land one unit in the last place away.
- * prev_kv_len (host array, may be NULL = all zeros) makes the call incremental: only kernels
- * with prev_kv_len[b] < s*c + w <= kv_len[b] are written; other rows of `kernels` are left
- * untouched.  Reads k, writes kernels. */
+ * prev_kv_len (device array of num_seqs entries, may be NULL = all zeros) makes the call
+ * incremental: only kernels with prev_kv_len[b] < s*c + w <= kv_len[b] are written; other rows
+ * of `kernels` are left untouched.  Reads k, writes kernels. */
 infllm2_status infllm2_compress_kernels(const infllm2_params* params, const infllm2_seqs* seqs,
                                         const void* k, const int32_t* prev_kv_len,
                                         void* kernels, void* stream);
@@ -119,7 +128,7 @@ infllm2_status infllm2_compress_kernels(const infllm2_params* params, const infl
  *   S[b]  = max of u[c] over the kernels overlapping block b ([s*c, s*c+w) meets
  *           [B*b, B*b+B)), or -inf if none is visible,
  * written for blocks b = 0 .. floor(i/B) at scores[row, g, b]; entries after floor(i/B) are
- * not written.  nb_stride >= floor((q_pos0+q_len-1)/B)+1 for every sequence.  bf16 scores use
+ * not written.  nb_stride >= ceil(max_kv_len / B) (every reachable block).  bf16 scores use
  * the group-summed query in float32 split into two bf16 parts on the matrix cores (relative
  * error about 2^-16 of sum |q . kernel|); f32 scores use float32 arithmetic.
  * params->score_mode = 1 takes the other reading of the same passage: each head's scores are
@@ -137,7 +146,7 @@ infllm2_status infllm2_block_scores(const infllm2_params* params, const infllm2_
  * forced blocks F = {0 .. n_init-1} U {floor(i/B)-n_local+1 .. floor(i/B)} plus the
  * topk-|F| best other blocks by (score descending, block index ascending; -0 equals +0).
  * Written ascending to block_idx[row, g, 0..topk-1], padded with -1.  Scores are read for
- * b <= floor(i/B) only.  At most 4096 reachable blocks per row. */
+ * b <= floor(i/B) only.  Supported up to ceil(max_kv_len / B) = 4096 reachable blocks. */
 infllm2_status infllm2_topk_select(const infllm2_params* params, const infllm2_seqs* seqs,
                                    const float* scores, int32_t nb_stride, int32_t* block_idx,
                                    void* stream);
@@ -161,8 +170,8 @@ infllm2_status infllm2_sparse_attn_prefill(const infllm2_params* params,
  * and lse[row, h] = log sum_j exp(scale * q . k_j) (may be NULL).  No block selection and no
  * block_idx: the window is given in tokens (>= 1; window >= i + 1 is causal attention).  Same
  * layouts as infllm2_sparse_attn_prefill; params->topk and the kernel constants are validated
- * but unused.  Supported: bf16, block_size 64, head_dim 64 or 128, Hq/Hkv 8 or 16, query
- * positions below 2048 * 64 (else INFLLM2_ERR_UNSUPPORTED). */
+ * but unused.  Supported: bf16, block_size 64, head_dim 64 or 128, Hq/Hkv 8 or 16 and
+ * max_kv_len <= 2048 * 64 (else INFLLM2_ERR_UNSUPPORTED). */
 infllm2_status infllm2_sliding_window_attn(const infllm2_params* params,
                                            const infllm2_seqs* seqs, int32_t window,
                                            const void* q, const void* k, const void* v,
@@ -184,8 +193,8 @@ size_t infllm2_backward_workspace_size(const infllm2_params* params, const infll
  * as infllm2_sparse_attn_prefill wrote them, plus dout [q_rows, Hq, d] (bf16).  Outputs are
  * float32: dq [q_rows, Hq, d] (every row of every sequence written), dk and dv
  * [kv_rows, Hkv, d] (every key row of every sequence overwritten; keys no row attends to get
- * 0).  Supported: bf16, block_size 64, head_dim 64 or 128, Hq/Hkv 8 or 16, at most 2048
- * reachable blocks per sequence (else INFLLM2_ERR_UNSUPPORTED).  dk and dv are summed with
+ * 0).  Supported: bf16, block_size 64, head_dim 64 or 128, Hq/Hkv 8 or 16 and max_kv_len <=
+ * 2048 * 64 (else INFLLM2_ERR_UNSUPPORTED).  dk and dv are summed with
  * atomic float32 additions, so their last bits may differ between calls; sequences that
  * share key rows receive the sum of their gradients. */
 infllm2_status infllm2_sparse_attn_backward(const infllm2_params* params,
@@ -197,8 +206,9 @@ infllm2_status infllm2_sparse_attn_backward(const infllm2_params* params,
                                             size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace infllm2_sparse_attn_decode and infllm2_decode_step need for
- * `total_q_rows` query rows (sum of q_len) split `num_splits` ways (0 = the automatic choice of
- * each call).  The workspace holds per-(row, KV head) counters, then the per-split partial
+ * `total_q_rows` rows of q (the q_rows of the calls' infllm2_seqs) split `num_splits` ways (0 =
+ * the automatic choice of each call).  The workspace holds per-(row, KV head) counters, indexed
+ * by the query row, then the per-split partial
  * results: it must be zero-filled before its first use, and every call leaves the counters
  * zero again.  Calls that share a workspace must not overlap
  * (enqueue them on one stream). */
@@ -216,7 +226,7 @@ infllm2_status infllm2_sparse_attn_decode(const infllm2_params* params, const in
                                           float* lse, void* stream);
 
 /* One decoding step in the method's order (csdn summary 2.1.1-2.1.3): semantic kernels
- * completed since prev_kv_len (host array, may be NULL), block scores into `scores` (nb_stride
+ * completed since prev_kv_len (device array, may be NULL), block scores into `scores` (nb_stride
  * floats per (row, KV head)), top-k into block_idx, then split-KV attention.  Arguments mean
  * what they mean in the separate calls, and the same checks apply; `workspace` is always
  * required here.  For bf16, block 64, kernels 32/16, d 64 or 128, groups of 8 or 16 and score

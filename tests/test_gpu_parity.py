@@ -121,6 +121,21 @@ def test_sixty_four_sequences_packed():
         check_sequence(wl, res, b, label="64 seqs")
 
 
+def test_hundred_sequences_packed():
+    """No cap on the sequence table: 100 packed sequences with seeded lengths from 0 to 1200
+    (empty, single-token and shorter-than-a-window ones among them), every row of every
+    sequence."""
+    p = synth.config_params("prefill32k")
+    rng = np.random.default_rng(52)
+    lens = [int(x) for x in rng.integers(0, 1200, 100)]
+    lens[:4] = [0, 1, 31, 64]
+    wl = synth.make_prefill("hundred", p, lens, seed=52)
+    log("case 100 packed sequences")
+    res = run_prefill_stages(wl)
+    for b in range(wl.num_seqs):
+        check_sequence(wl, res, b, label="100 seqs")
+
+
 def test_chunked_prefill_against_cache():
     """Queries for the last tokens only (q_pos0 > 0) attend to the whole cached sequence."""
     p = synth.config_params("prefill32k")
@@ -296,6 +311,75 @@ def test_decode_sixty_four_sequences():
     wl = synth.make_decode("dec-64", p, batch=64, max_len=6000, steps=2, seed=49, kv_len0=kv0)
     log("case decode 64 sequences")
     run_decode(wl, 2)
+
+
+def test_decode_hundred_sequences():
+    """A decoding batch of 100 caches (seeded lengths from 1 token), two steps."""
+    p = synth.config_params("decode128k")
+    rng = np.random.default_rng(53)
+    kv0 = [int(x) for x in rng.integers(1, 3990, 100)]
+    kv0[:3] = [1, 20, 63]
+    wl = synth.make_decode("dec-100", p, batch=100, max_len=4000, steps=2, seed=53, kv_len0=kv0)
+    log("case decode 100 sequences")
+    run_decode(wl, 2)
+
+
+def test_decode_step_graph_replayed_with_device_metadata():
+    """One decode step captured once in a HIP graph and replayed for three consecutive steps:
+    between replays only the device copies of the lengths, positions, previous lengths and the
+    new queries are rewritten.  Every replay equals the eagerly run step (indices and scores bit
+    for bit, outputs to float32 rounding) and is checked against the oracle."""
+    p = synth.config_params("decode128k")
+    B, Lmax, steps = 3, 4096, 3
+    wl = synth.make_decode("dec-graph", p, batch=B, max_len=Lmax, steps=steps, seed=54,
+                           kv_len0=[4000, 3000, 2000])
+    eager = run_decode(wl, steps, check=False, label="graph eager")
+    Ck = orc.num_kernels(Lmax, p.kernel_size, p.kernel_stride)
+    k = dev(wl.k.reshape(B * Lmax, p.num_kv_heads, p.head_dim), p.dtype)
+    v = dev(wl.v.reshape(B * Lmax, p.num_kv_heads, p.head_dim), p.dtype)
+    kern = torch.zeros((B * Ck, p.num_kv_heads, p.head_dim), dtype=k.dtype, device="cuda")
+    kv0 = wl.kv_len0.astype(np.int64)
+    s0 = lib.Seqs.decode(kv0, Lmax, Ck)
+    lib.compress_kernels(p, lib.Seqs(s0.q_start, np.zeros(B), np.zeros(B), s0.kv_start, kv0,
+                                     s0.kc_start), k, kern)
+    cuda = lambda a, dt: torch.tensor(np.asarray(a), dtype=dt, device="cuda")
+    q_start, q_len = cuda(np.arange(B), torch.int64), cuda(np.ones(B), torch.int32)
+    kv_start, kc_start = cuda(np.arange(B) * Lmax, torch.int64), cuda(np.arange(B) * Ck, torch.int64)
+    kv_len, q_pos0, prev = (cuda(kv0 + 1, torch.int32), cuda(kv0, torch.int32),
+                            cuda(kv0, torch.int32))
+    seqs = lib.Seqs.on_device(q_start, q_len, q_pos0, kv_start, kv_len, kc_start, max_q_len=1,
+                              max_kv_len=Lmax, q_rows=B)
+    q = dev(wl.q_steps[0], p.dtype)
+    bufs = lib.pipeline.decode_buffers(p, B, Lmax // p.block_size, 0, "cuda")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lib.decode_step(p, seqs, q, k, v, kern, prev, bufs)
+    torch.cuda.synchronize()
+    for st in range(steps):
+        kv = kv0 + st + 1
+        kv_len.copy_(cuda(kv, torch.int32))
+        q_pos0.copy_(cuda(kv - 1, torch.int32))
+        prev.copy_(cuda(kv - 1, torch.int32))
+        q.copy_(dev(wl.q_steps[st], p.dtype))
+        torch.cuda.synchronize()
+        log(f"case decode graph replay step {st}")
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {n: host(bufs[n]) for n in ("scores", "idx", "out", "lse")}
+        assert np.array_equal(got["idx"], eager[st]["idx"]), f"replay {st}: indices differ"
+        for r in range(B):
+            nb = int(kv[r] - 1) // p.block_size + 1
+            assert np.array_equal(got["scores"][r, :, :nb], eager[st]["scores"][r, :, :nb])
+        assert np.abs(got["out"] - eager[st]["out"]).max() <= 1e-2
+        assert np.abs(got["lse"] - eager[st]["lse"]).max() <= 1e-4
+        for b in range(B):
+            L = int(kv[b])
+            check_decode_seq(p, wl.k[b, :L], wl.v[b, :L], wl.q_steps[st][b:b + 1],
+                             host(kern[b * Ck:(b + 1) * Ck]), got["scores"][b:b + 1],
+                             got["idx"][b:b + 1], got["out"][b:b + 1], got["lse"][b:b + 1],
+                             f"graph step {st} seq {b}")
+    assert int(torch.count_nonzero(bufs["workspace"].view(torch.int32)[:decode_counters_bytes(B, p) // 4])) == 0
 
 
 @pytest.mark.parametrize("splits", [1, 3, 7])
