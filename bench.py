@@ -66,11 +66,12 @@ def attended_keys_total(seq_lens, block, topk):
     return tot
 
 
-def run_prefill(args, torch, pkg, synth):
-    wl = synth.make(args.workload)
+def run_prefill(args, torch, pkg, synth, workload=None, keep=True):
+    workload = workload or args.workload
+    wl = synth.make(workload)
     p = wl.params
     lens = [int(x) for x in wl.q_len]
-    log(f"workload {args.workload}: seqs {lens}, inputs drawn")
+    log(f"workload {workload}: seqs {lens}, inputs drawn")
     seqs = pkg.Seqs.packed_prefill(lens)
     dt = torch.bfloat16 if p.dtype == "bf16" else torch.float32
     q = torch.from_numpy(wl.q).cuda().to(dt)
@@ -123,14 +124,14 @@ def run_prefill(args, torch, pkg, synth):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     launches = (items + cus // 8 * 8 - 1) // (cus // 8 * 8)
     result = dict(
-        workload=args.workload, tokens=T, seq_lens=lens, p=p, ms_step=ms_step, stage=stage,
+        workload=workload, tokens=T, seq_lens=lens, p=p, ms_step=ms_step, stage=stage,
         flops=flops, tflops=tflops, keys=keys, launches=launches,
         stage_gbs={"compress": bytes_compress / (stage["compress"] * 1e-3) / 1e9,
                    "scores": bytes_scores / (stage["scores"] * 1e-3) / 1e9,
                    "topk": bytes_topk / (stage["topk"] * 1e-3) / 1e9},
         wl=wl, kernels_gpu=bufs["kernels"],
         gather=gather_bound(p, bufs["idx"].cpu().numpy(), lens, flops, stage["attention"]))
-    if args.no_backward and args.no_window and args.no_score_mode1 and args.no_chunk:
+    if not keep or (args.no_backward and args.no_window and args.no_score_mode1 and args.no_chunk):
         del q, k, v, bufs
     else:
         result["device"] = dict(q=q, k=k, v=v, seqs=seqs, idx=bufs["idx"], out=bufs["out"],
@@ -150,7 +151,7 @@ def run_chunk(args, torch, pkg, pre):
     k, v = dv_["k"], dv_["v"]
     seqs = pkg.Seqs(np.array([0]), np.array([C]), np.array([L - C]), np.array([0]), np.array([L]),
                     np.array([0]))
-    prev = np.array([L - C], np.int32)
+    prev = torch.tensor([L - C], dtype=torch.int32, device="cuda")
     nb = (L - 1) // p.block_size + 1
     dt = q.dtype
     scores = torch.empty((C, p.num_kv_heads, nb), dtype=torch.float32, device="cuda")
@@ -194,6 +195,30 @@ def run_chunk(args, torch, pkg, pre):
                 roofline={"kernel": "attn_tile (sparse_attn_prefill, q_pos0 > 0)", "bound": "mfma",
                           "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                           "frac": tflops / PEAK_BF16_TFLOPS, "flops_per_call": flops})
+
+
+def prefill_leg(args, torch, pkg, synth, workload):
+    """Another prefill configuration, timed like the headline one (whole step of the four calls
+    and its attention with the roofline against the bf16 peak); a parity-tested config, reported
+    beside the headline workload."""
+    r = run_prefill(args, torch, pkg, synth, workload=workload, keep=False)
+    st = r["stage"]
+    out = {"workload": workload, "seq_lens": r["seq_lens"], "ms_per_step": r["ms_step"],
+           "tokens_per_s": r["tokens"] / (r["ms_step"] * 1e-3), "stages_ms": st,
+           "stages_gbs": r["stage_gbs"],
+           "attention_tokens_per_s": r["tokens"] / (st["attention"] * 1e-3),
+           "roofline": {"kernel": "attn_tile (sparse_attn_prefill)", "bound": "mfma",
+                        "achieved": r["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": r["tflops"] / PEAK_BF16_TFLOPS, "traffic": None,
+                        "flops_per_call": r["flops"], "launches_per_call": r["launches"],
+                        "avg_launch_us": st["attention"] * 1e3 / r["launches"],
+                        "gather": r["gather"]}}
+    tr = measured_traffic(workload)
+    if tr is not None:
+        out["roofline"]["traffic"] = tr["fetch_bytes_per_call"] + tr["write_bytes_per_call"]
+    del r
+    torch.cuda.empty_cache()
+    return out
 
 
 def gather_bound(p, idx, seq_lens, flops, ms_attention):
@@ -457,11 +482,14 @@ def run_decode(args, torch, pkg, synth):
     bufs = pkg.pipeline.decode_buffers(p, B, nb, args.decode_splits, "cuda")
     stream = torch.cuda.current_stream()
     seqs = [pkg.Seqs.decode(kv0 + st + 1, Lmax, Ck) for st in range(args.decode_steps)]
-    prevs = [(kv0 + st).astype(np.int32) for st in range(args.decode_steps)]
+    prevs = [torch.tensor(kv0 + st, dtype=torch.int32, device="cuda")
+             for st in range(args.decode_steps)]
+    for sq in seqs:
+        sq.c(k.device)                  # the metadata's device copies, made before any timing
 
-    def all_steps():
+    def all_steps(on=stream):
         for st in range(args.decode_steps):
-            pkg.decode_step(p, seqs[st], qs[st], k, v, kern, prevs[st], bufs, stream=stream)
+            pkg.decode_step(p, seqs[st], qs[st], k, v, kern, prevs[st], bufs, stream=on)
 
     for _ in range(max(1, args.warmup)):
         pkg.compress_kernels(p, s0, k, kern, stream=stream)
@@ -513,6 +541,22 @@ def run_decode(args, torch, pkg, synth):
     stage_us = {n: float(np.mean([sev[st][i].elapsed_time(sev[st][i + 1]) * 1e3
                                   for st in range(args.decode_steps)]))
                 for i, n in enumerate(["compress", "scores", "topk", "attention"])}
+    # the same steps captured once as a HIP graph (the metadata is read from device memory when
+    # the kernels run) and replayed: host-inclusive wall time per step, launch and sync included
+    graph = torch.cuda.CUDAGraph()
+    pkg.compress_kernels(p, s0, k, kern, stream=stream)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        all_steps(on=None)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = 20
+    t2 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_us = (time.perf_counter() - t2) * 1e6 / (reps * args.decode_steps)
+    del graph
     # bytes a step must move: the kernel cache read for scoring, the selected K/V blocks, q/out
     kv_len = kv0 + args.decode_steps
     C = np.array([pkg.num_kernels(int(L), p.kernel_size, p.kernel_stride) for L in kv_len])
@@ -526,6 +570,7 @@ def run_decode(args, torch, pkg, synth):
     out = dict(us_per_step=us, us_per_step_sweeps=[round(x, 2) for x in sweeps],
                us_per_step_wall=wall * 1e6 / args.decode_steps,
                host_enqueue_us_per_step=enqueue * 1e6 / args.decode_steps,
+               us_per_step_graph_wall=graph_us,
                gpu_busy_while_enqueueing=bool(enqueue < SPIN_SECONDS), stages_us=stage_us,
                tokens_per_s=B / (us * 1e-6), batch=B, cache_len=int(Lmax),
                steps=args.decode_steps, bytes_per_step=total,
@@ -537,40 +582,49 @@ def run_decode(args, torch, pkg, synth):
 
 
 def cpu_baseline(pre, budget_s: float):
-    """The float64 oracle on the host cores over a bounded sample of the same workload."""
+    """The float64 oracle on the host cores: kernel compression, then block scores and top-k
+    for every query row of the sequence, then attention (on those indices) for rows spread
+    evenly over it until `budget_s` seconds have passed."""
     import multiprocessing as mp
     from oracle import infllm2_oracle as orc
     wl = pre["wl"]
     p = wl.params
+    # one GPU's share of the host: at most 16 processes, whatever the machine has
     workers = max(1, min(16, len(os.sched_getaffinity(0))))
     L = int(wl.q_len[0])
     sl_q, sl_k = wl.seq_slices(0)
     t0 = time.perf_counter()
     kern = orc.compress_kernels(wl.k[sl_k], p.kernel_size, p.kernel_stride, p.dtype)
     t_comp = time.perf_counter() - t0
+    idx = mp.RawArray("i", L * p.num_kv_heads * p.topk)
     global _CPU_STATE
-    _CPU_STATE = (wl.q[sl_q], wl.k[sl_k], wl.v[sl_k], p, kern)
-    # chunk c holds rows c, c + n_chunks, ...: every chunk spans the whole sequence, so the
-    # chunks finished within the budget are an evenly spread sample of its rows
-    n_chunks = max(1, L // 8)
-    chunks = (np.arange(c, L, n_chunks) for c in range(n_chunks))
+    _CPU_STATE = (wl.q[sl_q], wl.k[sl_k], wl.v[sl_k], p, kern, idx)
     ctx = mp.get_context("fork")
     with ctx.Pool(workers, initializer=_limit_threads) as pool:
+        # every row's indices: chunk c holds rows c, c + n, c + 2n, ... (balanced over positions)
+        n_idx = workers * 16
         t1 = time.perf_counter()
+        covered = sum(pool.map(_cpu_index_rows, [np.arange(c, L, n_idx) for c in range(n_idx)]))
+        t_idx = time.perf_counter() - t1
+        # attention on the oracle's own indices for evenly spread rows, within the budget
+        n_att = max(1, L // 8)
+        t2 = time.perf_counter()
         done = 0
-        for res in pool.imap_unordered(_cpu_rows, chunks):
+        for res in pool.imap_unordered(_cpu_attention_rows,
+                                       (np.arange(c, L, n_att) for c in range(n_att))):
             done += res
-            if time.perf_counter() - t1 > budget_s:
+            if time.perf_counter() - t2 > budget_s:
                 break
-        t_rows = time.perf_counter() - t1
-    per_row = t_rows / max(done, 1)
-    tok_s = L / (t_comp + per_row * L)
+        t_att = time.perf_counter() - t2
+    per_row = t_att / max(done, 1)
+    tok_s = L / (t_comp + t_idx + per_row * L)
     return {"value": tok_s, "unit": "tokens/s", "cores": workers, "kind": "oracle",
-            "cpu_model": _cpu_model(),
-            "sample": f"{args_workload_name(pre)}: full kernel compression ({t_comp:.1f} s) + "
-                      f"block scores, top-k and attention for {done} of {L} query rows spread evenly "
-                      f"over the sequence ({t_rows:.1f} s on {workers} single-threaded "
-                      f"processes), float64 numpy; tokens/s = L / (compression + L x mean "
+            "cpu_model": _cpu_model(), "index_rows": int(covered), "attention_rows": int(done),
+            "sample": f"{args_workload_name(pre)}: full kernel compression ({t_comp:.1f} s), block "
+                      f"scores and top-k for all {covered} of {L} query rows ({t_idx:.1f} s), "
+                      f"attention for {done} rows spread evenly over the sequence "
+                      f"({t_att:.1f} s); {workers} single-threaded processes, float64 numpy; "
+                      f"tokens/s = L / (compression + scores and top-k + L x mean attention "
                       f"time per row)"}
 
 
@@ -600,10 +654,20 @@ def _limit_threads():
         pass
 
 
-def _cpu_rows(rows):
+def _cpu_index_rows(rows):
     from oracle import infllm2_oracle as orc
-    q, k, v, p, kern = _CPU_STATE
-    orc.run_sequence(q, k, v, p, rows=rows, kernels=kern)
+    q, k, v, p, kern, idx = _CPU_STATE
+    res = orc.run_sequence(q, k, v, p, rows=rows, kernels=kern, with_attention=False)
+    out = np.frombuffer(idx, dtype=np.int32).reshape(-1, p.num_kv_heads, p.topk)
+    out[rows] = res.idx
+    return len(rows)
+
+
+def _cpu_attention_rows(rows):
+    from oracle import infllm2_oracle as orc
+    q, k, v, p, kern, idx = _CPU_STATE
+    sel = np.frombuffer(idx, dtype=np.int32).reshape(-1, p.num_kv_heads, p.topk)[rows]
+    orc.sparse_attention(np.asarray(q[rows], dtype=np.float64), rows, k, v, sel, p)
     return len(rows)
 
 
@@ -690,10 +754,12 @@ def main():
     ap.add_argument("--no-window", action="store_true")
     ap.add_argument("--no-score-mode1", action="store_true")
     ap.add_argument("--no-chunk", action="store_true")
+    ap.add_argument("--no-other-prefills", action="store_true",
+                    help="skip the 32K and varlen prefill legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the streaming-copy and GEMM rate measurements")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=8.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a streaming copy of MIB MiB (counter calibration)")
     ap.add_argument("--summarize-profile", nargs="+", metavar="ARG",
@@ -752,6 +818,12 @@ def main():
         line["roofline"]["traffic_split"] = {"fetch": tr["fetch_bytes_per_call"],
                                              "write": tr["write_bytes_per_call"],
                                              "unit": "bytes per call"}
+    if not args.no_other_prefills:
+        for name in ("prefill32k", "varlen"):
+            if name != pre["workload"]:
+                line[name] = prefill_leg(args, torch, pkg, synth, name)
+                log(f"{name}: {line[name]['ms_per_step']:.2f} ms per step, attention "
+                    f"{line[name]['roofline']['frac']:.3f} of bf16 peak")
     if not args.no_chunk:
         line["chunk"] = run_chunk(args, torch, pkg, pre)
         log(f"chunk: {line['chunk']['ms_per_chunk']:.2f} ms per {line['chunk']['chunk_tokens']} tokens")
