@@ -9,6 +9,6 @@ from ._lib import (  # noqa: F401
     F32, BF16, InfLLM2Error, Params, Seqs, library_path, load_library,
     compress_kernels, block_scores, topk_select, sparse_attn_prefill,
     decode_workspace_size, sparse_attn_decode, decode_step_fused, version, EXPORTED_SYMBOLS,
-    backward_workspace_size, sparse_attn_backward, sliding_window_attn,
+    backward_workspace_size, sparse_attn_backward, sliding_window_attn, decode_step_noalloc,
 )
 from .pipeline import prefill, decode_step, num_kernels  # noqa: F401

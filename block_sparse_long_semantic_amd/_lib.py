@@ -70,6 +70,8 @@ def _declare(lib):
         "infllm2_decode_step": (st, [P, S, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp,
                                      ctypes.c_int32, vp, ctypes.c_size_t, vp, vp, vp]),
         "infllm2_sliding_window_attn": (st, [P, S, ctypes.c_int32, vp, vp, vp, vp, vp, vp]),
+        "infllm2_decode_step_noalloc": (st, [P, S, vp, vp, vp, vp, vp, vp, ctypes.c_int32, vp,
+                                             ctypes.c_int32, vp, vp, vp]),
         "infllm2_backward_workspace_size": (ctypes.c_size_t, [P, S]),
         "infllm2_sparse_attn_backward": (st, [P, S, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                               ctypes.c_size_t, vp]),
@@ -410,6 +412,25 @@ def decode_step_fused(params, seqs: Seqs, q, k_cache, v_cache, kernels, prev_kv_
         workspace.numel() * workspace.element_size(), _ptr(out, "out", dt),
         _ptr(lse, "lse", torch.float32) if lse is not None else None,
         _stream(stream, q.device)), "infllm2_decode_step")
+
+
+def decode_step_noalloc(params, seqs: Seqs, q, k_cache, v_cache, kernels, prev_kv_len, scores,
+                        block_idx, out, lse, num_splits=0, stream=None):
+    """infllm2_decode_step_noalloc: the decode step with the library's own device workspace
+    (no workspace argument, nothing allocated by the library)."""
+    p = Params.from_any(params)
+    lib = load_library()
+    dt = _elem_dtype(p)
+    torch = _torch()
+    keep, prev = _device_ints(prev_kv_len, q.device, "prev_kv_len")
+    cp, cs = p.c(), seqs.c(q.device)
+    _check(lib.infllm2_decode_step_noalloc(
+        ctypes.byref(cp), ctypes.byref(cs), _ptr(q, "q", dt), _ptr(k_cache, "k_cache", dt),
+        _ptr(v_cache, "v_cache", dt), _ptr(kernels, "kernels", dt), prev,
+        _ptr(scores, "scores", torch.float32, 3), int(scores.shape[2]),
+        _ptr(block_idx, "block_idx", torch.int32), int(num_splits), _ptr(out, "out", dt),
+        _ptr(lse, "lse", torch.float32) if lse is not None else None,
+        _stream(stream, q.device)), "infllm2_decode_step_noalloc")
 
 
 def backward_workspace_size(params, seqs: Seqs) -> int:

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libinfllm2.so")
 SOURCES = ["compress.hip", "scores.hip", "topk.hip", "attn.hip", "attn_tile.hip", "attn_decode.hip",
-           "attn_bwd.hip", "api.cpp"]
+           "attn_bwd.hip", "noalloc.hip", "api.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -375,12 +375,16 @@ infllm2_status infllm2_sparse_attn_backward(const infllm2_params* params,
                     "sparse_attn_backward launch");
 }
 
-infllm2_status infllm2_decode_step(const infllm2_params* params, const infllm2_seqs* seqs,
+}  // extern "C"
+
+namespace {
+
+static infllm2_status decode_step_impl(const infllm2_params* params, const infllm2_seqs* seqs,
                                   const void* q, const void* k_cache, const void* v_cache,
                                   void* kernels, const int32_t* prev_kv_len, float* scores,
                                   int32_t nb_stride, int32_t* block_idx, int32_t num_splits,
                                   void* workspace, size_t workspace_bytes, void* out, float* lse,
-                                  void* stream) {
+                                  void* stream, bool noalloc) {
   Geom g;
   SeqTable t;
   infllm2_status st = check_params(params, &g);
@@ -393,6 +397,11 @@ infllm2_status infllm2_decode_step(const infllm2_params* params, const infllm2_s
     if (st != INFLLM2_OK) return st;
     st = infllm2_topk_select(params, seqs, scores, nb_stride, block_idx, stream);
     if (st != INFLLM2_OK) return st;
+    if (noalloc) {   // the attention's completion counters start at zero (see below)
+      const hipError_t e = infllm2::launch_fill_zero(
+          workspace, infllm2::decode_layout(t.q_rows * g.Hkv).part, static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) return hip_status(e, "decode_step_noalloc clear");
+    }
     return infllm2_sparse_attn_decode(params, seqs, q, k_cache, v_cache, block_idx, num_splits,
                                       workspace, workspace_bytes, out, lse, stream);
   }
@@ -417,12 +426,63 @@ infllm2_status infllm2_decode_step(const infllm2_params* params, const infllm2_s
   if (!aligned16(workspace)) return fail(INFLLM2_ERR_ALIGN, "workspace must be 16-byte aligned");
   if (workspace_bytes < need)
     return fail(INFLLM2_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  if (noalloc) {
+    // the completion counters must start at zero: a kernel clears them (every call leaves them
+    // zero, but the buffer is shared by every call on this GPU and outlives failed ones)
+    const hipError_t e = infllm2::launch_fill_zero(
+        workspace, infllm2::decode_layout(t.q_rows * g.Hkv).part, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_status(e, "decode_step_noalloc clear");
+  }
   st = infllm2_compress_kernels(params, seqs, k_cache, prev_kv_len, kernels, stream);
   if (st != INFLLM2_OK) return st;
   return hip_status(infllm2::launch_decode_step(g, t, q, kernels, k_cache, v_cache, scores,
                                                  nb_stride, block_idx, splits, workspace, out,
                                                  lse, static_cast<hipStream_t>(stream)),
                     "decode_step launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+infllm2_status infllm2_decode_step(const infllm2_params* params, const infllm2_seqs* seqs,
+                                  const void* q, const void* k_cache, const void* v_cache,
+                                  void* kernels, const int32_t* prev_kv_len, float* scores,
+                                  int32_t nb_stride, int32_t* block_idx, int32_t num_splits,
+                                  void* workspace, size_t workspace_bytes, void* out, float* lse,
+                                  void* stream) {
+  return decode_step_impl(params, seqs, q, k_cache, v_cache, kernels, prev_kv_len, scores,
+                          nb_stride, block_idx, num_splits, workspace, workspace_bytes, out, lse,
+                          stream, false);
+}
+
+infllm2_status infllm2_decode_step_noalloc(const infllm2_params* params, const infllm2_seqs* seqs,
+                                          const void* q, const void* k_cache,
+                                          const void* v_cache, void* kernels,
+                                          const int32_t* prev_kv_len, float* scores,
+                                          int32_t nb_stride, int32_t* block_idx,
+                                          int32_t num_splits, void* out, float* lse,
+                                          void* stream) {
+  Geom g;
+  infllm2_status st = check_params(params, &g);
+  if (st != INFLLM2_OK) return st;
+  if (seqs == nullptr) return fail(INFLLM2_ERR_NULL, "seqs is NULL");
+  if (seqs->q_rows < 0) return fail(INFLLM2_ERR_SHAPE, "negative bound q_rows %d", seqs->q_rows);
+  const int splits = num_splits > 0 ? num_splits : infllm2::decode_step_splits(g);
+  const size_t need = infllm2::decode_workspace(g, seqs->q_rows, std::max(splits,
+                                                decode_splits(g, params->dtype, seqs->q_rows,
+                                                              num_splits)));
+  if (need > infllm2::kNoAllocScratchBytes)
+    return fail(INFLLM2_ERR_WORKSPACE,
+                "decode step needs %zu bytes of workspace, above the %zu-byte static buffer of "
+                "infllm2_decode_step_noalloc (fewer rows or splits, or infllm2_decode_step with "
+                "a workspace)", need, infllm2::kNoAllocScratchBytes);
+  void* ws = nullptr;
+  const hipError_t e = infllm2::noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e, "decode_step_noalloc scratch lookup");
+  return decode_step_impl(params, seqs, q, k_cache, v_cache, kernels, prev_kv_len, scores,
+                          nb_stride, block_idx, num_splits, ws, infllm2::kNoAllocScratchBytes, out,
+                          lse, stream, true);
 }
 
 }  // extern "C"

@@ -155,6 +155,12 @@ __host__ __device__ inline DecodeLayout decode_layout(int pairs) {
   return L;
 }
 
+// The allocation-free decoding step's workspace: a file-scope device array (noalloc.hip) of this
+// many bytes per GPU; noalloc_scratch() gives its device address on the current device.
+constexpr size_t kNoAllocScratchBytes = size_t{16} << 20;
+hipError_t noalloc_scratch(void** ptr);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+
 // Launch entry points (one per translation unit).  All return hipSuccess or the launch error.
 hipError_t launch_compress(const Geom& g, int dtype, const SeqTable& t, const void* k,
                            void* kernels, hipStream_t stream);

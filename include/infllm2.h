@@ -242,6 +242,23 @@ infllm2_status infllm2_decode_step(const infllm2_params* params, const infllm2_s
                                   void* workspace, size_t workspace_bytes, void* out, float* lse,
                                   void* stream);
 
+/* infllm2_decode_step for callers that cannot allocate device memory (code under HIP graph
+ * capture that may not call hipMalloc, tight serving loops, harnesses that forbid allocation):
+ * the same step, arguments and results, without the workspace arguments.  Its workspace is a
+ * buffer the library keeps in device memory, 16 MiB on each GPU it runs on (held until the
+ * process ends); a step whose workspace (infllm2_decode_workspace_size for seqs->q_rows rows and
+ * num_splits) exceeds it returns INFLLM2_ERR_WORKSPACE and enqueues nothing.  The call allocates
+ * nothing; a kernel clears the buffer's completion counters before the step's attention.  Every
+ * call on one GPU shares that GPU's buffer, so calls that overlap on one GPU (other streams,
+ * other host threads) race: the caller must serialise them. */
+infllm2_status infllm2_decode_step_noalloc(const infllm2_params* params, const infllm2_seqs* seqs,
+                                          const void* q, const void* k_cache,
+                                          const void* v_cache, void* kernels,
+                                          const int32_t* prev_kv_len, float* scores,
+                                          int32_t nb_stride, int32_t* block_idx,
+                                          int32_t num_splits, void* out, float* lse,
+                                          void* stream);
+
 /* Static text for a status code. */
 const char* infllm2_status_string(infllm2_status status);
 
