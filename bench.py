@@ -41,13 +41,20 @@ ATTN_SOURCES = ["block_sparse_long_semantic_amd/csrc/attn_tile.hip",
                 "block_sparse_long_semantic_amd/csrc/internal.h"]
 BWD_SOURCES = ["block_sparse_long_semantic_amd/csrc/attn_bwd.hip",
                "block_sparse_long_semantic_amd/csrc/internal.h"]
+def _attn_form(kernel: str, bwd: str, win: str) -> bool:
+    """True for an attn_tile instance whose gradient and window flags (its 6th and 7th
+    template arguments) are the given ones."""
+    if not kernel.startswith("attn_tile<"):
+        return False
+    args = [a.strip() for a in kernel[kernel.index("<") + 1:kernel.rindex(">")].split(",")]
+    return len(args) >= 7 and args[5] == bwd and args[6] == win
+
+
 # kernels whose HBM traffic the committed counter summary records: role -> (name test, sources)
 TRAFFIC_ROLES = {
-    "prefill_attention": (lambda k: k.startswith("attn_tile") and k.endswith("false, false>"),
-                          ATTN_SOURCES),
-    "backward_dq": (lambda k: k.startswith("attn_tile") and k.endswith("true, false>"), ATTN_SOURCES),
-    "window_attention": (lambda k: k.startswith("attn_tile") and k.endswith("false, true>"),
-                         ATTN_SOURCES),
+    "prefill_attention": (lambda k: _attn_form(k, "false", "false"), ATTN_SOURCES),
+    "backward_dq": (lambda k: _attn_form(k, "true", "false"), ATTN_SOURCES),
+    "window_attention": (lambda k: _attn_form(k, "false", "true"), ATTN_SOURCES),
     "backward_dkv": (lambda k: k.startswith("bwd_dkv"), BWD_SOURCES),
 }
 
@@ -119,8 +126,11 @@ def run_prefill(args, torch, pkg, synth, workload=None, keep=True):
     bytes_scores = T * Hq * d * 2 + C * Hkv * d * 2 + causal_blocks * Hkv * 4
     bytes_topk = causal_blocks * Hkv * 4 + T * Hkv * p.topk * 4
     bytes_compress = T * Hkv * d * 2 + C * Hkv * d * 2
-    # the attention call launches its tiles in rounds of one workgroup per compute unit
-    items = sum((L + TILE_TOKENS - 1) // TILE_TOKENS for L in lens) * Hkv
+    # the attention call launches its tiles in rounds of one workgroup per compute unit; the
+    # grid covers the library's host bound on the tiles (it sees only the metadata's bounds:
+    # sequences, longest query run, total rows), not the exact count
+    n_seq, max_q = len(lens), max(lens)
+    items = min(n_seq * -(-max_q // TILE_TOKENS), -(-T // TILE_TOKENS) + n_seq) * Hkv
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     launches = (items + cus // 8 * 8 - 1) // (cus // 8 * 8)
     result = dict(
@@ -543,20 +553,22 @@ def run_decode(args, torch, pkg, synth):
                 for i, n in enumerate(["compress", "scores", "topk", "attention"])}
     # the same steps captured once as a HIP graph (the metadata is read from device memory when
     # the kernels run) and replayed: host-inclusive wall time per step, launch and sync included
-    graph = torch.cuda.CUDAGraph()
-    pkg.compress_kernels(p, s0, k, kern, stream=stream)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(graph):
-        all_steps(on=None)
-    graph.replay()
-    torch.cuda.synchronize()
-    reps = 20
-    t2 = time.perf_counter()
-    for _ in range(reps):
+    graph_us = None
+    if not args.no_decode_graph:
+        graph = torch.cuda.CUDAGraph()
+        pkg.compress_kernels(p, s0, k, kern, stream=stream)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            all_steps(on=None)
         graph.replay()
-    torch.cuda.synchronize()
-    graph_us = (time.perf_counter() - t2) * 1e6 / (reps * args.decode_steps)
-    del graph
+        torch.cuda.synchronize()
+        reps = 20
+        t2 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_us = (time.perf_counter() - t2) * 1e6 / (reps * args.decode_steps)
+        del graph
     # bytes a step must move: the kernel cache read for scoring, the selected K/V blocks, q/out
     kv_len = kv0 + args.decode_steps
     C = np.array([pkg.num_kernels(int(L), p.kernel_size, p.kernel_stride) for L in kv_len])
@@ -688,6 +700,56 @@ def _csv_rows(directory: str, suffix: str):
         return list(csv.DictReader(f))
 
 
+def summarize_counters(dirs, kernels=("attn_tile", "attn_decode", "decode_select", "scores_mfma",
+                                      "scores_decode", "topk_kernel", "topk_wide", "compress_kernel")):
+    """Per-kernel totals of every counter in one or more rocprofv3 --pmc runs (sums over the
+    kernel's dispatches), one table per run, plus derived ratios where their counters are
+    present.  GRBM_GUI_ACTIVE is summed over the 8 XCDs, so the MFMA busy fraction is
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 4 SIMDs x compute units)."""
+    cus = 256
+    for directory in dirs:
+        tot, disp = {}, {}
+        for r in _csv_rows(directory, "counter_collection.csv"):
+            k = _short(r["Kernel_Name"])
+            if not any(k.startswith(n) for n in kernels):
+                continue
+            d = tot.setdefault(k, {})
+            c = r["Counter_Name"]
+            c = c[:-4] if c.endswith("_sum") else c
+            d[c] = d.get(c, 0.0) + float(r["Counter_Value"])
+            disp.setdefault(k, set()).add(r["Dispatch_Id"])
+        names = sorted({c for d in tot.values() for c in d})
+        print(f"run `{os.path.basename(os.path.normpath(directory))}`\n")
+        print("| kernel | dispatches | " + " | ".join(names) + " |")
+        print("|---|---:|" + "---:|" * len(names))
+        for k, d in sorted(tot.items()):
+            print(f"| `{k}` | {len(disp[k])} | " +
+                  " | ".join(f"{d.get(c, 0.0):.4g}" for c in names) + " |")
+        print()
+        for k, d in sorted(tot.items()):
+            parts = []
+            g = d.get("GRBM_GUI_ACTIVE")
+            if g and "SQ_VALU_MFMA_BUSY_CYCLES" in d:
+                parts.append(f"MFMA busy {d['SQ_VALU_MFMA_BUSY_CYCLES'] / (g / 8 * 4 * cus):.3f}")
+            if "SQ_LDS_BANK_CONFLICT" in d and d.get("SQ_LDS_IDX_ACTIVE"):
+                parts.append(f"LDS bank-conflict cycles / LDS active {d['SQ_LDS_BANK_CONFLICT'] / d['SQ_LDS_IDX_ACTIVE']:.4f}")
+            if "SQ_WAIT_INST_ANY" in d and d.get("SQ_WAVE_CYCLES"):
+                parts.append(f"waiting / wave cycles {d['SQ_WAIT_INST_ANY'] / d['SQ_WAVE_CYCLES']:.3f}")
+            if d.get("SQ_INSTS_MFMA") and "SQ_INSTS_LDS" in d:
+                parts.append(f"LDS instructions per MFMA {d['SQ_INSTS_LDS'] / d['SQ_INSTS_MFMA']:.2f}")
+            if d.get("SQ_INSTS_MFMA") and "SQ_INSTS_SALU" in d:
+                parts.append(f"SALU instructions per MFMA {d['SQ_INSTS_SALU'] / d['SQ_INSTS_MFMA']:.2f}")
+            if "TCC_EA0_RDREQ_32B" in d and "TCC_EA0_RDREQ" in d:
+                rd = (d["TCC_EA0_RDREQ"] - d["TCC_EA0_RDREQ_32B"]) * 64 + d["TCC_EA0_RDREQ_32B"] * 32
+                parts.append(f"EA read bytes (64 B requests + 32 B requests) {rd / 2**20:.1f} MiB")
+            if "TCC_EA0_WRREQ_64B" in d and "TCC_EA0_WRREQ" in d:
+                wr = d["TCC_EA0_WRREQ_64B"] * 64 + (d["TCC_EA0_WRREQ"] - d["TCC_EA0_WRREQ_64B"]) * 32
+                parts.append(f"EA write bytes {wr / 2**20:.1f} MiB")
+            if parts:
+                print(f"- `{k}`: " + "; ".join(parts))
+        print()
+
+
 def summarize_profile(argv):
     """Markdown summary of rocprofv3 output (kernel statistics, or per-kernel HBM traffic from
     a FETCH_SIZE run and a WRITE_SIZE run scaled by the copy-calibration kernel)."""
@@ -695,10 +757,13 @@ def summarize_profile(argv):
         rows = _csv_rows(argv[1], "kernel_stats.csv")
         print("| kernel | calls | total ms | avg us | min us | max us | % |")
         print("|---|---:|---:|---:|---:|---:|---:|")
-        for r in rows[:12]:
+        for r in rows[:20]:
             print(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} "
                   f"| {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} "
                   f"| {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+        return
+    if argv[0] == "counters":
+        summarize_counters(argv[1:])
         return
     if argv[0] != "traffic" or len(argv) != 5:
         raise SystemExit("usage: --summarize-profile traffic FETCH_DIR WRITE_DIR WORKLOAD MIB")
@@ -750,6 +815,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=16)
     ap.add_argument("--decode-splits", type=int, default=0)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-decode-graph", action="store_true",
+                    help="skip the decode leg's graph replay (counter runs)")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-window", action="store_true")
     ap.add_argument("--no-score-mode1", action="store_true")
@@ -763,8 +830,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a streaming copy of MIB MiB (counter calibration)")
     ap.add_argument("--summarize-profile", nargs="+", metavar="ARG",
-                    help="stats DIR | traffic FETCH_DIR WRITE_DIR WORKLOAD MIB: print a "
-                         "summary of rocprofv3 csv output and exit (the traffic runs must "
+                    help="stats DIR | traffic FETCH_DIR WRITE_DIR WORKLOAD MIB | counters DIR...: "
+                         "print a summary of rocprofv3 csv output and exit (the traffic runs must "
                          "time one step with no warmup and --copy-calibration MIB)")
     args = ap.parse_args()
     if args.summarize_profile:
