@@ -405,9 +405,9 @@ static infllm2_status decode_step_impl(const infllm2_params* params, const infll
     return infllm2_sparse_attn_decode(params, seqs, q, k_cache, v_cache, block_idx, num_splits,
                                       workspace, workspace_bytes, out, lse, stream);
   }
-  // Fused form: the arguments are checked as the separate calls check them, then the kernels
-  // completed since prev_kv_len are compressed, one launch does scores and top-k, and one the
-  // attention.
+  // Fused form: the arguments are checked as the separate calls check them; one launch computes
+  // the kernels completed since prev_kv_len (storing them into `kernels`), the scores and the
+  // top-k, and one the attention.
   if (!q || !k_cache || !v_cache || !kernels || !scores || !block_idx || !out)
     return fail(INFLLM2_ERR_NULL, "q, k_cache, v_cache, kernels, scores, block_idx or out is NULL");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(kernels) ||
@@ -433,8 +433,7 @@ static infllm2_status decode_step_impl(const infllm2_params* params, const infll
         workspace, infllm2::decode_layout(t.q_rows * g.Hkv).part, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_status(e, "decode_step_noalloc clear");
   }
-  st = infllm2_compress_kernels(params, seqs, k_cache, prev_kv_len, kernels, stream);
-  if (st != INFLLM2_OK) return st;
+  t.prev_kv_len = prev_kv_len;
   return hip_status(infllm2::launch_decode_step(g, t, q, kernels, k_cache, v_cache, scores,
                                                  nb_stride, block_idx, splits, workspace, out,
                                                  lse, static_cast<hipStream_t>(stream)),

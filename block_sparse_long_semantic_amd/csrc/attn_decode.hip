@@ -114,6 +114,8 @@ __device__ __forceinline__ int agent_add(int* p, int v) {
 // workspace entries are indexed by the query row itself.
 struct DecRow {
   int row, pos, kv0, kv_len, kc0;
+  int seq;        // the row's sequence
+  bool last;      // the sequence's last query row
 };
 __device__ __forceinline__ bool dec_row(const SeqTable& t, int item, DecRow& r) {
   int b, j;
@@ -124,6 +126,8 @@ __device__ __forceinline__ bool dec_row(const SeqTable& t, int item, DecRow& r) 
   r.kv0 = sq.kv_start;
   r.kv_len = sq.kv_len;
   r.kc0 = sq.kc_start;
+  r.seq = b;
+  r.last = j == sq.q_len - 1;
   return true;
 }
 
@@ -487,26 +491,22 @@ attn_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* 
   const int w = tid >> 6;
 
   const int32_t* sel = idx + (static_cast<size_t>(r.row) * g.Hkv + kvh) * g.topk;
-  // the valid entries form a prefix (ascending, then -1): count them with ballots
-  int nsel = 0;
-  for (int base = 0; base < g.topk; base += 128) {
-    const int e0 = base + lane, e1 = base + 64 + lane;
-    const bool v0 = e0 < g.topk && sel[e0] >= 0;
-    const bool v1 = e1 < g.topk && sel[e1] >= 0;
-    const unsigned long long m1 = __ballot(v1);
-    nsel += __popcll(__ballot(v0)) + __popcll(m1);
-    if (~m1 != 0ull) break;
-  }
-  const int per = (nsel + nsplit - 1) / nsplit;
-  const int k_begin = min(nsel, sp * per);
-  const int k_end = min(nsel, k_begin + per);
+  // split sp takes entries sp*per .. sp*per + per - 1 of the selection (per from topk, so no
+  // wave waits to count the valid entries first); the valid entries form a prefix (ascending,
+  // then -1), so a wave stops at its first -1
+  const int per = (g.topk + nsplit - 1) / nsplit;
+  const int k_begin = min(g.topk, sp * per);
+  const int k_end = min(g.topk, k_begin + per);
 
   FoldCtx<D, G> c;
   WaveAcc<D> a;
   fold_init(c, a, g, q, k, v, r, kvh, (lds_u8*)&ring[w][0], lane);
   const int own = r.pos / 64;                       // indices past the row's own block: clamped
-  for (int kk = k_begin + w; kk < k_end; kk += NW)
-    fold_block(c, a, max(0, min(sel[kk], own)) * 64, lane);
+  for (int kk = k_begin + w; kk < k_end; kk += NW) {
+    const int blk = uniform(sel[kk]);
+    if (blk < 0) break;
+    fold_block(c, a, min(blk, own) * 64, lane);
+  }
 
   float acc[16 * D / (64 * NW)], M, L;
   merge_waves<D, NW>(a, &ring[0][0], wm_s, wl_s, tid, acc, M, L);
@@ -528,17 +528,35 @@ constexpr int kSelectThreads = 64 * kSelectWaves;
 constexpr int kChunkBlocks = 128;               // blocks per score work item
 constexpr int kMaxKeysPerThread = 8;            // selection over at most 8 * 512 blocks
 
+// A kernel row's 8 bf16 columns dotted with the group-summed query's (float32 FMAs in column
+// order; the row total is the DPP group sum over the row's lanes).
+__device__ __forceinline__ float kernel_dot8(const uint4 k, const float (&qv)[8]) {
+  const uint32_t w4[4] = {k.x, k.y, k.z, k.w};
+  float dot = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    dot = fmaf(__uint_as_float(w4[e] << 16), qv[2 * e], dot);
+    dot = fmaf(__uint_as_float(w4[e] & 0xFFFF0000u), qv[2 * e + 1], dot);
+  }
+  return dot;
+}
+
 // Block scores of one chunk: blocks blk0 .. blk0+127 (those <= own) of query row `r`, kv head
 // kvh, from kernels 4*blk0-1 .. 4*blk0+511 (the first one is the halo of block blk0).  The
 // group-summed query stays in float32; each kernel row is read by D/8 lanes (16 bytes each),
 // dotted with float32 FMAs and reduced across the lanes by DPP moves; every kernel load is
 // issued before the query sum.  Kernel scores go to LDS, then 128 threads max-pool them onto the blocks.
+// Kernels c >= c_new are not in the cache yet (completed since the last compression): after the
+// cached rows are scored, they are computed from the keys (window_mean_bf16x8, the compression's
+// own arithmetic) and scored, and stored by the chunk that owns them (not the halo) when
+// `writer` is set.
 template <int D, int G>
 __device__ __forceinline__ void score_chunk(const Geom& g, const SeqTable& t, const DecRow& r,
                                             int kvh, int blk0, int own,
                                             const uint16_t* __restrict__ q,
-                                            const uint16_t* __restrict__ kern, float* srow,
-                                            float* qs, float* u, int tid) {
+                                            const uint16_t* __restrict__ keys,
+                                            uint16_t* __restrict__ kern, int c_new, bool writer,
+                                            float* srow, float* qs, float* u, int tid) {
   constexpr int LPR = D / 8;              // lanes per kernel row
   constexpr int RPI = 64 / LPR;           // rows per wave instruction
   constexpr int NROW = 4 * kChunkBlocks + 1;
@@ -552,14 +570,17 @@ __device__ __forceinline__ void score_chunk(const Geom& g, const SeqTable& t, co
   const int col = (lane % LPR) * 8;
   const size_t kbase = static_cast<size_t>(r.kc0) * g.Hkv * D + static_cast<size_t>(kvh) * D;
   uint4 kv[PER];
+  unsigned fresh = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int it = w + NW * i;
     const int rr = it * RPI + lane / LPR;
     const int cc = c0 - 1 + rr;
     const bool ok = it < NIT && rr < NROW && cc >= 0 && cc < C && 16 * cc + 31 <= r.pos;
-    kv[i] = ok ? *reinterpret_cast<const uint4*>(kern + kbase + static_cast<size_t>(cc) * g.Hkv * D + col)
-               : make_uint4(0u, 0u, 0u, 0u);
+    kv[i] = ok && cc < c_new
+                ? *reinterpret_cast<const uint4*>(kern + kbase + static_cast<size_t>(cc) * g.Hkv * D + col)
+                : make_uint4(0u, 0u, 0u, 0u);
+    fresh |= static_cast<unsigned>(ok && cc >= c_new) << i;
   }
   for (int e = tid; e < D; e += kSelectThreads) {
     float qh[G];                                        // all heads' loads in flight at once
@@ -580,15 +601,26 @@ __device__ __forceinline__ void score_chunk(const Geom& g, const SeqTable& t, co
     const int rr = it * RPI + lane / LPR;
     const int cc = c0 - 1 + rr;
     const bool ok = it < NIT && rr < NROW && cc >= 0 && cc < C && 16 * cc + 31 <= r.pos;
-    const uint32_t w4[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
-    float dot = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      dot = fmaf(__uint_as_float(w4[e] << 16), qv[2 * e], dot);
-      dot = fmaf(__uint_as_float(w4[e] & 0xFFFF0000u), qv[2 * e + 1], dot);
-    }
-    dot = group_sum<LPR>(dot);
+    const float dot = group_sum<LPR>(kernel_dot8(kv[i], qv));
     if (lane % LPR == 0 && it < NIT && rr < NROW) u[rr] = ok ? dot : -INFINITY;
+  }
+  if (fresh != 0) {   // rare (a new kernel every 16 decoded tokens); whole rows of lanes
+    const size_t rs = static_cast<size_t>(g.Hkv) * D;
+#pragma unroll 1
+    for (int i = 0; i < PER; ++i) {
+      if ((fresh >> i) & 1u) {
+        const int rr = (w + NW * i) * RPI + lane / LPR;
+        const int cc = c0 - 1 + rr;
+        const uint4 kf = window_mean_bf16x8(
+            keys + (static_cast<size_t>(r.kv0) + static_cast<size_t>(g.s) * cc) * rs +
+                static_cast<size_t>(kvh) * D + col,
+            rs, g.w);
+        if (writer && rr >= 1)
+          *reinterpret_cast<uint4*>(kern + kbase + static_cast<size_t>(cc) * rs + col) = kf;
+        const float dot = group_sum<LPR>(kernel_dot8(kf, qv));
+        if (lane % LPR == 0) u[rr] = dot;
+      }
+    }
   }
   __syncthreads();
   if (tid < kChunkBlocks) {
@@ -603,11 +635,35 @@ __device__ __forceinline__ void score_chunk(const Geom& g, const SeqTable& t, co
   }
 }
 
+// The new kernels of kernel chunk `chunk` (kernels 512 chunk .. 512 chunk + 511) that no query
+// row scores (the cache runs past the sequence's last query position), computed and stored by
+// the sequence's last row's workgroup of that chunk.
+template <int D>
+__device__ __forceinline__ void compress_unscored(const Geom& g, const DecRow& r, int kvh,
+                                                  int chunk, int c_new,
+                                                  const uint16_t* __restrict__ keys,
+                                                  uint16_t* __restrict__ kern, int tid) {
+  const int c0 = 4 * kChunkBlocks * chunk;
+  const int lo = max(max(c0, c_new), num_kernels(r.pos + 1, g.w, g.s));
+  const int hi = min(c0 + 4 * kChunkBlocks, num_kernels(r.kv_len, g.w, g.s));
+  const size_t rs = static_cast<size_t>(g.Hkv) * D;
+  for (int it = tid; it < (hi - lo) * (D / 8); it += kSelectThreads) {
+    const int cc = lo + it / (D / 8);
+    const int col = (it % (D / 8)) * 8;
+    *reinterpret_cast<uint4*>(kern + (static_cast<size_t>(r.kc0) + cc) * rs +
+                              static_cast<size_t>(kvh) * D + col) =
+        window_mean_bf16x8(keys + (static_cast<size_t>(r.kv0) + static_cast<size_t>(g.s) * cc) * rs +
+                               static_cast<size_t>(kvh) * D + col,
+                           rs, g.w);
+  }
+}
+
 template <int D, int G>
 __global__ void __launch_bounds__(kSelectThreads)
 decode_select(Geom g, SeqTable t, const uint16_t* __restrict__ q,
-              const uint16_t* __restrict__ kern, float* __restrict__ scores, int nb_stride,
-              int32_t* __restrict__ idx, void* __restrict__ workspace) {
+              const uint16_t* __restrict__ keys, uint16_t* __restrict__ kern,
+              float* __restrict__ scores, int nb_stride, int32_t* __restrict__ idx,
+              void* __restrict__ workspace) {
   __shared__ __attribute__((aligned(16))) uint32_t stage[kMaxKeysPerThread * kSelectThreads];
   __shared__ float qs[D];
   __shared__ WgSelectLds<kSelectWaves> sm;
@@ -622,13 +678,18 @@ decode_select(Geom g, SeqTable t, const uint16_t* __restrict__ q,
   const int pair = r.row * g.Hkv + kvh;
   const int own = r.pos / 64;
   const int n_chunks = own / kChunkBlocks + 1;
+  // kernels below c_new are in the cache; the sequence's last row stores the others
+  const int c_new = t.prev_kv_len != nullptr
+                        ? num_kernels(min(uniform(t.prev_kv_len[r.seq]), r.kv_len), g.w, g.s)
+                        : 0;
+  if (r.last) compress_unscored<D>(g, r, kvh, chunk, c_new, keys, kern, tid);
   if (chunk >= n_chunks) return;                       // whole workgroup
   const int pairs = t.q_rows * g.Hkv;
   int* score_done = reinterpret_cast<int*>(static_cast<char*>(workspace) +
                                            decode_layout(pairs).score_done);
   float* srow = scores + (static_cast<size_t>(r.row) * g.Hkv + kvh) * nb_stride;
-  score_chunk<D, G>(g, t, r, kvh, chunk * kChunkBlocks, own, q, kern, srow, qs,
-                    reinterpret_cast<float*>(stage), tid);
+  score_chunk<D, G>(g, t, r, kvh, chunk * kChunkBlocks, own, q, keys, kern, c_new, r.last, srow,
+                    qs, reinterpret_cast<float*>(stage), tid);
   wait_vmcnt<0>();                                     // this wave's scores are stored
   __syncthreads();
   if (tid == 0) s_last = agent_add(score_done + pair, 1) == n_chunks - 1;
@@ -694,9 +755,10 @@ hipError_t launch_attn_decode(const Geom& g, const SeqTable& t, const void* q, c
                                              stream);
 }
 
-// kernels must already hold every complete kernel.
+// kernels must hold every kernel completed by t.prev_kv_len (null: none); the scoring launch
+// computes and stores the rest.
 hipError_t launch_decode_step(const Geom& g, const SeqTable& t, const void* q,
-                               const void* kernels, const void* k, const void* v, float* scores,
+                               void* kernels, const void* k, const void* v, float* scores,
                                int nb_stride, int32_t* idx, int nsplit, void* workspace,
                                void* out, float* lse, hipStream_t stream) {
   const int rows = bound_rows(t);
@@ -706,12 +768,13 @@ hipError_t launch_decode_step(const Geom& g, const SeqTable& t, const void* q,
   if (static_cast<long long>(rows) * g.Hkv > 65535) return hipErrorInvalidValue;
   const dim3 grid(max_chunks, rows * g.Hkv);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
-  const uint16_t* kc = static_cast<const uint16_t*>(kernels);
+  uint16_t* kc = static_cast<uint16_t*>(kernels);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
   bool launched = false;
 #define INFLLM2_SEL_CASE(DD, GG)                                                                \
   if (!launched && g.d == DD && g.G == GG) {                                                    \
     hipLaunchKernelGGL((decode_select<DD, GG>), grid, dim3(kSelectThreads), 0, stream, g, t, qq, \
-                       kc, scores, nb_stride, idx, workspace);                                  \
+                       kk, kc, scores, nb_stride, idx, workspace);                              \
     launched = true;                                                                            \
   }
   INFLLM2_SEL_CASE(128, 16)

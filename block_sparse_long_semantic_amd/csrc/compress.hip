@@ -6,7 +6,7 @@
 // Exactness: window sums are accumulated in float64.  With p significant bits per input (8 for
 // bf16, 24 for f32) and w terms, no partial sum rounds while the window's nonzero inputs span at
 // most 53 - p - ceil(log2 w) binary exponents (40 for bf16 at w = 32); then the single rounding
-// to the storage dtype below (to nearest even, straight from float64) is the exact mean's
+// to the storage dtype (to nearest even, straight from float64) is the exact mean's
 // rounding.  Wider windows may round in the sum (at most one unit in the last place off).
 #include <algorithm>
 
@@ -17,18 +17,6 @@ namespace {
 
 constexpr int kTile = 16;        // kernels per workgroup
 constexpr int kThreads = 256;
-
-// float64 -> bf16 bits, round to nearest even, in one step (no float32 double rounding).
-// Keeps sign, 11 exponent bits and 7 fraction bits of the binary64 encoding; the rounded
-// binary64 value then converts exactly to float32, whose top half is the bf16 encoding.
-__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
-  unsigned long long u = static_cast<unsigned long long>(__double_as_longlong(x));
-  const unsigned long long lsb = (u >> 45) & 1ull;
-  u += 0x00000FFFFFFFFFFFull + lsb;            // 2^44 - 1 + lsb
-  u &= ~((1ull << 45) - 1ull);
-  const float f = static_cast<float>(__longlong_as_double(static_cast<long long>(u)));
-  return static_cast<uint16_t>(__float_as_uint(f) >> 16);
-}
 
 // A persistent grid walks the tiles of 16 kernels of every sequence (the kernels completed
 // after prev_kv_len[b]); the host knows only a bound on their number.
@@ -56,43 +44,28 @@ compress_kernel(Geom g, SeqTable t, const void* __restrict__ k, void* __restrict
       const int c = c0 + it / ncg;
       const int cg = it % ncg;
       if (c >= c_hi) break;                    // items are ordered by kernel
-      double acc[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = 0.0;
       const size_t row0 = static_cast<size_t>(sq.kv_start) + static_cast<size_t>(g.s) * c;
-#pragma unroll 8
-      for (int r = 0; r < g.w; ++r) {
-        const size_t off = (row0 + r) * cols + static_cast<size_t>(cg) * 8;
-        if constexpr (kBf16) {
-          const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(k) + off);
-          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+      const size_t orow = static_cast<size_t>(sq.kc_start) + c;
+      const size_t ooff = orow * cols + static_cast<size_t>(cg) * 8;
+      if constexpr (kBf16) {
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + ooff) = window_mean_bf16x8(
+            static_cast<const uint16_t*>(k) + row0 * cols + static_cast<size_t>(cg) * 8, cols, g.w);
+      } else {
+        double acc[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[2 * e] += static_cast<double>(__uint_as_float(w4[e] << 16));
-            acc[2 * e + 1] += static_cast<double>(__uint_as_float(w4[e] & 0xFFFF0000u));
-          }
-        } else {
+        for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+#pragma unroll 8
+        for (int r = 0; r < g.w; ++r) {
+          const size_t off = (row0 + r) * cols + static_cast<size_t>(cg) * 8;
           const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(k) + off);
           const float4 a = p[0], c2 = p[1];
           const float f[8] = {a.x, a.y, a.z, a.w, c2.x, c2.y, c2.z, c2.w};
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[e] += static_cast<double>(f[e]);
         }
-      }
-      const size_t orow = static_cast<size_t>(sq.kc_start) + c;
-      const size_t ooff = orow * cols + static_cast<size_t>(cg) * 8;
-      double mean[8];
+        double mean[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) mean[e] = pow2 ? acc[e] * inv_w : acc[e] / g.w;
-      if constexpr (kBf16) {
-        uint32_t w4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w4[e] = static_cast<uint32_t>(f64_to_bf16_rne(mean[2 * e])) |
-                  (static_cast<uint32_t>(f64_to_bf16_rne(mean[2 * e + 1])) << 16);
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + ooff) =
-            make_uint4(w4[0], w4[1], w4[2], w4[3]);
-      } else {
+        for (int e = 0; e < 8; ++e) mean[e] = pow2 ? acc[e] * inv_w : acc[e] / g.w;
         float4* p = reinterpret_cast<float4*>(static_cast<float*>(out) + ooff);
         p[0] = make_float4(static_cast<float>(mean[0]), static_cast<float>(mean[1]),
                            static_cast<float>(mean[2]), static_cast<float>(mean[3]));

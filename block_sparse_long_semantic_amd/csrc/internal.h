@@ -129,6 +129,50 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
+// float64 -> bf16 bits, round to nearest even, in one step (no float32 double rounding).
+// Keeps sign, 11 exponent bits and 7 fraction bits of the binary64 encoding; the rounded
+// binary64 value then converts exactly to float32, whose top half is the bf16 encoding.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+  unsigned long long u = static_cast<unsigned long long>(__double_as_longlong(x));
+  const unsigned long long lsb = (u >> 45) & 1ull;
+  u += 0x00000FFFFFFFFFFFull + lsb;            // 2^44 - 1 + lsb
+  u &= ~((1ull << 45) - 1ull);
+  const float f = static_cast<float>(__longlong_as_double(static_cast<long long>(u)));
+  return static_cast<uint16_t>(__float_as_uint(f) >> 16);
+}
+
+// One semantic kernel's 8 consecutive bf16 columns: the mean of w key rows starting at p (row
+// stride `rs` elements), summed in float64 in row order and rounded once to bf16.  Every
+// kernel the library writes in bf16 comes from here (the compression launch and the decode
+// step's scoring launch), so both write the same bits.
+__device__ __forceinline__ uint4 window_mean_bf16x8(const uint16_t* __restrict__ p, size_t rs,
+                                                   int w) {
+  double acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+#pragma unroll 8
+  for (int r = 0; r < w; ++r) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p + static_cast<size_t>(r) * rs);
+    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += static_cast<double>(__uint_as_float(w4[e] << 16));
+      acc[2 * e + 1] += static_cast<double>(__uint_as_float(w4[e] & 0xFFFF0000u));
+    }
+  }
+  const bool pow2 = (w & (w - 1)) == 0;
+  const double inv_w = 1.0 / static_cast<double>(w);
+  uint32_t o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const double m0 = pow2 ? acc[2 * e] * inv_w : acc[2 * e] / w;
+    const double m1 = pow2 ? acc[2 * e + 1] * inv_w : acc[2 * e + 1] / w;
+    o[e] = static_cast<uint32_t>(f64_to_bf16_rne(m0)) |
+           (static_cast<uint32_t>(f64_to_bf16_rne(m1)) << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // float -> bf16, round to nearest, ties to even (finite inputs).
 __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   uint32_t u = __float_as_uint(x);
@@ -213,8 +257,10 @@ hipError_t launch_attn_decode(const Geom& g, const SeqTable& t, const void* q, c
 // (decode_select), then the split-KV attention.
 bool decode_step_supported(const Geom& g, int dtype, const SeqTable& t);
 int decode_step_splits(const Geom& g);
+// Fused decode step: scores + top-k in one launch (kernels completed since t.prev_kv_len are
+// computed there and stored into `kernels`), the attention in a second.
 hipError_t launch_decode_step(const Geom& g, const SeqTable& t, const void* q,
-                               const void* kernels, const void* k, const void* v, float* scores,
+                               void* kernels, const void* k, const void* v, float* scores,
                                int nb_stride, int32_t* idx, int nsplit, void* workspace,
                                void* out, float* lse, hipStream_t stream);
 hipError_t launch_attn_combine(const Geom& g, int dtype, const SeqTable& t, int splits,

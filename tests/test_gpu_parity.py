@@ -567,6 +567,56 @@ def test_decode_several_rows_per_sequence():
                          res["out"][r], res["lse"][r], f"rows seq {b}")
 
 
+def test_decode_step_compresses_kernels_past_the_queries():
+    """The decode step stores every kernel completed since prev_kv_len, also those past its query
+    rows' positions: a cache that runs past the last query (rows at 2000 of 3000 tokens, at 9000
+    of 20000), prev_kv_len from 0 (every kernel new) to past the queries, and two rows of one
+    sequence; the kernel rows never written are poisoned with NaN."""
+    p = synth.config_params("decode128k")
+    lens, prev, pos0, nq, Lmax = [3000, 3000, 3000, 20000], [0, 2500, 1500, 8000], \
+        [2000, 2000, 1999, 9000], [1, 1, 2, 1], 20000
+    B = len(lens)
+    wl = synth.make_decode("dec-past", p, batch=B, max_len=Lmax, steps=1, seed=51)
+    rng = np.random.default_rng(52)
+    qs = [synth.make_upstream_grad((n, p.num_q_heads, p.head_dim), int(rng.integers(1 << 30)))
+          for n in nq]
+    Ck = orc.num_kernels(Lmax, p.kernel_size, p.kernel_stride)
+    k = dev(wl.k.reshape(B * Lmax, p.num_kv_heads, p.head_dim), p.dtype)
+    v = dev(wl.v.reshape(B * Lmax, p.num_kv_heads, p.head_dim), p.dtype)
+    kern = torch.full((B * Ck, p.num_kv_heads, p.head_dim), float("nan"), dtype=k.dtype,
+                      device="cuda")
+    kc = np.arange(B) * Ck
+    lib.compress_kernels(p, lib.Seqs(np.arange(B), np.zeros(B), np.zeros(B), np.arange(B) * Lmax,
+                                     prev, kc), k, kern)
+    q_start = np.concatenate([[0], np.cumsum(nq)[:-1]])
+    seqs = lib.Seqs(q_start, nq, pos0, np.arange(B) * Lmax, lens, kc)
+    bufs = lib.pipeline.decode_buffers(p, sum(nq), Lmax // 64 + 1, 0, "cuda")
+    log("case decode step, cache past the queries")
+    lib.decode_step(p, seqs, dev(np.concatenate(qs), p.dtype), k, v, kern,
+                    np.array(prev, dtype=np.int32), bufs)
+    torch.cuda.synchronize()
+    res = {n: host(bufs[n]) for n in ("scores", "idx", "out", "lse")}
+    gk_all = host(kern)
+    for b in range(B):
+        L = lens[b]
+        ks, vs = wl.k[b, :L], wl.v[b, :L]
+        kern_ref = orc.compress_kernels(ks, p.kernel_size, p.kernel_stride, p.dtype)
+        gk = gk_all[kc[b]:kc[b] + kern_ref.shape[0]]
+        assert np.array_equal(gk, kern_ref), f"seq {b}: kernels differ"
+        r = slice(int(q_start[b]), int(q_start[b]) + nq[b])
+        ref = orc.run_sequence(qs[b], ks, vs, p, q_pos0=pos0[b], kernels=kern_ref,
+                               with_attention=False)
+        nbq = int(ref.positions[-1]) // p.block_size + 1
+        gs = res["scores"][r][:, :, :nbq]
+        bound = cmp.score_bound(qs[b].astype(np.float64), kern_ref, ref.positions, p, nbq)
+        cmp.check_scores(gs, ref.scores[:, :, :nbq], bound, ref.positions, p)
+        assert np.array_equal(res["idx"][r], orc.select_all(gs.astype(np.float64), ref.positions, p))
+        cmp.check_indices(res["idx"][r], ref.idx, ref.scores[:, :, :nbq], ref.positions, p)
+        O, Ls = orc.sparse_attention(qs[b].astype(np.float64), ref.positions, ks, vs,
+                                     res["idx"][r], p)
+        cmp.check_attention(res["out"][r], res["lse"][r], O, Ls, p.dtype)
+
+
 def test_decode_longest_cache():
     """A 262144-token cache: 4096 blocks, the most a selection takes."""
     p = synth.config_params("decode128k")
