@@ -390,7 +390,10 @@ static infllm2_status decode_step_impl(const infllm2_params* params, const infll
   infllm2_status st = check_params(params, &g);
   if (st != INFLLM2_OK) return st;
   if ((st = build_table(seqs, g, true, &t)) != INFLLM2_OK) return st;
-  if (!infllm2::decode_step_supported(g, params->dtype, t)) {
+  if (num_splits < 0 || num_splits > g.topk)
+    return fail(INFLLM2_ERR_SHAPE, "num_splits %d outside 0..topk", num_splits);
+  const int splits = num_splits > 0 ? num_splits : infllm2::decode_step_splits(g);
+  if (!infllm2::decode_step_supported(g, params->dtype, t, splits)) {
     st = infllm2_compress_kernels(params, seqs, k_cache, prev_kv_len, kernels, stream);
     if (st != INFLLM2_OK) return st;
     st = infllm2_block_scores(params, seqs, q, kernels, scores, nb_stride, stream);
@@ -406,8 +409,8 @@ static infllm2_status decode_step_impl(const infllm2_params* params, const infll
                                       workspace, workspace_bytes, out, lse, stream);
   }
   // Fused form: the arguments are checked as the separate calls check them; one launch computes
-  // the kernels completed since prev_kv_len (storing them into `kernels`), the scores and the
-  // top-k, and one the attention.
+  // the kernels completed since prev_kv_len (storing them into `kernels`) and the scores, one
+  // the top-k and the attention.
   if (!q || !k_cache || !v_cache || !kernels || !scores || !block_idx || !out)
     return fail(INFLLM2_ERR_NULL, "q, k_cache, v_cache, kernels, scores, block_idx or out is NULL");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(kernels) ||
@@ -418,9 +421,6 @@ static infllm2_status decode_step_impl(const infllm2_params* params, const infll
     return fail(INFLLM2_ERR_SHAPE, "nb_stride %d below the %d reachable blocks", nb_stride, need_nb);
   if (need_nb > 4096)
     return fail(INFLLM2_ERR_UNSUPPORTED, "%d reachable blocks exceed 4096", need_nb);
-  if (num_splits < 0 || num_splits > g.topk)
-    return fail(INFLLM2_ERR_SHAPE, "num_splits %d outside 0..topk", num_splits);
-  const int splits = num_splits > 0 ? num_splits : infllm2::decode_step_splits(g);
   const size_t need = infllm2::decode_workspace(g, t.q_rows, splits);
   if (workspace == nullptr) return fail(INFLLM2_ERR_NULL, "workspace is NULL");
   if (!aligned16(workspace)) return fail(INFLLM2_ERR_ALIGN, "workspace must be 16-byte aligned");

@@ -14,18 +14,20 @@
 // separate combine launch is needed.  It resets the counter, leaving the workspace ready for the
 // next call.
 //
-// decode_select -- block scores (section 2.1.2: the group-summed query against every semantic
-// kernel, max-pooled onto blocks) and the group-shared top-k (2.1.1-2.1.2) of a decoding step in
-// one launch: one workgroup per chunk of 128 blocks of a (row, kv head) computes the chunk's
-// scores; the workgroup that completes the last chunk of the pair -- counted with an agent-scope
-// atomic in the workspace -- selects its blocks right away (a radix select over the
-// order-preserving score keys, in LDS) and zeroes the counter for the next call.  No workgroup
-// ever waits for another, so the launch needs no co-residency.  The attention over the
-// selection is the next launch (attn_decode).
+// The decode step (infllm2_decode_step) is two launches.  decode_scores: block scores (section
+// 2.1.2: the group-summed query against every semantic kernel, max-pooled onto blocks), one
+// workgroup per chunk of 128 blocks of a (row, kv head); the kernels completed since the last
+// compression are computed there from the keys and stored.  Then attn_decode in its selecting
+// form: every split workgroup of a (row, kv head) first runs the group-shared top-k (2.1.1-2.1.2)
+// of the pair itself, from the stored scores (a radix select over the order-preserving score
+// keys, in LDS), keeps the part of the selection its split folds, and the first split writes the
+// whole selection out.  The selection is computed once per split instead of once per pair, but
+// no workgroup waits for another's and the indices never make a round trip through memory
+// before the fold.
 //
-// Data crossing workgroups (scores, selections, partials, counters) moves through agent-scope
-// atomic stores and loads, which are coherent across the XCDs' separate L2s by themselves; a
-// fence would instead write back and invalidate a whole L2.
+// Data crossing workgroups of one launch (partials, counters) moves through agent-scope atomic
+// stores and loads, which are coherent across the XCDs' separate L2s by themselves; a fence
+// would instead write back and invalidate a whole L2.
 #include <algorithm>
 
 #include "dpp.h"
@@ -44,6 +46,8 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kMaxKeysPerThread = 8;      // the decode step's selection: at most 8 * 512 blocks
+constexpr int kMaxSplitBlocks = 256;      // ... and at most 256 selected blocks per split
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -472,12 +476,17 @@ __device__ __forceinline__ void finish_split(const Geom& g, int row, int kvh, in
   if (tid == 0) agent_store(split_done + pair, 0);   // ready for the next call
 }
 
-template <int D, int G, int NW>
+// SEL: the selecting form of the decode step -- the workgroup selects the pair's blocks from
+// `scores` (nb_stride floats per (row, kv head)) and writes the selection to idx when it is the
+// pair's first split; otherwise idx is the given selection.
+template <int D, int G, int NW, bool SEL>
 __global__ void __launch_bounds__(64 * NW)
 attn_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-            const uint16_t* __restrict__ v, const int32_t* __restrict__ idx, int nsplit,
+            const uint16_t* __restrict__ v, int32_t* __restrict__ idx,
+            const float* __restrict__ scores, int nb_stride, int nsplit,
             void* __restrict__ workspace, uint16_t* __restrict__ out, float* __restrict__ lse) {
   constexpr int MAT = 64 * D * 2;                          // one block of V
+  static_assert(!SEL || NW * MAT >= kMaxKeysPerThread * 64 * NW * 4, "selection keys fit the ring");
   __shared__ __attribute__((aligned(16))) unsigned char ring[NW][MAT];
   __shared__ float wm_s[NW][16], wl_s[NW][16];
   __shared__ int s_last;
@@ -490,13 +499,31 @@ attn_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* 
   const int lane = tid & 63;
   const int w = tid >> 6;
 
-  const int32_t* sel = idx + (static_cast<size_t>(r.row) * g.Hkv + kvh) * g.topk;
   // split sp takes entries sp*per .. sp*per + per - 1 of the selection (per from topk, so no
   // wave waits to count the valid entries first); the valid entries form a prefix (ascending,
   // then -1), so a wave stops at its first -1
   const int per = (g.topk + nsplit - 1) / nsplit;
   const int k_begin = min(g.topk, sp * per);
   const int k_end = min(g.topk, k_begin + per);
+  int32_t* const pair_idx = idx + (static_cast<size_t>(r.row) * g.Hkv + kvh) * g.topk;
+  const int32_t* sel = pair_idx;
+  if constexpr (SEL) {
+    // the pair's selection, in LDS: its keys in the ring's first bytes (the ring is unused
+    // until the fold), this split's entries in s_sel
+    __shared__ WgSelectLds<NW> sm;
+    __shared__ int32_t s_sel[kMaxSplitBlocks];
+    for (int e = tid; e < per; e += 64 * NW) s_sel[e] = -1;
+    const bool first = sp == 0;
+    wg_select<NW, kMaxKeysPerThread>(
+        g, r.pos / 64, scores + (static_cast<size_t>(r.row) * g.Hkv + kvh) * nb_stride,
+        [&](int e, int blk) {
+          if (first) pair_idx[e] = blk;
+          if (e >= k_begin && e < k_end) s_sel[e - k_begin] = blk;
+        },
+        reinterpret_cast<uint32_t*>(&ring[0][0]), sm, tid);
+    __syncthreads();                                  // s_sel written, the ring free again
+    sel = s_sel - k_begin;
+  }
 
   FoldCtx<D, G> c;
   WaveAcc<D> a;
@@ -518,15 +545,14 @@ attn_decode(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* 
                          reinterpret_cast<float*>(ws + lay.part), pairs, tid, &s_last, out, lse);
 }
 
-// waves of the attention workgroups: alone (given indices), and after decode_select
+// waves of the attention workgroups: alone (given indices), and in the decode step
 constexpr int kSplitWaves = 4;
 constexpr int kStepWaves = 8;
 
-// ------------------------------------------------------------------------- scores + selection
-constexpr int kSelectWaves = 8;
-constexpr int kSelectThreads = 64 * kSelectWaves;
+// ------------------------------------------------------------------------------ block scores
+constexpr int kScoreWaves = 8;
+constexpr int kScoreThreads = 64 * kScoreWaves;
 constexpr int kChunkBlocks = 128;               // blocks per score work item
-constexpr int kMaxKeysPerThread = 8;            // selection over at most 8 * 512 blocks
 
 // A kernel row's 8 bf16 columns dotted with the group-summed query's (float32 FMAs in column
 // order; the row total is the DPP group sum over the row's lanes).
@@ -561,7 +587,7 @@ __device__ __forceinline__ void score_chunk(const Geom& g, const SeqTable& t, co
   constexpr int RPI = 64 / LPR;           // rows per wave instruction
   constexpr int NROW = 4 * kChunkBlocks + 1;
   constexpr int NIT = (NROW + RPI - 1) / RPI;
-  constexpr int NW = kSelectWaves;
+  constexpr int NW = kScoreWaves;
   constexpr int PER = (NIT + NW - 1) / NW;
   const int lane = tid & 63;
   const int w = tid >> 6;
@@ -582,7 +608,7 @@ __device__ __forceinline__ void score_chunk(const Geom& g, const SeqTable& t, co
                 : make_uint4(0u, 0u, 0u, 0u);
     fresh |= static_cast<unsigned>(ok && cc >= c_new) << i;
   }
-  for (int e = tid; e < D; e += kSelectThreads) {
+  for (int e = tid; e < D; e += kScoreThreads) {
     float qh[G];                                        // all heads' loads in flight at once
 #pragma unroll
     for (int h = 0; h < G; ++h) qh[h] = bf16_to_f32(q[(static_cast<size_t>(r.row) * g.Hq + kvh * G + h) * D + e]);
@@ -630,7 +656,7 @@ __device__ __forceinline__ void score_chunk(const Geom& g, const SeqTable& t, co
       float best = u[4 * tid];
 #pragma unroll
       for (int e = 1; e < 5; ++e) best = fmaxf(best, u[4 * tid + e]);
-      agent_store(srow + blk, best * g.scale);
+      srow[blk] = best * g.scale;
     }
   }
 }
@@ -647,7 +673,7 @@ __device__ __forceinline__ void compress_unscored(const Geom& g, const DecRow& r
   const int lo = max(max(c0, c_new), num_kernels(r.pos + 1, g.w, g.s));
   const int hi = min(c0 + 4 * kChunkBlocks, num_kernels(r.kv_len, g.w, g.s));
   const size_t rs = static_cast<size_t>(g.Hkv) * D;
-  for (int it = tid; it < (hi - lo) * (D / 8); it += kSelectThreads) {
+  for (int it = tid; it < (hi - lo) * (D / 8); it += kScoreThreads) {
     const int cc = lo + it / (D / 8);
     const int col = (it % (D / 8)) * 8;
     *reinterpret_cast<uint4*>(kern + (static_cast<size_t>(r.kc0) + cc) * rs +
@@ -659,23 +685,18 @@ __device__ __forceinline__ void compress_unscored(const Geom& g, const DecRow& r
 }
 
 template <int D, int G>
-__global__ void __launch_bounds__(kSelectThreads)
-decode_select(Geom g, SeqTable t, const uint16_t* __restrict__ q,
+__global__ void __launch_bounds__(kScoreThreads)
+decode_scores(Geom g, SeqTable t, const uint16_t* __restrict__ q,
               const uint16_t* __restrict__ keys, uint16_t* __restrict__ kern,
-              float* __restrict__ scores, int nb_stride, int32_t* __restrict__ idx,
-              void* __restrict__ workspace) {
-  __shared__ __attribute__((aligned(16))) uint32_t stage[kMaxKeysPerThread * kSelectThreads];
+              float* __restrict__ scores, int nb_stride) {
+  __shared__ __attribute__((aligned(16))) float u[4 * kChunkBlocks + 4];
   __shared__ float qs[D];
-  __shared__ WgSelectLds<kSelectWaves> sm;
-  __shared__ int s_last;
-  static_assert(kMaxKeysPerThread * kSelectThreads >= 4 * kChunkBlocks + 4, "score staging fits");
 
   const int tid = threadIdx.x;
   const int chunk = blockIdx.x;
   const int kvh = static_cast<int>(blockIdx.y) % g.Hkv;
   DecRow r;
   if (!dec_row(t, static_cast<int>(blockIdx.y) / g.Hkv, r)) return;
-  const int pair = r.row * g.Hkv + kvh;
   const int own = r.pos / 64;
   const int n_chunks = own / kChunkBlocks + 1;
   // kernels below c_new are in the cache; the sequence's last row stores the others
@@ -684,21 +705,9 @@ decode_select(Geom g, SeqTable t, const uint16_t* __restrict__ q,
                         : 0;
   if (r.last) compress_unscored<D>(g, r, kvh, chunk, c_new, keys, kern, tid);
   if (chunk >= n_chunks) return;                       // whole workgroup
-  const int pairs = t.q_rows * g.Hkv;
-  int* score_done = reinterpret_cast<int*>(static_cast<char*>(workspace) +
-                                           decode_layout(pairs).score_done);
   float* srow = scores + (static_cast<size_t>(r.row) * g.Hkv + kvh) * nb_stride;
   score_chunk<D, G>(g, t, r, kvh, chunk * kChunkBlocks, own, q, keys, kern, c_new, r.last, srow,
-                    qs, reinterpret_cast<float*>(stage), tid);
-  wait_vmcnt<0>();                                     // this wave's scores are stored
-  __syncthreads();
-  if (tid == 0) s_last = agent_add(score_done + pair, 1) == n_chunks - 1;
-  __syncthreads();
-  if (!s_last) return;
-  // the pair's last chunk: select, and zero the counter for the next call (its last user)
-  wg_select<kSelectWaves, kMaxKeysPerThread>(
-      g, own, srow, idx + (static_cast<size_t>(r.row) * g.Hkv + kvh) * g.topk, stage, sm, tid);
-  if (tid == 0) agent_store(score_done + pair, 0);
+                    qs, u, tid);
 }
 
 }  // namespace
@@ -715,16 +724,18 @@ size_t decode_workspace(const Geom& g, int rows, int nsplit) {
 
 int decode_step_splits(const Geom& g) { return (g.topk + kStepWaves - 1) / kStepWaves; }
 
-bool decode_step_supported(const Geom& g, int dtype, const SeqTable& t) {
+bool decode_step_supported(const Geom& g, int dtype, const SeqTable& t, int nsplit) {
   if (!attn_decode_supported(g, dtype) || g.w != 32 || g.s != 16 || g.score_mode != 0) return false;
   if (static_cast<long long>(bound_rows(t)) * g.Hkv > 65535) return false;  // a grid row per pair
-  return bound_blocks(t, 64) <= kMaxKeysPerThread * kSelectThreads;
+  if (nsplit < 1 || (g.topk + nsplit - 1) / nsplit > kMaxSplitBlocks) return false;
+  return bound_blocks(t, 64) <= kMaxKeysPerThread * 64 * kStepWaves;
 }
 
-template <int NW>
+template <int NW, bool SEL>
 static hipError_t launch_split_attention(const Geom& g, const SeqTable& t, const void* q,
-                                         const void* k, const void* v, const int32_t* idx,
-                                         int nsplit, void* workspace, void* out, float* lse,
+                                         const void* k, const void* v, int32_t* idx,
+                                         const float* scores, int nb_stride, int nsplit,
+                                         void* workspace, void* out, float* lse,
                                          hipStream_t stream) {
   const int rows = bound_rows(t);
   if (rows == 0) return hipSuccess;
@@ -736,8 +747,8 @@ static hipError_t launch_split_attention(const Geom& g, const SeqTable& t, const
   uint16_t* oo = static_cast<uint16_t*>(out);
 #define INFLLM2_DEC_CASE(DD, GG)                                                                \
   if (g.d == DD && g.G == GG) {                                                                 \
-    hipLaunchKernelGGL((attn_decode<DD, GG, NW>), grid, dim3(64 * NW), 0, stream, g, t, qq, kk, \
-                       vv, idx, nsplit, workspace, oo, lse);                                    \
+    hipLaunchKernelGGL((attn_decode<DD, GG, NW, SEL>), grid, dim3(64 * NW), 0, stream, g, t, qq, \
+                       kk, vv, idx, scores, nb_stride, nsplit, workspace, oo, lse);             \
     return hipGetLastError();                                                                   \
   }
   INFLLM2_DEC_CASE(128, 16)
@@ -751,12 +762,13 @@ static hipError_t launch_split_attention(const Geom& g, const SeqTable& t, const
 hipError_t launch_attn_decode(const Geom& g, const SeqTable& t, const void* q, const void* k,
                               const void* v, const int32_t* idx, int nsplit, void* workspace,
                               void* out, float* lse, hipStream_t stream) {
-  return launch_split_attention<kSplitWaves>(g, t, q, k, v, idx, nsplit, workspace, out, lse,
-                                             stream);
+  return launch_split_attention<kSplitWaves, false>(g, t, q, k, v, const_cast<int32_t*>(idx),
+                                                    nullptr, 0, nsplit, workspace, out, lse,
+                                                    stream);
 }
 
 // kernels must hold every kernel completed by t.prev_kv_len (null: none); the scoring launch
-// computes and stores the rest.
+// computes and stores the rest.  The attention launch selects the blocks (and writes idx).
 hipError_t launch_decode_step(const Geom& g, const SeqTable& t, const void* q,
                                void* kernels, const void* k, const void* v, float* scores,
                                int nb_stride, int32_t* idx, int nsplit, void* workspace,
@@ -773,8 +785,8 @@ hipError_t launch_decode_step(const Geom& g, const SeqTable& t, const void* q,
   bool launched = false;
 #define INFLLM2_SEL_CASE(DD, GG)                                                                \
   if (!launched && g.d == DD && g.G == GG) {                                                    \
-    hipLaunchKernelGGL((decode_select<DD, GG>), grid, dim3(kSelectThreads), 0, stream, g, t, qq, \
-                       kk, kc, scores, nb_stride, idx, workspace);                              \
+    hipLaunchKernelGGL((decode_scores<DD, GG>), grid, dim3(kScoreThreads), 0, stream, g, t, qq, \
+                       kk, kc, scores, nb_stride);                                              \
     launched = true;                                                                            \
   }
   INFLLM2_SEL_CASE(128, 16)
@@ -785,8 +797,8 @@ hipError_t launch_decode_step(const Geom& g, const SeqTable& t, const void* q,
   if (!launched) return hipErrorInvalidValue;
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_split_attention<kStepWaves>(g, t, q, k, v, idx, nsplit, workspace, out, lse,
-                                            stream);
+  return launch_split_attention<kStepWaves, true>(g, t, q, k, v, idx, scores, nb_stride, nsplit,
+                                                  workspace, out, lse, stream);
 }
 
 }  // namespace infllm2

@@ -253,12 +253,11 @@ size_t decode_workspace(const Geom& g, int rows, int nsplit);
 hipError_t launch_attn_decode(const Geom& g, const SeqTable& t, const void* q, const void* k,
                               const void* v, const int32_t* idx, int nsplit, void* workspace,
                               void* out, float* lse, hipStream_t stream);
-// One decoding step after the kernels are compressed: block scores and top-k in one launch
-// (decode_select), then the split-KV attention.
-bool decode_step_supported(const Geom& g, int dtype, const SeqTable& t);
+// The fused decode step: block scores in one launch (decode_scores, which also computes and
+// stores the kernels completed since t.prev_kv_len), then the split-KV attention in its
+// selecting form (each split workgroup runs the pair's top-k itself; the first writes it out).
+bool decode_step_supported(const Geom& g, int dtype, const SeqTable& t, int nsplit);
 int decode_step_splits(const Geom& g);
-// Fused decode step: scores + top-k in one launch (kernels completed since t.prev_kv_len are
-// computed there and stored into `kernels`), the attention in a second.
 hipError_t launch_decode_step(const Geom& g, const SeqTable& t, const void* q,
                                void* kernels, const void* k, const void* v, float* scores,
                                int nb_stride, int32_t* idx, int nsplit, void* workspace,

@@ -1,7 +1,8 @@
 // Group-shared top-k selection of one (query row, KV head) by a whole workgroup (MiniCPM4 paper
 // summary, section 2.1.1: each query token selects its most relevant KV blocks; section 2.1.2:
 // one selection per query-head group), for launches with few rows (decoding): the selection
-// kernel's small-batch form and the decode step's scoring launch.
+// kernel's small-batch form, and the decode step's attention launch, where every split
+// workgroup of a (row, KV head) selects the pair's blocks itself.
 //
 // Scores map to order-preserving unsigned keys (-0 ranks as +0).  Forced blocks (the first
 // n_init and the n_local ending at the query's own block) are always taken; among the others
@@ -43,27 +44,27 @@ struct WgSelectLds {
 };
 
 // Group-shared top-k of one (row, kv head) by a workgroup of NW waves, from its stored block
-// scores srow[0 .. own] (up to KPT per thread).  The (topk - forced)-th largest order-preserving
-// key among the non-forced blocks is located by a radix select over the keys' actual range: the
-// first pass bins (key - min) >> s into 256 LDS counters (s the smallest shift that fits
-// max - min), each later pass splits the chosen bin 256 ways.  It stops when every key of the
-// chosen bin is wanted, or the bin holds a single key value (taken in block order), or the bin
-// holds at most 64 keys: then one wave ranks those keys exactly (key descending, block
-// ascending) and marks the wanted ones.  `keys` (LDS, one word per block) holds the keys for the
-// ordered output.  Scores are read with agent-scope loads, so they may come from other
-// workgroups of the same launch; the indices are written with plain stores (the next launch
-// reads them).  Every thread of the workgroup must call it.
-template <int NW, int KPT>
-__device__ __forceinline__ void wg_select(const Geom& g, int own, const float* srow,
-                                          int32_t* out_idx, uint32_t* keys, WgSelectLds<NW>& sm,
-                                          int tid) {
+// scores srow[0 .. own] (up to KPT per thread); the p-th entry of the ascending selection goes
+// out as emit(p, block) (p < topk; -1 for the padding of a row with at most topk blocks).  The
+// (topk - forced)-th largest order-preserving key among the non-forced blocks is located by a
+// radix select over the keys' actual range: the first pass bins (key - min) >> s into 256 LDS
+// counters (s the smallest shift that fits max - min), each later pass splits the chosen bin 256
+// ways.  It stops when every key of the chosen bin is wanted, or the bin holds a single key value
+// (taken in block order), or the bin holds at most 64 keys: then one wave ranks those keys
+// exactly (key descending, block ascending) and marks the wanted ones.  `keys` (LDS, one word
+// per block) holds the keys for the ordered output.  Scores are read with agent-scope loads, so
+// they may come from other workgroups of the same launch.  Every thread of the workgroup must
+// call it.
+template <int NW, int KPT, typename Emit>
+__device__ __forceinline__ void wg_select(const Geom& g, int own, const float* srow, Emit emit,
+                                          uint32_t* keys, WgSelectLds<NW>& sm, int tid) {
   constexpr int T = 64 * NW;
   constexpr uint32_t kTaken = 0xFFFFFFFFu;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int nb = own + 1;
   if (nb <= g.topk) {
-    for (int e = tid; e < g.topk; e += T) out_idx[e] = e < nb ? e : -1;
+    for (int e = tid; e < g.topk; e += T) emit(e, e < nb ? e : -1);
     return;
   }
   const int local_lo = max(0, own - g.n_local + 1);
@@ -221,7 +222,7 @@ __device__ __forceinline__ void wg_select(const Geom& g, int own, const float* s
       take = eq_seen < want;
       ++eq_seen;
     }
-    if (take && p < g.topk) out_idx[p] = blk;           // p < topk unless keys are NaN
+    if (take && p < g.topk) emit(p, blk);               // p < topk unless keys are NaN
     p += take ? 1 : 0;
   }
 }

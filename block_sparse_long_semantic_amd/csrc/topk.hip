@@ -216,8 +216,10 @@ topk_wide(Geom g, SeqTable t, const float* __restrict__ scores, int nb_stride,
   const int row = uniform(static_cast<int>(t.q_start[b])) + j;
   const int pos = uniform(t.q_pos0[b]) + j;
   const size_t pair = static_cast<size_t>(row) * g.Hkv + kvh;
-  wg_select<kWideWaves, kWideKeys>(g, pos / g.B, scores + pair * nb_stride, idx + pair * g.topk,
-                                   keys, sm, static_cast<int>(threadIdx.x));
+  int32_t* out = idx + pair * g.topk;
+  wg_select<kWideWaves, kWideKeys>(g, pos / g.B, scores + pair * nb_stride,
+                                   [&](int e, int blk) { out[e] = blk; }, keys, sm,
+                                   static_cast<int>(threadIdx.x));
 }
 
 }  // namespace

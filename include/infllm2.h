@@ -230,11 +230,12 @@ infllm2_status infllm2_sparse_attn_decode(const infllm2_params* params, const in
  * floats per (row, KV head)), top-k into block_idx, then split-KV attention.  Arguments mean
  * what they mean in the separate calls, and the same checks apply; `workspace` is always
  * required here.  For bf16, block 64, kernels 32/16, d 64 or 128, groups of 8 or 16 and score
- * mode 0, the kernels completed since prev_kv_len, the scores and the top-k run as one launch
- * (new kernels are computed from k_cache where they are scored and stored into `kernels`; the
- * last workgroup to finish a (row, KV head)'s scores selects its blocks) and the attention as a
- * second; the results equal those of the separate calls (kernels, scores and indices exactly,
- * outputs to float32 rounding).  Otherwise the
+ * mode 0 (and at most 256 selected blocks per split), the kernels completed since prev_kv_len
+ * and the scores run as one launch (new kernels are computed from k_cache where they are scored
+ * and stored into `kernels`), the top-k and the attention as a second (every split workgroup of
+ * a (row, KV head) selects the pair's blocks itself; the first writes them to block_idx); the
+ * results equal those of the separate calls (kernels, scores and indices exactly, outputs to
+ * float32 rounding).  Otherwise the
  * separate calls are chained on `stream`; the first failing call's status is returned and
  * nothing after it is enqueued. */
 infllm2_status infllm2_decode_step(const infllm2_params* params, const infllm2_seqs* seqs,
