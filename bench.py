@@ -32,7 +32,12 @@ sys.path.insert(0, ROOT)
 METRIC = "sparse-attn prefill tokens/s @128K + decode µs/token; % MFMA/HBM roofline"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
-TILE_TOKENS = 16          # query tokens per attention work item
+def tile_tokens(p) -> int:
+    """Query tokens per prefill attention work item: 16, or 32 when a group has 8 query heads
+    (two tokens' heads then share the 16 columns of each matrix-core tile)."""
+    return 32 if p.num_q_heads // p.num_kv_heads == 8 else 16
+
+
 WINDOW = 6144             # sliding-window leg: 96 blocks x 64 tokens
 CHUNK = 16384             # chunked-prefill leg: the last 16K tokens against a 112K cache
 SPIN_CYCLES = 24_000_000  # GPU spin before the timed decode steps (about 10 ms at 2.4 GHz)
@@ -129,8 +134,8 @@ def run_prefill(args, torch, pkg, synth, workload=None, keep=True):
     # the attention call launches its tiles in rounds of one workgroup per compute unit; the
     # grid covers the library's host bound on the tiles (it sees only the metadata's bounds:
     # sequences, longest query run, total rows), not the exact count
-    n_seq, max_q = len(lens), max(lens)
-    items = min(n_seq * -(-max_q // TILE_TOKENS), -(-T // TILE_TOKENS) + n_seq) * Hkv
+    n_seq, max_q, TT = len(lens), max(lens), tile_tokens(p)
+    items = min(n_seq * -(-max_q // TT), -(-T // TT) + n_seq) * Hkv
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     launches = (items + cus // 8 * 8 - 1) // (cus // 8 * 8)
     result = dict(
@@ -234,20 +239,21 @@ def prefill_leg(args, torch, pkg, synth, workload):
 def gather_bound(p, idx, seq_lens, flops, ms_attention):
     """The prefill attention's gather: K/V bytes of every (token, KV head)'s selected blocks
     (idx: host array [rows, Hkv, topk] of one packed prefill) against the bytes the tile kernel
-    stages (each 16-token tile loads the union of its tokens' selected blocks once), the reuse
-    factor and the staging rate achieved."""
+    stages (each tile loads the union of its tokens' selected blocks once), the reuse factor and
+    the staging rate achieved."""
     block_bytes = 2 * p.block_size * p.head_dim * 2                 # K and V, bf16
+    TT = tile_tokens(p)
     selected = int((idx >= 0).sum()) * block_bytes
     staged_blocks = 0
     start = 0
     for L in seq_lens:
         sel = idx[start:start + L]
         start += L
-        pad = (-L) % 16
+        pad = (-L) % TT
         if pad:
             sel = np.concatenate([sel, np.full((pad,) + sel.shape[1:], -1, sel.dtype)])
-        t = np.sort(sel.reshape(-1, 16, sel.shape[1], sel.shape[2]).transpose(0, 2, 1, 3)
-                    .reshape(-1, 16 * sel.shape[2]), axis=1)
+        t = np.sort(sel.reshape(-1, TT, sel.shape[1], sel.shape[2]).transpose(0, 2, 1, 3)
+                    .reshape(-1, TT * sel.shape[2]), axis=1)
         new = np.ones(t.shape, bool)
         new[:, 1:] = t[:, 1:] != t[:, :-1]
         staged_blocks += int((new & (t >= 0)).sum())
@@ -258,8 +264,8 @@ def gather_bound(p, idx, seq_lens, flops, ms_attention):
             "flop_per_staged_byte": flops / staged,
             "staging_rate_gbs": rate / 1e9,
             "staging_bytes_per_clk_per_cu": rate / 256 / 2.4e9,
-            "note": "16-token tiles; each tile stages the union of its tokens' selected blocks "
-                    "(K and V) from L2 into LDS once"}
+            "note": f"{TT}-token tiles; each tile stages the union of its tokens' selected "
+                    "blocks (K and V) from L2 into LDS once"}
 
 
 def run_score_mode1(args, torch, pkg, pre):

@@ -49,7 +49,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kT = 16;            // query tokens per workgroup of the gradient and window forms
 constexpr int kWaves = 8;         // their waves per workgroup (tokens per wave = kT / kWaves)
-constexpr int kTF = 16;           // query tokens per workgroup of the sparse forward
+constexpr int kTF = 16;           // query tokens per workgroup of the sparse forward (G = 16)
+constexpr int kTF8 = 32;          // ... at G = 8 (two tokens' heads stacked per MFMA group)
 constexpr int kWavesF = 8;        // its waves (two per SIMD, 2 tokens each)
 constexpr bool kRounds = true;    // launch items in rounds of one workgroup per CU
 constexpr int kMaxUnion = 2048;   // reachable blocks per tile handled by this kernel
@@ -211,6 +212,11 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   constexpr int MAT = 64 * D * 2;            // bytes of one 64-key matrix
   constexpr int NTHR = 64 * NW;
   constexpr int T = NW * TPW;                // query tokens of the tile
+  // tokens per 16-column MFMA group: two tokens' 8 heads share the columns in the forward form
+  constexpr int TPC = (!BWD && !WIN && G < 16) ? 16 / G : 1;
+  constexpr int CG = TPW / TPC;              // column groups per wave
+  static_assert(TPC * G == 16 || TPC == 1, "a column group is one token or fills 16 columns");
+  static_assert(TPW % TPC == 0, "whole column groups per wave");
   static_assert(T <= 32 && 32 % T != 1, "tile of at most 32 tokens");
   constexpr int MPW = (T & (T - 1)) == 0 ? 32 / T : 1;  // token masks per bitmap word
   constexpr uint32_t TMASK = T == 32 ? 0xFFFFFFFFu : (1u << T) - 1u;
@@ -466,25 +472,29 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
     }
   };
 
-  // ---- per-token state (token tw = TPW*w + tt).  m_run is shared by the 4 lanes of a head (log2
+  // ---- per-column-group state.  The 16 MFMA columns of a group hold TPC tokens' G heads
+  // (TPC = 16 / G stacked tokens in the forward form at G = 8, else 1): column c16 is token
+  // TPW*w + TPC*tt + c16 / G, head c16 % G.  m_run is shared by the 4 lanes of a column (log2
   // units, possibly stale by < kLazy); l_run is this lane's partial row sum.
   // Backward: dof = dout in the same B-operand order as q, lse2 = lse * log2(e) and dl = delta
   // for head c16 (+inf / 0 on unused lanes, so their probabilities are 0), o accumulates the
   // dQ^T tiles (dims x heads).
-  bf16x8 qf[TPW][KS];
-  bf16x8 dof[TPW][KS];
-  f32x4 o[TPW][NT];
-  float m_run[TPW], l_run[TPW];
-  float lse2[TPW], dl[TPW];
+  bf16x8 qf[CG][KS];
+  bf16x8 dof[CG][KS];
+  f32x4 o[CG][NT];
+  float m_run[CG], l_run[CG];
+  float lse2[CG], dl[CG];
+  const int ct = TPC == 1 ? 0 : c16 / G;     // the lane column's token within its group
+  const int hd = TPC == 1 ? c16 : c16 % G;   // ... and its head
 #pragma unroll
-  for (int tt = 0; tt < TPW; ++tt) {
-    const int tw = TPW * w + tt;
+  for (int tt = 0; tt < CG; ++tt) {
+    const int tw = TPW * w + TPC * tt + ct;
     m_run[tt] = -INFINITY;
     l_run[tt] = 0.f;
 #pragma unroll
     for (int n = 0; n < NT; ++n) o[tt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bool live = tw < nq && c16 < G;
-    const size_t hrow = static_cast<size_t>(row0 + tw) * Hq + kvh * G + c16;
+    const bool live = tw < nq && hd < G;
+    const size_t hrow = static_cast<size_t>(row0 + tw) * Hq + kvh * G + hd;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qf[tt][ks] = live ? *reinterpret_cast<const bf16x8*>(q + hrow * D + 32 * ks + 8 * q4)
@@ -563,9 +573,11 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
     const lds_bf16x8* Kp = (const lds_bf16x8*)(uintptr_t)(k_lane + slot_off);
     const uint32_t vaddr = v_lane + slot_off;
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-      if (!(wm & (1u << tt))) continue;
-      const int pos = pos0 + TPW * w + tt;
+    for (int tt = 0; tt < CG; ++tt) {
+      const uint32_t gm = (wm >> (TPC * tt)) & ((1u << TPC) - 1u);   // the group's tokens
+      if (gm == 0u) continue;
+      const int pos = pos0 + TPW * w + TPC * tt + ct;                 // this lane's token
+      const int pos_lo = pos0 + TPW * w + TPC * tt;                   // the group's first token
       if constexpr (BWD) {
         // S^T = K Q^T and dP^T = V dO^T in the same key order; P = exp(S*scale - lse) from the
         // forward's statistics (no running max), dS = P (dP - delta), dQ += dS K.
@@ -648,9 +660,12 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
 #pragma unroll
           for (int i = 0; i < 4; ++i) sv[s][tp][i] = acc4[s][tp][i];
       // keys past the query or the sequence end (only in the query's own block or the tail),
-      // and with a window, keys before it
-      if (key0 + 63 > pos || key0 + 64 > kv_len || (WIN && key0 <= pos - g.window)) {
-        const int lim = min(pos, kv_len - 1) - key0;
+      // with a window, keys before it, and every key of a stacked token that did not choose
+      // the block
+      const bool partial = TPC > 1 && gm != (1u << TPC) - 1u;
+      if (partial || key0 + 63 > pos_lo || key0 + 64 > kv_len || (WIN && key0 <= pos - g.window)) {
+        int lim = min(pos, kv_len - 1) - key0;
+        if (TPC > 1 && !((gm >> ct) & 1u)) lim = -1;
         const int lo = WIN ? pos - g.window + 1 - key0 : 0;
 #pragma unroll
         for (int s = 0; s < 2; ++s)
@@ -676,7 +691,9 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
         float bm = fmaxf(mx, __shfl_xor(mx, 16));
         bm = fmaxf(bm, __shfl_xor(bm, 32));
         const float m_new = fmaxf(m_run[tt], bm);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[tt] - m_new);
+        // a stacked column with no key yet keeps -inf (its sums are still 0)
+        const float alpha = (TPC > 1 && m_new == -INFINITY) ? 1.f
+                                                             : __builtin_amdgcn_exp2f(m_run[tt] - m_new);
         l_run[tt] *= alpha;
         m_run[tt] = m_new;
 #pragma unroll
@@ -686,7 +703,7 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
           for (int n = 0; n < NT; ++n) o[tt][n][i] *= a_i;
         }
       }
-      const float mneg = -m_run[tt];
+      const float mneg = (TPC > 1 && m_run[tt] == -INFINITY) ? 0.f : -m_run[tt];
       float psum = 0.f;
 #pragma unroll
       for (int s = 0; s < 2; ++s)
@@ -765,28 +782,30 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
     return;
   }
 
-  // ---- epilogue: combine the 4 lanes' partial sums, normalise and store
+  // ---- epilogue: combine the 4 lanes' partial sums, normalise and store.  Accumulator row h
+  // (4 q4 + i) is column h of S: token TPW*w + TPC*tt + h / G, head h % G.
 #pragma unroll
-  for (int tt = 0; tt < TPW; ++tt) {
-    const int tw = TPW * w + tt;
-    if (tw >= nq) continue;
+  for (int tt = 0; tt < CG; ++tt) {
+    if (TPW * w + TPC * tt >= nq) continue;
     float l = l_run[tt];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     if (stalled) l = __builtin_nanf("");     // never expected: flags the row instead of hanging
-    const size_t orow = static_cast<size_t>(row0 + tw) * Hq + kvh * G;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * q4 + i;
+      const int tw = TPW * w + TPC * tt + (TPC == 1 ? 0 : h / G);
+      const int hh = TPC == 1 ? h : h % G;
       const float inv = 1.f / __shfl(l, h);
-      if (h < G) {
-        uint16_t* op = out + (orow + h) * D;
+      if (hh < G && tw < nq) {
+        uint16_t* op = out + ((static_cast<size_t>(row0 + tw) * Hq + kvh * G + hh) * D);
 #pragma unroll
         for (int n = 0; n < NT; ++n) op[16 * n + c16] = f32_to_bf16(o[tt][n][i] * inv);
       }
     }
-    if (lse != nullptr && q4 == 0 && c16 < G)
-      lse[orow + c16] = (m_run[tt] + log2f(l)) * kLn2;
+    const int tl = TPW * w + TPC * tt + ct;
+    if (lse != nullptr && q4 == 0 && hd < G && tl < nq)
+      lse[static_cast<size_t>(row0 + tl) * Hq + kvh * G + hd] = (m_run[tt] + log2f(l)) * kLn2;
   }
 }
 
@@ -814,11 +833,15 @@ int device_cus() {
 
 // Items are launched in rounds of one workgroup per compute unit, so that the workgroups
 // sharing an XCD start together on neighbouring tiles and walk the same KV blocks at the same
-// time (their L2 then serves each block to all of them).  The forward runs tiles of kTF rows.
+// time (their L2 then serves each block to all of them).  The forward runs tiles of kTF rows
+// (kTF8 at G = 8, where a wave's 4 tokens fill two 16-column MFMA groups).
+static int attn_tile_rows(const Geom& g) { return g.G == 8 ? kTF8 : kTF; }
+
 hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, const void* k,
                             const void* v, const int32_t* idx, void* out, float* lse,
                             hipStream_t stream) {
-  const int n_items = bound_tiles(t, kTF) * g.Hkv;   // a bound: the kernel counts the tiles
+  const int TF = attn_tile_rows(g);
+  const int n_items = bound_tiles(t, TF) * g.Hkv;     // a bound: the kernel counts the tiles
   if (n_items == 0) return hipSuccess;
   const int round = kRounds ? (device_cus() / 8) * 8 : (n_items + 7) / 8 * 8;
   const uint16_t* qq = static_cast<const uint16_t*>(q);
@@ -827,9 +850,9 @@ hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, con
   uint16_t* oo = static_cast<uint16_t*>(out);
   for (int base = 0; base < n_items; base += round) {
     const int grid = std::min(round, (n_items - base + 7) / 8 * 8);
-#define INFLLM2_TILE_CASE(DD, GG, NS)                                                         \
+#define INFLLM2_TILE_CASE(DD, GG, NS, TFF)                                                    \
   if (g.d == DD && g.G == GG) {                                                               \
-    hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWavesF, kTF / kWavesF, false, false, true>),   \
+    hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWavesF, TFF / kWavesF, false, false, true>),   \
                        dim3(grid),                                                            \
                        dim3(64 * kWavesF), 0, stream, g, t, qq, kk, vv, idx, oo, lse, n_items,\
                        base, nullptr, nullptr, nullptr, nullptr);                             \
@@ -837,10 +860,10 @@ hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, con
     if (e != hipSuccess) return e;                                                            \
     continue;                                                                                 \
   }
-    INFLLM2_TILE_CASE(128, 16, 4)
-    INFLLM2_TILE_CASE(128, 8, 4)
-    INFLLM2_TILE_CASE(64, 16, 8)
-    INFLLM2_TILE_CASE(64, 8, 8)
+    INFLLM2_TILE_CASE(128, 16, 4, kTF)
+    INFLLM2_TILE_CASE(128, 8, 4, kTF8)
+    INFLLM2_TILE_CASE(64, 16, 8, kTF)
+    INFLLM2_TILE_CASE(64, 8, 8, kTF8)
 #undef INFLLM2_TILE_CASE
     return hipErrorInvalidValue;
   }

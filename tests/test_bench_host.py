@@ -20,7 +20,7 @@ def test_gather_bound_counts_tile_unions():
     idx[:16, 1, :2] = [5, 6]               # 16 tokens share 2 blocks
     idx[3, 1, 2] = 9                       # one token adds a block of its own
     idx[16:, 0, :1] = 7                    # ragged tile: 4 tokens, 1 block
-    p = types.SimpleNamespace(block_size=64, head_dim=128)
+    p = types.SimpleNamespace(block_size=64, head_dim=128, num_q_heads=32, num_kv_heads=2)
     g = bench.gather_bound(p, idx, [20], 1e9, 2.0)
     blk = 2 * 64 * 128 * 2
     assert g["selected_bytes"] == (16 * 4 + 16 * 2 + 1 + 4) * blk
@@ -32,9 +32,21 @@ def test_gather_bound_counts_tile_unions():
 def test_gather_bound_packed_sequences_tile_separately():
     # two sequences of 16 rows each selecting the same block: tiles do not straddle sequences
     idx = np.zeros((32, 1, 1), np.int32)
-    p = types.SimpleNamespace(block_size=64, head_dim=64)
+    p = types.SimpleNamespace(block_size=64, head_dim=64, num_q_heads=16, num_kv_heads=1)
     g = bench.gather_bound(p, idx, [16, 16], 1.0, 1.0)
     assert g["staged_bytes"] == 2 * (2 * 64 * 64 * 2)
+
+
+def test_gather_bound_uses_32_token_tiles_at_group_8():
+    # groups of 8 heads run 32-token tiles: 40 rows are a full tile and a ragged one of 8
+    idx = np.full((40, 1, 2), -1, np.int32)
+    idx[:16, 0, 0] = 1                     # first half of tile 0
+    idx[16:32, 0, 0] = 2                   # second half of tile 0
+    idx[32:, 0, 0] = 1                     # the ragged tile
+    p = types.SimpleNamespace(block_size=64, head_dim=64, num_q_heads=16, num_kv_heads=2)
+    g = bench.gather_bound(p, idx, [40], 1.0, 1.0)
+    assert g["staged_bytes"] == 3 * (2 * 64 * 64 * 2)
+    assert bench.tile_tokens(p) == 32
 
 
 def test_more_than_one_gpu_is_refused():
