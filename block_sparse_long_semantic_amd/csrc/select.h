@@ -36,7 +36,8 @@ template <int NW>
 struct WgSelectLds {
   int hist[2][256];
   int wsum[NW][2];
-  uint32_t wmin[NW], wmax[NW];
+  uint32_t wmin[NW], wmax[NW], wlow[NW];
+  int wquads[NW];
   uint32_t bin_key[64];
   int bin_blk[64];
   int nbin;
@@ -91,11 +92,24 @@ __device__ __forceinline__ void wg_select(const Geom& g, int own, const float* s
       kmax = max(kmax, kr[e]);
     }
   }
+  // A lower bound of the wanted key: the smallest of the thread quads' largest candidate keys.
+  // Every quad that holds a candidate has one at or above it, so once at least `want` quads do,
+  // the wanted key (the want-th largest) is at or above it too, and the first pass bins only the
+  // keys from there up.
+  uint32_t qmax = 0u;
+#pragma unroll
+  for (int e = 0; e < KPT; ++e) qmax = max(qmax, kr[e]);
+  qmax = max(qmax, dpp_u32<kDppXor1>(qmax));
+  qmax = max(qmax, dpp_u32<kDppXor2>(qmax));
+  const uint32_t qlow = wave_min_u32(qmax != 0u ? qmax : 0xFFFFFFFFu);
+  const int nquads = __popcll(__ballot(qmax != 0u && (lane & 3) == 0));
   kmin = wave_min_u32(kmin);
   kmax = wave_max_u32(kmax);
   if (lane == 0) {
     sm.wmin[w] = kmin;
     sm.wmax[w] = kmax;
+    sm.wlow[w] = qlow;
+    sm.wquads[w] = nquads;
   }
   if (tid < 256) {
     sm.hist[0][tid] = 0;
@@ -103,12 +117,17 @@ __device__ __forceinline__ void wg_select(const Geom& g, int own, const float* s
   }
   if (tid == 0) sm.nbin = 0;
   __syncthreads();
+  uint32_t low = 0xFFFFFFFFu;
+  int quads = 0;
 #pragma unroll
   for (int ww = 0; ww < NW; ++ww) {
     kmin = min(kmin, sm.wmin[ww]);
     kmax = max(kmax, sm.wmax[ww]);
+    low = min(low, sm.wlow[ww]);
+    quads += sm.wquads[ww];
   }
   int want = g.topk - n_forced;                         // still wanted in the current bin
+  if (quads >= want) kmin = max(kmin, low);             // keys below cannot be the wanted one
   // keys >= hi are taken, keys in [lo, hi) in block order until `want` are (want == 0: none)
   uint64_t lo = uint64_t{1} << 32, hi = uint64_t{1} << 32;
   if (want > 0) {

@@ -107,6 +107,19 @@ def test_edge_sequences():
         check_sequence(wl, res, b, label="edge")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_edge_sequences_group8(d):
+    """Groups of 8 heads run 32-token tiles in which two tokens' heads share each matrix-core
+    column group: sequences whose last tile is ragged at every parity (a lone token in its pair,
+    a pair split by the sequence end), packed together; every row."""
+    p = replace(synth.config_params("varlen"), head_dim=d)
+    wl = synth.make_prefill("edge-g8", p, [0, 1, 2, 17, 31, 32, 33, 47, 65, 130, 700], seed=34)
+    log(f"case edge lengths, group 8, d {d}")
+    res = run_prefill_stages(wl)
+    for b in range(wl.num_seqs):
+        check_sequence(wl, res, b, label=f"edge g8 d{d}")
+
+
 def test_sixty_four_sequences_packed():
     """The largest sequence table (64 packed sequences) with seeded lengths from 0 to 1500,
     among them empty, single-token and shorter-than-a-window ones: every row of every sequence."""
