@@ -285,7 +285,7 @@ size_t infllm2_decode_workspace_size(const infllm2_params* params, int32_t total
   Geom g;
   if (check_params(params, &g) != INFLLM2_OK || total_q_rows < 0 || num_splits < 0) return 0;
   // enough for infllm2_sparse_attn_decode and for the two-launch form of infllm2_decode_step
-  const int step = num_splits > 0 ? num_splits : infllm2::decode_step_splits(g);
+  const int step = num_splits > 0 ? num_splits : infllm2::decode_step_splits(g, total_q_rows);
   const int splits = std::max(decode_splits(g, params->dtype, total_q_rows, num_splits), step);
   return infllm2::decode_workspace(g, total_q_rows, splits);
 }
@@ -392,7 +392,7 @@ static infllm2_status decode_step_impl(const infllm2_params* params, const infll
   if ((st = build_table(seqs, g, true, &t)) != INFLLM2_OK) return st;
   if (num_splits < 0 || num_splits > g.topk)
     return fail(INFLLM2_ERR_SHAPE, "num_splits %d outside 0..topk", num_splits);
-  const int splits = num_splits > 0 ? num_splits : infllm2::decode_step_splits(g);
+  const int splits = num_splits > 0 ? num_splits : infllm2::decode_step_splits(g, t.q_rows);
   if (!infllm2::decode_step_supported(g, params->dtype, t, splits)) {
     st = infllm2_compress_kernels(params, seqs, k_cache, prev_kv_len, kernels, stream);
     if (st != INFLLM2_OK) return st;
@@ -467,7 +467,7 @@ infllm2_status infllm2_decode_step_noalloc(const infllm2_params* params, const i
   if (st != INFLLM2_OK) return st;
   if (seqs == nullptr) return fail(INFLLM2_ERR_NULL, "seqs is NULL");
   if (seqs->q_rows < 0) return fail(INFLLM2_ERR_SHAPE, "negative bound q_rows %d", seqs->q_rows);
-  const int splits = num_splits > 0 ? num_splits : infllm2::decode_step_splits(g);
+  const int splits = num_splits > 0 ? num_splits : infllm2::decode_step_splits(g, seqs->q_rows);
   const size_t need = infllm2::decode_workspace(g, seqs->q_rows, std::max(splits,
                                                 decode_splits(g, params->dtype, seqs->q_rows,
                                                               num_splits)));

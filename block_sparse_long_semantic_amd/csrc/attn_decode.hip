@@ -722,7 +722,15 @@ size_t decode_workspace(const Geom& g, int rows, int nsplit) {
          static_cast<size_t>(pairs) * nsplit * g.G * (g.d + 2) * sizeof(float);
 }
 
-int decode_step_splits(const Geom& g) { return (g.topk + kStepWaves - 1) / kStepWaves; }
+// Splits of the decode step's attention: at least one selected block per wave, and up to twice
+// that many splits while the (row, KV head) pairs leave compute units without a workgroup (at
+// batch 8 x 2 KV heads: 16 splits, one workgroup per compute unit).
+int decode_step_splits(const Geom& g, int rows) {
+  const long long base = (g.topk + kStepWaves - 1) / kStepWaves;
+  const long long pairs = std::max<long long>(1, static_cast<long long>(rows) * g.Hkv);
+  const long long fill = device_cus() / pairs;
+  return static_cast<int>(std::min<long long>(std::min(std::max(fill, base), 2 * base), g.topk));
+}
 
 bool decode_step_supported(const Geom& g, int dtype, const SeqTable& t, int nsplit) {
   if (!attn_decode_supported(g, dtype) || g.w != 32 || g.s != 16 || g.score_mode != 0) return false;

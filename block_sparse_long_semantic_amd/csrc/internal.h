@@ -257,7 +257,7 @@ hipError_t launch_attn_decode(const Geom& g, const SeqTable& t, const void* q, c
 // stores the kernels completed since t.prev_kv_len), then the split-KV attention in its
 // selecting form (each split workgroup runs the pair's top-k itself; the first writes it out).
 bool decode_step_supported(const Geom& g, int dtype, const SeqTable& t, int nsplit);
-int decode_step_splits(const Geom& g);
+int decode_step_splits(const Geom& g, int rows);
 hipError_t launch_decode_step(const Geom& g, const SeqTable& t, const void* q,
                                void* kernels, const void* k, const void* v, float* scores,
                                int nb_stride, int32_t* idx, int nsplit, void* workspace,
