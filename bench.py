@@ -706,7 +706,7 @@ def _csv_rows(directory: str, suffix: str):
         return list(csv.DictReader(f))
 
 
-def summarize_counters(dirs, kernels=("attn_tile", "attn_decode", "decode_select", "scores_mfma",
+def summarize_counters(dirs, kernels=("attn_tile", "attn_decode", "decode_scores", "scores_mfma",
                                       "scores_decode", "topk_kernel", "topk_wide", "compress_kernel")):
     """Per-kernel totals of every counter in one or more rocprofv3 --pmc runs (sums over the
     kernel's dispatches), one table per run, plus derived ratios where their counters are
@@ -745,12 +745,14 @@ def summarize_counters(dirs, kernels=("attn_tile", "attn_decode", "decode_select
                 parts.append(f"LDS instructions per MFMA {d['SQ_INSTS_LDS'] / d['SQ_INSTS_MFMA']:.2f}")
             if d.get("SQ_INSTS_MFMA") and "SQ_INSTS_SALU" in d:
                 parts.append(f"SALU instructions per MFMA {d['SQ_INSTS_SALU'] / d['SQ_INSTS_MFMA']:.2f}")
+            # request sizes as the streaming copy kernel shows them on this GPU: 128-byte reads
+            # (none of 32 bytes), 64-byte writes
             if "TCC_EA0_RDREQ_32B" in d and "TCC_EA0_RDREQ" in d:
-                rd = (d["TCC_EA0_RDREQ"] - d["TCC_EA0_RDREQ_32B"]) * 64 + d["TCC_EA0_RDREQ_32B"] * 32
-                parts.append(f"EA read bytes (64 B requests + 32 B requests) {rd / 2**20:.1f} MiB")
+                rd = (d["TCC_EA0_RDREQ"] - d["TCC_EA0_RDREQ_32B"]) * 128 + d["TCC_EA0_RDREQ_32B"] * 32
+                parts.append(f"EA reads {d['TCC_EA0_RDREQ']:.4g} requests = {rd / 2**20:.1f} MiB at 128 B")
             if "TCC_EA0_WRREQ_64B" in d and "TCC_EA0_WRREQ" in d:
                 wr = d["TCC_EA0_WRREQ_64B"] * 64 + (d["TCC_EA0_WRREQ"] - d["TCC_EA0_WRREQ_64B"]) * 32
-                parts.append(f"EA write bytes {wr / 2**20:.1f} MiB")
+                parts.append(f"EA writes {wr / 2**20:.1f} MiB at 64 B")
             if parts:
                 print(f"- `{k}`: " + "; ".join(parts))
         print()
