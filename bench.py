@@ -33,9 +33,9 @@ METRIC = "sparse-attn prefill tokens/s @128K + decode µs/token; % MFMA/HBM roof
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 def tile_tokens(p) -> int:
-    """Query tokens per prefill attention work item: 16, or 32 when a group has 8 query heads
-    (two tokens' heads then share the 16 columns of each matrix-core tile)."""
-    return 32 if p.num_q_heads // p.num_kv_heads == 8 else 16
+    """Query tokens per prefill attention work item: 24 (3 per wave), or 32 when a group has 8
+    query heads (two tokens' heads then share the 16 columns of each matrix-core tile)."""
+    return 32 if p.num_q_heads // p.num_kv_heads == 8 else 24
 
 
 WINDOW = 6144             # sliding-window leg: 96 blocks x 64 tokens

@@ -2,9 +2,10 @@
 // each token attends only to its most relevant KV blocks; FlashAttention-style online
 // softmax).
 //
-// Design (one workgroup = 8 waves = one tile of T = 16 consecutive query tokens of one
-// sequence and one KV head):
-//   * Union: the tile's 16 selected-block lists are OR-ed into a per-block 16-bit token mask in
+// Design (one workgroup = 8 waves = one tile of T consecutive query tokens of one sequence and
+// one KV head: T = 24 in the sparse forward at groups of 16 heads, 32 at groups of 8, 16 in the
+// gradient and window forms):
+//   * Union: the tile's T selected-block lists are OR-ed into a per-block T-bit token mask in
 //     LDS and compacted into a list of (block, mask).  Each union block's K and V (64 keys x d,
 //     bf16) are staged into LDS once for all tokens that chose it.  The forward and gradient
 //     forms stream the list in the order of the waves' progress (each wave's needed blocks,
@@ -17,9 +18,11 @@
 //     its transposing reads want.  The last wave to finish with a slot (an LDS counter against
 //     the number of waves whose tokens chose the block) refills it with block u + NS and
 //     raises the slot's ready word once the loads have landed; waits poll that word, bounded.
-//   * Compute: wave w owns tokens 2w and 2w + 1 (registers: Q operand, O accumulator, running
-//     max and sum).  For every union block it processes only its tokens whose mask bit is set:
-//       S^T = K Q^T   16 keys x 16 heads per v_mfma_f32_16x16x32_bf16 (A = K from LDS)
+//   * Compute: wave w owns tokens TPW*w .. TPW*w + TPW - 1 (T / 8 of them; registers: Q operand,
+//     O accumulator, running max and sum per 16-column group, a group holding one token's 16
+//     heads or two tokens' 8).  For every union block it processes only its groups with a
+//     token whose mask bit is set:
+//       S^T = K Q^T   16 keys x 16 columns per v_mfma_f32_16x16x32_bf16 (A = K from LDS)
 //       online softmax over the 64 keys (exp2; the running max moves only when a block's max
 //                     exceeds it by more than kLazy, decided for the whole wave)
 //       O  += P V     16 heads x 16 dims per MFMA; B = V read with ds_read_b64_tr_b16, which
@@ -49,7 +52,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kT = 16;            // query tokens per workgroup of the gradient and window forms
 constexpr int kWaves = 8;         // their waves per workgroup (tokens per wave = kT / kWaves)
-constexpr int kTF = 16;           // query tokens per workgroup of the sparse forward (G = 16)
+constexpr int kTF = 24;           // query tokens per workgroup of the sparse forward (G = 16)
 constexpr int kTF8 = 32;          // ... at G = 8 (two tokens' heads stacked per MFMA group)
 constexpr int kWavesF = 8;        // its waves (two per SIMD, 2 tokens each)
 constexpr bool kRounds = true;    // launch items in rounds of one workgroup per CU

@@ -14,23 +14,30 @@ import bench  # noqa: E402
 
 
 def test_gather_bound_counts_tile_unions():
-    # sequence of 20 rows (a full 16-row tile and a ragged one of 4), 2 KV heads, top-4
-    idx = np.full((20, 2, 4), -1, np.int32)
-    idx[:16, 0, :] = [0, 1, 2, 3]          # 16 tokens share 4 blocks
-    idx[:16, 1, :2] = [5, 6]               # 16 tokens share 2 blocks
+    # groups of 16 heads run 24-token tiles: 30 rows are a full tile and a ragged one of 6;
+    # 2 KV heads, top-4
+    idx = np.full((30, 2, 4), -1, np.int32)
+    idx[:24, 0, :] = [0, 1, 2, 3]          # 24 tokens share 4 blocks
+    idx[:24, 1, :2] = [5, 6]               # 24 tokens share 2 blocks
     idx[3, 1, 2] = 9                       # one token adds a block of its own
-    idx[16:, 0, :1] = 7                    # ragged tile: 4 tokens, 1 block
+    idx[20, 0, :1] = 8                     # rows 20 and 25 share block 8 across the tile edge:
+    idx[25, 0, :1] = 8                     # staged once per tile, twice in all
+    idx[24:, 1, :1] = 7                    # ragged tile: 6 tokens, 1 block
     p = types.SimpleNamespace(block_size=64, head_dim=128, num_q_heads=32, num_kv_heads=2)
-    g = bench.gather_bound(p, idx, [20], 1e9, 2.0)
+    assert bench.tile_tokens(p) == 24
+    g = bench.gather_bound(p, idx, [30], 1e9, 2.0)
     blk = 2 * 64 * 128 * 2
-    assert g["selected_bytes"] == (16 * 4 + 16 * 2 + 1 + 4) * blk
-    assert g["staged_bytes"] == (4 + 3 + 1) * blk
-    assert abs(g["reuse_tokens_per_staged_block"] - 101 / 8) < 1e-12
-    assert abs(g["staging_rate_gbs"] - 8 * blk / 2e-3 / 1e9) < 1e-9
+    selected = 23 * 4 + 1 * 4 + 24 * 2 + 1 + 1 + 6
+    assert g["selected_bytes"] == selected * blk
+    # tile 0: head 0 {0,1,2,3,8}, head 1 {5,6,9}; tile 1: head 0 {8}, head 1 {7}
+    assert g["staged_bytes"] == (5 + 3 + 1 + 1) * blk
+    assert abs(g["reuse_tokens_per_staged_block"] - selected / 10) < 1e-12
+    assert abs(g["staging_rate_gbs"] - 10 * blk / 2e-3 / 1e9) < 1e-9
 
 
 def test_gather_bound_packed_sequences_tile_separately():
     # two sequences of 16 rows each selecting the same block: tiles do not straddle sequences
+    # (one 24-token tile each)
     idx = np.zeros((32, 1, 1), np.int32)
     p = types.SimpleNamespace(block_size=64, head_dim=64, num_q_heads=16, num_kv_heads=1)
     g = bench.gather_bound(p, idx, [16, 16], 1.0, 1.0)
