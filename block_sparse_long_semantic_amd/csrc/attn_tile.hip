@@ -50,7 +50,8 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kT = 16;            // query tokens per workgroup of the gradient and window forms
+constexpr int kT = 16;            // query tokens per workgroup of the gradient form
+constexpr int kTW = 16;           // ... of the window form
 constexpr int kWaves = 8;         // their waves per workgroup (tokens per wave = kT / kWaves)
 constexpr int kTF = 24;           // query tokens per workgroup of the sparse forward (G = 16)
 constexpr int kTF8 = 32;          // ... at G = 8 (two tokens' heads stacked per MFMA group)
@@ -912,7 +913,7 @@ hipError_t launch_attn_tile_dq(const Geom& g, const SeqTable& t, const void* q, 
 hipError_t launch_attn_tile_window(const Geom& g, const SeqTable& t, const void* q,
                                    const void* k, const void* v, void* out, float* lse,
                                    hipStream_t stream) {
-  const int n_items = bound_tiles(t, kT) * g.Hkv;
+  const int n_items = bound_tiles(t, kTW) * g.Hkv;
   if (n_items == 0) return hipSuccess;
   const int round = kRounds ? (device_cus() / 8) * 8 : (n_items + 7) / 8 * 8;
   const uint16_t* qq = static_cast<const uint16_t*>(q);
@@ -923,7 +924,7 @@ hipError_t launch_attn_tile_window(const Geom& g, const SeqTable& t, const void*
     const int grid = std::min(round, (n_items - base + 7) / 8 * 8);
 #define INFLLM2_WIN_CASE(DD, GG, NS)                                                          \
   if (g.d == DD && g.G == GG) {                                                               \
-    hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWaves, kT / kWaves, false, true>), dim3(grid), \
+    hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWaves, kTW / kWaves, false, true>), dim3(grid), \
                        dim3(64 * kWaves), 0, stream, g, t, qq, kk, vv, nullptr, oo, lse,      \
                        n_items, base, nullptr, nullptr, nullptr, nullptr);                    \
     const hipError_t e = hipGetLastError();                                                   \
