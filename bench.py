@@ -32,10 +32,24 @@ sys.path.insert(0, ROOT)
 METRIC = "sparse-attn prefill tokens/s @128K + decode µs/token; % MFMA/HBM roofline"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
-def tile_tokens(p) -> int:
-    """Query tokens per prefill attention work item: 24 (3 per wave), or 32 when a group has 8
-    query heads (two tokens' heads then share the 16 columns of each matrix-core tile)."""
-    return 32 if p.num_q_heads // p.num_kv_heads == 8 else 24
+def _tile_bound(lens, rows: int) -> int:
+    """The library's host bound on the tiles of `rows` tokens (it sees the metadata's bounds only:
+    sequences, longest query run, total rows)."""
+    n_seq, max_q, T = len(lens), max(lens), sum(lens)
+    return min(n_seq * -(-max_q // rows), -(-T // rows) + n_seq)
+
+
+def tile_tokens(p, lens, cus: int = 256) -> int:
+    """Query tokens per prefill attention work item, chosen as the library chooses: 32 when a
+    group has 8 query heads (two tokens' heads share the 16 columns of each matrix-core tile);
+    else 24 (3 per wave) unless, in rounds of one workgroup per compute unit, 24-token rounds
+    (each ~1.4 times as long) would not beat 16-token ones."""
+    if p.num_q_heads // p.num_kv_heads == 8:
+        return 32
+    rnd = max(8, cus // 8 * 8)
+    r24 = -(-_tile_bound(lens, 24) * p.num_kv_heads // rnd)
+    r16 = -(-_tile_bound(lens, 16) * p.num_kv_heads // rnd)
+    return 24 if r24 * 7 < r16 * 5 else 16
 
 
 WINDOW = 6144             # sliding-window leg: 96 blocks x 64 tokens
@@ -134,9 +148,9 @@ def run_prefill(args, torch, pkg, synth, workload=None, keep=True):
     # the attention call launches its tiles in rounds of one workgroup per compute unit; the
     # grid covers the library's host bound on the tiles (it sees only the metadata's bounds:
     # sequences, longest query run, total rows), not the exact count
-    n_seq, max_q, TT = len(lens), max(lens), tile_tokens(p)
-    items = min(n_seq * -(-max_q // TT), -(-T // TT) + n_seq) * Hkv
     cus = torch.cuda.get_device_properties(0).multi_processor_count
+    TT = tile_tokens(p, lens, cus)
+    items = _tile_bound(lens, TT) * Hkv
     launches = (items + cus // 8 * 8 - 1) // (cus // 8 * 8)
     result = dict(
         workload=workload, tokens=T, seq_lens=lens, p=p, ms_step=ms_step, stage=stage,
@@ -145,7 +159,7 @@ def run_prefill(args, torch, pkg, synth, workload=None, keep=True):
                    "scores": bytes_scores / (stage["scores"] * 1e-3) / 1e9,
                    "topk": bytes_topk / (stage["topk"] * 1e-3) / 1e9},
         wl=wl, kernels_gpu=bufs["kernels"],
-        gather=gather_bound(p, bufs["idx"].cpu().numpy(), lens, flops, stage["attention"]))
+        gather=gather_bound(p, bufs["idx"].cpu().numpy(), lens, flops, stage["attention"], TT))
     if not keep or (args.no_backward and args.no_window and args.no_score_mode1 and args.no_chunk):
         del q, k, v, bufs
     else:
@@ -236,13 +250,12 @@ def prefill_leg(args, torch, pkg, synth, workload):
     return out
 
 
-def gather_bound(p, idx, seq_lens, flops, ms_attention):
+def gather_bound(p, idx, seq_lens, flops, ms_attention, TT):
     """The prefill attention's gather: K/V bytes of every (token, KV head)'s selected blocks
     (idx: host array [rows, Hkv, topk] of one packed prefill) against the bytes the tile kernel
     stages (each tile loads the union of its tokens' selected blocks once), the reuse factor and
     the staging rate achieved."""
     block_bytes = 2 * p.block_size * p.head_dim * 2                 # K and V, bf16
-    TT = tile_tokens(p)
     selected = int((idx >= 0).sum()) * block_bytes
     staged_blocks = 0
     start = 0

@@ -54,6 +54,7 @@ constexpr int kT = 16;            // query tokens per workgroup of the gradient 
 constexpr int kTW = 16;           // ... of the window form
 constexpr int kWaves = 8;         // their waves per workgroup (tokens per wave = kT / kWaves)
 constexpr int kTF = 24;           // query tokens per workgroup of the sparse forward (G = 16)
+constexpr int kTF16 = 16;         // ... when 24-token tiles would leave a round mostly empty
 constexpr int kTF8 = 32;          // ... at G = 8 (two tokens' heads stacked per MFMA group)
 constexpr int kWavesF = 8;        // its waves (two per SIMD, 2 tokens each)
 constexpr bool kRounds = true;    // launch items in rounds of one workgroup per CU
@@ -837,14 +838,23 @@ int device_cus() {
 
 // Items are launched in rounds of one workgroup per compute unit, so that the workgroups
 // sharing an XCD start together on neighbouring tiles and walk the same KV blocks at the same
-// time (their L2 then serves each block to all of them).  The forward runs tiles of kTF rows
-// (kTF8 at G = 8, where a wave's 4 tokens fill two 16-column MFMA groups).
-static int attn_tile_rows(const Geom& g) { return g.G == 8 ? kTF8 : kTF; }
+// time (their L2 then serves each block to all of them).  The forward runs tiles of kTF8 rows at
+// G = 8 (a wave's 4 tokens fill two 16-column MFMA groups) and of kTF or kTF16 rows at G = 16: a
+// round of 24-token tiles takes ~1.4 times as long as one of 16-token tiles (measured at 128K:
+// 0.77 against 0.55 ms) for 1.5 times the tokens, so 24 is used unless its last round would be
+// mostly empty (rounds24 * 1.4 >= rounds16: 16K-token chunks, few tiles).
+static int attn_tile_rows(const Geom& g, const SeqTable& t) {
+  if (g.G == 8) return kTF8;
+  const long long round = std::max(8, (device_cus() / 8) * 8);
+  const long long r24 = (static_cast<long long>(bound_tiles(t, kTF)) * g.Hkv + round - 1) / round;
+  const long long r16 = (static_cast<long long>(bound_tiles(t, kTF16)) * g.Hkv + round - 1) / round;
+  return r24 * 7 < r16 * 5 ? kTF : kTF16;
+}
 
 hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, const void* k,
                             const void* v, const int32_t* idx, void* out, float* lse,
                             hipStream_t stream) {
-  const int TF = attn_tile_rows(g);
+  const int TF = attn_tile_rows(g, t);
   const int n_items = bound_tiles(t, TF) * g.Hkv;     // a bound: the kernel counts the tiles
   if (n_items == 0) return hipSuccess;
   const int round = kRounds ? (device_cus() / 8) * 8 : (n_items + 7) / 8 * 8;
@@ -855,7 +865,7 @@ hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, con
   for (int base = 0; base < n_items; base += round) {
     const int grid = std::min(round, (n_items - base + 7) / 8 * 8);
 #define INFLLM2_TILE_CASE(DD, GG, NS, TFF)                                                    \
-  if (g.d == DD && g.G == GG) {                                                               \
+  if (g.d == DD && g.G == GG && TF == TFF) {                                                  \
     hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWavesF, TFF / kWavesF, false, false, true>),   \
                        dim3(grid),                                                            \
                        dim3(64 * kWavesF), 0, stream, g, t, qq, kk, vv, idx, oo, lse, n_items,\
@@ -865,8 +875,10 @@ hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, con
     continue;                                                                                 \
   }
     INFLLM2_TILE_CASE(128, 16, 4, kTF)
+    INFLLM2_TILE_CASE(128, 16, 4, kTF16)
     INFLLM2_TILE_CASE(128, 8, 4, kTF8)
     INFLLM2_TILE_CASE(64, 16, 8, kTF)
+    INFLLM2_TILE_CASE(64, 16, 8, kTF16)
     INFLLM2_TILE_CASE(64, 8, 8, kTF8)
 #undef INFLLM2_TILE_CASE
     return hipErrorInvalidValue;

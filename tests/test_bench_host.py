@@ -14,8 +14,7 @@ import bench  # noqa: E402
 
 
 def test_gather_bound_counts_tile_unions():
-    # groups of 16 heads run 24-token tiles: 30 rows are a full tile and a ragged one of 6;
-    # 2 KV heads, top-4
+    # 24-token tiles: 30 rows are a full tile and a ragged one of 6; 2 KV heads, top-4
     idx = np.full((30, 2, 4), -1, np.int32)
     idx[:24, 0, :] = [0, 1, 2, 3]          # 24 tokens share 4 blocks
     idx[:24, 1, :2] = [5, 6]               # 24 tokens share 2 blocks
@@ -24,8 +23,7 @@ def test_gather_bound_counts_tile_unions():
     idx[25, 0, :1] = 8                     # staged once per tile, twice in all
     idx[24:, 1, :1] = 7                    # ragged tile: 6 tokens, 1 block
     p = types.SimpleNamespace(block_size=64, head_dim=128, num_q_heads=32, num_kv_heads=2)
-    assert bench.tile_tokens(p) == 24
-    g = bench.gather_bound(p, idx, [30], 1e9, 2.0)
+    g = bench.gather_bound(p, idx, [30], 1e9, 2.0, 24)
     blk = 2 * 64 * 128 * 2
     selected = 23 * 4 + 1 * 4 + 24 * 2 + 1 + 1 + 6
     assert g["selected_bytes"] == selected * blk
@@ -40,7 +38,7 @@ def test_gather_bound_packed_sequences_tile_separately():
     # (one 24-token tile each)
     idx = np.zeros((32, 1, 1), np.int32)
     p = types.SimpleNamespace(block_size=64, head_dim=64, num_q_heads=16, num_kv_heads=1)
-    g = bench.gather_bound(p, idx, [16, 16], 1.0, 1.0)
+    g = bench.gather_bound(p, idx, [16, 16], 1.0, 1.0, 24)
     assert g["staged_bytes"] == 2 * (2 * 64 * 64 * 2)
 
 
@@ -51,9 +49,19 @@ def test_gather_bound_uses_32_token_tiles_at_group_8():
     idx[16:32, 0, 0] = 2                   # second half of tile 0
     idx[32:, 0, 0] = 1                     # the ragged tile
     p = types.SimpleNamespace(block_size=64, head_dim=64, num_q_heads=16, num_kv_heads=2)
-    g = bench.gather_bound(p, idx, [40], 1.0, 1.0)
+    assert bench.tile_tokens(p, [40]) == 32
+    g = bench.gather_bound(p, idx, [40], 1.0, 1.0, 32)
     assert g["staged_bytes"] == 3 * (2 * 64 * 64 * 2)
-    assert bench.tile_tokens(p) == 32
+
+
+def test_tile_tokens_follow_the_round_count():
+    # groups of 16: 24-token tiles unless 16-token ones need nearly as few rounds (x 1.4)
+    p = types.SimpleNamespace(num_q_heads=32, num_kv_heads=2)
+    assert bench.tile_tokens(p, [131072], 256) == 24      # 43 rounds against 64
+    assert bench.tile_tokens(p, [32768], 256) == 24       # 11 against 16
+    assert bench.tile_tokens(p, [16384], 256) == 16       # 6 against 8
+    assert bench.tile_tokens(p, [1000, 1000], 256) == 16  # one round either way
+    assert bench.tile_tokens(p, [3000, 2000], 256) == 24  # 2 rounds against 3
 
 
 def test_more_than_one_gpu_is_refused():

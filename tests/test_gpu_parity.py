@@ -89,6 +89,18 @@ def test_8b_shape_ragged_all_rows(L):
         assert hit.all(), f"needle block {nd.block} missed"
 
 
+def test_24_token_tiles_ragged_all_rows():
+    """Enough tiles for the forward to choose 24-token tiles (3 tokens per wave; 2 rounds of
+    one workgroup per compute unit against 3 at 16 tokens), in packed sequences whose last tiles
+    hold 17, 22, 17 and 8 tokens: every row."""
+    p = synth.config_params("prefill32k")
+    wl = synth.make_prefill("tiles-24", p, [1001, 1030, 977, 2000], seed=35)
+    log("case 24-token tiles, ragged")
+    res = run_prefill_stages(wl)
+    for b in range(wl.num_seqs):
+        check_sequence(wl, res, b, label="24-token tiles")
+
+
 def test_varlen_packed_small_all_rows():
     wl = synth.make("varlen", length_scale=1 / 16)
     log("case varlen 1/16")
