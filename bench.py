@@ -40,12 +40,12 @@ def _tile_bound(lens, rows: int) -> int:
 
 
 def tile_tokens(p, lens, cus: int = 256) -> int:
-    """Query tokens per prefill attention work item, chosen as the library chooses: 32 when a
-    group has 8 query heads (two tokens' heads share the 16 columns of each matrix-core tile);
-    else 24 (3 per wave) unless, in rounds of one workgroup per compute unit, 24-token rounds
-    (each ~1.4 times as long) would not beat 16-token ones."""
+    """Query tokens per prefill attention work item, chosen as the library chooses: when a group
+    has 8 query heads (two tokens' heads share the 16 columns of each matrix-core tile), 64 at
+    head_dim 64 and 32 at 128; else 24 (3 per wave) unless, in rounds of one workgroup per
+    compute unit, 24-token rounds (each ~1.4 times as long) would not beat 16-token ones."""
     if p.num_q_heads // p.num_kv_heads == 8:
-        return 32
+        return 64 if p.head_dim == 64 else 32
     rnd = max(8, cus // 8 * 8)
     r24 = -(-_tile_bound(lens, 24) * p.num_kv_heads // rnd)
     r16 = -(-_tile_bound(lens, 16) * p.num_kv_heads // rnd)

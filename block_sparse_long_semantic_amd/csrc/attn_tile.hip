@@ -56,6 +56,7 @@ constexpr int kWaves = 8;         // their waves per workgroup (tokens per wave 
 constexpr int kTF = 24;           // query tokens per workgroup of the sparse forward (G = 16)
 constexpr int kTF16 = 16;         // ... when 24-token tiles would leave a round mostly empty
 constexpr int kTF8 = 32;          // ... at G = 8 (two tokens' heads stacked per MFMA group)
+constexpr int kTF8S = 64;         // ... at G = 8 and head_dim 64 (the smaller accumulators fit)
 constexpr int kWavesF = 8;        // its waves (two per SIMD, 2 tokens each)
 constexpr bool kRounds = true;    // launch items in rounds of one workgroup per CU
 constexpr int kMaxUnion = 2048;   // reachable blocks per tile handled by this kernel
@@ -188,12 +189,27 @@ __device__ __forceinline__ int kswz(int row) {
   else return ((row >> 2) & 6) | ((row >> 1) & 1);
 }
 
+// Scheduling groups for NK k-steps of PER LDS reads feeding PER MFMAs each: the reads of the
+// first AHEAD k-steps, then per k-step its MFMAs, each followed by one read AHEAD k-steps on.
+template <int NK, int PER, int AHEAD>
+__device__ __forceinline__ void sched_reads_ahead() {
+  constexpr int kDsRead = 0x100, kMfma = 0x008;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, AHEAD * PER, 0);
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+      if (ks + AHEAD < NK) __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+    }
+}
+
 // Number of waves (groups of TPW consecutive token bits) with any bit set in a token mask.
-template <int TPW, int NW>
-__device__ __forceinline__ int count_wave_groups(uint32_t m) {
+template <int TPW, int NW, typename M>
+__device__ __forceinline__ int count_wave_groups(M m) {
   int n = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) n += ((m >> (TPW * w)) & ((1u << TPW) - 1u)) != 0u;
+  for (int w = 0; w < NW; ++w) n += ((m >> (TPW * w)) & ((M{1} << TPW) - 1u)) != 0u;
   return n;
 }
 
@@ -222,12 +238,19 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   constexpr int CG = TPW / TPC;              // column groups per wave
   static_assert(TPC * G == 16 || TPC == 1, "a column group is one token or fills 16 columns");
   static_assert(TPW % TPC == 0, "whole column groups per wave");
-  static_assert(T <= 32 && 32 % T != 1, "tile of at most 32 tokens");
-  constexpr int MPW = (T & (T - 1)) == 0 ? 32 / T : 1;  // token masks per bitmap word
-  constexpr uint32_t TMASK = T == 32 ? 0xFFFFFFFFu : (1u << T) - 1u;
+  // token masks: 32 bits, or 64 for tiles of more than 32 tokens
+  using MaskT = typename std::conditional<(T > 32), unsigned long long, uint32_t>::type;
+  constexpr int MB = 8 * static_cast<int>(sizeof(MaskT));
+  static_assert(T <= MB && MB % T != 1, "tile of at most 64 tokens");
+  constexpr int MPW = (T & (T - 1)) == 0 ? MB / T : 1;  // token masks per bitmap word
+  constexpr MaskT TMASK = T == MB ? ~MaskT{0} : (MaskT{1} << T) - 1u;
   __shared__ __attribute__((aligned(16))) unsigned char ring[NS][2][MAT];
-  __shared__ uint32_t bitmap[kMaxUnion / MPW];
-  __shared__ uint32_t umask[kMaxUnion];      // union list: token mask of entry u
+  // the bitmap of the union build lives at the end of the ring, which is free until staging
+  // (the stream-order sort uses its start)
+  constexpr int BITMAP_BYTES = kMaxUnion / MPW * static_cast<int>(sizeof(MaskT));
+  static_assert(BITMAP_BYTES + 4 * kMaxUnion <= NS * 2 * MAT, "bitmap and sort keys fit the ring");
+  MaskT* const bitmap = reinterpret_cast<MaskT*>(&ring[0][0][0] + NS * 2 * MAT - BITMAP_BYTES);
+  __shared__ MaskT umask[kMaxUnion];         // union list: token mask of entry u
   __shared__ uint16_t ublk[kMaxUnion];       //             its block index
   __shared__ int wave_tot[NW];
   __shared__ int ready[NS];
@@ -262,16 +285,16 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   const int Hq = g.Hq, Hkv = g.Hkv;
 
   // ---- union of the tile's selected blocks
-  for (int e = tid; e < (nbt + MPW - 1) / MPW; e += NTHR) bitmap[e] = 0u;
+  for (int e = tid; e < (nbt + MPW - 1) / MPW; e += NTHR) bitmap[e] = MaskT{0};
   __syncthreads();
   if constexpr (WIN) {
     // token tok needs the blocks meeting [pos - window + 1, pos]
     const int blo = max(0, pos0 - g.window + 1) / 64;
     for (int blk = blo + tid; blk < nbt; blk += NTHR) {
-      uint32_t m = 0u;
+      MaskT m = 0u;
       for (int tok = 0; tok < nq; ++tok) {
         const int pos = pos0 + tok;
-        if (64 * blk <= pos && 64 * blk + 63 > pos - g.window) m |= 1u << tok;
+        if (64 * blk <= pos && 64 * blk + 63 > pos - g.window) m |= MaskT{1} << tok;
       }
       if (m != 0u) atomicOr(&bitmap[blk / MPW], m << (T * (blk % MPW)));
     }
@@ -279,7 +302,7 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
     for (int e = tid; e < nq * g.topk; e += NTHR) {
       const int tok = e / g.topk;
       const int blk = idx[(static_cast<size_t>(row0 + tok) * Hkv + kvh) * g.topk + (e - tok * g.topk)];
-      if (blk >= 0) atomicOr(&bitmap[blk / MPW], (1u << tok) << (T * (blk % MPW)));
+      if (blk >= 0) atomicOr(&bitmap[blk / MPW], (MaskT{1} << tok) << (T * (blk % MPW)));
     }
   }
   __syncthreads();
@@ -287,7 +310,7 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
     // each thread compacts KPT consecutive blocks; block-wide exclusive scan of the counts
     constexpr int KPT = kMaxUnion / NTHR;
     const int b0 = tid * KPT;
-    uint32_t m8[KPT];
+    MaskT m8[KPT];
     int cnt = 0;
 #pragma unroll
     for (int e = 0; e < KPT; ++e) {
@@ -330,7 +353,7 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
     for (int e = tid; e < npow2; e += NTHR) skey[e] = e < n_union ? 0u : 0xFFFFFFFFu;
     __syncthreads();
     {
-      const uint32_t wbits = ((1u << TPW) - 1u) << (TPW * w);
+      const MaskT wbits = ((MaskT{1} << TPW) - 1u) << (TPW * w);
       int n_w = 0;
       for (int base = 0; base < n_union; base += 64) {
         const bool nd = base + lane < n_union && (umask[base + lane] & wbits) != 0u;
@@ -366,7 +389,7 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
       }
     }
     constexpr int EPT = kMaxUnion / NTHR;
-    uint32_t pm[EPT];
+    MaskT pm[EPT];
     uint16_t pb[EPT];
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
@@ -549,15 +572,18 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   bool stalled = false;
   // The wave reads 64 list entries at a time and jumps straight to the blocks its tokens chose.
   for (int ubase = 0; ubase < n_union && !stalled; ubase += 64) {
-    const uint32_t chunk = ubase + lane < n_union ? umask[ubase + lane] : 0u;
+    const MaskT chunk = ubase + lane < n_union ? umask[ubase + lane] : MaskT{0};
     const int chunk_blk = ubase + lane < n_union ? static_cast<int>(ublk[ubase + lane]) : 0;
-    unsigned long long todo = __ballot(((chunk >> (TPW * w)) & ((1u << TPW) - 1u)) != 0u);
+    unsigned long long todo = __ballot(((chunk >> (TPW * w)) & ((MaskT{1} << TPW) - 1u)) != 0u);
    while (todo != 0ull) {
     const int bit = __builtin_ctzll(todo);
     todo &= todo - 1ull;
     const int u = ubase + bit;
-    const uint32_t ent = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(chunk), bit));
-    const uint32_t wm = (ent >> (TPW * w)) & ((1u << TPW) - 1u);
+    MaskT ent = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(chunk), bit));
+    if constexpr (sizeof(MaskT) == 8)
+      ent |= static_cast<MaskT>(static_cast<uint32_t>(
+                 __builtin_amdgcn_readlane(static_cast<int>(chunk >> 32), bit))) << 32;
+    const uint32_t wm = static_cast<uint32_t>((ent >> (TPW * w)) & ((MaskT{1} << TPW) - 1u));
     const int slot = u % NS;
     if (lds_peek(&ready[slot]) != u) {
       if (pending >= 0) {
@@ -594,18 +620,27 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
             sa[s][tp] = f32x4{0.f, 0.f, 0.f, 0.f};
             pa4[s][tp] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
+        bf16x8 ka[KS][2][2], va[KS][2][2];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
           for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int tp = 0; tp < 2; ++tp) {
-              const int J = ((2 * s + tp) * KS + ks) * 64;
-              sa[s][tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Kp[J], qf[tt][ks], sa[s][tp], 0, 0, 0);
-              pa4[s][tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  *(const lds_bf16x8*)(uintptr_t)(kofs[ks] + slot_off + MAT + (32 * s + 4 * tp) * 2 * D),
-                  dof[tt][ks], pa4[s][tp], 0, 0, 0);
+              ka[ks][s][tp] = Kp[((2 * s + tp) * KS + ks) * 64];
+              va[ks][s][tp] =
+                  *(const lds_bf16x8*)(uintptr_t)(kofs[ks] + slot_off + MAT + (32 * s + 4 * tp) * 2 * D);
             }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int tp = 0; tp < 2; ++tp) {
+              sa[s][tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks][s][tp], qf[tt][ks], sa[s][tp], 0, 0, 0);
+              pa4[s][tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[ks][s][tp], dof[tt][ks], pa4[s][tp], 0, 0, 0);
+            }
+        sched_reads_ahead<KS, 8, 1>();
         const int lim = (key0 + 63 > pos || key0 + 64 > kv_len) ? min(pos, kv_len - 1) - key0 : 63;
         const float nl = -lse2[tt];
         const float dd = dl[tt];
@@ -648,15 +683,25 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int tp = 0; tp < 2; ++tp) acc4[s][tp] = f32x4{0.f, 0.f, 0.f, 0.f};
+      bf16x8 kf[KS][2][2];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
           for (int tp = 0; tp < 2; ++tp)
-            acc4[s][tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                *(const lds_bf16x8*)(uintptr_t)(kofs[ks] + slot_off + (32 * s + 4 * tp) * 2 * D),
-                qf[tt][ks], acc4[s][tp], 0, 0, 0);
+            kf[ks][s][tp] = *(const lds_bf16x8*)(uintptr_t)(kofs[ks] + slot_off + (32 * s + 4 * tp) * 2 * D);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int tp = 0; tp < 2; ++tp)
+            acc4[s][tp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks][s][tp], qf[tt][ks], acc4[s][tp], 0, 0, 0);
+      // instruction order: the first two k-steps' reads, then the MFMAs, each followed by a
+      // read two k-steps ahead (left to itself the scheduler waits for nearly every read right
+      // before its MFMA)
+      sched_reads_ahead<KS, 4, 2>();
       float sv[2][2][4];
 #pragma unroll
       for (int s = 0; s < 2; ++s)
@@ -747,7 +792,7 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
       pending = -1;
     }
     // done accounting; the last of the block's waves refills the slot
-    const uint32_t mk = ent;
+    const MaskT mk = ent;
     const int needers = count_wave_groups<TPW, NW>(mk);
     int old = 0;
     if (lane == 0) old = atomicAdd(&done[slot], 1);
@@ -844,7 +889,7 @@ int device_cus() {
 // 0.77 against 0.55 ms) for 1.5 times the tokens, so 24 is used unless its last round would be
 // mostly empty (rounds24 * 1.4 >= rounds16: 16K-token chunks, few tiles).
 static int attn_tile_rows(const Geom& g, const SeqTable& t) {
-  if (g.G == 8) return kTF8;
+  if (g.G == 8) return g.d == 64 ? kTF8S : kTF8;
   const long long round = std::max(8, (device_cus() / 8) * 8);
   const long long r24 = (static_cast<long long>(bound_tiles(t, kTF)) * g.Hkv + round - 1) / round;
   const long long r16 = (static_cast<long long>(bound_tiles(t, kTF16)) * g.Hkv + round - 1) / round;
@@ -879,7 +924,7 @@ hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, con
     INFLLM2_TILE_CASE(128, 8, 4, kTF8)
     INFLLM2_TILE_CASE(64, 16, 8, kTF)
     INFLLM2_TILE_CASE(64, 16, 8, kTF16)
-    INFLLM2_TILE_CASE(64, 8, 8, kTF8)
+    INFLLM2_TILE_CASE(64, 8, 8, kTF8S)
 #undef INFLLM2_TILE_CASE
     return hipErrorInvalidValue;
   }

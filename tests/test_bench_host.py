@@ -48,10 +48,12 @@ def test_gather_bound_uses_32_token_tiles_at_group_8():
     idx[:16, 0, 0] = 1                     # first half of tile 0
     idx[16:32, 0, 0] = 2                   # second half of tile 0
     idx[32:, 0, 0] = 1                     # the ragged tile
-    p = types.SimpleNamespace(block_size=64, head_dim=64, num_q_heads=16, num_kv_heads=2)
+    p = types.SimpleNamespace(block_size=64, head_dim=128, num_q_heads=16, num_kv_heads=2)
     assert bench.tile_tokens(p, [40]) == 32
+    assert bench.tile_tokens(types.SimpleNamespace(head_dim=64, num_q_heads=16, num_kv_heads=2),
+                             [40]) == 64
     g = bench.gather_bound(p, idx, [40], 1.0, 1.0, 32)
-    assert g["staged_bytes"] == 3 * (2 * 64 * 64 * 2)
+    assert g["staged_bytes"] == 3 * (2 * 64 * 128 * 2)
 
 
 def test_tile_tokens_follow_the_round_count():

@@ -121,11 +121,13 @@ def test_edge_sequences():
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_edge_sequences_group8(d):
-    """Groups of 8 heads run 32-token tiles in which two tokens' heads share each matrix-core
-    column group: sequences whose last tile is ragged at every parity (a lone token in its pair,
-    a pair split by the sequence end), packed together; every row."""
+    """Groups of 8 heads run 64-token (head_dim 64) or 32-token (128) tiles in which two tokens'
+    heads share each matrix-core column group: sequences whose last tile is ragged at every
+    parity (a lone token in its pair, a pair split by the sequence end) or full, packed
+    together; every row."""
     p = replace(synth.config_params("varlen"), head_dim=d)
-    wl = synth.make_prefill("edge-g8", p, [0, 1, 2, 17, 31, 32, 33, 47, 65, 130, 700], seed=34)
+    wl = synth.make_prefill("edge-g8", p, [0, 1, 2, 17, 31, 32, 33, 47, 63, 64, 65, 127, 130, 700],
+                            seed=34)
     log(f"case edge lengths, group 8, d {d}")
     res = run_prefill_stages(wl)
     for b in range(wl.num_seqs):
