@@ -7,8 +7,11 @@ Parity rules:
               (float32 accumulation over G*d <= 2048 terms plus the two-part bf16 query)
   indices     equal sets except swaps between blocks whose oracle scores differ by less than
               1e-3 relative; forced blocks always present; sizes equal
-  attention   max |O - O_oracle(on the HIP path's own indices)| <= 2e-2 (bf16) / 1e-4 (f32);
-              |lse - lse_oracle| <= 1e-3 (bf16) / 1e-5 (f32)
+  attention   |O - O_oracle(on the HIP path's own indices)| <= 2e-2 (bf16) / 1e-4 (f32)
+              elementwise, and for bf16 outputs of magnitude >= 4 one bf16 unit in the last
+              place of the oracle's value (2^-5 there: the output format cannot hold such a
+              value closer than half of it, and the probabilities enter the P V product as
+              bf16 MFMA operands); |lse - lse_oracle| <= 1e-3 (bf16) / 1e-5 (f32)
   gradients   |g - g_oracle| <= 2^-7 * m elementwise, m the magnitude of the same sum taken
               over absolute values (backward_magnitudes); see there for the error budget
 """
@@ -97,11 +100,29 @@ def check_indices(gpu_idx: np.ndarray, ref_idx: np.ndarray, ref_scores: np.ndarr
     return IndexReport(n * p.num_kv_heads, exact, band)
 
 
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Unit in the last place of bfloat16 (8 significant bits) at magnitude |x|."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), np.finfo(np.float64).tiny)))
+    return np.exp2(e - 7)
+
+
+def out_tolerance(ref_out: np.ndarray, dtype: str) -> np.ndarray:
+    """Elementwise output tolerance (see the module docstring)."""
+    if dtype == "bf16":
+        return np.maximum(OUT_TOL[dtype], bf16_ulp(ref_out))
+    return np.full(ref_out.shape, OUT_TOL[dtype])
+
+
 def check_attention(out: np.ndarray, lse: np.ndarray, ref_out: np.ndarray, ref_lse: np.ndarray,
                     dtype: str):
-    err = float(np.abs(out.astype(np.float64) - ref_out).max()) if out.size else 0.0
+    d = np.abs(out.astype(np.float64) - ref_out)
+    err = float(d.max()) if out.size else 0.0
     lerr = float(np.abs(lse.astype(np.float64) - ref_lse).max()) if lse.size else 0.0
-    assert err <= OUT_TOL[dtype], f"output max-abs error {err} > {OUT_TOL[dtype]}"
+    if out.size:
+        tol = out_tolerance(ref_out, dtype)
+        i = np.unravel_index(np.argmax(d - tol), d.shape)
+        assert d[i] <= tol[i], (f"output error {d[i]} > {tol[i]} at {i} (oracle {ref_out[i]}, "
+                                f"max-abs error {err})")
     assert lerr <= LSE_TOL[dtype], f"lse max-abs error {lerr} > {LSE_TOL[dtype]}"
     return err, lerr
 

@@ -445,10 +445,10 @@ def test_decode_f32_tiny_shape():
 # ------------------------------------------------------------------------- full sizes
 
 def whole_tiles(L, n_windows=8, needle_rows=()):
-    """Every row of n_windows windows of 96 consecutive rows aligned to 96 (whole tiles of 16,
-    24 or 32 query rows): spread over the sequence, the last window, and one holding a needle
+    """Every row of n_windows windows of 192 consecutive rows aligned to 192 (whole tiles of 16,
+    24, 32 or 64 query rows): spread over the sequence, the last window, and one holding a needle
     query (when there is one)."""
-    W = 96
+    W = 192
     last = max(0, (L - 1) // W)
     starts = {int(x) for x in np.linspace(0, last, n_windows - 1).round()} | {last}
     if len(needle_rows):
