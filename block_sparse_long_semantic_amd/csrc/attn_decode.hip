@@ -16,7 +16,7 @@
 //
 // The decode step (infllm2_decode_step) is two launches.  decode_scores: block scores (section
 // 2.1.2: the group-summed query against every semantic kernel, max-pooled onto blocks), one
-// workgroup per chunk of 128 blocks of a (row, kv head); the kernels completed since the last
+// workgroup per chunk of 64 blocks of a (row, kv head); the kernels completed since the last
 // compression are computed there from the keys and stored.  Then attn_decode in its selecting
 // form: every split workgroup of a (row, kv head) first runs the group-shared top-k (2.1.1-2.1.2)
 // of the pair itself, from the stored scores (a radix select over the order-preserving score
@@ -552,7 +552,7 @@ constexpr int kStepWaves = 8;
 // ------------------------------------------------------------------------------ block scores
 constexpr int kScoreWaves = 8;
 constexpr int kScoreThreads = 64 * kScoreWaves;
-constexpr int kChunkBlocks = 128;               // blocks per score work item
+constexpr int kChunkBlocks = 64;                // blocks per score work item
 
 // A kernel row's 8 bf16 columns dotted with the group-summed query's (float32 FMAs in column
 // order; the row total is the DPP group sum over the row's lanes).
@@ -661,9 +661,9 @@ __device__ __forceinline__ void score_chunk(const Geom& g, const SeqTable& t, co
   }
 }
 
-// The new kernels of kernel chunk `chunk` (kernels 512 chunk .. 512 chunk + 511) that no query
-// row scores (the cache runs past the sequence's last query position), computed and stored by
-// the sequence's last row's workgroup of that chunk.
+// The new kernels of chunk `chunk` (its 4 kChunkBlocks kernels, from 4 kChunkBlocks chunk on)
+// that no query row scores (the cache runs past the sequence's last query position), computed
+// and stored by the sequence's last row's workgroup of that chunk.
 template <int D>
 __device__ __forceinline__ void compress_unscored(const Geom& g, const DecRow& r, int kvh,
                                                   int chunk, int c_new,

@@ -26,11 +26,6 @@ __device__ __forceinline__ int prefix_count(unsigned long long mask) {
                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
 }
 
-// Relaxed agent-scope load: coherent across the XCDs' L2s without a fence.
-__device__ __forceinline__ uint32_t coherent_load(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // LDS of wg_select.
 template <int NW>
 struct WgSelectLds {
@@ -53,9 +48,8 @@ struct WgSelectLds {
 // ways.  It stops when every key of the chosen bin is wanted, or the bin holds a single key value
 // (taken in block order), or the bin holds at most 64 keys: then one wave ranks those keys
 // exactly (key descending, block ascending) and marks the wanted ones.  `keys` (LDS, one word
-// per block) holds the keys for the ordered output.  Scores are read with agent-scope loads, so
-// they may come from other workgroups of the same launch.  Every thread of the workgroup must
-// call it.
+// per block) holds the keys for the ordered output.  The scores must come from an earlier launch
+// (plain loads).  Every thread of the workgroup must call it.
 template <int NW, int KPT, typename Emit>
 __device__ __forceinline__ void wg_select(const Geom& g, int own, const float* srow, Emit emit,
                                           uint32_t* keys, WgSelectLds<NW>& sm, int tid) {
@@ -76,9 +70,7 @@ __device__ __forceinline__ void wg_select(const Geom& g, int own, const float* s
   float sc[KPT];
 #pragma unroll
   for (int e = 0; e < KPT; ++e)
-    sc[e] = e < npt ? __uint_as_float(coherent_load(reinterpret_cast<const uint32_t*>(srow) +
-                                                 min(e * T + tid, nb - 1)))
-                    : 0.f;
+    sc[e] = e < npt ? srow[min(e * T + tid, nb - 1)] : 0.f;
   uint32_t kr[KPT];
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
