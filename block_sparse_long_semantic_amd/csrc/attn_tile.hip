@@ -243,7 +243,7 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   constexpr int MB = 8 * static_cast<int>(sizeof(MaskT));
   static_assert(T <= MB && MB % T != 1, "tile of at most 64 tokens");
   constexpr int MPW = (T & (T - 1)) == 0 ? MB / T : 1;  // token masks per bitmap word
-  constexpr MaskT TMASK = T == MB ? ~MaskT{0} : (MaskT{1} << T) - 1u;
+  constexpr MaskT TMASK = T == MB ? ~MaskT{0} : (MaskT{1} << (T % MB)) - 1u;
   __shared__ __attribute__((aligned(16))) unsigned char ring[NS][2][MAT];
   // the bitmap of the union build lives at the end of the ring, which is free until staging
   // (the stream-order sort uses its start)
@@ -567,7 +567,8 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   // its tokens chose.  Slot u % NS holds stream entry u once ready[slot] == u.  The last wave to finish a block
   // (counted in done[slot] against the number of waves that need it) refills the slot with block
   // u + NS and publishes it after its loads have landed: right away if it is about to wait for a
-  // block itself, otherwise after its next block of work.  Every wait is bounded.
+  // block itself, otherwise after its next block of work, running at raised wave priority
+  // until then.  Every wait is bounded.
   int pending = -1;       // stream entry this wave loaded and has not published yet
   bool stalled = false;
   // The wave reads 64 list entries at a time and jumps straight to the blocks its tokens chose.
@@ -590,6 +591,7 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
         wait_vmcnt<0>();
         lds_store(&ready[pending % NS], pending);
         pending = -1;
+        __builtin_amdgcn_s_setprio(0);
       }
       int spins = 0;
       while (lds_peek(&ready[slot]) != u) {
@@ -790,16 +792,20 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
       wait_vmcnt<0>();
       lds_store(&ready[pending % NS], pending);
       pending = -1;
+      __builtin_amdgcn_s_setprio(0);
     }
     // done accounting; the last of the block's waves refills the slot
     const MaskT mk = ent;
     const int needers = count_wave_groups<TPW, NW>(mk);
     int old = 0;
     if (lane == 0) old = atomicAdd(&done[slot], 1);
-    old = __shfl(old, 0);
+    old = __builtin_amdgcn_readfirstlane(old);
     if (old + 1 == needers) {
       if (lane == 0) lds_store(&done[slot], 0);
       if (u + NS < n_union) {
+        // other waves wait for this refill: the wave issues it and runs at raised priority
+        // until it has published it (its SIMD's other wave yields issue slots meanwhile)
+        __builtin_amdgcn_s_setprio(2);
         produce(u + NS, slot, 0, 1);
         pending = u + NS;
       }
