@@ -3,8 +3,8 @@
 // softmax).
 //
 // Design (one workgroup = 8 waves = one tile of T consecutive query tokens of one sequence and
-// one KV head: T = 24 in the sparse forward at groups of 16 heads, 32 at groups of 8, 16 in the
-// gradient and window forms):
+// one KV head: T = 24 in the sparse forward at groups of 16 heads, 32 at groups of 8 (64 at
+// head_dim 64), 16 in the gradient and window forms):
 //   * Union: the tile's T selected-block lists are OR-ed into a per-block T-bit token mask in
 //     LDS and compacted into a list of (block, mask).  Each union block's K and V (64 keys x d,
 //     bf16) are staged into LDS once for all tokens that chose it.  The forward and gradient
@@ -17,7 +17,8 @@
 //     XOR-swizzled by kswz(r), so that an A-operand read spans all banks; V in the unit order
 //     its transposing reads want.  The last wave to finish with a slot (an LDS counter against
 //     the number of waves whose tokens chose the block) refills it with block u + NS and
-//     raises the slot's ready word once the loads have landed; waits poll that word, bounded.
+//     raises the slot's ready word once the loads have landed (at raised wave priority until
+//     then); waits poll that word, bounded.
 //   * Compute: wave w owns tokens TPW*w .. TPW*w + TPW - 1 (T / 8 of them; registers: Q operand,
 //     O accumulator, running max and sum per 16-column group, a group holding one token's 16
 //     heads or two tokens' 8).  For every union block it processes only its groups with a
@@ -890,7 +891,8 @@ int device_cus() {
 // Items are launched in rounds of one workgroup per compute unit, so that the workgroups
 // sharing an XCD start together on neighbouring tiles and walk the same KV blocks at the same
 // time (their L2 then serves each block to all of them).  The forward runs tiles of kTF8 rows at
-// G = 8 (a wave's 4 tokens fill two 16-column MFMA groups) and of kTF or kTF16 rows at G = 16: a
+// G = 8 (a wave's 4 tokens fill two 16-column MFMA groups; kTF8S rows, 8 tokens in four groups,
+// at head_dim 64, whose accumulators are half as large) and of kTF or kTF16 rows at G = 16: a
 // round of 24-token tiles takes ~1.4 times as long as one of 16-token tiles (measured at 128K:
 // 0.77 against 0.55 ms) for 1.5 times the tokens, so 24 is used unless its last round would be
 // mostly empty (rounds24 * 1.4 >= rounds16: 16K-token chunks, few tiles).
