@@ -58,7 +58,7 @@ constexpr int kTF = 24;           // query tokens per workgroup of the sparse fo
 constexpr int kTF16 = 16;         // ... when 24-token tiles would leave a round mostly empty
 constexpr int kTF8 = 32;          // ... at G = 8 (two tokens' heads stacked per MFMA group)
 constexpr int kTF8S = 64;         // ... at G = 8 and head_dim 64 (the smaller accumulators fit)
-constexpr int kWavesF = 8;        // its waves (two per SIMD, 2 tokens each)
+constexpr int kWavesF = 8;        // its waves (two per SIMD, TF / 8 tokens each)
 constexpr bool kRounds = true;    // launch items in rounds of one workgroup per CU
 constexpr int kMaxUnion = 2048;   // reachable blocks per tile handled by this kernel
 constexpr float kLazy = 8.f;      // log2 headroom before the running max is moved
