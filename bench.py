@@ -32,11 +32,13 @@ sys.path.insert(0, ROOT)
 METRIC = "sparse-attn prefill tokens/s @128K + decode µs/token; % MFMA/HBM roofline"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
-def _tile_bound(lens, rows: int) -> int:
-    """The library's host bound on the tiles of `rows` tokens (it sees the metadata's bounds only:
-    sequences, longest query run, total rows)."""
+def _group_bound(lens, rows: int, gs: int, hkv: int) -> int:
+    """The library's host bound on the groups of gs consecutive tiles of `rows` tokens (one XCD's
+    share of a round; it sees the metadata's bounds only: sequences, longest query run, total
+    rows)."""
     n_seq, max_q, T = len(lens), max(lens), sum(lens)
-    return min(n_seq * -(-max_q // rows), -(-T // rows) + n_seq)
+    per_seq = -(-(-(-max_q // rows)) // gs)
+    return min(n_seq * per_seq, -(-T // (rows * gs)) + n_seq) * hkv
 
 
 def tile_tokens(p, lens, cus: int = 256) -> int:
@@ -46,9 +48,9 @@ def tile_tokens(p, lens, cus: int = 256) -> int:
     compute unit, 24-token rounds (each ~1.4 times as long) would not beat 16-token ones."""
     if p.num_q_heads // p.num_kv_heads == 8:
         return 64 if p.head_dim == 64 else 32
-    rnd = max(8, cus // 8 * 8)
-    r24 = -(-_tile_bound(lens, 24) * p.num_kv_heads // rnd)
-    r16 = -(-_tile_bound(lens, 16) * p.num_kv_heads // rnd)
+    gs = max(1, cus // 8)
+    r24 = -(-_group_bound(lens, 24, gs, p.num_kv_heads) // 8)
+    r16 = -(-_group_bound(lens, 16, gs, p.num_kv_heads) // 8)
     return 24 if r24 * 7 < r16 * 5 else 16
 
 
@@ -145,13 +147,13 @@ def run_prefill(args, torch, pkg, synth, workload=None, keep=True):
     bytes_scores = T * Hq * d * 2 + C * Hkv * d * 2 + causal_blocks * Hkv * 4
     bytes_topk = causal_blocks * Hkv * 4 + T * Hkv * p.topk * 4
     bytes_compress = T * Hkv * d * 2 + C * Hkv * d * 2
-    # the attention call launches its tiles in rounds of one workgroup per compute unit; the
-    # grid covers the library's host bound on the tiles (it sees only the metadata's bounds:
-    # sequences, longest query run, total rows), not the exact count
+    # the attention call launches its tiles in rounds of one workgroup per compute unit, 8
+    # groups of CUs / 8 tiles each; the rounds cover the library's host bound on the groups (it
+    # sees only the metadata's bounds: sequences, longest query run, total rows), not the exact
+    # count
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     TT = tile_tokens(p, lens, cus)
-    items = _tile_bound(lens, TT) * Hkv
-    launches = (items + cus // 8 * 8 - 1) // (cus // 8 * 8)
+    launches = -(-_group_bound(lens, TT, max(1, cus // 8), Hkv) // 8)
     result = dict(
         workload=workload, tokens=T, seq_lens=lens, p=p, ms_step=ms_step, stage=stage,
         flops=flops, tflops=tflops, keys=keys, launches=launches,

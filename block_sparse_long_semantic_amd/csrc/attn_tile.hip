@@ -30,12 +30,14 @@
 //                     transposes 4x16 bf16 tiles across each 16-lane group, so V needs no
 //                     transposed copy.  The key order inside each 32-key step makes the
 //                     S^T fragment a lane holds exactly its P operand.
-//   * Scheduling: work items go in rounds of one workgroup per compute unit, laid out so that
-//     each XCD (blockIdx % 8) runs consecutive tiles of one KV head, which select from the
-//     same blocks and share that XCD's L2.
+//   * Scheduling: launches go in rounds of one workgroup per compute unit; in a round each XCD
+//     (blockIdx % 8) runs a group of consecutive tiles of one (sequence, KV head), which select
+//     from the same blocks and share that XCD's L2.  Groups are taken by their position in the
+//     sequence, highest first, so that the eight groups of a round take about as long.
 #include <algorithm>
 #include <atomic>
 
+#include "dpp.h"
 #include "internal.h"
 
 namespace infllm2 {
@@ -59,7 +61,6 @@ constexpr int kTF16 = 16;         // ... when 24-token tiles would leave a round
 constexpr int kTF8 = 32;          // ... at G = 8 (two tokens' heads stacked per MFMA group)
 constexpr int kTF8S = 64;         // ... at G = 8 and head_dim 64 (the smaller accumulators fit)
 constexpr int kWavesF = 8;        // its waves (two per SIMD, TF / 8 tokens each)
-constexpr bool kRounds = true;    // launch items in rounds of one workgroup per CU
 constexpr int kMaxUnion = 2048;   // reachable blocks per tile handled by this kernel
 constexpr float kLazy = 8.f;      // log2 headroom before the running max is moved
 constexpr int kSpinLimit = 1 << 20;  // bounded waits (about 30 ms): a protocol error never hangs
@@ -205,6 +206,60 @@ __device__ __forceinline__ void sched_reads_ahead() {
     }
 }
 
+// Work items of the tile launches are groups of gs consecutive tiles of one (sequence, KV head),
+// the tiles one XCD runs in one round.  Group j of a sequence (tiles gs*j .. gs*j + gs - 1) is at
+// level j; groups are numbered from the highest level down, then by sequence, then by KV head,
+// so that the eight groups of a round lie at about the same position in their sequences and take
+// about as long (a tile's work grows with its position: more reachable blocks).  Finds the
+// sequence, KV head and level of group gi; false past the last group.  groups(s) is the number
+// of groups of sequence s.  Every lane of a full wave calls it with the same gi; the results are
+// wave-uniform.  One pass over the sequences per distinct group count.
+template <typename F>
+__device__ __forceinline__ bool locate_group(const SeqTable& t, int gi, int hkv, F groups, int& b,
+                                             int& kvh, int& level) {
+  const int lane = threadIdx.x & 63;
+  int lev = -1;                                   // the highest level
+  for (int base = 0; base < t.n; base += 64) {
+    const int gl = base + lane < t.n ? groups(base + lane) : 0;
+    lev = max(lev, static_cast<int>(wave_max_u32(static_cast<uint32_t>(gl))) - 1);
+  }
+  long long acc = 0;                              // groups above level lev
+  while (lev >= 0) {
+    // c groups at each of the levels nxt + 1 .. lev (the same sequences have a group there)
+    int c = 0, nxt = -1;
+    for (int base = 0; base < t.n; base += 64) {
+      const int gl = base + lane < t.n ? groups(base + lane) : 0;
+      c += __popcll(__ballot(gl > lev));
+      nxt = max(nxt, static_cast<int>(wave_max_u32(static_cast<uint32_t>(gl <= lev ? gl : 0))) - 1);
+    }
+    c *= hkv;
+    const long long span = static_cast<long long>(lev - nxt) * c;
+    if (gi - acc < span) {
+      const int off = static_cast<int>(gi - acc);
+      level = uniform(lev - off / c);
+      const int r = off % c;
+      kvh = uniform(r % hkv);
+      int rs = r / hkv;                           // the rs-th sequence having a group at lev
+      for (int base = 0; base < t.n; base += 64) {
+        const int gl = base + lane < t.n ? groups(base + lane) : 0;
+        const unsigned long long m = __ballot(gl > lev);
+        const int pc = __popcll(m);
+        if (rs < pc) {
+          const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+          b = uniform(base + __ffsll(static_cast<unsigned long long>(__ballot(gl > lev && below == rs))) - 1);
+          return true;
+        }
+        rs -= pc;
+      }
+      return false;
+    }
+    acc += span;
+    lev = nxt;
+  }
+  return false;
+}
+
 // Number of waves (groups of TPW consecutive token bits) with any bit set in a token mask.
 template <int TPW, int NW, typename M>
 __device__ __forceinline__ int count_wave_groups(M m) {
@@ -225,7 +280,7 @@ template <int D, int G, int NS, int NW, int TPW, bool BWD, bool WIN = false, boo
 __global__ void __launch_bounds__(64 * NW, 1)
 attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
           const uint16_t* __restrict__ v, const int32_t* __restrict__ idx,
-          uint16_t* __restrict__ out, float* __restrict__ lse, int n_items, int item_base,
+          uint16_t* __restrict__ out, float* __restrict__ lse, int group_base,
           const uint16_t* __restrict__ dout, const float* __restrict__ lse_in,
           const float* __restrict__ delta, float* __restrict__ dq) {
   constexpr int KS = D / 32;
@@ -257,19 +312,16 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   __shared__ int ready[NS];
   __shared__ int done[NS];
 
-  // XCD-aware: workgroup b runs on XCD b % 8; the XCD's workgroups take consecutive items
-  const int per_xcd = gridDim.x / 8;
-  const int item =
-      item_base + static_cast<int>(blockIdx.x % 8) * per_xcd + static_cast<int>(blockIdx.x / 8);
-  if (item >= n_items) return;
-  auto tiles_of = [&](int s) { return (t.q_len[s] + T - 1) / T; };
-  const int n_tiles = count_items(t, tiles_of);
-  if (item >= n_tiles * g.Hkv) return;
-  const int kvh = item / n_tiles;
-  const int tile = item - kvh * n_tiles;
-  int b, lt;
-  locate(t, tile, tiles_of, b, lt);
+  // XCD-aware: workgroup b runs on XCD b % 8, which takes group group_base + b % 8; its
+  // workgroups take the group's consecutive tiles
+  const int gs = static_cast<int>(gridDim.x) / 8;
+  auto groups_of = [&](int s) { return ((t.q_len[s] + T - 1) / T + gs - 1) / gs; };
+  int b, kvh, level;
+  if (!locate_group(t, group_base + static_cast<int>(blockIdx.x % 8), g.Hkv, groups_of, b, kvh, level))
+    return;
+  const int lt = level * gs + static_cast<int>(blockIdx.x / 8);
   const Seq sq = load_seq(t, b);
+  if (lt * T >= sq.q_len) return;
   const int r0 = lt * T;
   const int nq = min(T, sq.q_len - r0);
   const int row0 = sq.q_start + r0;
@@ -888,19 +940,34 @@ int device_cus() {
   return n;
 }
 
-// Items are launched in rounds of one workgroup per compute unit, so that the workgroups
+// Tiles are launched in rounds of one workgroup per compute unit, so that the workgroups
 // sharing an XCD start together on neighbouring tiles and walk the same KV blocks at the same
-// time (their L2 then serves each block to all of them).  The forward runs tiles of kTF8 rows at
+// time (their L2 then serves each block to all of them): a round is 8 groups of gs = CUs / 8
+// consecutive tiles (locate_group).  Without the per-round restart the workgroups of an XCD
+// drift apart and stop sharing staged blocks in its L2.  The forward runs tiles of kTF8 rows at
 // G = 8 (a wave's 4 tokens fill two 16-column MFMA groups; kTF8S rows, 8 tokens in four groups,
 // at head_dim 64, whose accumulators are half as large) and of kTF or kTF16 rows at G = 16: a
 // round of 24-token tiles takes ~1.4 times as long as one of 16-token tiles (measured at 128K:
 // 0.77 against 0.55 ms) for 1.5 times the tokens, so 24 is used unless its last round would be
 // mostly empty (rounds24 * 1.4 >= rounds16: 16K-token chunks, few tiles).
+static int group_tiles() { return std::max(1, device_cus() / 8); }
+
+// Bound on the number of tile groups of a launch (tiles of `rows` rows, gs tiles per group): at
+// most ceil(ceil(max_q_len / rows) / gs) per (sequence, KV head), and, since a sequence of len
+// rows has fewer than len / (rows gs) + 1 groups, at most ceil(q_rows / (rows gs)) + n in all.
+static int bound_groups(const SeqTable& t, int rows, int gs, int hkv) {
+  const long long per_seq = ((static_cast<long long>(t.max_q_len) + rows - 1) / rows + gs - 1) / gs;
+  const long long a = static_cast<long long>(t.n) * per_seq;
+  const long long span = static_cast<long long>(rows) * gs;
+  const long long c = (static_cast<long long>(t.q_rows) + span - 1) / span + t.n;
+  return static_cast<int>((a < c ? a : c) * hkv);
+}
+
 static int attn_tile_rows(const Geom& g, const SeqTable& t) {
   if (g.G == 8) return g.d == 64 ? kTF8S : kTF8;
-  const long long round = std::max(8, (device_cus() / 8) * 8);
-  const long long r24 = (static_cast<long long>(bound_tiles(t, kTF)) * g.Hkv + round - 1) / round;
-  const long long r16 = (static_cast<long long>(bound_tiles(t, kTF16)) * g.Hkv + round - 1) / round;
+  const int gs = group_tiles();
+  const long long r24 = (bound_groups(t, kTF, gs, g.Hkv) + 7) / 8;
+  const long long r16 = (bound_groups(t, kTF16, gs, g.Hkv) + 7) / 8;
   return r24 * 7 < r16 * 5 ? kTF : kTF16;
 }
 
@@ -908,21 +975,21 @@ hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, con
                             const void* v, const int32_t* idx, void* out, float* lse,
                             hipStream_t stream) {
   const int TF = attn_tile_rows(g, t);
-  const int n_items = bound_tiles(t, TF) * g.Hkv;     // a bound: the kernel counts the tiles
-  if (n_items == 0) return hipSuccess;
-  const int round = kRounds ? (device_cus() / 8) * 8 : (n_items + 7) / 8 * 8;
+  const int gs = group_tiles();
+  const int n_groups = bound_groups(t, TF, gs, g.Hkv);   // a bound: the kernel finds the groups
+  if (n_groups == 0) return hipSuccess;
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   uint16_t* oo = static_cast<uint16_t*>(out);
-  for (int base = 0; base < n_items; base += round) {
-    const int grid = std::min(round, (n_items - base + 7) / 8 * 8);
+  for (int base = 0; base < n_groups; base += 8) {
+    const int grid = 8 * gs;
 #define INFLLM2_TILE_CASE(DD, GG, NS, TFF)                                                    \
   if (g.d == DD && g.G == GG && TF == TFF) {                                                  \
     hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWavesF, TFF / kWavesF, false, false, true>),   \
                        dim3(grid),                                                            \
-                       dim3(64 * kWavesF), 0, stream, g, t, qq, kk, vv, idx, oo, lse, n_items,\
-                       base, nullptr, nullptr, nullptr, nullptr);                             \
+                       dim3(64 * kWavesF), 0, stream, g, t, qq, kk, vv, idx, oo, lse, base,  \
+                       nullptr, nullptr, nullptr, nullptr);                                   \
     const hipError_t e = hipGetLastError();                                                   \
     if (e != hipSuccess) return e;                                                            \
     continue;                                                                                 \
@@ -946,21 +1013,21 @@ hipError_t launch_attn_tile_dq(const Geom& g, const SeqTable& t, const void* q, 
                                const void* v, const int32_t* idx, const void* dout,
                                const float* lse, const float* delta, float* dq,
                                hipStream_t stream) {
-  const int n_items = bound_tiles(t, kT) * g.Hkv;
-  if (n_items == 0) return hipSuccess;
-  const int round = kRounds ? (device_cus() / 8) * 8 : (n_items + 7) / 8 * 8;
+  const int gs = group_tiles();
+  const int n_groups = bound_groups(t, kT, gs, g.Hkv);
+  if (n_groups == 0) return hipSuccess;
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   const uint16_t* dd = static_cast<const uint16_t*>(dout);
-  for (int base = 0; base < n_items; base += round) {
-    const int grid = std::min(round, (n_items - base + 7) / 8 * 8);
+  for (int base = 0; base < n_groups; base += 8) {
+    const int grid = 8 * gs;
 #define INFLLM2_DQ_CASE(DD, GG, NS)                                                           \
   if (g.d == DD && g.G == GG) {                                                               \
     hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWaves, kT / kWaves, true, false, true>),       \
                        dim3(grid),                                                            \
                        dim3(64 * kWaves), 0, stream, g, t, qq, kk, vv, idx, nullptr, nullptr, \
-                       n_items, base, dd, lse, delta, dq);                                    \
+                       base, dd, lse, delta, dq);                                             \
     const hipError_t e = hipGetLastError();                                                   \
     if (e != hipSuccess) return e;                                                            \
     continue;                                                                                 \
@@ -978,20 +1045,20 @@ hipError_t launch_attn_tile_dq(const Geom& g, const SeqTable& t, const void* q, 
 hipError_t launch_attn_tile_window(const Geom& g, const SeqTable& t, const void* q,
                                    const void* k, const void* v, void* out, float* lse,
                                    hipStream_t stream) {
-  const int n_items = bound_tiles(t, kTW) * g.Hkv;
-  if (n_items == 0) return hipSuccess;
-  const int round = kRounds ? (device_cus() / 8) * 8 : (n_items + 7) / 8 * 8;
+  const int gs = group_tiles();
+  const int n_groups = bound_groups(t, kTW, gs, g.Hkv);
+  if (n_groups == 0) return hipSuccess;
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   uint16_t* oo = static_cast<uint16_t*>(out);
-  for (int base = 0; base < n_items; base += round) {
-    const int grid = std::min(round, (n_items - base + 7) / 8 * 8);
+  for (int base = 0; base < n_groups; base += 8) {
+    const int grid = 8 * gs;
 #define INFLLM2_WIN_CASE(DD, GG, NS)                                                          \
   if (g.d == DD && g.G == GG) {                                                               \
     hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWaves, kTW / kWaves, false, true>), dim3(grid), \
                        dim3(64 * kWaves), 0, stream, g, t, qq, kk, vv, nullptr, oo, lse,      \
-                       n_items, base, nullptr, nullptr, nullptr, nullptr);                    \
+                       base, nullptr, nullptr, nullptr, nullptr);                             \
     const hipError_t e = hipGetLastError();                                                   \
     if (e != hipSuccess) return e;                                                            \
     continue;                                                                                 \
