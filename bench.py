@@ -54,6 +54,7 @@ def tile_tokens(p, lens, cus: int = 256) -> int:
     return 24 if r24 * 7 < r16 * 5 else 16
 
 
+ROUNDS_PER_LAUNCH = 3     # the library's tile-schedule rounds per attention launch
 WINDOW = 6144             # sliding-window leg: 96 blocks x 64 tokens
 CHUNK = 16384             # chunked-prefill leg: the last 16K tokens against a 112K cache
 SPIN_CYCLES = 24_000_000  # GPU spin before the timed decode steps (about 10 ms at 2.4 GHz)
@@ -147,13 +148,13 @@ def run_prefill(args, torch, pkg, synth, workload=None, keep=True):
     bytes_scores = T * Hq * d * 2 + C * Hkv * d * 2 + causal_blocks * Hkv * 4
     bytes_topk = causal_blocks * Hkv * 4 + T * Hkv * p.topk * 4
     bytes_compress = T * Hkv * d * 2 + C * Hkv * d * 2
-    # the attention call launches its tiles in rounds of one workgroup per compute unit, 8
-    # groups of CUs / 8 tiles each; the rounds cover the library's host bound on the groups (it
-    # sees only the metadata's bounds: sequences, longest query run, total rows), not the exact
-    # count
+    # the attention call schedules its tiles in rounds of one workgroup per compute unit, 8
+    # groups of CUs / 8 tiles each, ROUNDS_PER_LAUNCH rounds per launch; the rounds cover the
+    # library's host bound on the groups (it sees only the metadata's bounds: sequences,
+    # longest query run, total rows), not the exact count
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     TT = tile_tokens(p, lens, cus)
-    launches = -(-_group_bound(lens, TT, max(1, cus // 8), Hkv) // 8)
+    launches = -(-_group_bound(lens, TT, max(1, cus // 8), Hkv) // (8 * ROUNDS_PER_LAUNCH))
     result = dict(
         workload=workload, tokens=T, seq_lens=lens, p=p, ms_step=ms_step, stage=stage,
         flops=flops, tflops=tflops, keys=keys, launches=launches,

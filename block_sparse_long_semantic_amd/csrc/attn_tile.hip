@@ -62,6 +62,7 @@ constexpr int kTF8 = 32;          // ... at G = 8 (two tokens' heads stacked per
 constexpr int kTF8S = 64;         // ... at G = 8 and head_dim 64 (the smaller accumulators fit)
 constexpr int kWavesF = 8;        // its waves (two per SIMD, TF / 8 tokens each)
 constexpr int kMaxUnion = 2048;   // reachable blocks per tile handled by this kernel
+constexpr int kRoundsPerLaunch = 3;  // rounds of the tile schedule per kernel launch
 constexpr float kLazy = 8.f;      // log2 headroom before the running max is moved
 constexpr int kSpinLimit = 1 << 20;  // bounded waits (about 30 ms): a protocol error never hangs
 constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3 for gfx9-family raw buffers
@@ -312,14 +313,16 @@ attn_tile(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __
   __shared__ int ready[NS];
   __shared__ int done[NS];
 
-  // XCD-aware: workgroup b runs on XCD b % 8, which takes group group_base + b % 8; its
-  // workgroups take the group's consecutive tiles
-  const int gs = static_cast<int>(gridDim.x) / 8;
+  // XCD-aware: workgroup b runs on XCD b % 8; the launch holds kRoundsPerLaunch rounds of 8
+  // groups of gs tiles, round r of it (b / 8gs) giving group group_base + 8r + b % 8 to that XCD,
+  // whose workgroups take the group's consecutive tiles
+  const int gs = static_cast<int>(gridDim.x) / (8 * kRoundsPerLaunch);
   auto groups_of = [&](int s) { return ((t.q_len[s] + T - 1) / T + gs - 1) / gs; };
   int b, kvh, level;
-  if (!locate_group(t, group_base + static_cast<int>(blockIdx.x % 8), g.Hkv, groups_of, b, kvh, level))
+  const int bx = static_cast<int>(blockIdx.x);
+  if (!locate_group(t, group_base + 8 * (bx / (8 * gs)) + bx % 8, g.Hkv, groups_of, b, kvh, level))
     return;
-  const int lt = level * gs + static_cast<int>(blockIdx.x / 8);
+  const int lt = level * gs + (bx / 8) % gs;
   const Seq sq = load_seq(t, b);
   if (lt * T >= sq.q_len) return;
   const int r0 = lt * T;
@@ -940,11 +943,14 @@ int device_cus() {
   return n;
 }
 
-// Tiles are launched in rounds of one workgroup per compute unit, so that the workgroups
+// Tiles are scheduled in rounds of one workgroup per compute unit, so that the workgroups
 // sharing an XCD start together on neighbouring tiles and walk the same KV blocks at the same
 // time (their L2 then serves each block to all of them): a round is 8 groups of gs = CUs / 8
-// consecutive tiles (locate_group).  Without the per-round restart the workgroups of an XCD
-// drift apart and stop sharing staged blocks in its L2.  The forward runs tiles of kTF8 rows at
+// consecutive tiles (locate_group).  A launch holds kRoundsPerLaunch rounds: the next round's
+// workgroups take the compute units the current round's tail frees (measured at 128K: 29.6 ms
+// with one round per launch, 29.2 / 29.0 / 29.2 with 2 / 3 / 4, 30.2 with every round in one
+// launch, whose workgroups drift apart and stop sharing staged blocks in the XCD's L2).  The
+// forward runs tiles of kTF8 rows at
 // G = 8 (a wave's 4 tokens fill two 16-column MFMA groups; kTF8S rows, 8 tokens in four groups,
 // at head_dim 64, whose accumulators are half as large) and of kTF or kTF16 rows at G = 16: a
 // round of 24-token tiles takes ~1.4 times as long as one of 16-token tiles (measured at 128K:
@@ -982,8 +988,8 @@ hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, con
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   uint16_t* oo = static_cast<uint16_t*>(out);
-  for (int base = 0; base < n_groups; base += 8) {
-    const int grid = 8 * gs;
+  for (int base = 0; base < n_groups; base += 8 * kRoundsPerLaunch) {
+    const int grid = 8 * kRoundsPerLaunch * gs;
 #define INFLLM2_TILE_CASE(DD, GG, NS, TFF)                                                    \
   if (g.d == DD && g.G == GG && TF == TFF) {                                                  \
     hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWavesF, TFF / kWavesF, false, false, true>),   \
@@ -1020,8 +1026,8 @@ hipError_t launch_attn_tile_dq(const Geom& g, const SeqTable& t, const void* q, 
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   const uint16_t* dd = static_cast<const uint16_t*>(dout);
-  for (int base = 0; base < n_groups; base += 8) {
-    const int grid = 8 * gs;
+  for (int base = 0; base < n_groups; base += 8 * kRoundsPerLaunch) {
+    const int grid = 8 * kRoundsPerLaunch * gs;
 #define INFLLM2_DQ_CASE(DD, GG, NS)                                                           \
   if (g.d == DD && g.G == GG) {                                                               \
     hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWaves, kT / kWaves, true, false, true>),       \
@@ -1052,8 +1058,8 @@ hipError_t launch_attn_tile_window(const Geom& g, const SeqTable& t, const void*
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   uint16_t* oo = static_cast<uint16_t*>(out);
-  for (int base = 0; base < n_groups; base += 8) {
-    const int grid = 8 * gs;
+  for (int base = 0; base < n_groups; base += 8 * kRoundsPerLaunch) {
+    const int grid = 8 * kRoundsPerLaunch * gs;
 #define INFLLM2_WIN_CASE(DD, GG, NS)                                                          \
   if (g.d == DD && g.G == GG) {                                                               \
     hipLaunchKernelGGL((attn_tile<DD, GG, NS, kWaves, kTW / kWaves, false, true>), dim3(grid), \
