@@ -41,17 +41,13 @@ def _group_bound(lens, rows: int, gs: int, hkv: int) -> int:
     return min(n_seq * per_seq, -(-T // (rows * gs)) + n_seq) * hkv
 
 
-def tile_tokens(p, lens, cus: int = 256) -> int:
+def tile_tokens(p) -> int:
     """Query tokens per prefill attention work item, chosen as the library chooses: when a group
     has 8 query heads (two tokens' heads share the 16 columns of each matrix-core tile), 64 at
-    head_dim 64 and 32 at 128; else 24 (3 per wave) unless, in rounds of one workgroup per
-    compute unit, 24-token rounds (each ~1.4 times as long) would not beat 16-token ones."""
+    head_dim 64 and 32 at 128; else 24 (3 per wave)."""
     if p.num_q_heads // p.num_kv_heads == 8:
         return 64 if p.head_dim == 64 else 32
-    gs = max(1, cus // 8)
-    r24 = -(-_group_bound(lens, 24, gs, p.num_kv_heads) // 8)
-    r16 = -(-_group_bound(lens, 16, gs, p.num_kv_heads) // 8)
-    return 24 if r24 * 7 < r16 * 5 else 16
+    return 24
 
 
 ROUNDS_PER_LAUNCH = 3     # the library's tile-schedule rounds per attention launch
@@ -153,7 +149,7 @@ def run_prefill(args, torch, pkg, synth, workload=None, keep=True):
     # library's host bound on the groups (it sees only the metadata's bounds: sequences,
     # longest query run, total rows), not the exact count
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    TT = tile_tokens(p, lens, cus)
+    TT = tile_tokens(p)
     launches = -(-_group_bound(lens, TT, max(1, cus // 8), Hkv) // (8 * ROUNDS_PER_LAUNCH))
     result = dict(
         workload=workload, tokens=T, seq_lens=lens, p=p, ms_step=ms_step, stage=stage,

@@ -57,7 +57,6 @@ constexpr int kT = 16;            // query tokens per workgroup of the gradient 
 constexpr int kTW = 16;           // ... of the window form
 constexpr int kWaves = 8;         // their waves per workgroup (tokens per wave = kT / kWaves)
 constexpr int kTF = 24;           // query tokens per workgroup of the sparse forward (G = 16)
-constexpr int kTF16 = 16;         // ... when 24-token tiles would leave a round mostly empty
 constexpr int kTF8 = 32;          // ... at G = 8 (two tokens' heads stacked per MFMA group)
 constexpr int kTF8S = 64;         // ... at G = 8 and head_dim 64 (the smaller accumulators fit)
 constexpr int kWavesF = 8;        // its waves (two per SIMD, TF / 8 tokens each)
@@ -950,12 +949,11 @@ int device_cus() {
 // workgroups take the compute units the current round's tail frees (measured at 128K: 29.6 ms
 // with one round per launch, 29.2 / 29.0 / 29.2 with 2 / 3 / 4, 30.2 with every round in one
 // launch, whose workgroups drift apart and stop sharing staged blocks in the XCD's L2).  The
-// forward runs tiles of kTF8 rows at
-// G = 8 (a wave's 4 tokens fill two 16-column MFMA groups; kTF8S rows, 8 tokens in four groups,
-// at head_dim 64, whose accumulators are half as large) and of kTF or kTF16 rows at G = 16: a
-// round of 24-token tiles takes ~1.4 times as long as one of 16-token tiles (measured at 128K:
-// 0.77 against 0.55 ms) for 1.5 times the tokens, so 24 is used unless its last round would be
-// mostly empty (rounds24 * 1.4 >= rounds16: 16K-token chunks, few tiles).
+// forward runs tiles of kTF8 rows at G = 8 (a wave's 4 tokens fill two 16-column MFMA groups;
+// kTF8S rows, 8 tokens in four groups, at head_dim 64, whose accumulators are half as large) and
+// of kTF rows at G = 16 (a round of 24-token tiles takes ~1.4 times as long as one of 16-token
+// tiles for 1.5 times the tokens; with the next round filling a round's tail, 24 also beats 16 on
+// a 16K-token chunk of few rounds: 5.28 against 5.37 ms).
 static int group_tiles() { return std::max(1, device_cus() / 8); }
 
 // Bound on the number of tile groups of a launch (tiles of `rows` rows, gs tiles per group): at
@@ -969,18 +967,15 @@ static int bound_groups(const SeqTable& t, int rows, int gs, int hkv) {
   return static_cast<int>((a < c ? a : c) * hkv);
 }
 
-static int attn_tile_rows(const Geom& g, const SeqTable& t) {
+static int attn_tile_rows(const Geom& g) {
   if (g.G == 8) return g.d == 64 ? kTF8S : kTF8;
-  const int gs = group_tiles();
-  const long long r24 = (bound_groups(t, kTF, gs, g.Hkv) + 7) / 8;
-  const long long r16 = (bound_groups(t, kTF16, gs, g.Hkv) + 7) / 8;
-  return r24 * 7 < r16 * 5 ? kTF : kTF16;
+  return kTF;
 }
 
 hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, const void* k,
                             const void* v, const int32_t* idx, void* out, float* lse,
                             hipStream_t stream) {
-  const int TF = attn_tile_rows(g, t);
+  const int TF = attn_tile_rows(g);
   const int gs = group_tiles();
   const int n_groups = bound_groups(t, TF, gs, g.Hkv);   // a bound: the kernel finds the groups
   if (n_groups == 0) return hipSuccess;
@@ -1001,10 +996,8 @@ hipError_t launch_attn_tile(const Geom& g, const SeqTable& t, const void* q, con
     continue;                                                                                 \
   }
     INFLLM2_TILE_CASE(128, 16, 4, kTF)
-    INFLLM2_TILE_CASE(128, 16, 4, kTF16)
     INFLLM2_TILE_CASE(128, 8, 4, kTF8)
     INFLLM2_TILE_CASE(64, 16, 8, kTF)
-    INFLLM2_TILE_CASE(64, 16, 8, kTF16)
     INFLLM2_TILE_CASE(64, 8, 8, kTF8S)
 #undef INFLLM2_TILE_CASE
     return hipErrorInvalidValue;

@@ -49,21 +49,25 @@ def test_gather_bound_uses_32_token_tiles_at_group_8():
     idx[16:32, 0, 0] = 2                   # second half of tile 0
     idx[32:, 0, 0] = 1                     # the ragged tile
     p = types.SimpleNamespace(block_size=64, head_dim=128, num_q_heads=16, num_kv_heads=2)
-    assert bench.tile_tokens(p, [40]) == 32
-    assert bench.tile_tokens(types.SimpleNamespace(head_dim=64, num_q_heads=16, num_kv_heads=2),
-                             [40]) == 64
+    assert bench.tile_tokens(p) == 32
+    assert bench.tile_tokens(types.SimpleNamespace(head_dim=64, num_q_heads=16, num_kv_heads=2)) == 64
     g = bench.gather_bound(p, idx, [40], 1.0, 1.0, 32)
     assert g["staged_bytes"] == 3 * (2 * 64 * 128 * 2)
 
 
-def test_tile_tokens_follow_the_round_count():
-    # groups of 16: 24-token tiles unless 16-token ones need nearly as few rounds (x 1.4)
-    p = types.SimpleNamespace(num_q_heads=32, num_kv_heads=2)
-    assert bench.tile_tokens(p, [131072], 256) == 24      # 43 rounds against 64
-    assert bench.tile_tokens(p, [32768], 256) == 24       # 11 against 16
-    assert bench.tile_tokens(p, [16384], 256) == 16       # 6 against 8
-    assert bench.tile_tokens(p, [1000, 1000], 256) == 16  # one round either way
-    assert bench.tile_tokens(p, [3000, 2000], 256) == 24  # 2 rounds against 3
+def test_tile_tokens_at_groups_of_16():
+    # groups of 16: 24-token tiles (3 per wave) at every length
+    p = types.SimpleNamespace(num_q_heads=32, num_kv_heads=2, head_dim=128)
+    assert bench.tile_tokens(p) == 24
+    assert bench.tile_tokens(types.SimpleNamespace(num_q_heads=32, num_kv_heads=2, head_dim=64)) == 24
+
+
+def test_launches_cover_the_group_bound():
+    # rounds of 8 groups of 32 tiles, three rounds per launch: 128K at 24 tokens has 171 groups
+    # per KV head (43 rounds, 15 launches); the varlen batch's bound is 72 groups (3 launches)
+    assert bench._group_bound([131072], 24, 32, 2) == 342
+    assert -(-bench._group_bound([131072], 24, 32, 2) // (8 * bench.ROUNDS_PER_LAUNCH)) == 15
+    assert bench._group_bound([8192, 16384, 32768, 8192], 64, 32, 2) == 72
 
 
 def test_more_than_one_gpu_is_refused():
