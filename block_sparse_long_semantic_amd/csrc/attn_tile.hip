@@ -3,8 +3,8 @@
 // softmax).
 //
 // Design (one workgroup = 8 waves = one tile of T consecutive query tokens of one sequence and
-// one KV head: T = 24 in the sparse forward at groups of 16 heads, 32 at groups of 8 (64 at
-// head_dim 64), 16 in the gradient and window forms):
+// one KV head: T = 24 in the sparse forward at groups of 16 heads and in the window form, 32 in
+// the sparse forward at groups of 8 (64 at head_dim 64), 16 in the gradient form):
 //   * Union: the tile's T selected-block lists are OR-ed into a per-block T-bit token mask in
 //     LDS and compacted into a list of (block, mask).  Each union block's K and V (64 keys x d,
 //     bf16) are staged into LDS once for all tokens that chose it.  The forward and gradient
@@ -54,7 +54,8 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kT = 16;            // query tokens per workgroup of the gradient form
-constexpr int kTW = 16;           // ... of the window form
+constexpr int kTW = 24;           // ... of the window form (3 tokens per wave: 13.2 ms at 128K
+                                  // and window 6144, against 13.8 with 16)
 constexpr int kWaves = 8;         // their waves per workgroup (tokens per wave = kT / kWaves)
 constexpr int kTF = 24;           // query tokens per workgroup of the sparse forward (G = 16)
 constexpr int kTF8 = 32;          // ... at G = 8 (two tokens' heads stacked per MFMA group)
