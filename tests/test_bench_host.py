@@ -101,3 +101,16 @@ def test_traffic_summary_scales_by_copy_calibration(tmp_path, capsys):
             if ln.startswith("bench-data: ")]
     fwd = [r for r in recs if r["role"] == "prefill_attention"]
     assert fwd and fwd[0]["fetch_bytes_per_call"] == 1500.0 * 1024 * 2
+
+
+def test_group_bound_covers_every_group():
+    # the launches cover a host bound on the tile groups computed from the metadata's bounds only
+    # (sequences, longest run, total rows); it must never fall below the true count, or tiles
+    # would be skipped
+    rng = np.random.default_rng(7)
+    for _ in range(500):
+        n = int(rng.integers(1, 40))
+        lens = [int(x) for x in rng.integers(1, 5000, n)]
+        rows, gs, hkv = int(rng.choice([16, 24, 32, 64])), int(rng.choice([1, 8, 32])), int(rng.integers(1, 5))
+        actual = sum(-(-(-(-L // rows)) // gs) for L in lens) * hkv
+        assert bench._group_bound(lens, rows, gs, hkv) >= actual
