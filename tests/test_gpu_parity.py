@@ -90,9 +90,9 @@ def test_8b_shape_ragged_all_rows(L):
 
 
 def test_24_token_tiles_ragged_all_rows():
-    """Enough tiles for the forward to choose 24-token tiles (3 tokens per wave; 2 rounds of
-    one workgroup per compute unit against 3 at 16 tokens), in packed sequences whose last tiles
-    hold 17, 22, 17 and 8 tokens: every row."""
+    """24-token tiles (3 tokens per wave) in packed sequences whose last tiles hold 17, 22, 17
+    and 8 tokens, spanning 2, 2, 2 and 3 groups of 32 tiles: the launch schedule's levels 0 and 1
+    hold every sequence, level 2 only the last; every row."""
     p = synth.config_params("prefill32k")
     wl = synth.make_prefill("tiles-24", p, [1001, 1030, 977, 2000], seed=35)
     log("case 24-token tiles, ragged")
