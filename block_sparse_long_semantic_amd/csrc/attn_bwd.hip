@@ -404,7 +404,7 @@ bwd_dkv(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __re
         const float* __restrict__ lse, const float* __restrict__ delta,
         const int* __restrict__ seg_off, const int* __restrict__ item_off,
         const int* __restrict__ list, int n_seg, int n_blocks, float* __restrict__ dk,
-        float* __restrict__ dv) {
+        float* __restrict__ dv, int* __restrict__ work) {
   constexpr int CPR = D / 8;               // 16-byte chunks per row
   constexpr int KS = D / 32;
   constexpr int NT = D / 16;
@@ -439,7 +439,21 @@ bwd_dkv(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __re
                         16u * static_cast<uint32_t>(((c16 & 3) >> 1) ^ (tx & 1)) +
                         8u * static_cast<uint32_t>(c16 & 1);
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  // Work items are taken in order from a shared counter (zero at launch), kGrab at a time: they
+  // still run row window by row window, and a workgroup that finishes early takes more, so the
+  // last workgroups end within a few items of each other (a fixed item-to-workgroup assignment
+  // leaves the slowest of the persistent workgroups well behind the mean)
+  constexpr int kGrab = 4;
+  __shared__ int s_item;
+  for (int item = 0, item_end = 0;; ++item) {
+    if (item == item_end) {
+      __syncthreads();                                   // every thread has read s_item
+      if (tid == 0) s_item = atomicAdd(work, kGrab);
+      __syncthreads();
+      item = uniform(s_item);
+      item_end = item + kGrab;
+    }
+    if (item >= n_items) break;
     // segment of the item: the last s with item_off[s] <= item
     int lo = 0, hi = n_seg;
     while (hi - lo > 1) {
@@ -637,7 +651,7 @@ size_t bwd_workspace(const Geom& g, const SeqTable& t) {
   auto al = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t n_seg = static_cast<size_t>(bwd_segments(g, t));
   const size_t entries = static_cast<size_t>(bound_rows(t)) * g.Hkv * g.topk;
-  return al(static_cast<size_t>(t.q_rows) * g.Hq * 4) + al(n_seg * 4) + 2 * al((n_seg + 1) * 4) +
+  return al(static_cast<size_t>(t.q_rows) * g.Hq * 4) + 3 * al((n_seg + 1) * 4) +
          al(std::max<size_t>(entries, 1) * 4);
 }
 
@@ -653,8 +667,8 @@ hipError_t launch_attn_bwd(const Geom& g, const SeqTable& t, const void* q, cons
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   float* delta = reinterpret_cast<float*>(ws);
   ws += al(static_cast<size_t>(t.q_rows) * g.Hq * 4);
-  int* cnt = reinterpret_cast<int*>(ws);
-  ws += al(static_cast<size_t>(n_seg) * 4);
+  int* cnt = reinterpret_cast<int*>(ws);               // n_seg counts, then the dK/dV work counter
+  ws += al((static_cast<size_t>(n_seg) + 1) * 4);
   int* seg_off = reinterpret_cast<int*>(ws);
   ws += al((static_cast<size_t>(n_seg) + 1) * 4);
   int* item_off = reinterpret_cast<int*>(ws);
@@ -678,8 +692,8 @@ hipError_t launch_attn_bwd(const Geom& g, const SeqTable& t, const void* q, cons
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(zero_ints, dim3(std::min((n_seg + 255) / 256, 1024)), dim3(256), 0, stream,
-                     cnt, n_seg);
+  hipLaunchKernelGGL(zero_ints, dim3(std::min((n_seg + 256) / 256, 1024)), dim3(256), 0, stream,
+                     cnt, n_seg + 1);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (g.d == 128) {
     hipLaunchKernelGGL(bwd_prep<128>, dim3(rows), dim3(256), 0, stream, g, t, oo, dd, idx,
@@ -699,14 +713,16 @@ hipError_t launch_attn_bwd(const Geom& g, const SeqTable& t, const void* q, cons
   if ((e = launch_attn_tile_dq(g, t, q, k, v, idx, dout, lse, delta, dq, stream)) != hipSuccess)
     return e;
 
-  // dK, dV: persistent grid over the work items (their count is known on the device only)
+  // dK, dV: persistent grid over the work items (their count is known on the device only),
+  // taken from the counter after the segment counts
   const long long bound = static_cast<long long>(rows) * g.Hkv * g.topk / kChunk + n_seg;
   const int cus = device_cus();
   const int grid = static_cast<int>(std::max<long long>(1, std::min<long long>(bound, 2LL * cus)));
 #define INFLLM2_DKV_CASE(DD, GG)                                                                \
   if (g.d == DD && g.G == GG) {                                                                 \
     hipLaunchKernelGGL((bwd_dkv<DD, GG>), dim3(grid), dim3(256), 0, stream, g, t, qq, kk, vv, dd, \
-                       lse, delta, seg_off, item_off, list, n_seg, n_blocks, dk, dv);           \
+                       lse, delta, seg_off, item_off, list, n_seg, n_blocks, dk, dv,            \
+                       cnt + n_seg);                                                            \
     return hipGetLastError();                                                                   \
   }
   INFLLM2_DKV_CASE(128, 16)

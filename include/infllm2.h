@@ -179,7 +179,8 @@ infllm2_status infllm2_sliding_window_attn(const infllm2_params* params,
 
 /* Bytes of device workspace infllm2_sparse_attn_backward needs for these sequences (0 if the
  * arguments are invalid or the geometry is unsupported).  It holds delta, the reverse block
- * index and its offsets; its contents need no initialisation and are scratch between calls. */
+ * index, its offsets and a work counter of the key/value gradient pass; its contents need no
+ * initialisation (the call zeroes what must start at zero) and are scratch between calls. */
 size_t infllm2_backward_workspace_size(const infllm2_params* params, const infllm2_seqs* seqs);
 
 /* Gradients of infllm2_sparse_attn_prefill (model card "Efficient Model Architecture" and
