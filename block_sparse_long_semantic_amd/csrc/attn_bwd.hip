@@ -441,9 +441,10 @@ bwd_dkv(Geom g, SeqTable t, const uint16_t* __restrict__ q, const uint16_t* __re
 
   // Work items are taken in order from a shared counter (zero at launch), kGrab at a time: they
   // still run row window by row window, and a workgroup that finishes early takes more, so the
-  // last workgroups end within a few items of each other (a fixed item-to-workgroup assignment
-  // leaves the slowest of the persistent workgroups well behind the mean)
-  constexpr int kGrab = 4;
+  // last workgroups end within an item or two of each other (a fixed item-to-workgroup assignment
+  // leaves the slowest of the persistent workgroups well behind the mean; at 128K the backward
+  // call measured 78.1 / 78.3 / 79.0 / 79.8 ms with 1 / 2 / 4 / 8 items per update)
+  constexpr int kGrab = 1;
   __shared__ int s_item;
   for (int item = 0, item_end = 0;; ++item) {
     if (item == item_end) {
